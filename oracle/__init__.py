@@ -1,0 +1,9 @@
+"""Float64 CPU oracle for exact attention (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path never calls it: it shares no code
+with the HIP library and imports nothing from it.
+"""
+from .attention import attention_forward, attention_rows, scores_row
+
+__all__ = ["attention_forward", "attention_rows", "scores_row"]

@@ -1,0 +1,136 @@
+"""Float64 oracle: exact softmax(Q K^T / sqrt(D)) V plus the row log-sum-exp.
+
+Test infrastructure only (tests, the smoke check and the benchmark's
+CPU-baseline leg); the product path never calls it.
+
+What it computes, per batch b and head h, in float64 on the stored input
+values:
+
+* scale = 1 / sqrt(D)  (every page divides the scores by sqrt of the head
+  dimension: "Build a FlashAttention Kernel from Scratch", Step 3;
+  "Building a FlashAttention-2 Forward Kernel in Pure NumPy", Step 2;
+  "Python Attention Mechanisms Explained", The Core Idea)
+* the key set of query i is A_i = {j : 0 <= j < Nk, and j <= i if causal}.
+  The causal mask keeps the diagonal (the first page's comment on its Step 3
+  mask says lower triangle including the diagonal; the printed call drops
+  it, which would leave row 0 empty).  For Nq != Nk the mask is aligned at
+  the top-left (absolute indices), the plainest reading: the pages only show
+  square causal examples.
+* s_ij = scale * sum_d q[i,d] k[j,d]  for j in A_i
+* m_i = max_j s_ij,  l_i = sum_j exp(s_ij - m_i)
+* LSE_i = m_i + ln(l_i)  (natural log; the "log-sum-exp" the FlashAttention-2
+  page names, i.e. scipy.special.logsumexp of the masked scaled scores)
+* O_i = sum_j exp(s_ij - m_i) v[j,:] / l_i
+
+The pages state that the tiled method reaches exactly this result, so the
+oracle is the definition written out, not the online algorithm.  Rows are
+processed in chunks against all keys at once, the row blocking of the first
+page's Step 6 (with the mask in absolute indices); this is exact, not
+online.  Masked entries become -inf before the max.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = ["attention_forward", "attention_rows", "scores_row"]
+
+
+def _as_f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # a torch CPU tensor of any dtype
+        x = x.detach().to("cpu").double().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _check(q, k, v):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be (B, H, N, D)")
+    B, H, Nq, D = q.shape
+    if k.shape[:2] != (B, H) or k.shape[3] != D or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q{q.shape} k{k.shape} v{v.shape}")
+    if Nq < 1 or k.shape[2] < 1 or D < 1:
+        raise ValueError("empty attention is undefined (every row needs a key)")
+    return B, H, Nq, k.shape[2], D
+
+
+def _rows_block(qi, kh, vh, row_idx, causal, scale):
+    """Exact attention for a block of query rows against all keys of one head.
+
+    qi: (R, D) query rows, row_idx: (R,) their absolute indices.
+    Returns O (R, D) and LSE (R,).
+    """
+    s = (qi @ kh.T) * scale  # (R, Nk)
+    if causal:
+        keys = np.arange(kh.shape[0])
+        s = np.where(keys[None, :] <= row_idx[:, None], s, -np.inf)
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])  # exp(-inf) = 0 for masked keys
+    l = e.sum(axis=1)
+    o = (e @ vh) / l[:, None]
+    lse = m + np.log(l)
+    return o, lse
+
+
+def attention_forward(q, k, v, causal: bool, row_chunk: int = 256):
+    """Exact attention over whole tensors.
+
+    q: (B, H, Nq, D); k, v: (B, H, Nk, D); any real dtype (widened to float64).
+    Returns (O float64 (B, H, Nq, D), LSE float64 (B, H, Nq)).
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, H, Nq, Nk, D = _check(q, k, v)
+    scale = 1.0 / math.sqrt(D)
+    O = np.empty((B, H, Nq, D))
+    L = np.empty((B, H, Nq))
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, Nq, row_chunk):
+                r1 = min(r0 + row_chunk, Nq)
+                o, lse = _rows_block(q[b, h, r0:r1], k[b, h], v[b, h],
+                                     np.arange(r0, r1), causal, scale)
+                O[b, h, r0:r1] = o
+                L[b, h, r0:r1] = lse
+    return O, L
+
+
+def attention_rows(q, k, v, causal: bool, rows):
+    """Exact attention for selected query rows only.
+
+    rows: iterable of (b, h, i).  Inputs may be torch tensors or arrays; only
+    the needed head slices are widened.  Returns (O (R, D), LSE (R,)).
+    """
+    rows = [tuple(int(x) for x in r) for r in rows]
+    D = q.shape[-1]
+    scale = 1.0 / math.sqrt(D)
+    O = np.empty((len(rows), D))
+    L = np.empty(len(rows))
+    by_head = {}
+    for n, (b, h, i) in enumerate(rows):
+        by_head.setdefault((b, h), []).append((n, i))
+    for (b, h), items in by_head.items():
+        kh = _as_f64(k[b, h])
+        vh = _as_f64(v[b, h])
+        idx = np.array([i for _, i in items])
+        if hasattr(q, "detach"):
+            import torch
+
+            qi = _as_f64(q[b, h][torch.as_tensor(idx)])
+        else:
+            qi = _as_f64(q[b, h])[idx]
+        o, lse = _rows_block(qi, kh, vh, idx, causal, scale)
+        for r, (n, _) in enumerate(items):
+            O[n] = o[r]
+            L[n] = lse[r]
+    return O, L
+
+
+def scores_row(q, k, b: int, h: int, i: int, causal: bool):
+    """Scaled, masked float64 scores of one query row (masked keys -> -inf)."""
+    D = q.shape[-1]
+    qi = _as_f64(q[b, h, i])
+    kh = _as_f64(k[b, h])
+    s = (kh @ qi) * (1.0 / math.sqrt(D))
+    if causal:
+        s = np.where(np.arange(kh.shape[0]) <= i, s, -np.inf)
+    return s

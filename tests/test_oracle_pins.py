@@ -1,0 +1,82 @@
+"""The float64 oracle against brute force, closed forms, worked examples,
+scipy, invariants and an independent online-softmax tiled implementation."""
+import numpy as np
+import pytest
+
+import oracle
+import pins
+
+
+def _impl(q, k, v, causal):
+    return oracle.attention_forward(q, k, v, causal)
+
+
+def _impl_chunked(q, k, v, causal):
+    # row chunks smaller than the shapes, so that chunk edges are exercised
+    return oracle.attention_forward(q, k, v, causal, row_chunk=3)
+
+
+@pytest.mark.parametrize("check", pins.ALL_CHECKS, ids=lambda f: f.__name__)
+def test_oracle_pinned(check):
+    check(_impl)
+
+
+@pytest.mark.parametrize("check", [pins.check_brute_force, pins.check_online_tiled,
+                                   pins.check_causal_row0_and_last], ids=lambda f: f.__name__)
+def test_oracle_row_chunking(check):
+    check(_impl_chunked)
+
+
+def test_attention_rows_matches_forward():
+    r = np.random.default_rng(3)
+    q = r.standard_normal((2, 3, 37, 16))
+    k = r.standard_normal((2, 3, 53, 16))
+    v = r.standard_normal((2, 3, 53, 16))
+    for causal in (False, True):
+        O, L = oracle.attention_forward(q, k, v, causal)
+        rows = [(1, 2, 0), (0, 0, 36), (1, 1, 17), (0, 2, 5), (1, 2, 36)]
+        Or, Lr = oracle.attention_rows(q, k, v, causal, rows)
+        for n, (b, h, i) in enumerate(rows):
+            assert np.max(np.abs(Or[n] - O[b, h, i])) <= 1e-13
+            assert abs(Lr[n] - L[b, h, i]) <= 1e-13
+
+
+def test_attention_rows_torch_inputs():
+    torch = pytest.importorskip("torch")
+    r = np.random.default_rng(4)
+    q = r.standard_normal((1, 2, 20, 8)).astype(np.float32)
+    k = r.standard_normal((1, 2, 30, 8)).astype(np.float32)
+    v = r.standard_normal((1, 2, 30, 8)).astype(np.float32)
+    O, L = oracle.attention_forward(q, k, v, True)
+    Or, Lr = oracle.attention_rows(torch.from_numpy(q).to(torch.bfloat16).float(),
+                                   torch.from_numpy(k), torch.from_numpy(v), True, [(0, 1, 19)])
+    assert Or.shape == (1, 8) and np.isfinite(Lr).all()
+    Or, Lr = oracle.attention_rows(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                                   True, [(0, 1, 19), (0, 0, 3)])
+    assert np.max(np.abs(Or[0] - O[0, 1, 19])) <= 1e-13
+    assert abs(Lr[1] - L[0, 0, 3]) <= 1e-13
+
+
+def test_empty_is_rejected():
+    with pytest.raises(ValueError):
+        oracle.attention_forward(np.zeros((1, 1, 0, 4)), np.zeros((1, 1, 3, 4)), np.zeros((1, 1, 3, 4)), False)
+    with pytest.raises(ValueError):
+        oracle.attention_forward(np.zeros((1, 1, 2, 4)), np.zeros((1, 1, 0, 4)), np.zeros((1, 1, 0, 4)), False)
+
+
+def test_online_reference_matches_page_grid_dtype_free():
+    # The online recurrence is tile-size invariant: two very different tilings
+    # agree to rounding (a pin of the reference itself, independent of the oracle).
+    from online_reference import online_tiled_attention
+
+    r = np.random.default_rng(11)
+    q = r.standard_normal((1, 2, 90, 32))
+    k = r.standard_normal((1, 2, 70, 32))
+    v = r.standard_normal((1, 2, 70, 32))
+    for causal in (False, True):
+        a = online_tiled_attention(q, k, v, causal, 1, 1)
+        b = online_tiled_attention(q, k, v, causal, 90, 70)
+        c = online_tiled_attention(q, k, v, causal, 7, 13, skip_masked_tiles=False)
+        for x, y in ((a, b), (a, c)):
+            assert np.max(np.abs(x[0] - y[0])) <= 1e-12
+            assert np.max(np.abs(x[1] - y[1])) <= 1e-12

@@ -1,0 +1,149 @@
+"""Seeded synthetic workloads for exact tiled attention.
+
+This module holds no attention arithmetic.  It only knows the workload
+shapes and how their inputs are drawn, so that the float64 oracle and the
+HIP path can consume the very same input values.
+
+Recipe (the pages fix only "Q, K, V drawn i.i.d. N(0,1) from a seed"):
+
+* ``numpy.random.default_rng(seed)`` draws Q, then K, then V as float64
+  ``standard_normal`` arrays of the full shape (the generator style of
+  "Building a FlashAttention-2 Forward Kernel in Pure NumPy", Step 5).
+* Q is multiplied by ``q_scale`` (4 for the peaky long-context workload;
+  a power of two, so it commutes with rounding).
+* The values are rounded to the storage dtype with round-to-nearest-even:
+  float64 -> float32 for fp32; float64 -> float32 -> bfloat16 for bf16;
+  float64 -> float16 for fp16.
+
+Both sides receive the rounded values: the HIP path as device tensors of
+the storage dtype, the oracle as the same values widened to float64.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Tuple
+
+import numpy as np
+
+__all__ = [
+    "Workload",
+    "WORKLOADS",
+    "HEADLINE",
+    "draw_float64",
+    "round_to_dtype",
+    "make_inputs",
+    "make_p1_legacy_inputs",
+    "conv_flops",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    D: int
+    dtype: str  # "fp32" | "fp16" | "bf16"
+    causal: bool
+    seed: int
+    q_scale: float = 1.0
+    note: str = ""
+
+    @property
+    def q_shape(self) -> Tuple[int, int, int, int]:
+        return (self.B, self.H, self.Nq, self.D)
+
+    @property
+    def kv_shape(self) -> Tuple[int, int, int, int]:
+        return (self.B, self.H, self.Nk, self.D)
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+def _w(*a, **kw) -> Workload:
+    w = Workload(*a, **kw)
+    return w
+
+
+# The five measured workloads, then parity-only tail variants.
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        _w("c1_fp32_causal_b2h4n128d64", 2, 4, 128, 128, 64, "fp32", True, 0,
+           note="small causal case the oracle finishes in well under a second"),
+        _w("c2_fp32_b1h8n1024d64", 1, 8, 1024, 1024, 64, "fp32", False, 1,
+           note="non-causal; many K/V tiles exercise the online rescale"),
+        _w("c3_bf16_causal_b4h16n4096d128", 4, 16, 4096, 4096, 128, "bf16", True, 2,
+           note="headline: bf16 causal N=4096 D=128, fp32 accumulation"),
+        _w("c4_bf16_causal_b1h32n16384d128_q4", 1, 32, 16384, 16384, 128, "bf16", True, 3,
+           q_scale=4.0, note="long context; Q x4 gives peaky softmax rows"),
+        _w("c5_fp16_cross_b8h32q512k8192d64", 8, 32, 512, 8192, 64, "fp16", False, 4,
+           note="non-causal cross-attention, Nq != Nk"),
+        # ragged tails (parity only)
+        _w("c5t_fp16_cross_b8h32q511k8191d64", 8, 32, 511, 8191, 64, "fp16", False, 4,
+           note="C5 with ragged Nq and Nk tails"),
+        _w("c1t_fp32_causal_b1h2q77k131d64", 1, 2, 77, 131, 64, "fp32", True, 5,
+           note="ragged, Nq != Nk, causal top-left"),
+        _w("c1t_fp32_b1h2q77k131d64", 1, 2, 77, 131, 64, "fp32", False, 5,
+           note="ragged, Nq != Nk, non-causal"),
+        _w("c3t_bf16_causal_b1h3n1000d128", 1, 3, 1000, 1000, 128, "bf16", True, 6,
+           note="bf16 D=128 causal with a ragged tail"),
+    ]
+}
+
+HEADLINE = "c3_bf16_causal_b4h16n4096d128"
+
+
+def draw_float64(w: Workload, seed: int | None = None):
+    """Draw Q, K, V as float64 N(0,1) (Q times ``q_scale``), before rounding."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    q = rng.standard_normal(w.q_shape)
+    k = rng.standard_normal(w.kv_shape)
+    v = rng.standard_normal(w.kv_shape)
+    if w.q_scale != 1.0:
+        q *= w.q_scale
+    return q, k, v
+
+
+def round_to_dtype(x: np.ndarray, dtype: str):
+    """Round a float64 array RNE to ``dtype``; returns a torch CPU tensor."""
+    import torch
+
+    if dtype == "fp32":
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if dtype == "fp16":
+        return torch.from_numpy(np.ascontiguousarray(x.astype(np.float16)))
+    if dtype == "bf16":
+        # torch's float32 -> bfloat16 conversion rounds to nearest even.
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def make_inputs(w: Workload, seed: int | None = None):
+    """Return (q, k, v) as contiguous torch CPU tensors of the storage dtype."""
+    q, k, v = draw_float64(w, seed)
+    return tuple(round_to_dtype(x, w.dtype) for x in (q, k, v))
+
+
+def make_p1_legacy_inputs():
+    """The worked example of "Build a FlashAttention Kernel from Scratch with
+    Python and NumPy" (Step 2): legacy ``np.random.seed(0)`` and ``randn`` in
+    Q, K, V order, shape (2, 4, 128, 64), float32."""
+    import torch
+
+    state = np.random.get_state()
+    try:
+        np.random.seed(0)
+        arrs = [np.random.randn(2, 4, 128, 64).astype(np.float32) for _ in range(3)]
+    finally:
+        np.random.set_state(state)
+    return tuple(torch.from_numpy(a) for a in arrs)
+
+
+def conv_flops(B: int, H: int, Nq: int, Nk: int, D: int, causal: bool) -> float:
+    """FLOP convention of the metric: 4*B*H*Nq*Nk*D, halved when causal."""
+    f = 4.0 * B * H * Nq * Nk * D
+    return f / 2.0 if causal else f
