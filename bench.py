@@ -1,0 +1,200 @@
+"""Benchmark of the exact tiled attention forward on one MI355X.
+
+A step is one fa_fwd call over the whole batch of the workload (all of the
+hot path: Q-tile load, K/V streaming, both MFMA contractions, online softmax,
+causal skipping, epilogue), inputs already resident in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--all]
+
+Prints one JSON line (rank 0).  Throughput is the metric's convention:
+FLOPs = 4*B*H*Nq*Nk*D, halved when causal, per second, in TFLOP/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "attention fwd TFLOP/s and % of dense MFMA peak, bf16 causal N=4096 D=128"
+# Published MI355X dense peaks (TFLOP/s) by compute dtype.
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default=workloads.HEADLINE)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle sample")
+    p.add_argument("--all", action="store_true", help="one line per measured workload (c1..c5)")
+    return p.parse_args()
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def cpu_baseline(w: workloads.Workload, target_s: float):
+    """The float64 oracle, as it stands, on whole (b, h) heads of the same
+    workload, head after head until about ``target_s`` seconds have passed."""
+    import numpy as np
+
+    import oracle
+
+    q, k, v = workloads.make_inputs(w)
+    heads = 0
+    t_total = 0.0
+    BH = w.B * w.H
+    while heads < BH and t_total < target_s:
+        b, h = divmod(heads, w.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        qh, kh, vh = (x[sl].double().numpy() for x in (q, k, v))
+        t0 = time.perf_counter()
+        oracle.attention_forward(qh, kh, vh, w.causal)
+        t_total += time.perf_counter() - t0
+        heads += 1
+    flops = workloads.conv_flops(1, heads, w.Nq, w.Nk, w.D, w.causal)
+    return {
+        "value": round(flops / t_total / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": f"{heads} of {BH} (b,h) heads of {w.name}, full rows, float64, {t_total:.1f} s",
+    }
+
+
+def bench_one(w: workloads.Workload, steps: int, warmup: int):
+    import torch
+
+    import exact_tiled_attention_15_amd as fa
+
+    fa.load_library()
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in workloads.make_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    code = fa._dtype_code(q)
+
+    def step():
+        rc = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       w.B, w.H, w.Nq, w.Nk, w.D, int(w.causal), code, sptr)
+        if rc != 0:
+            raise fa.FaError(rc)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # Whole timed region: K back-to-back launches between two events on the
+    # launch stream.
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_region = e0.elapsed_time(e1) / steps
+    # Per-launch events (same stream) for the median launch duration.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in evs]
+    flops = workloads.conv_flops(w.B, w.H, w.Nq, w.Nk, w.D, w.causal)
+    tflops = flops / (ms_region * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    return {
+        "ms_per_step": ms_region,
+        "wall_s": wall,
+        "median_launch_ms": statistics.median(per),
+        "min_launch_ms": min(per),
+        "tflops": tflops,
+        "peak": peak,
+        "flops": flops,
+    }
+
+
+def line_for(w, r, steps, warmup, cpu):
+    props = {}
+    try:
+        import torch
+
+        p = torch.cuda.get_device_properties(0)
+        props = {"gpu": p.name, "cus": p.multi_processor_count,
+                 "gcn_arch": getattr(p, "gcnArchName", "")}
+    except Exception:
+        pass
+    return {
+        "metric": METRIC,
+        "value": round(r["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "D": w.D,
+                   "causal": w.causal, "seed": w.seed, "q_scale": w.q_scale,
+                   "flops_per_step": r["flops"], "parallelism": "single GPU",
+                   "median_launch_ms": round(r["median_launch_ms"], 5),
+                   "min_launch_ms": round(r["min_launch_ms"], 5), **props},
+        "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 3), "peak": r["peak"],
+                     "unit": "TFLOP/s", "frac": round(r["tflops"] / r["peak"], 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {a.gpus}); the attention forward "
+              "shards over (batch, head) with no communication, so there is no multi-GPU "
+              "step to time here.", file=sys.stderr)
+        sys.exit(2)
+    names = ([n for n in workloads.WORKLOADS if n[:2] in ("c1", "c2", "c3", "c4", "c5") and "t_" not in n[:4]]
+             if a.all else [a.workload])
+    for n in names:
+        w = workloads.WORKLOADS[n]
+        r = bench_one(w, a.steps, a.warmup)
+        cpu = None
+        if not a.no_cpu_baseline and n == names[0]:
+            cpu = cpu_baseline(w, a.cpu_seconds)
+        print(json.dumps(line_for(w, r, a.steps, a.warmup, cpu)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

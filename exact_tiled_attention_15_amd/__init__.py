@@ -1,0 +1,117 @@
+"""Exact tiled attention forward on AMD MI355X (gfx950): Python binding.
+
+A thin ctypes layer over the C ABI in ``include/fa.h`` (``libfa.so``, built
+in-tree by ``exact_tiled_attention_15_amd.build``).  It only marshals
+arguments: every step of the attention runs in the HIP kernels.  PyTorch is
+used for device memory and the current stream.
+
+There is no fallback: if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["fa_fwd", "fa_status_str", "forward", "load_library", "LIB_PATH",
+           "FA_DTYPE_FP32", "FA_DTYPE_FP16", "FA_DTYPE_BF16", "FA_OK", "FaError",
+           "EXPORTED_SYMBOLS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_DTYPE_FP32, FA_DTYPE_FP16, FA_DTYPE_BF16 = 0, 1, 2
+FA_OK = 0
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_status_str")
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(fa_status_str(status))
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libfa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"{p} is missing: build it with `python -m exact_tiled_attention_15_amd.build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(p)
+    lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int64] * 5 + \
+        [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_status_str.argtypes = [ctypes.c_int]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def fa_status_str(status: int) -> str:
+    return load_library().fa_status_str(int(status)).decode()
+
+
+def fa_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int, Nk: int, D: int,
+           causal: int, dtype: int, stream: int | None) -> int:
+    """Call the C ``fa_fwd`` with raw device addresses; returns the status code."""
+    return load_library().fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, D, int(causal), int(dtype), stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    codes = {torch.float32: FA_DTYPE_FP32, torch.float16: FA_DTYPE_FP16,
+             torch.bfloat16: FA_DTYPE_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def forward(q, k, v, causal: bool = False, out=None, lse=None, stream=None):
+    """Exact attention forward on the GPU.
+
+    q: (B, H, Nq, D), k/v: (B, H, Nk, D), contiguous device tensors of one
+    dtype (float32, float16 or bfloat16), D in {64, 128}.  Returns
+    (O (B, H, Nq, D) in the input dtype, LSE (B, H, Nq) float32).  ``out`` and
+    ``lse`` may be given preallocated; ``stream`` defaults to torch's current
+    stream.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be (B, H, N, D)")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, D) or tuple(v.shape) != (B, H, Nk, D):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if q.device != k.device or q.device != v.device:
+        raise ValueError("q, k, v must be on one device")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (B, H, Nq) tensor")
+    if stream is None:
+        with torch.cuda.device(q.device):
+            stream = torch.cuda.current_stream().cuda_stream
+    with torch.cuda.device(q.device):
+        rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    B, H, Nq, Nk, D, bool(causal), _dtype_code(q), stream)
+    if rc != FA_OK:
+        raise FaError(rc)
+    return out, lse

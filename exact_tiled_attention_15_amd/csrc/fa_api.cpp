@@ -1,0 +1,92 @@
+// C ABI of the exact tiled attention forward pass: argument validation
+// (before any HIP call) and dispatch to the gfx950 kernels.
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+// Half-open byte ranges [a, a+na) and [b, b+nb) intersect.
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  if (na <= 0 || nb <= 0) return false;
+  return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+int validate(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int dtype, bool* empty) {
+  if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || D < 0) return FA_ERR_SHAPE;
+  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  int64_t BH, rows, qel, kel;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, Nq, &rows) || !mul_ok(rows, D, &qel)) return FA_ERR_SHAPE;
+  *empty = (rows == 0);
+  if (*empty) return FA_OK;
+  if (Nk < 1) return FA_ERR_SHAPE;  // a query row with no key has no softmax
+  if (!mul_ok(BH, Nk, &kel) || !mul_ok(kel, D, &kel)) return FA_ERR_SHAPE;
+  // Kernel index arithmetic: per-head row counts and the grid are 32-bit;
+  // element offsets are 64-bit.
+  const int64_t nqt = (Nq + 127) / 128;
+  if (Nq > INT32_MAX / 2 || Nk > INT32_MAX / 2 || BH > INT32_MAX) return FA_ERR_SHAPE;
+  int64_t grid;
+  if (!mul_ok(BH, nqt, &grid) || grid > INT32_MAX) return FA_ERR_SHAPE;
+  const int64_t esz = (dtype == FA_DTYPE_FP32) ? 4 : 2;
+  int64_t qbytes, kbytes, lbytes;
+  if (!mul_ok(qel, esz, &qbytes) || !mul_ok(kel, esz, &kbytes) || !mul_ok(rows, 4, &lbytes))
+    return FA_ERR_SHAPE;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGN;
+  if ((uintptr_t)lse & 3u) return FA_ERR_ALIGN;
+  if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k, kbytes) ||
+      overlaps(o, qbytes, v, kbytes) || overlaps(lse, lbytes, q, qbytes) ||
+      overlaps(lse, lbytes, k, kbytes) || overlaps(lse, lbytes, v, kbytes) ||
+      overlaps(o, qbytes, lse, lbytes))
+    return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                      int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal, int dtype,
+                      void* stream) {
+  bool empty = false;
+  const int st = validate(q, k, v, o, lse, B, H, Nq, Nk, D, dtype, &empty);
+  if (st != FA_OK || empty) return st;
+  FaLaunch a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.BH = B * H;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.D = (int)D;
+  a.causal = causal != 0;
+  a.dtype = dtype;
+  a.stream = stream;
+  return fa_launch_fwd(a) == 0 ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" const char* fa_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative, empty-key or too large shape";
+    case FA_ERR_HEAD_DIM: return "FA_ERR_HEAD_DIM: head dimension must be 64 or 128";
+    case FA_ERR_DTYPE: return "FA_ERR_DTYPE: unknown dtype code";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: q/k/v/o must be 16-byte aligned and lse 4-byte aligned";
+    case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or the other output";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch error";
+    default: return "unknown fa_status code";
+  }
+}

@@ -1,0 +1,89 @@
+/*
+ * fa.h -- C ABI of the exact tiled attention forward pass for AMD MI355X
+ * (gfx950 / CDNA4).
+ *
+ * The operation (per batch b and head h), as defined on the pages
+ * "Build a FlashAttention Kernel from Scratch with Python and NumPy"
+ * (Steps 3-5), "Building a FlashAttention-2 Forward Kernel in Pure NumPy"
+ * (Architecture Overview, Steps 2-4) and "Python Attention Mechanisms
+ * Explained" (The Core Idea; Causal Masking):
+ *
+ *     s_ij   = (q_i . k_j) / sqrt(D)          for kept keys j
+ *     O_i    = sum_j exp(s_ij) v_j / sum_j exp(s_ij)
+ *     LSE_i  = ln sum_j exp(s_ij)
+ *
+ * computed tile by tile with an online softmax (running row max and running
+ * exp-sum, rescaled as new key tiles arrive) so that the Nq x Nk score
+ * matrix never exists in memory.  Keys kept: all j < Nk, or, with
+ * causal != 0, j <= i (diagonal kept, indices aligned at the top-left when
+ * Nq != Nk).  Accumulation is fp32 for every dtype; O is rounded to the
+ * input dtype with round-to-nearest-even; LSE is fp32 (natural log).
+ *
+ * Ownership: the caller allocates and owns every buffer.  The library keeps
+ * no pointer after a call returns, allocates nothing, copies nothing and
+ * does not synchronise; work is enqueued on `stream` and completes
+ * asynchronously.  Calls are re-entrant and thread-safe (no global mutable
+ * state).  Every element of o and lse is written.
+ *
+ * Errors: arguments are validated before any HIP call; a non-zero status
+ * means nothing was enqueued.  FA_ERR_HIP reports a launch error.  Faults
+ * during execution surface at the caller's next synchronisation on
+ * `stream`.  NaN or Inf inputs are not checked and propagate to the rows
+ * they touch.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_DTYPE_FP32 = 0, /* IEEE binary32 */
+  FA_DTYPE_FP16 = 1, /* IEEE binary16 */
+  FA_DTYPE_BF16 = 2  /* bfloat16 */
+} fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,     /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,    /* negative size, Nk < 1 with rows to compute, or too large */
+  FA_ERR_HEAD_DIM = 3, /* D not in {64, 128} */
+  FA_ERR_DTYPE = 4,    /* unknown dtype code */
+  FA_ERR_ALIGN = 5,    /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
+  FA_ERR_ALIAS = 6,    /* o or lse overlaps an input, or o overlaps lse */
+  FA_ERR_HIP = 7       /* the HIP runtime reported an error at launch */
+} fa_status;
+
+/*
+ * fa_fwd -- exact attention forward.
+ *
+ *   q    device pointer, [B, H, Nq, D] contiguous row-major, `dtype`
+ *   k    device pointer, [B, H, Nk, D] contiguous row-major, `dtype`
+ *   v    device pointer, [B, H, Nk, D] contiguous row-major, `dtype`
+ *   o    device pointer, [B, H, Nq, D] contiguous row-major, `dtype` (output)
+ *   lse  device pointer, [B, H, Nq] contiguous fp32 (output, natural log)
+ *   B, H, Nq, Nk, D   sizes; D in {64, 128}.  B*H*Nq == 0 is a valid no-op
+ *        (pointers may then be NULL); otherwise Nk >= 1.
+ *   causal  0: every key is kept; non-zero: key j kept for query i iff j <= i
+ *   dtype   an fa_dtype code
+ *   stream  a hipStream_t, or NULL for the null stream
+ *
+ * All pointers refer to memory of the current HIP device.  Scale is fixed at
+ * 1/sqrt(D) (every page divides by the square root of the head dimension).
+ * Returns an fa_status code.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+           int causal, int dtype, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fa_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

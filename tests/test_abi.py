@@ -1,0 +1,83 @@
+"""The C ABI on the CPU: the library loads, exports every symbol that
+include/fa.h declares, and rejects bad arguments before any HIP call (these
+calls return before touching a device, so they run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_tiled_attention_15_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+# Fake, well-aligned, non-overlapping "device" addresses: validation only
+# compares them, it never dereferences them.
+Q, K, V, O, L = (1 << 40), (2 << 40), (3 << 40), (4 << 40), (5 << 40)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_exports():
+    assert declared_functions() == sorted(fa.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True, text=True)
+    if out.returncode == 0:
+        syms = {line.split()[-1] for line in out.stdout.splitlines() if line.strip()}
+        for name in declared_functions():
+            assert name in syms, f"{name} not exported"
+
+
+def test_status_strings():
+    for code, tag in [(0, "FA_OK"), (1, "FA_ERR_NULL"), (2, "FA_ERR_SHAPE"), (3, "FA_ERR_HEAD_DIM"),
+                      (4, "FA_ERR_DTYPE"), (5, "FA_ERR_ALIGN"), (6, "FA_ERR_ALIAS"), (7, "FA_ERR_HIP")]:
+        assert fa.fa_status_str(code).startswith(tag)
+    assert "unknown" in fa.fa_status_str(99)
+
+
+def call(q=Q, k=K, v=V, o=O, lse=L, B=2, H=4, Nq=128, Nk=128, D=64, causal=1, dtype=2):
+    return fa.fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, D, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(o=0), 1), (dict(lse=0), 1),
+    (dict(B=-1), 2), (dict(H=-3), 2), (dict(Nq=-1), 2), (dict(Nk=0), 2), (dict(Nk=-5), 2),
+    (dict(D=32), 3), (dict(D=0), 3), (dict(D=256), 3), (dict(D=-64), 2),
+    (dict(dtype=3), 4), (dict(dtype=-1), 4),
+    (dict(q=Q + 8), 5), (dict(k=K + 4), 5), (dict(v=V + 2), 5), (dict(o=O + 1), 5), (dict(lse=L + 2), 5),
+    (dict(o=Q), 6), (dict(o=K + 64), 6), (dict(lse=V + 1024), 6), (dict(lse=O + 16), 6),
+    (dict(B=1 << 40, H=1 << 40), 2), (dict(Nq=1 << 40), 2), (dict(Nk=1 << 40), 2),
+    (dict(B=1 << 20, H=1 << 12, Nq=1 << 12), 2),
+])
+def test_validation_codes(kw, code):
+    assert call(**kw) == code
+
+
+def test_empty_is_noop():
+    # B*H*Nq == 0 enqueues nothing; pointers may be NULL and Nk may be 0.
+    assert call(B=0, q=0, k=0, v=0, o=0, lse=0) == 0
+    assert call(H=0, Nk=0) == 0
+    assert call(Nq=0, q=0, o=0, lse=0) == 0
+
+
+def test_python_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q)
+
+
+def test_no_cpu_fallback_when_library_missing(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        fa.load_library(str(tmp_path / "libfa.so"))

@@ -1,0 +1,111 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on
+identical seeded inputs, element by element at oracle-friendly sizes and on
+sampled rows at the full workload sizes."""
+import numpy as np
+import pytest
+
+import workloads
+from parity_util import TOL, compare_full, compare_sampled, log, run_gpu, sample_rows, to_gpu
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+W = workloads.WORKLOADS
+
+
+def _case(w, seed=None):
+    log(f"case {w.name} B={w.B} H={w.H} Nq={w.Nq} Nk={w.Nk} D={w.D} {w.dtype} causal={w.causal}")
+    cpu = workloads.make_inputs(w, seed)
+    return cpu, to_gpu(cpu)
+
+
+@pytest.mark.parametrize("name", ["c1_fp32_causal_b2h4n128d64", "c2_fp32_b1h8n1024d64",
+                                  "c1t_fp32_causal_b1h2q77k131d64", "c1t_fp32_b1h2q77k131d64",
+                                  "c3t_bf16_causal_b1h3n1000d128"])
+def test_parity_full(name):
+    w = W[name]
+    cpu, gpu = _case(w)
+    o, l = run_gpu(*gpu, w.causal)
+    compare_full(w, cpu, o, l, "full")
+
+
+def test_parity_p1_worked_example_inputs():
+    # the first page's own Step 2 inputs (legacy seed 0, randn), causal, fp32
+    w = W["c1_fp32_causal_b2h4n128d64"]
+    cpu = workloads.make_p1_legacy_inputs()
+    o, l = run_gpu(*to_gpu(cpu), True)
+    compare_full(w, cpu, o, l, "p1-inputs")
+
+
+SMALL = [(dt, D, causal, Nq, Nk)
+         for dt in ("bf16", "fp16", "fp32")
+         for D in (64, 128)
+         for causal in (False, True)
+         for (Nq, Nk) in ((300, 300), (257, 517), (130, 70))]
+
+
+@pytest.mark.parametrize("dt,D,causal,Nq,Nk", SMALL)
+def test_parity_small_grid(dt, D, causal, Nq, Nk):
+    w = workloads.Workload(f"grid_{dt}_d{D}_{'c' if causal else 'n'}_{Nq}x{Nk}", 2, 3, Nq, Nk, D, dt,
+                           causal, 77 + Nq + D)
+    cpu, gpu = _case(w)
+    o, l = run_gpu(*gpu, w.causal)
+    compare_full(w, cpu, o, l, "grid")
+
+
+@pytest.mark.parametrize("name", ["c3_bf16_causal_b4h16n4096d128",
+                                  "c4_bf16_causal_b1h32n16384d128_q4",
+                                  "c5_fp16_cross_b8h32q512k8192d64",
+                                  "c5t_fp16_cross_b8h32q511k8191d64"])
+def test_parity_full_size_sampled(name):
+    w = W[name]
+    cpu, gpu = _case(w)
+    o, l = run_gpu(*gpu, w.causal)
+    compare_sampled(w, cpu, o, l, sample_rows(w), "sampled")
+    # a property that holds at any size: O is a convex combination of V rows
+    vmax = gpu[2].float().abs().amax(dim=(2, 3))
+    assert bool((o.float().abs().amax(dim=(2, 3)) <= vmax + TOL[w.dtype][0]).all())
+
+
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("fp16", 64), ("fp32", 64)])
+def test_edge_shapes(dt, D):
+    for (Nq, Nk, causal) in ((1, 1, False), (1, 1, True), (1, 4099, False), (3, 1, True),
+                             (200, 5, True), (5, 200, True), (129, 129, True), (64, 64, False)):
+        w = workloads.Workload(f"edge_{dt}_{Nq}x{Nk}", 1, 2, Nq, Nk, D, dt, causal, Nq * 7 + Nk)
+        cpu, gpu = _case(w)
+        o, l = run_gpu(*gpu, causal)
+        compare_full(w, cpu, o, l, "edge")
+
+
+def test_empty_batch_is_noop():
+    import exact_tiled_attention_15_amd as fa
+
+    q = torch.empty(0, 2, 16, 64, device="cuda:0", dtype=torch.bfloat16)
+    o, l = fa.forward(q, q, q, True)
+    assert o.shape == (0, 2, 16, 64) and l.shape == (0, 2, 16)
+
+
+@pytest.mark.parametrize("name", ["c3t_bf16_causal_b1h3n1000d128", "c2_fp32_b1h8n1024d64"])
+def test_deterministic(name):
+    w = W[name]
+    _, gpu = _case(w)
+    o1, l1 = run_gpu(*gpu, w.causal)
+    o2, l2 = run_gpu(*gpu, w.causal)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "run-to-run results differ"
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32"])
+def test_gpu_invariants(dt):
+    w = workloads.Workload("inv", 1, 2, 300, 300, 128 if dt != "fp32" else 64, dt, True, 9)
+    cpu, gpu = _case(w)
+    q, k, v = gpu
+    # causal row 0 sees only key 0: O = V[0] exactly (weight 1), LSE = s00
+    o, l = run_gpu(q, k, v, True)
+    assert torch.equal(o[:, :, 0], v[:, :, 0])
+    s00 = (q[:, :, 0].double() * k[:, :, 0].double()).sum(-1) / np.sqrt(w.D)
+    assert float((l[:, :, 0].double() - s00).abs().max()) <= TOL[dt][1]
+    # constant V -> constant O
+    c = torch.linspace(-2, 3, w.D, device=q.device).to(q.dtype)
+    vc = c.expand_as(v).contiguous()
+    o, _ = run_gpu(q, k, vc, False)
+    assert float((o.float() - c.float()).abs().max()) <= TOL[dt][0]
