@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--all", action="store_true", help="one line per measured workload (c1..c5)")
+    p.add_argument("--copy-calib-mib", type=int, default=0,
+                   help="after timing, run 3 plain device copies of this many MiB (a reference "
+                        "kernel of known traffic for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     return p.parse_args()
 
 
@@ -194,6 +197,16 @@ def main():
         if not a.no_cpu_baseline and n == names[0]:
             cpu = cpu_baseline(w, a.cpu_seconds)
         print(json.dumps(line_for(w, r, a.steps, a.warmup, cpu)), flush=True)
+    if a.copy_calib_mib > 0:
+        import torch
+
+        n = a.copy_calib_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copy calibration: 3 x {a.copy_calib_mib} MiB device copies", file=sys.stderr)
 
 
 if __name__ == "__main__":

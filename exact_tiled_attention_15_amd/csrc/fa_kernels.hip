@@ -105,6 +105,156 @@ __device__ __forceinline__ void tile_of_block(int nqt, int BH, int& bh, int& qt)
 // ---------------------------------------------------------------------------
 // 16-bit kernel (bf16 / fp16), D in {64, 128}, 64-key tiles.
 // ---------------------------------------------------------------------------
+// Buffer resources: 32-bit byte offsets from a per-head base, with the
+// hardware range check (loads past num_records return 0, stores past it are
+// dropped), which handles the ragged Nq / Nk tails.
+constexpr int kBufFlags = 0x00020000;  // gfx9 buffer descriptor word 3 (32-bit data format)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufFlags);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((vector_size(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS tile layout for a BC x D tile of 16-bit values (K or V), in bytes:
+// rows are taken in groups of 8; inside a group, 16-byte chunk c of the 8
+// rows sits in one 128-byte line, at row slot (R & 7) XOR 4*(c & 1):
+//   off(R, c) = (R / 8) * 16 D + 128 c + 16 * ((R & 7) ^ (4 (c & 1))).
+// A wave's operand reads (8 rows x 16 B for the K operand, 4 rows x 32 B
+// for the transposing V reads) then touch distinct banks, and every read
+// address is a per-lane base plus a compile-time offset.
+// Global byte offset (within a tile) of the 16 bytes that lane `lane` of
+// the G-th 1 KB direct-to-LDS load must fetch so that LDS byte 1024 G +
+// 16 lane ends up holding the chunk that the layout above puts there.
+template <int D>
+__device__ __forceinline__ int dma_src_off(int G, int lane) {
+  const int o = G * 1024 + 16 * lane;
+  const int c = (o % (16 * D)) / 128;
+  const int R = (o / (16 * D)) * 8 + (((o % 128) / 16) ^ ((c & 1) << 2));
+  return R * (2 * D) + c * 16;
+}
+
+// Per-wave constants of the 16-bit kernel.
+struct Wave16 {
+  int lane, hf, l32, wave;
+  int wq0;    // first query row of the wave
+  int wkend;  // keys [0, wkend) are needed by the wave
+  int wklim;  // smallest last-visible key over the wave's rows
+  int klim;   // last key this lane's row may see
+  int kbase;  // LDS byte offset of this lane's K-operand reads
+  int vbase;  // LDS byte offset of this lane's transposing V-operand reads
+};
+
+// One K/V tile of the 16-bit kernel.  If `next` is set, first issue the
+// direct-to-LDS loads of tile j+1 into `dst` (the stage that was read two
+// tiles ago); then, if the wave needs tile j, run S^T = K Q^T, the mask, the
+// online-softmax update and O^T += V^T P^T on the stage `src`; finally wait
+// for this wave's loads and meet the other waves at the barrier.  `src` and
+// `dst` are distinct __shared__ arrays, so the compiler knows the loads in
+// flight never alias the operand reads.
+template <int DT, int D, bool CAUSAL>
+__device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes, int j, bool next,
+                                       const unsigned char* src, unsigned char* dst,
+                                       const Wave16& w, const u32x4 (&qf)[D / 16],
+                                       f32x16 (&oacc)[D / 32], float& mref, float& l, float sl2) {
+  constexpr int BC = 64;
+  constexpr int TILEB = BC * D * 2;
+  constexpr int NI = TILEB / 1024 / 4;  // 1 KB direct-to-LDS loads per wave per tensor
+  constexpr int NKK = D / 16, NDT = D / 32;
+  // mref is raised only when a tile's row max exceeds it by more than kTau
+  // (log2 units), so P = exp2(t - mref) stays below 2^kTau; O and l always
+  // share mref, so O / l and mref + log2(l) are exact whatever mref is.
+  constexpr float kTau = 8.0f;
+
+  if (next) {
+    const auto rk = make_rsrc(Kh, kbytes);
+    const auto rv = make_rsrc(Vh, kbytes);
+    unsigned char* d0 = dst + w.wave * NI * 1024;
+#pragma unroll
+    for (int I = 0; I < NI; ++I) {
+      const int go = dma_src_off<D>(w.wave * NI + I, w.lane);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(d0 + I * 1024), 16, go, (j + 1) * TILEB, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(d0 + TILEB + I * 1024), 16, go, (j + 1) * TILEB,
+                                               0, 0);
+    }
+  }
+  const int k0 = j * BC;
+  if (k0 < w.wkend) {
+    const unsigned char* ks = src;
+    const unsigned char* vs = src + TILEB;
+    f32x16 s[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      s[n] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const u32x4 a = *(const u32x4*)(ks + w.kbase + n * 64 * D + kk * 256);
+        s[n] = mfma_32x32x16<DT>(a, qf[kk], s[n]);
+      }
+    }
+    // Mask (diagonal and tail tiles only): key = k0 + 4*hf + off(n, r).
+    if (k0 + BC - 1 > w.wklim) {
+      const int lim = w.klim - (k0 + 4 * w.hf);
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[n][r] = (32 * n + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[n][r];
+    }
+    // Row max of the raw scores (scale > 0 commutes with max).
+    float mx = s[0][0];
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int r = (n == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[n][r]);
+    mx = pair_max(mx) * sl2;
+    if (__builtin_amdgcn_ballot_w64(mx > mref + kTau)) {
+      const float mnew = fmaxf(mref, mx);
+      const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+      mref = mnew;
+    }
+    const float nm = -mref;
+    u32x4 pf[2][2];
+    // l sums the fp32 P (its rounding to 16 bits would leave a relative
+    // error of up to 2^-9 in the LSE of rows that see few keys).
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[n][8 * hh + 2 * i], sl2, nm));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[n][8 * hh + 2 * i + 1], sl2, nm));
+          pf[n][hh][i] = pack2<DT>(p0, p1);
+          ls0 += p0;
+          ls1 += p1;
+        }
+    l += ls0 + ls1;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int off = w.vbase + (4 * n + 2 * hh) * (16 * D) + dt * 512;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + off));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + off + 16 * D));
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+          const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
+          oacc[dt] = mfma_32x32x16<DT>(a, pf[n][hh], oacc[dt]);
+        }
+  }
+  wait_vmem();
+  __syncthreads();
+}
+
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fa_fwd_16(const u16* __restrict__ Qg,
                                                          const u16* __restrict__ Kg,
@@ -113,205 +263,101 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_16(const u16* __restrict__
                                                          float* __restrict__ Lg, int BH, int Nq,
                                                          int Nk, int nqt, float sl2) {
   constexpr int BC = 64;
-  constexpr int KSTR = D + 8;     // K row stride (elements): +16 B breaks bank aliasing
-  constexpr int VSTR = BC + 8;    // V^T row stride (elements)
-  constexpr int KST = BC * KSTR;  // elements per K stage
-  constexpr int VST = D * VSTR;   // elements per V^T stage
-  constexpr int NKK = D / 16;     // MFMA steps over the head dimension
-  constexpr int NDT = D / 32;     // 32-wide output column tiles
-  constexpr int KPT = BC * D / 8 / kThreads;  // 16-byte K chunks per thread
-  constexpr int VJOBS = (BC / 4) * (D / 8);   // 4-key x 8-column V blocks per tile
-  static_assert(KPT >= 1 && VJOBS <= kThreads, "tile shape");
+  constexpr int ROWB = D * 2;             // bytes per row
+  constexpr int TILEB = BC * ROWB;        // bytes per K (or V) tile
+  constexpr int NI = TILEB / 1024 / 4;    // 1 KB direct-to-LDS loads per wave per tensor
+  constexpr int NKK = D / 16;             // MFMA steps over the head dimension
+  constexpr int NDT = D / 32;             // 32-wide output column tiles
+  static_assert(NI >= 1, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) u16 smem[2 * (KST + VST)];
+  // Two stages, each a K tile followed by a V tile; tile j lives in stage j % 2.
+  __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * TILEB];
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int hf = lane >> 5, l32 = lane & 31;
+  Wave16 w;
+  const int tid = threadIdx.x;
+  w.lane = tid & 63;
+  w.wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  w.hf = w.lane >> 5;
+  w.l32 = w.lane & 31;
   int bh, qt;
   tile_of_block(nqt, BH, bh, qt);
   const int q0 = qt * kBR;
-  const size_t qoff = (size_t)bh * Nq * D, koff = (size_t)bh * Nk * D;
-  const u16* Q = Qg + qoff;
-  const u16* K = Kg + koff;
-  const u16* V = Vg + koff;
+  const u16* Kh = Kg + (size_t)bh * Nk * D;
+  const u16* Vh = Vg + (size_t)bh * Nk * D;
+  const int kbytes = Nk * ROWB;
 
   const int kend = CAUSAL ? min(Nk, min(q0 + kBR, Nq)) : Nk;  // keys [0, kend) are needed
   const int nt = (kend + BC - 1) / BC;
-  const bool ktail = (nt * BC > Nk);              // the last tile runs past Nk
-  const int wq0 = q0 + 32 * wave;                  // this wave's first query row
-  const int myq = wq0 + l32;                       // this lane's query row
-  const int wkend = CAUSAL ? min(kend, wq0 + 32) : kend;  // keys this wave needs
-  // last key this lane may see
-  const int klim = CAUSAL ? min(myq, Nk - 1) : Nk - 1;
-
-  // Q fragment: lane holds Q[myq][16*kk + 8*hf .. +7] for kk = 0..NKK-1.
-  u32x4 qf[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    qf[kk] = (myq < Nq) ? *(const u32x4*)(Q + (size_t)myq * D + 16 * kk + 8 * hf) : u32x4{0, 0, 0, 0};
+  w.wq0 = q0 + 32 * w.wave;
+  const int myq = w.wq0 + w.l32;
+  w.wkend = CAUSAL ? min(kend, w.wq0 + 32) : kend;
+  w.klim = CAUSAL ? min(myq, Nk - 1) : Nk - 1;
+  w.wklim = CAUSAL ? min(w.wq0, Nk - 1) : Nk - 1;
+  // K operand (S^T = K Q^T): row 32n + l32, chunk 2kk + hf.  V operand
+  // (O^T = V^T P^T, transposing reads): 16-lane group g reads rows
+  // rowbase + i/4 at columns 32dt + 16g + 4(i%4), i = lane % 16.
+  w.kbase = (w.l32 >> 3) * (16 * D) + w.hf * 128 + (((w.l32 & 7) ^ (w.hf << 2)) << 4);
+  {
+    const int vi = w.l32 & 15, vg = w.l32 >> 4;
+    w.vbase = vg * 256 + ((vi & 3) >> 1) * 128 + (((4 * w.hf + (vi >> 2)) ^ (((vi & 3) >> 1) << 2)) << 4) +
+              8 * (vi & 1);
   }
 
-  // Per-thread staging of the next K/V tile.
-  u32x4 kr[KPT];
-  u32x4 vr[4];
-  const int g4 = tid & 15, db = tid >> 4;  // V job: keys 4*g4..+3, columns 8*db..+7
-  const bool vjob = (VJOBS == kThreads) || (tid < VJOBS);
-  const int krow0 = tid / (D / 8), kcol = (tid % (D / 8)) * 8;  // K chunk i: row krow0 + i*(256/(D/8))
-  constexpr int KROWS_PER_PASS = kThreads / (D / 8);
-
-  // Full tiles load unguarded; the tile that runs past Nk clamps the row and
-  // zero-fills (zero V rows keep 0 * V finite for masked keys).
-  auto load_tile = [&](int j, bool guard) {
-    const int k0 = j * BC;
-    if (!guard) {
+  // Tile 0 into stage 0.
+  {
+    const auto rk = make_rsrc(Kh, kbytes);
+    const auto rv = make_rsrc(Vh, kbytes);
 #pragma unroll
-      for (int i = 0; i < KPT; ++i)
-        kr[i] = *(const u32x4*)(K + (size_t)(k0 + krow0 + i * KROWS_PER_PASS) * D + kcol);
-      if (vjob) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vr[r] = *(const u32x4*)(V + (size_t)(k0 + 4 * g4 + r) * D + 8 * db);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int key = k0 + krow0 + i * KROWS_PER_PASS;
-        const u32x4 x = *(const u32x4*)(K + (size_t)min(key, Nk - 1) * D + kcol);
-        kr[i] = (key < Nk) ? x : u32x4{0, 0, 0, 0};
-      }
-      if (vjob) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = k0 + 4 * g4 + r;
-          const u32x4 x = *(const u32x4*)(V + (size_t)min(key, Nk - 1) * D + 8 * db);
-          vr[r] = (key < Nk) ? x : u32x4{0, 0, 0, 0};
-        }
-      }
+    for (int I = 0; I < NI; ++I) {
+      const int go = dma_src_off<D>(w.wave * NI + I, w.lane);
+      unsigned char* d0 = stage0 + (w.wave * NI + I) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)d0, 16, go, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(d0 + TILEB), 16, go, 0, 0, 0);
     }
-  };
-
-  // V^T positions inside a 16-key group: keys 0-3 -> 0-3, 8-11 -> 4-7,
-  // 4-7 -> 8-11, 12-15 -> 12-15, so that the 8 keys one lane feeds to a PV
-  // MFMA are contiguous.
-  const int vpos = (g4 >> 2) * 16 + ((((g4 & 3) & 1) << 1) | ((g4 & 3) >> 1)) * 4;
-  auto store_tile = [&](int stage) {
-    u16* ks = smem + stage * (KST + VST);
-    u16* vs = ks + KST;
+  }
+  // Q fragment (B operand of S^T): lane holds Q[myq][16*kk + 8*hf .. +7];
+  // rows past Nq read as zero.
+  u32x4 qf[NKK];
+  {
+    const auto rQ = make_rsrc(Qg + (size_t)bh * Nq * D, Nq * ROWB);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) *(u32x4*)(ks + (krow0 + i * KROWS_PER_PASS) * KSTR + kcol) = kr[i];
-    if (vjob) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const unsigned e01 = __builtin_amdgcn_perm(vr[1][j], vr[0][j], 0x05040100u);
-        const unsigned e23 = __builtin_amdgcn_perm(vr[3][j], vr[2][j], 0x05040100u);
-        const unsigned o01 = __builtin_amdgcn_perm(vr[1][j], vr[0][j], 0x07060302u);
-        const unsigned o23 = __builtin_amdgcn_perm(vr[3][j], vr[2][j], 0x07060302u);
-        *(u32x2*)(vs + (8 * db + 2 * j) * VSTR + vpos) = u32x2{e01, e23};
-        *(u32x2*)(vs + (8 * db + 2 * j + 1) * VSTR + vpos) = u32x2{o01, o23};
-      }
-    }
-  };
-
-  // Running state.  mref is a reference maximum in the scaled log2 domain;
-  // it is raised only when a tile's row max exceeds it by more than kTau, so
-  // P = exp2(t - mref) stays below 2^kTau.  O and l always share mref, so the
-  // final O / l and mref + log2(l) are exact whatever mref is.
-  constexpr float kTau = 8.0f;
+    for (int kk = 0; kk < NKK; ++kk)
+      qf[kk] = __builtin_amdgcn_raw_buffer_load_b128(rQ, (32 * w.wave + w.l32) * ROWB + (16 * kk + 8 * w.hf) * 2,
+                                                     q0 * ROWB, 0);
+  }
   float mref = kMinit, l = 0.f;
   f32x16 oacc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
+  wait_vmem();
+  __syncthreads();
 
-  load_tile(0, ktail && nt == 1);
-  for (int j = 0; j < nt; ++j) {
-    const int stage = j & 1;
-    store_tile(stage);
-    __syncthreads();
-    if (j + 1 < nt) load_tile(j + 1, ktail && (j + 2 == nt));
-    const int k0 = j * BC;
-    if (k0 < wkend) {
-      const u16* ks = smem + stage * (KST + VST);
-      const u16* vs = ks + KST;
-      f32x16 s[2];
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        s[n] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const u32x4 a = *(const u32x4*)(ks + (32 * n + l32) * KSTR + 16 * kk + 8 * hf);
-          s[n] = mfma_32x32x16<DT>(a, qf[kk], s[n]);
-        }
-      }
-      // Mask (diagonal and tail tiles only): key = k0 + 4*hf + off(n, r).
-      if ((k0 + BC - 1 > klim_wave_max(wq0, Nk, CAUSAL)) ) {
-        const int lim = klim - (k0 + 4 * hf);
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            s[n][r] = (32 * n + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[n][r];
-      }
-      // Row max of the raw scores (scale > 0 commutes with max).
-      float mx = s[0][0];
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int r = (n == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[n][r]);
-      mx = pair_max(mx) * sl2;
-      if (__builtin_amdgcn_ballot_w64(mx > mref + kTau)) {
-        const float mnew = fmaxf(mref, mx);
-        const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
-        l *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
-        mref = mnew;
-      }
-      const float nm = -mref;
-      u32x4 pf[2][2];
-      // l sums the fp32 P (its rounding to 16 bits would leave a relative
-      // error of up to 2^-9 in the LSE of rows that see few keys).
-      float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[n][8 * hh + 2 * i], sl2, nm));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[n][8 * hh + 2 * i + 1], sl2, nm));
-            pf[n][hh][i] = pack2<DT>(p0, p1);
-            ls0 += p0;
-            ls1 += p1;
-          }
-      l += ls0 + ls1;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const u32x4 a = *(const u32x4*)(vs + (32 * dt + l32) * VSTR + 32 * n + 16 * hh + 8 * hf);
-            oacc[dt] = mfma_32x32x16<DT>(a, pf[n][hh], oacc[dt]);
-          }
-    }
+  for (int j = 0; j < nt; j += 2) {
+    tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j, j + 1 < nt, stage0, stage1, w, qf, oacc, mref, l, sl2);
+    if (j + 1 < nt)
+      tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 1, j + 2 < nt, stage1, stage0, w, qf, oacc, mref, l, sl2);
   }
 
-  // Epilogue: combine the two half-row sums, normalise, round, store.
+  // Epilogue: combine the two half-row sums, normalise, round to 16 bits,
+  // store (rows past Nq are dropped by the buffer range check).
   const float lt = pair_sum(l);
-  if (myq < Nq) {
-    const float inv = 1.0f / lt;
-    u16* O = Og + qoff + (size_t)myq * D;
+  const float inv = 1.0f / lt;
+  const auto rO = make_rsrc(Og + (size_t)bh * Nq * D, Nq * ROWB);
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+  for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * dt + 8 * g + 4 * hf;
-        u32x2 w;
-        w[0] = pack2<DT>(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv);
-        w[1] = pack2<DT>(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
-        *(u32x2*)(O + d) = w;
-      }
-    if (hf == 0) Lg[(size_t)bh * Nq + myq] = (mref + __log2f(lt)) * kLn2;
+    for (int g = 0; g < 4; ++g) {
+      u32x2 v;
+      v[0] = pack2<DT>(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv);
+      v[1] = pack2<DT>(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
+      __builtin_amdgcn_raw_buffer_store_b64(v, rO, (32 * w.wave + w.l32) * ROWB + (32 * dt + 8 * g + 4 * w.hf) * 2,
+                                            q0 * ROWB, 0);
+    }
+  if (w.hf == 0) {
+    const auto rL = make_rsrc(Lg + (size_t)bh * Nq, Nq * 4);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, (mref + __log2f(lt)) * kLn2), rL,
+                                          (32 * w.wave + w.l32) * 4, q0 * 4, 0);
   }
 }
 
