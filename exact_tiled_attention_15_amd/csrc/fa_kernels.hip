@@ -119,21 +119,25 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// LDS tile layout for a BC x D tile of 16-bit values (K or V), in bytes:
-// rows are taken in groups of 8; inside a group, 16-byte chunk c of the 8
-// rows sits in one 128-byte line, at row slot (R & 7) XOR 4*(c & 1):
-//   off(R, c) = (R / 8) * 16 D + 128 c + 16 * ((R & 7) ^ (4 (c & 1))).
-// A wave's operand reads (8 rows x 16 B for the K operand, 4 rows x 32 B
-// for the transposing V reads) then touch distinct banks, and every read
-// address is a per-lane base plus a compile-time offset.
+// LDS tile layout for a BC x D tile of 16-bit values (K or V), in bytes.
+// The gfx950 LDS serves 256 bytes per clock (64 banks of 4 bytes), so rows
+// are taken in groups of 16 and 16-byte chunk c of the 16 rows shares one
+// 256-byte line, at row slot (R % 16) XOR 4 (c % 4):
+//   off(R, c) = (R / 16) * 32 D + 256 c + 16 ((R % 16) ^ (4 (c % 4))).
+// A K-operand read (16 lanes = 16 rows x one chunk) and a transposing
+// V-operand read (32 lanes = 4 rows x 4 chunks) then each cover one whole
+// 256-byte line, and every read address is one of two per-lane bases plus
+// a compile-time offset.
+
 // Global byte offset (within a tile) of the 16 bytes that lane `lane` of
 // the G-th 1 KB direct-to-LDS load must fetch so that LDS byte 1024 G +
 // 16 lane ends up holding the chunk that the layout above puts there.
 template <int D>
 __device__ __forceinline__ int dma_src_off(int G, int lane) {
   const int o = G * 1024 + 16 * lane;
-  const int c = (o % (16 * D)) / 128;
-  const int R = (o / (16 * D)) * 8 + (((o % 128) / 16) ^ ((c & 1) << 2));
+  const int rem = o % (32 * D);
+  const int c = rem / 256;
+  const int R = (o / (32 * D)) * 16 + (((rem % 256) / 16) ^ ((c & 3) << 2));
   return R * (2 * D) + c * 16;
 }
 
@@ -144,43 +148,77 @@ struct Wave16 {
   int wkend;  // keys [0, wkend) are needed by the wave
   int wklim;  // smallest last-visible key over the wave's rows
   int klim;   // last key this lane's row may see
-  int kbase;  // LDS byte offset of this lane's K-operand reads
-  int vbase;  // LDS byte offset of this lane's transposing V-operand reads
+  int kb[2];  // LDS byte offsets of this lane's K-operand reads (even / odd kk)
+  int vb[2];  // LDS byte offsets of this lane's transposing V-operand reads (q = 0 / 1)
 };
 
-// One K/V tile of the 16-bit kernel.  If `next` is set, first issue the
-// direct-to-LDS loads of tile j+1 into `dst` (the stage that was read two
-// tiles ago); then, if the wave needs tile j, run S^T = K Q^T, the mask, the
-// online-softmax update and O^T += V^T P^T on the stage `src`; finally wait
-// for this wave's loads and meet the other waves at the barrier.  `src` and
-// `dst` are distinct __shared__ arrays, so the compiler knows the loads in
-// flight never alias the operand reads.
+// 16-bit kernel shape: a workgroup of 8 waves owns 256 query rows (32 per
+// wave), streams 64-key K/V tiles through a 4-stage LDS ring (three tiles
+// in flight while one is consumed).
+constexpr int kThreads16 = 512;
+constexpr int kBR16 = 256;
+constexpr int kStages = 4;
+
+// Wait until this wave's loads of tile j have landed (at most `ahead` later
+// tiles, NV loads each, may still be in flight), then meet the other waves:
+// afterwards every wave's share of tile j is in LDS and every wave has
+// finished reading tile j-1.  s_waitcnt needs an immediate, hence the switch.
+template <int NV>
+__device__ __forceinline__ void wait_tile_and_barrier(int ahead) {
+  constexpr int kBase = 0xF70;  // expcnt and lgkmcnt fields at "no wait"; lgkmcnt set below
+  asm volatile("" ::: "memory");
+  if (ahead >= 2) {
+    __builtin_amdgcn_s_waitcnt((kBase & ~0xF00) | (2 * NV));  // vmcnt(2 NV) lgkmcnt(0)
+  } else if (ahead == 1) {
+    __builtin_amdgcn_s_waitcnt((kBase & ~0xF00) | NV);        // vmcnt(NV) lgkmcnt(0)
+  } else {
+    __builtin_amdgcn_s_waitcnt(kBase & ~0xF00);               // vmcnt(0) lgkmcnt(0)
+  }
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Direct-to-LDS loads of K/V tile t into `dst` (this wave's NI 1 KB pieces of
+// the K tile and of the V tile).
+template <int D>
+__device__ __forceinline__ void issue_tile16(const u16* Kh, const u16* Vh, int kbytes, int t,
+                                             unsigned char* dst, const Wave16& w) {
+  constexpr int TILEB = 64 * D * 2;
+  constexpr int NI = TILEB / 1024 / (kThreads16 / 64);
+  const auto rk = make_rsrc(Kh, kbytes);
+  const auto rv = make_rsrc(Vh, kbytes);
+  unsigned char* d0 = dst + w.wave * NI * 1024;
+#pragma unroll
+  for (int I = 0; I < NI; ++I) {
+    const int go = dma_src_off<D>(w.wave * NI + I, w.lane);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(d0 + I * 1024), 16, go, t * TILEB, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(d0 + TILEB + I * 1024), 16, go, t * TILEB, 0, 0);
+  }
+}
+
+// One K/V tile of the 16-bit kernel: wait for tile j (stage `src`), then
+// start the loads of tile j+3 into `dst` (the stage of tile j-1, which every
+// wave has finished with), then, if the wave needs tile j, run
+// S^T = K Q^T, the mask, the online-softmax update and O^T += V^T P^T.
+// `src` and `dst` are distinct __shared__ arrays, so the compiler knows the
+// loads in flight never alias the operand reads.
 template <int DT, int D, bool CAUSAL>
-__device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes, int j, bool next,
+__device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes, int j, int nt,
                                        const unsigned char* src, unsigned char* dst,
                                        const Wave16& w, const u32x4 (&qf)[D / 16],
                                        f32x16 (&oacc)[D / 32], float& mref, float& l, float sl2) {
   constexpr int BC = 64;
   constexpr int TILEB = BC * D * 2;
-  constexpr int NI = TILEB / 1024 / 4;  // 1 KB direct-to-LDS loads per wave per tensor
+  constexpr int NV = 2 * (TILEB / 1024 / (kThreads16 / 64));  // loads per wave per tile
   constexpr int NKK = D / 16, NDT = D / 32;
   // mref is raised only when a tile's row max exceeds it by more than kTau
   // (log2 units), so P = exp2(t - mref) stays below 2^kTau; O and l always
   // share mref, so O / l and mref + log2(l) are exact whatever mref is.
   constexpr float kTau = 8.0f;
 
-  if (next) {
-    const auto rk = make_rsrc(Kh, kbytes);
-    const auto rv = make_rsrc(Vh, kbytes);
-    unsigned char* d0 = dst + w.wave * NI * 1024;
-#pragma unroll
-    for (int I = 0; I < NI; ++I) {
-      const int go = dma_src_off<D>(w.wave * NI + I, w.lane);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(d0 + I * 1024), 16, go, (j + 1) * TILEB, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(d0 + TILEB + I * 1024), 16, go, (j + 1) * TILEB,
-                                               0, 0);
-    }
-  }
+  wait_tile_and_barrier<NV>(min(2, nt - 1 - j));
+  if (j + kStages - 1 < nt) issue_tile16<D>(Kh, Vh, kbytes, j + kStages - 1, dst, w);
+
   const int k0 = j * BC;
   if (k0 < w.wkend) {
     const unsigned char* ks = src;
@@ -191,7 +229,7 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
       s[n] = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const u32x4 a = *(const u32x4*)(ks + w.kbase + n * 64 * D + kk * 256);
+        const u32x4 a = *(const u32x4*)(ks + w.kb[kk & 1] + n * 64 * D + (kk >> 1) * 1024);
         s[n] = mfma_32x32x16<DT>(a, qf[kk], s[n]);
       }
     }
@@ -243,36 +281,35 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
       for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int off = w.vbase + (4 * n + 2 * hh) * (16 * D) + dt * 512;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + off));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + off + 16 * D));
+          const int off = (2 * n + hh) * (32 * D) + dt * 1024;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + w.vb[0] + off));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + w.vb[1] + off));
           const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
           const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
           oacc[dt] = mfma_32x32x16<DT>(a, pf[n][hh], oacc[dt]);
         }
   }
-  wait_vmem();
-  __syncthreads();
 }
 
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fa_fwd_16(const u16* __restrict__ Qg,
-                                                         const u16* __restrict__ Kg,
-                                                         const u16* __restrict__ Vg,
-                                                         u16* __restrict__ Og,
-                                                         float* __restrict__ Lg, int BH, int Nq,
-                                                         int Nk, int nqt, float sl2) {
+__global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict__ Qg,
+                                                           const u16* __restrict__ Kg,
+                                                           const u16* __restrict__ Vg,
+                                                           u16* __restrict__ Og,
+                                                           float* __restrict__ Lg, int BH, int Nq,
+                                                           int Nk, int nqt, float sl2) {
   constexpr int BC = 64;
   constexpr int ROWB = D * 2;             // bytes per row
   constexpr int TILEB = BC * ROWB;        // bytes per K (or V) tile
-  constexpr int NI = TILEB / 1024 / 4;    // 1 KB direct-to-LDS loads per wave per tensor
   constexpr int NKK = D / 16;             // MFMA steps over the head dimension
   constexpr int NDT = D / 32;             // 32-wide output column tiles
-  static_assert(NI >= 1, "tile shape");
+  static_assert(TILEB / 1024 % (kThreads16 / 64) == 0, "tile shape");
 
-  // Two stages, each a K tile followed by a V tile; tile j lives in stage j % 2.
+  // The LDS ring: tile j lives in stage j % 4 (a K tile followed by a V tile).
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * TILEB];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage2[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage3[2 * TILEB];
 
   Wave16 w;
   const int tid = threadIdx.x;
@@ -282,42 +319,39 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_16(const u16* __restrict__
   w.l32 = w.lane & 31;
   int bh, qt;
   tile_of_block(nqt, BH, bh, qt);
-  const int q0 = qt * kBR;
+  const int q0 = qt * kBR16;
   const u16* Kh = Kg + (size_t)bh * Nk * D;
   const u16* Vh = Vg + (size_t)bh * Nk * D;
   const int kbytes = Nk * ROWB;
 
-  const int kend = CAUSAL ? min(Nk, min(q0 + kBR, Nq)) : Nk;  // keys [0, kend) are needed
+  const int kend = CAUSAL ? min(Nk, min(q0 + kBR16, Nq)) : Nk;  // keys [0, kend) are needed
   const int nt = (kend + BC - 1) / BC;
   w.wq0 = q0 + 32 * w.wave;
   const int myq = w.wq0 + w.l32;
   w.wkend = CAUSAL ? min(kend, w.wq0 + 32) : kend;
   w.klim = CAUSAL ? min(myq, Nk - 1) : Nk - 1;
   w.wklim = CAUSAL ? min(w.wq0, Nk - 1) : Nk - 1;
-  // K operand (S^T = K Q^T): row 32n + l32, chunk 2kk + hf.  V operand
-  // (O^T = V^T P^T, transposing reads): 16-lane group g reads rows
-  // rowbase + i/4 at columns 32dt + 16g + 4(i%4), i = lane % 16.
-  w.kbase = (w.l32 >> 3) * (16 * D) + w.hf * 128 + (((w.l32 & 7) ^ (w.hf << 2)) << 4);
+  // K operand (S^T = K Q^T): row 32n + l32, chunk c = 2kk + hf, so the
+  // slot XOR (4 (c % 4)) depends on the parity of kk.  V operand (O^T =
+  // V^T P^T, transposing reads): 16-lane group g reads rows
+  // 32n + 16hh + 8q + 4hf + i/4 at columns 32dt + 16g + 4(i%4), i = lane % 16,
+  // i.e. chunk 4dt + 2g + (i%4)/2 and half (i%2) of it.
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int c = 2 * par + w.hf;
+    w.kb[par] = (w.l32 >> 4) * (32 * D) + c * 256 + (((w.l32 & 15) ^ (c << 2)) << 4);
+  }
   {
     const int vi = w.l32 & 15, vg = w.l32 >> 4;
-    w.vbase = vg * 256 + ((vi & 3) >> 1) * 128 + (((4 * w.hf + (vi >> 2)) ^ (((vi & 3) >> 1) << 2)) << 4) +
-              8 * (vi & 1);
+    const int c = 2 * vg + ((vi & 3) >> 1);  // chunk within the 4-chunk (64-column) block
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      w.vb[q] = c * 256 + (((8 * q + 4 * w.hf + (vi >> 2)) ^ (c << 2)) << 4) + 8 * (vi & 1);
   }
 
-  // Tile 0 into stage 0.
-  {
-    const auto rk = make_rsrc(Kh, kbytes);
-    const auto rv = make_rsrc(Vh, kbytes);
-#pragma unroll
-    for (int I = 0; I < NI; ++I) {
-      const int go = dma_src_off<D>(w.wave * NI + I, w.lane);
-      unsigned char* d0 = stage0 + (w.wave * NI + I) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)d0, 16, go, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(d0 + TILEB), 16, go, 0, 0, 0);
-    }
-  }
   // Q fragment (B operand of S^T): lane holds Q[myq][16*kk + 8*hf .. +7];
-  // rows past Nq read as zero.
+  // rows past Nq read as zero.  Issued before the K/V loads: loads complete
+  // in order, so waiting for a K/V tile also covers Q.
   u32x4 qf[NKK];
   {
     const auto rQ = make_rsrc(Qg + (size_t)bh * Nq * D, Nq * ROWB);
@@ -326,17 +360,21 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_16(const u16* __restrict__
       qf[kk] = __builtin_amdgcn_raw_buffer_load_b128(rQ, (32 * w.wave + w.l32) * ROWB + (16 * kk + 8 * w.hf) * 2,
                                                      q0 * ROWB, 0);
   }
+  // Tiles 0..2 into stages 0..2.
+  issue_tile16<D>(Kh, Vh, kbytes, 0, stage0, w);
+  if (nt > 1) issue_tile16<D>(Kh, Vh, kbytes, 1, stage1, w);
+  if (nt > 2) issue_tile16<D>(Kh, Vh, kbytes, 2, stage2, w);
+
   float mref = kMinit, l = 0.f;
   f32x16 oacc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
-  wait_vmem();
-  __syncthreads();
 
-  for (int j = 0; j < nt; j += 2) {
-    tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j, j + 1 < nt, stage0, stage1, w, qf, oacc, mref, l, sl2);
-    if (j + 1 < nt)
-      tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 1, j + 2 < nt, stage1, stage0, w, qf, oacc, mref, l, sl2);
+  for (int j = 0; j < nt; j += kStages) {
+    tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j, nt, stage0, stage3, w, qf, oacc, mref, l, sl2);
+    if (j + 1 < nt) tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 1, nt, stage1, stage0, w, qf, oacc, mref, l, sl2);
+    if (j + 2 < nt) tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 2, nt, stage2, stage1, w, qf, oacc, mref, l, sl2);
+    if (j + 3 < nt) tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 3, nt, stage3, stage2, w, qf, oacc, mref, l, sl2);
   }
 
   // Epilogue: combine the two half-row sums, normalise, round to 16 bits,
@@ -518,38 +556,39 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_32(const float* __restrict
 }
 
 template <typename KernelT, typename T>
-int launch(KernelT kern, const FaLaunch& a, int nqt, float sl2) {
-  const dim3 grid((unsigned)(a.BH * nqt)), block(kThreads);
+int launch(KernelT kern, const FaLaunch& a, int rows_per_block, int threads, float sl2) {
+  const int nqt = (int)((a.Nq + rows_per_block - 1) / rows_per_block);
+  const dim3 grid((unsigned)(a.BH * nqt)), block(threads);
   hipLaunchKernelGGL(kern, grid, block, 0, (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k,
                      (const T*)a.v, (T*)a.o, a.lse, (int)a.BH, (int)a.Nq, (int)a.Nk, nqt, sl2);
   return (int)hipGetLastError();
 }
 
 template <int DT, int D>
-int dispatch16(const FaLaunch& a, int nqt, float sl2) {
-  if (a.causal) return launch<decltype(&fa_fwd_16<DT, D, true>), u16>(&fa_fwd_16<DT, D, true>, a, nqt, sl2);
-  return launch<decltype(&fa_fwd_16<DT, D, false>), u16>(&fa_fwd_16<DT, D, false>, a, nqt, sl2);
+int dispatch16(const FaLaunch& a, float sl2) {
+  if (a.causal)
+    return launch<decltype(&fa_fwd_16<DT, D, true>), u16>(&fa_fwd_16<DT, D, true>, a, kBR16, kThreads16, sl2);
+  return launch<decltype(&fa_fwd_16<DT, D, false>), u16>(&fa_fwd_16<DT, D, false>, a, kBR16, kThreads16, sl2);
 }
 
 template <int D>
-int dispatch32(const FaLaunch& a, int nqt, float sl2) {
-  if (a.causal) return launch<decltype(&fa_fwd_32<D, true>), float>(&fa_fwd_32<D, true>, a, nqt, sl2);
-  return launch<decltype(&fa_fwd_32<D, false>), float>(&fa_fwd_32<D, false>, a, nqt, sl2);
+int dispatch32(const FaLaunch& a, float sl2) {
+  if (a.causal) return launch<decltype(&fa_fwd_32<D, true>), float>(&fa_fwd_32<D, true>, a, kBR, kThreads, sl2);
+  return launch<decltype(&fa_fwd_32<D, false>), float>(&fa_fwd_32<D, false>, a, kBR, kThreads, sl2);
 }
 
 }  // namespace
 
 int fa_launch_fwd(const FaLaunch& a) {
-  const int nqt = (int)((a.Nq + kBR - 1) / kBR);
   // log2(e)/sqrt(D), computed in double and rounded once.
   const float sl2 = (float)(1.4426950408889634074 / __builtin_sqrt((double)a.D));
   (void)hipGetLastError();  // clear a stale error so that the check below is ours
   switch (a.dtype) {
     case kBF16:
-      return a.D == 64 ? dispatch16<kBF16, 64>(a, nqt, sl2) : dispatch16<kBF16, 128>(a, nqt, sl2);
+      return a.D == 64 ? dispatch16<kBF16, 64>(a, sl2) : dispatch16<kBF16, 128>(a, sl2);
     case kFP16:
-      return a.D == 64 ? dispatch16<kFP16, 64>(a, nqt, sl2) : dispatch16<kFP16, 128>(a, nqt, sl2);
+      return a.D == 64 ? dispatch16<kFP16, 64>(a, sl2) : dispatch16<kFP16, 128>(a, sl2);
     default:
-      return a.D == 64 ? dispatch32<64>(a, nqt, sl2) : dispatch32<128>(a, nqt, sl2);
+      return a.D == 64 ? dispatch32<64>(a, sl2) : dispatch32<128>(a, sl2);
   }
 }
