@@ -33,8 +33,8 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default=workloads.HEADLINE)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -44,6 +44,33 @@ def parse():
                    help="after timing, run 3 plain device copies of this many MiB (a reference "
                         "kernel of known traffic for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     return p.parse_args()
+
+
+def kernel_tag(w: workloads.Workload) -> str:
+    if w.dtype == "fp32":
+        return f"fa_fwd_32_d{w.D}_{'causal' if w.causal else 'noncausal'}"
+    return f"fa_fwd_16_{w.dtype}_d{w.D}_{'causal' if w.causal else 'noncausal'}"
+
+
+def measured_traffic(w: workloads.Workload):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary of this kernel and workload, or None when there is none or the
+    kernel source has changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag(w)}__{w.name}__hbm_traffic_and_counters.md")
+    src = os.path.join(ROOT, "exact_tiled_attention_15_amd", "csrc", "fa_kernels.hip")
+    if not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":")[0] in ("kernel_source_sha256", "traffic_bytes_per_launch"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def blas_threads() -> int:
@@ -176,7 +203,7 @@ def line_for(w, r, steps, warmup, cpu):
                    "min_launch_ms": round(r["min_launch_ms"], 5), **props},
         "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 3), "peak": r["peak"],
                      "unit": "TFLOP/s", "frac": round(r["tflops"] / r["peak"], 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(w)},
         "cpu_baseline": cpu,
     }
 
