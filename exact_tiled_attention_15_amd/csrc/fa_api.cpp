@@ -42,6 +42,9 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   int64_t qbytes, kbytes, lbytes;
   if (!mul_ok(qel, esz, &qbytes) || !mul_ok(kel, esz, &kbytes) || !mul_ok(rows, 4, &lbytes))
     return FA_ERR_SHAPE;
+  // The kernels address one head through 32-bit buffer offsets, which reach
+  // up to 256 rows past the end (a partial last Q tile, padding K/V tiles).
+  if ((Nq + 256) * D * esz > INT32_MAX || (Nk + 256) * D * esz > INT32_MAX) return FA_ERR_SHAPE;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGN;
   if ((uintptr_t)lse & 3u) return FA_ERR_ALIGN;

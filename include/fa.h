@@ -49,7 +49,10 @@ typedef enum {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,     /* a required pointer is NULL */
-  FA_ERR_SHAPE = 2,    /* negative size, Nk < 1 with rows to compute, or too large */
+  FA_ERR_SHAPE = 2,    /* negative size, Nk < 1 with rows to compute, or too large
+                          ((N + 256) * D * element size must stay below 2^31 for
+                          N = Nq and N = Nk: one head is addressed with 32-bit
+                          offsets) */
   FA_ERR_HEAD_DIM = 3, /* D not in {64, 128} */
   FA_ERR_DTYPE = 4,    /* unknown dtype code */
   FA_ERR_ALIGN = 5,    /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */

@@ -59,6 +59,10 @@ def call(q=Q, k=K, v=V, o=O, lse=L, B=2, H=4, Nq=128, Nk=128, D=64, causal=1, dt
     (dict(o=Q), 6), (dict(o=K + 64), 6), (dict(lse=V + 1024), 6), (dict(lse=O + 16), 6),
     (dict(B=1 << 40, H=1 << 40), 2), (dict(Nq=1 << 40), 2), (dict(Nk=1 << 40), 2),
     (dict(B=1 << 20, H=1 << 12, Nq=1 << 12), 2),
+    # one head's K or Q slice (plus 256 rows of slack) reaching 2^31 bytes:
+    # past the kernels' 32-bit offsets
+    (dict(B=1, H=1, Nq=16, Nk=(1 << 23) - 256, D=128, dtype=2), 2),
+    (dict(B=1, H=1, Nq=(1 << 22) - 256, Nk=16, D=128, dtype=0), 2),
 ])
 def test_validation_codes(kw, code):
     assert call(**kw) == code
