@@ -196,6 +196,26 @@ __device__ __forceinline__ void issue_tile16(const u16* Kh, const u16* Vh, int k
   }
 }
 
+// K operand of score MFMA i (block n = i / (D/16), step kk = i % (D/16)):
+// row 32n + l32, chunk 2kk + hf of the tile.
+template <int D>
+__device__ __forceinline__ u32x4 ks_operand(const unsigned char* ks, const Wave16& w, int i) {
+  const int n = i / (D / 16), kk = i % (D / 16);
+  return *(const u32x4*)(ks + w.kb[kk & 1] + n * 64 * D + (kk >> 1) * 1024);
+}
+
+// V^T operand of PV MFMA i (output block dt = i / 4, keys 32n + 16hh with
+// n = (i / 2) % 2, hh = i % 2), from two transposing 64-bit reads.
+template <int D>
+__device__ __forceinline__ u32x4 vt_operand(const unsigned char* vs, const Wave16& w, int i) {
+  const int dt = i >> 2, n = (i >> 1) & 1, hh = i & 1;
+  const int off = (2 * n + hh) * (32 * D) + dt * 1024;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + w.vb[0] + off));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + w.vb[1] + off));
+  const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+}
+
 // One K/V tile of the 16-bit kernel: wait for tile j (stage `src`), then
 // start the loads of tile j+3 into `dst` (the stage of tile j-1, which every
 // wave has finished with), then, if the wave needs tile j, run
@@ -223,15 +243,18 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
   if (k0 < w.wkend) {
     const unsigned char* ks = src;
     const unsigned char* vs = src + TILEB;
-    f32x16 s[2];
+    // S^T = K Q^T.  The K operands are read kPre MFMAs ahead of their use
+    // (LDS latency, not bandwidth, bounds these reads).
+    constexpr int NQK = 2 * NKK, kPre = NKK;
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    u32x4 ka[NQK];
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      s[n] = f32x16{};
+    for (int i = 0; i < kPre; ++i) ka[i] = ks_operand<D>(ks, w, i);
+    __builtin_amdgcn_sched_barrier(0);  // keep the early reads early
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const u32x4 a = *(const u32x4*)(ks + w.kb[kk & 1] + n * 64 * D + (kk >> 1) * 1024);
-        s[n] = mfma_32x32x16<DT>(a, qf[kk], s[n]);
-      }
+    for (int i = 0; i < NQK; ++i) {
+      if (i + kPre < NQK) ka[i + kPre] = ks_operand<D>(ks, w, i + kPre);
+      s[i / NKK] = mfma_32x32x16<DT>(ka[i], qf[i % NKK], s[i / NKK]);
     }
     // Mask (diagonal and tail tiles only): key = k0 + 4*hf + off(n, r).
     if (k0 + BC - 1 > w.wklim) {
@@ -275,19 +298,17 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
           ls1 += p1;
         }
     l += ls0 + ls1;
+    // O^T += V^T P^T, V^T operands read vPre MFMAs ahead.
+    constexpr int NPV = 4 * NDT, vPre = 4;
+    u32x4 va[NPV];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+    for (int i = 0; i < vPre; ++i) va[i] = vt_operand<D>(vs, w, i);
+    __builtin_amdgcn_sched_barrier(0);  // keep the early reads early
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int off = (2 * n + hh) * (32 * D) + dt * 1024;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + w.vb[0] + off));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + w.vb[1] + off));
-          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-          const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
-          oacc[dt] = mfma_32x32x16<DT>(a, pf[n][hh], oacc[dt]);
-        }
+    for (int i = 0; i < NPV; ++i) {
+      if (i + vPre < NPV) va[i + vPre] = vt_operand<D>(vs, w, i + vPre);
+      oacc[i >> 2] = mfma_32x32x16<DT>(va[i], pf[(i >> 1) & 1][i & 1], oacc[i >> 2]);
+    }
   }
 }
 
