@@ -52,23 +52,35 @@ def kernel_tag(w: workloads.Workload) -> str:
     return f"fa_fwd_16_{w.dtype}_d{w.D}_{'causal' if w.causal else 'noncausal'}"
 
 
+KERNEL_SOURCE = os.path.join(ROOT, "exact_tiled_attention_15_amd", "csrc", "fa_kernels.hip")
+
+
+def kernel_code_sha256(path: str = KERNEL_SOURCE) -> str:
+    """SHA-256 of the kernel source with // comments and blank lines removed:
+    it names the code the counters were taken on, and survives comment edits."""
+    import hashlib
+
+    lines = []
+    for line in open(path, encoding="utf-8"):
+        code = line.split("//", 1)[0].rstrip()
+        if code:
+            lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def measured_traffic(w: workloads.Workload):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     summary of this kernel and workload, or None when there is none or the
-    kernel source has changed since the counters were taken."""
-    import hashlib
-
+    kernel code has changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"{kernel_tag(w)}__{w.name}__hbm_traffic_and_counters.md")
-    src = os.path.join(ROOT, "exact_tiled_attention_15_amd", "csrc", "fa_kernels.hip")
     if not os.path.exists(path):
         return None
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     fields = {}
     for line in open(path):
-        if ":" in line and line.split(":")[0] in ("kernel_source_sha256", "traffic_bytes_per_launch"):
+        if ":" in line and line.split(":")[0] in ("kernel_code_sha256", "traffic_bytes_per_launch"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+    if fields.get("kernel_code_sha256") != kernel_code_sha256() or "traffic_bytes_per_launch" not in fields:
         return None
     return int(fields["traffic_bytes_per_launch"])
 

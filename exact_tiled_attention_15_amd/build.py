@@ -18,7 +18,9 @@ ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+# The kernels never need NaN-preserving max/min (no input-quieting
+# v_max x, x before each v_max of an MFMA result).
+FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}", "-fno-honor-nans",
          "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 
 

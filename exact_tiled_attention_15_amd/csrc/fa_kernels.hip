@@ -9,10 +9,11 @@
 // K/V tiles streamed through it) and the causal tile skipping of "Python
 // Attention Mechanisms Explained" (Causal Masking and Incremental Decoding).
 //
-// Work decomposition: one workgroup of 4 waves per (batch*head, Q tile of
-// 128 rows); each wave owns 32 query rows.  K/V tiles of 64 keys are
-// streamed from HBM through registers into a double-buffered LDS stage (one
-// barrier per tile).
+// Work decomposition: one workgroup per (batch*head, Q tile); each wave owns
+// 32 query rows.  16-bit kernel: 8 waves (256 rows), K/V tiles of 64 keys
+// loaded straight from HBM into a 4-stage LDS ring (one barrier per tile).
+// fp32 kernel: 4 waves (128 rows), K/V staged through registers into a
+// double-buffered LDS stage.
 //
 // Data layout inside a wave (16-bit types): the score tile is computed
 // transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_{bf16,f16}: K (from LDS)
@@ -152,47 +153,62 @@ struct Wave16 {
   int vb[2];  // LDS byte offsets of this lane's transposing V-operand reads (q = 0 / 1)
 };
 
-// 16-bit kernel shape: a workgroup of 8 waves owns 256 query rows (32 per
-// wave), streams 64-key K/V tiles through a 4-stage LDS ring (three tiles
+// 16-bit kernel shape: a workgroup of kWaves16 waves owns 32 query rows per
+// wave, streams 64-key K/V tiles through a 4-stage LDS ring (three tiles
 // in flight while one is consumed).
-constexpr int kThreads16 = 512;
-constexpr int kBR16 = 256;
+#ifndef FA_WAVES16
+#define FA_WAVES16 8
+#endif
+constexpr int kWaves16 = FA_WAVES16;  // waves per workgroup
+constexpr int kThreads16 = 64 * kWaves16;
+constexpr int kBR16 = 32 * kWaves16;  // query rows per workgroup
 constexpr int kStages = 4;
 
-// Wait until this wave's loads of tile j have landed (at most `ahead` later
-// tiles, NV loads each, may still be in flight), then meet the other waves:
-// afterwards every wave's share of tile j is in LDS and every wave has
-// finished reading tile j-1.  s_waitcnt needs an immediate, hence the switch.
-template <int NV>
-__device__ __forceinline__ void wait_tile_and_barrier(int ahead) {
-  constexpr int kBase = 0xF70;  // expcnt and lgkmcnt fields at "no wait"; lgkmcnt set below
+// Wait until this wave's loads of tile j have landed (the `later` loads this
+// wave issued for later tiles may still be in flight), then meet the other
+// waves: afterwards every wave's share of tile j is in LDS and every wave
+// has finished reading the tile before.  s_waitcnt needs an immediate,
+// hence the switch (`later` is wave-uniform and even).
+__device__ __forceinline__ void wait_tile_and_barrier(int later) {
+  constexpr int kLgkm0 = 0x070;  // expcnt: no wait, lgkmcnt(0), vmcnt(0) (low bits)
   asm volatile("" ::: "memory");
-  if (ahead >= 2) {
-    __builtin_amdgcn_s_waitcnt((kBase & ~0xF00) | (2 * NV));  // vmcnt(2 NV) lgkmcnt(0)
-  } else if (ahead == 1) {
-    __builtin_amdgcn_s_waitcnt((kBase & ~0xF00) | NV);        // vmcnt(NV) lgkmcnt(0)
-  } else {
-    __builtin_amdgcn_s_waitcnt(kBase & ~0xF00);               // vmcnt(0) lgkmcnt(0)
+  switch (later) {
+    case 8: __builtin_amdgcn_s_waitcnt(kLgkm0 | 8); break;
+    case 6: __builtin_amdgcn_s_waitcnt(kLgkm0 | 6); break;
+    case 4: __builtin_amdgcn_s_waitcnt(kLgkm0 | 4); break;
+    case 2: __builtin_amdgcn_s_waitcnt(kLgkm0 | 2); break;
+    default: __builtin_amdgcn_s_waitcnt(kLgkm0); break;
   }
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// Direct-to-LDS loads of K/V tile t into `dst` (this wave's NI 1 KB pieces of
-// the K tile and of the V tile).
+// Number of 1 KB direct-to-LDS loads (K and V together) that wave `wave`
+// issues per tile: the 1 KB pieces G = wave, wave + waves, ... of each
+// tensor's tile.
+template <int D>
+__device__ __forceinline__ int loads_per_tile(int wave) {
+  constexpr int NG = 64 * D * 2 / 1024;
+  return 2 * ((NG - wave + kWaves16 - 1) / kWaves16);
+}
+
+// Direct-to-LDS loads of K/V tile t into `dst`: this wave's 1 KB pieces
+// G = wave, wave + waves, ... of the K tile and of the V tile.
 template <int D>
 __device__ __forceinline__ void issue_tile16(const u16* Kh, const u16* Vh, int kbytes, int t,
                                              unsigned char* dst, const Wave16& w) {
   constexpr int TILEB = 64 * D * 2;
-  constexpr int NI = TILEB / 1024 / (kThreads16 / 64);
+  constexpr int NG = TILEB / 1024;
   const auto rk = make_rsrc(Kh, kbytes);
   const auto rv = make_rsrc(Vh, kbytes);
-  unsigned char* d0 = dst + w.wave * NI * 1024;
 #pragma unroll
-  for (int I = 0; I < NI; ++I) {
-    const int go = dma_src_off<D>(w.wave * NI + I, w.lane);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(d0 + I * 1024), 16, go, t * TILEB, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(d0 + TILEB + I * 1024), 16, go, t * TILEB, 0, 0);
+  for (int I = 0; I < (NG + kWaves16 - 1) / kWaves16; ++I) {
+    const int G = w.wave + kWaves16 * I;
+    if (G < NG) {
+      const int go = dma_src_off<D>(G, w.lane);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst + G * 1024), 16, go, t * TILEB, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst + TILEB + G * 1024), 16, go, t * TILEB, 0, 0);
+    }
   }
 }
 
@@ -229,14 +245,13 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
                                        f32x16 (&oacc)[D / 32], float& mref, float& l, float sl2) {
   constexpr int BC = 64;
   constexpr int TILEB = BC * D * 2;
-  constexpr int NV = 2 * (TILEB / 1024 / (kThreads16 / 64));  // loads per wave per tile
   constexpr int NKK = D / 16, NDT = D / 32;
   // mref is raised only when a tile's row max exceeds it by more than kTau
   // (log2 units), so P = exp2(t - mref) stays below 2^kTau; O and l always
   // share mref, so O / l and mref + log2(l) are exact whatever mref is.
   constexpr float kTau = 8.0f;
 
-  wait_tile_and_barrier<NV>(min(2, nt - 1 - j));
+  wait_tile_and_barrier(loads_per_tile<D>(w.wave) * min(2, nt - 1 - j));
   if (j + kStages - 1 < nt) issue_tile16<D>(Kh, Vh, kbytes, j + kStages - 1, dst, w);
 
   const int k0 = j * BC;
@@ -256,6 +271,13 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
       if (i + kPre < NQK) ka[i + kPre] = ks_operand<D>(ks, w, i + kPre);
       s[i / NKK] = mfma_32x32x16<DT>(ka[i], qf[i % NKK], s[i / NKK]);
     }
+    // The first V^T operands of the PV are read now, so that the softmax
+    // hides their latency (at D = 64 the PV is short, and fewer pay off).
+    constexpr int NPV = 4 * NDT, vPre = D == 128 ? 8 : 4;
+    u32x4 va[NPV];
+#pragma unroll
+    for (int i = 0; i < vPre; ++i) va[i] = vt_operand<D>(vs, w, i);
+    __builtin_amdgcn_sched_barrier(0);
     // Mask (diagonal and tail tiles only): key = k0 + 4*hf + off(n, r).
     if (k0 + BC - 1 > w.wklim) {
       const int lim = w.klim - (k0 + 4 * w.hf);
@@ -299,11 +321,6 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
         }
     l += ls0 + ls1;
     // O^T += V^T P^T, V^T operands read vPre MFMAs ahead.
-    constexpr int NPV = 4 * NDT, vPre = 4;
-    u32x4 va[NPV];
-#pragma unroll
-    for (int i = 0; i < vPre; ++i) va[i] = vt_operand<D>(vs, w, i);
-    __builtin_amdgcn_sched_barrier(0);  // keep the early reads early
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       if (i + vPre < NPV) va[i + vPre] = vt_operand<D>(vs, w, i + vPre);
@@ -324,7 +341,6 @@ __global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict
   constexpr int TILEB = BC * ROWB;        // bytes per K (or V) tile
   constexpr int NKK = D / 16;             // MFMA steps over the head dimension
   constexpr int NDT = D / 32;             // 32-wide output column tiles
-  static_assert(TILEB / 1024 % (kThreads16 / 64) == 0, "tile shape");
 
   // The LDS ring: tile j lives in stage j % 4 (a K tile followed by a V tile).
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * TILEB];

@@ -53,6 +53,28 @@ def test_parity_small_grid(dt, D, causal, Nq, Nk):
     compare_full(w, cpu, o, l, "grid")
 
 
+@pytest.mark.parametrize("dt,D,causal", [("bf16", 128, True), ("bf16", 128, False), ("fp16", 64, True),
+                                         ("fp16", 128, False), ("fp32", 64, True)])
+def test_parity_reference_moves(dt, D, causal):
+    # Keys whose norm grows along the sequence (K row j scaled by
+    # 1 + a j/Nk, Q by a): each row's running max climbs tile after tile, so
+    # the softmax reference moves mid-stream (about one move per row for
+    # a = 3) and every rescale path of the kernel (l and O, with PV work in
+    # flight) is exercised.  fp32 takes a = 2 (|LSE| up to ~22 rather than
+    # ~44): its absolute LSE tolerance of 1e-5 is a few fp32 ulps of such
+    # values, below what the rounding of larger scores allows.
+    w = workloads.Workload(f"moves_{dt}_d{D}_{'c' if causal else 'n'}", 1, 2, 700, 700, D, dt, causal, 4242 + D)
+    q64, k64, v64 = workloads.draw_float64(w)
+    a = 2.0 if dt == "fp32" else 3.0
+    ramp = 1.0 + a * np.arange(w.Nk, dtype=np.float64) / w.Nk
+    q64 = q64 * a
+    k64 = k64 * ramp[None, None, :, None]
+    cpu = tuple(workloads.round_to_dtype(x, dt) for x in (q64, k64, v64))
+    log(f"case {w.name} (growing key norms)")
+    o, l = run_gpu(*to_gpu(cpu), causal)
+    compare_full(w, cpu, o, l, "moves")
+
+
 @pytest.mark.parametrize("name", ["c3_bf16_causal_b4h16n4096d128",
                                   "c4_bf16_causal_b1h32n16384d128_q4",
                                   "c5_fp16_cross_b8h32q512k8192d64",
