@@ -149,8 +149,11 @@ struct Wave16 {
   int wkend;  // keys [0, wkend) are needed by the wave
   int wklim;  // smallest last-visible key over the wave's rows
   int klim;   // last key this lane's row may see
-  int kb[2];  // LDS byte offsets of this lane's K-operand reads (even / odd kk)
-  int vb[2];  // LDS byte offsets of this lane's transposing V-operand reads (q = 0 / 1)
+  // LDS byte offsets of this lane's K-operand reads (even / odd kk) and of
+  // its transposing V-operand reads (q = 0 / 1), each plain (lo) and plus
+  // 64 KB (hi); see ks_operand.
+  int kb_lo[2], kb_hi[2];
+  int vb_lo[2], vb_hi[2];
 };
 
 // 16-bit kernel shape: a workgroup of kWaves16 waves owns 32 query rows per
@@ -164,20 +167,21 @@ constexpr int kThreads16 = 64 * kWaves16;
 constexpr int kBR16 = 32 * kWaves16;  // query rows per workgroup
 constexpr int kStages = 4;
 
-// Wait until this wave's loads of tile j have landed (the `later` loads this
-// wave issued for later tiles may still be in flight), then meet the other
-// waves: afterwards every wave's share of tile j is in LDS and every wave
-// has finished reading the tile before.  s_waitcnt needs an immediate,
+// Wait until at most `later` of this wave's direct-to-LDS loads and LGKM
+// of its LDS operations are still in flight (each counter completes in
+// issue order), then meet the other waves.  s_waitcnt takes an immediate,
 // hence the switch (`later` is wave-uniform and even).
+template <int LGKM = 0>
 __device__ __forceinline__ void wait_tile_and_barrier(int later) {
-  constexpr int kLgkm0 = 0x070;  // expcnt: no wait, lgkmcnt(0), vmcnt(0) (low bits)
+  static_assert(LGKM >= 0 && LGKM < 16, "lgkmcnt field");
+  constexpr int kBase = 0x070 | (LGKM << 8);  // expcnt: no wait; lgkmcnt(LGKM); vmcnt in the low bits
   asm volatile("" ::: "memory");
   switch (later) {
-    case 8: __builtin_amdgcn_s_waitcnt(kLgkm0 | 8); break;
-    case 6: __builtin_amdgcn_s_waitcnt(kLgkm0 | 6); break;
-    case 4: __builtin_amdgcn_s_waitcnt(kLgkm0 | 4); break;
-    case 2: __builtin_amdgcn_s_waitcnt(kLgkm0 | 2); break;
-    default: __builtin_amdgcn_s_waitcnt(kLgkm0); break;
+    case 8: __builtin_amdgcn_s_waitcnt(kBase | 8); break;
+    case 6: __builtin_amdgcn_s_waitcnt(kBase | 6); break;
+    case 4: __builtin_amdgcn_s_waitcnt(kBase | 4); break;
+    case 2: __builtin_amdgcn_s_waitcnt(kBase | 2); break;
+    default: __builtin_amdgcn_s_waitcnt(kBase); break;
   }
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -212,12 +216,28 @@ __device__ __forceinline__ void issue_tile16(const u16* Kh, const u16* Vh, int k
   }
 }
 
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+// LDS operand reads.  A ring stage may lie above 64 KB, past the reach of
+// the ds_read immediate offset, so each lane's offsets exist twice, plain
+// (lo) and plus 64 KB (hi), both kept opaque to the compiler; a read takes
+// the copy that matches its stage's 64 KB window (`lds_bias`, a link-time
+// constant), so that it is one base register plus an immediate below 64 KB,
+// and its pointer still derives from the stage array, so the compiler still
+// knows which array it reads (and that the loads in flight write others).
+__device__ __forceinline__ unsigned lds_bias(const unsigned char* p) {
+  return (unsigned)(uintptr_t)(const lds_u8*)p & 0xFFFF0000u;
+}
+
 // K operand of score MFMA i (block n = i / (D/16), step kk = i % (D/16)):
 // row 32n + l32, chunk 2kk + hf of the tile.
 template <int D>
 __device__ __forceinline__ u32x4 ks_operand(const unsigned char* ks, const Wave16& w, int i) {
   const int n = i / (D / 16), kk = i % (D / 16);
-  return *(const u32x4*)(ks + w.kb[kk & 1] + n * 64 * D + (kk >> 1) * 1024);
+  const unsigned bias = lds_bias(ks);
+  const int base = bias ? w.kb_hi[kk & 1] : w.kb_lo[kk & 1];
+  return *(const lds_u32x4*)((const lds_u8*)ks + (base + (n * 64 * D + (kk >> 1) * 1024 - (int)bias)));
 }
 
 // V^T operand of PV MFMA i (output block dt = i / 4, keys 32n + 16hh with
@@ -225,19 +245,25 @@ __device__ __forceinline__ u32x4 ks_operand(const unsigned char* ks, const Wave1
 template <int D>
 __device__ __forceinline__ u32x4 vt_operand(const unsigned char* vs, const Wave16& w, int i) {
   const int dt = i >> 2, n = (i >> 1) & 1, hh = i & 1;
-  const int off = (2 * n + hh) * (32 * D) + dt * 1024;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + w.vb[0] + off));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + w.vb[1] + off));
+  const unsigned bias = lds_bias(vs);
+  const int off = (2 * n + hh) * (32 * D) + dt * 1024 - (int)bias;
+  const int b0 = bias ? w.vb_hi[0] : w.vb_lo[0], b1 = bias ? w.vb_hi[1] : w.vb_lo[1];
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((const lds_u8*)vs + (b0 + off)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((const lds_u8*)vs + (b1 + off)));
   const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
   return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
 }
 
-// One K/V tile of the 16-bit kernel: wait for tile j (stage `src`), then
-// start the loads of tile j+3 into `dst` (the stage of tile j-1, which every
-// wave has finished with), then, if the wave needs tile j, run
-// S^T = K Q^T, the mask, the online-softmax update and O^T += V^T P^T.
-// `src` and `dst` are distinct __shared__ arrays, so the compiler knows the
-// loads in flight never alias the operand reads.
+// One K/V tile of the 16-bit kernel (stage `src`).  Tile j is complete in
+// LDS since the previous tile's barrier (each barrier waits for the tile
+// after its own), so the wave first reads the first K operands of its score
+// MFMAs and only then waits for tile j+1 and meets the other waves, which
+// hides the reads' latency behind the barrier.  Then it starts the loads of
+// tile j+3 into `dst` (the stage of tile j-1, which every wave has finished
+// with) and, if it needs tile j, runs S^T = K Q^T, the mask, the
+// online-softmax update and O^T += V^T P^T.  `src` and `dst` are distinct
+// __shared__ arrays, so the compiler knows the loads in flight never alias
+// the operand reads.
 template <int DT, int D, bool CAUSAL>
 __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes, int j, int nt,
                                        const unsigned char* src, unsigned char* dst,
@@ -250,22 +276,26 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
   // (log2 units), so P = exp2(t - mref) stays below 2^kTau; O and l always
   // share mref, so O / l and mref + log2(l) are exact whatever mref is.
   constexpr float kTau = 8.0f;
-
-  wait_tile_and_barrier(loads_per_tile<D>(w.wave) * min(2, nt - 1 - j));
-  if (j + kStages - 1 < nt) issue_tile16<D>(Kh, Vh, kbytes, j + kStages - 1, dst, w);
+  // S^T = K Q^T.  The K operands are read kPre MFMAs ahead of their use
+  // (LDS latency, not bandwidth, bounds these reads).
+  constexpr int NQK = 2 * NKK, kPre = NKK;
 
   const int k0 = j * BC;
-  if (k0 < w.wkend) {
-    const unsigned char* ks = src;
-    const unsigned char* vs = src + TILEB;
-    // S^T = K Q^T.  The K operands are read kPre MFMAs ahead of their use
-    // (LDS latency, not bandwidth, bounds these reads).
-    constexpr int NQK = 2 * NKK, kPre = NKK;
-    f32x16 s[2] = {f32x16{}, f32x16{}};
-    u32x4 ka[NQK];
+  const bool mine = k0 < w.wkend;
+  const unsigned char* ks = src;
+  const unsigned char* vs = src + TILEB;
+  u32x4 ka[NQK];
+  if (mine) {
 #pragma unroll
     for (int i = 0; i < kPre; ++i) ka[i] = ks_operand<D>(ks, w, i);
-    __builtin_amdgcn_sched_barrier(0);  // keep the early reads early
+  }
+  // Loads complete in order: only tile j+2's may still be in flight; the
+  // kPre reads just issued may be too (older LDS reads have completed).
+  wait_tile_and_barrier<kPre>(j + 2 < nt ? loads_per_tile<D>(w.wave) : 0);
+  if (j + kStages - 1 < nt) issue_tile16<D>(Kh, Vh, kbytes, j + kStages - 1, dst, w);
+
+  if (mine) {
+    f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       if (i + kPre < NQK) ka[i + kPre] = ks_operand<D>(ks, w, i + kPre);
@@ -293,9 +323,12 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
     for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int r = (n == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[n][r]);
-    mx = pair_max(mx) * sl2;
+    // Half-row max in the scaled log2 domain: a row's max exceeds mref + kTau
+    // exactly when one of its halves does, so the lane-pair exchange is only
+    // needed on the (rare) path that moves the reference.
+    mx *= sl2;
     if (__builtin_amdgcn_ballot_w64(mx > mref + kTau)) {
-      const float mnew = fmaxf(mref, mx);
+      const float mnew = fmaxf(mref, pair_max(mx));
       const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
       l *= alpha;
 #pragma unroll
@@ -376,14 +409,21 @@ __global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
     const int c = 2 * par + w.hf;
-    w.kb[par] = (w.l32 >> 4) * (32 * D) + c * 256 + (((w.l32 & 15) ^ (c << 2)) << 4);
+    w.kb_lo[par] = (w.l32 >> 4) * (32 * D) + c * 256 + (((w.l32 & 15) ^ (c << 2)) << 4);
+    w.kb_hi[par] = w.kb_lo[par] + 65536;
+    asm volatile("" : "+v"(w.kb_lo[par]));
+    asm volatile("" : "+v"(w.kb_hi[par]));
   }
   {
     const int vi = w.l32 & 15, vg = w.l32 >> 4;
     const int c = 2 * vg + ((vi & 3) >> 1);  // chunk within the 4-chunk (64-column) block
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      w.vb[q] = c * 256 + (((8 * q + 4 * w.hf + (vi >> 2)) ^ (c << 2)) << 4) + 8 * (vi & 1);
+    for (int q = 0; q < 2; ++q) {
+      w.vb_lo[q] = c * 256 + (((8 * q + 4 * w.hf + (vi >> 2)) ^ (c << 2)) << 4) + 8 * (vi & 1);
+      w.vb_hi[q] = w.vb_lo[q] + 65536;
+      asm volatile("" : "+v"(w.vb_lo[q]));
+      asm volatile("" : "+v"(w.vb_hi[q]));
+    }
   }
 
   // Q fragment (B operand of S^T): lane holds Q[myq][16*kk + 8*hf .. +7];
@@ -407,6 +447,8 @@ __global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
 
+  // Tile 0 must be complete before tile16(0) reads its first K operands.
+  wait_tile_and_barrier(nt > 2 ? loads_per_tile<D>(w.wave) : 0);
   for (int j = 0; j < nt; j += kStages) {
     tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j, nt, stage0, stage3, w, qf, oacc, mref, l, sl2);
     if (j + 1 < nt) tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 1, nt, stage1, stage0, w, qf, oacc, mref, l, sl2);
