@@ -12,7 +12,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fa_fwd", "fa_status_str", "forward", "load_library", "LIB_PATH",
+__all__ = ["fa_fwd", "fa_fwd_scaled", "fa_status_str", "forward", "load_library", "LIB_PATH",
            "FA_DTYPE_FP32", "FA_DTYPE_FP16", "FA_DTYPE_BF16", "FA_OK", "FaError",
            "EXPORTED_SYMBOLS"]
 
@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_DTYPE_FP32, FA_DTYPE_FP16, FA_DTYPE_BF16 = 0, 1, 2
 FA_OK = 0
-EXPORTED_SYMBOLS = ("fa_fwd", "fa_status_str")
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_scaled", "fa_status_str")
 
 _lib = None
 
@@ -45,6 +45,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fa_fwd.restype = ctypes.c_int
     lib.fa_fwd.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int64] * 5 + \
         [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_fwd_scaled.restype = ctypes.c_int
+    lib.fa_fwd_scaled.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + \
+        [ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [ctypes.c_int]
     if path is None:
@@ -62,6 +65,13 @@ def fa_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int, Nk
     return load_library().fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, D, int(causal), int(dtype), stream)
 
 
+def fa_fwd_scaled(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int, Nk: int,
+                  D: int, softmax_scale: float, causal: int, dtype: int, stream: int | None) -> int:
+    """Call the C ``fa_fwd_scaled`` with raw device addresses; returns the status code."""
+    return load_library().fa_fwd_scaled(q, k, v, o, lse, B, H, Nq, Nk, D, float(softmax_scale),
+                                        int(causal), int(dtype), stream)
+
+
 def _dtype_code(t) -> int:
     import torch
 
@@ -72,14 +82,14 @@ def _dtype_code(t) -> int:
     return codes[t.dtype]
 
 
-def forward(q, k, v, causal: bool = False, out=None, lse=None, stream=None):
+def forward(q, k, v, causal: bool = False, out=None, lse=None, stream=None, softmax_scale=None):
     """Exact attention forward on the GPU.
 
     q: (B, H, Nq, D), k/v: (B, H, Nk, D), contiguous device tensors of one
-    dtype (float32, float16 or bfloat16), D in {64, 128}.  Returns
+    dtype (float32, float16 or bfloat16), D in {32, 64, 128}.  Returns
     (O (B, H, Nq, D) in the input dtype, LSE (B, H, Nq) float32).  ``out`` and
     ``lse`` may be given preallocated; ``stream`` defaults to torch's current
-    stream.
+    stream; ``softmax_scale`` (default 1/sqrt(D)) multiplies q.k.
     """
     import torch
 
@@ -110,8 +120,12 @@ def forward(q, k, v, causal: bool = False, out=None, lse=None, stream=None):
         with torch.cuda.device(q.device):
             stream = torch.cuda.current_stream().cuda_stream
     with torch.cuda.device(q.device):
-        rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                    B, H, Nq, Nk, D, bool(causal), _dtype_code(q), stream)
+        if softmax_scale is None:
+            rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, H, Nq, Nk, D, bool(causal), _dtype_code(q), stream)
+        else:
+            rc = fa_fwd_scaled(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                               B, H, Nq, Nk, D, softmax_scale, bool(causal), _dtype_code(q), stream)
     if rc != FA_OK:
         raise FaError(rc)
     return out, lse

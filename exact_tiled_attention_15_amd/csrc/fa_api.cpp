@@ -1,5 +1,6 @@
 // C ABI of the exact tiled attention forward pass: argument validation
 // (before any HIP call) and dispatch to the gfx950 kernels.
+#include <math.h>
 #include <stdint.h>
 
 #include "../../include/fa.h"
@@ -25,7 +26,7 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int dtype, bool* empty) {
   if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || D < 0) return FA_ERR_SHAPE;
-  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
   int64_t BH, rows, qel, kel;
   if (!mul_ok(B, H, &BH) || !mul_ok(BH, Nq, &rows) || !mul_ok(rows, D, &qel)) return FA_ERR_SHAPE;
   *empty = (rows == 0);
@@ -56,14 +57,21 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   return FA_OK;
 }
 
-}  // namespace
+// The kernels work in the log2 domain with scale * log2(e) as one fp32
+// factor; it must be a normal, finite, positive float.
+bool scale_ok(double scale) {
+  if (!(scale > 0.0) || !isfinite(scale)) return false;
+  const float sl2 = (float)(scale * 1.4426950408889634074);
+  return isnormal(sl2) && isfinite(sl2);
+}
 
-extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
-                      int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal, int dtype,
-                      void* stream) {
+int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+        int64_t Nq, int64_t Nk, int64_t D, const double* scale, int causal, int dtype, void* stream) {
   bool empty = false;
   const int st = validate(q, k, v, o, lse, B, H, Nq, Nk, D, dtype, &empty);
-  if (st != FA_OK || empty) return st;
+  if (st != FA_OK) return st;
+  if (scale && !scale_ok(*scale)) return FA_ERR_SCALE;
+  if (empty) return FA_OK;
   FaLaunch a;
   a.q = q;
   a.k = k;
@@ -76,8 +84,23 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   a.D = (int)D;
   a.causal = causal != 0;
   a.dtype = dtype;
+  a.scale = scale ? *scale : 1.0 / sqrt((double)D);
   a.stream = stream;
   return fa_launch_fwd(a) == 0 ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                      int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal, int dtype,
+                      void* stream) {
+  return fwd(q, k, v, o, lse, B, H, Nq, Nk, D, nullptr, causal, dtype, stream);
+}
+
+extern "C" int fa_fwd_scaled(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                             double softmax_scale, int causal, int dtype, void* stream) {
+  return fwd(q, k, v, o, lse, B, H, Nq, Nk, D, &softmax_scale, causal, dtype, stream);
 }
 
 extern "C" const char* fa_status_str(int status) {
@@ -85,11 +108,12 @@ extern "C" const char* fa_status_str(int status) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative, empty-key or too large shape";
-    case FA_ERR_HEAD_DIM: return "FA_ERR_HEAD_DIM: head dimension must be 64 or 128";
+    case FA_ERR_HEAD_DIM: return "FA_ERR_HEAD_DIM: head dimension must be 32, 64 or 128";
     case FA_ERR_DTYPE: return "FA_ERR_DTYPE: unknown dtype code";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: q/k/v/o must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or the other output";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch error";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: softmax_scale must be a finite number > 0";
     default: return "unknown fa_status code";
   }
 }

@@ -16,6 +16,7 @@ struct FaLaunch {
   int D;
   int causal;
   int dtype;  // fa_dtype
+  double scale;  // softmax scale applied to q.k (validated: finite, > 0)
   void* stream;
 };
 

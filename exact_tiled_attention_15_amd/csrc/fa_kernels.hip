@@ -23,12 +23,14 @@
 // in a lane pair (l, l^32), so the row max needs a single exchange across
 // the half-waves and the row sum needs none until the end.  P^T is fed
 // straight from those registers (rounded to bf16/fp16) as the B operand of
-// O^T = V^T P^T, whose A operand is read from a transposed, key-permuted
-// copy of the V tile in LDS.  O^T (fp32) stays in registers.  The fp32 path
+// O^T = V^T P^T, whose A operand comes from the row-major (swizzled) V tile
+// in LDS through transposing reads (ds_read_b64_tr_b16).  O^T (fp32) stays
+// in registers.  The fp32 path
 // uses v_mfma_f32_32x32x2_f32 with the same accumulator layout, P stays
 // fp32, and V stays row-major in LDS.
 //
-// Softmax runs in the log2 domain: t = s * (log2(e)/sqrt(D)), p = exp2(t - m)
+// Softmax runs in the log2 domain: t = s * scale * log2(e) (scale = 1/sqrt(D)
+// unless given), p = exp2(t - m)
 // on v_exp_f32; LSE = (m + log2 l) * ln 2 at the end.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -104,7 +106,7 @@ __device__ __forceinline__ void tile_of_block(int nqt, int BH, int& bh, int& qt)
 }
 
 // ---------------------------------------------------------------------------
-// 16-bit kernel (bf16 / fp16), D in {64, 128}, 64-key tiles.
+// 16-bit kernel (bf16 / fp16), D in {32, 64, 128}, 64-key tiles.
 // ---------------------------------------------------------------------------
 // Buffer resources: 32-bit byte offsets from a per-head base, with the
 // hardware range check (loads past num_records return 0, stores past it are
@@ -479,7 +481,7 @@ __global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// fp32 kernel, D in {64, 128}, v_mfma_f32_32x32x2_f32.
+// fp32 kernel, D in {32, 64, 128}, v_mfma_f32_32x32x2_f32.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fa_fwd_32(const float* __restrict__ Qg,
@@ -488,7 +490,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_32(const float* __restrict
                                                          float* __restrict__ Og,
                                                          float* __restrict__ Lg, int BH, int Nq,
                                                          int Nk, int nqt, float sl2) {
-  constexpr int BC = (D == 64) ? 64 : 32;
+  constexpr int BC = (D <= 64) ? 64 : 32;
   constexpr int NSUB = BC / 32;
   constexpr int STR = D + 4;      // row stride (floats) of K and V in LDS
   constexpr int ST = BC * STR;    // floats per K (or V) stage
@@ -659,15 +661,17 @@ int dispatch32(const FaLaunch& a, float sl2) {
 }  // namespace
 
 int fa_launch_fwd(const FaLaunch& a) {
-  // log2(e)/sqrt(D), computed in double and rounded once.
-  const float sl2 = (float)(1.4426950408889634074 / __builtin_sqrt((double)a.D));
+  // scale * log2(e), computed in double and rounded once.
+  const float sl2 = (float)(a.scale * 1.4426950408889634074);
   (void)hipGetLastError();  // clear a stale error so that the check below is ours
   switch (a.dtype) {
     case kBF16:
-      return a.D == 64 ? dispatch16<kBF16, 64>(a, sl2) : dispatch16<kBF16, 128>(a, sl2);
+      return a.D == 32 ? dispatch16<kBF16, 32>(a, sl2)
+           : a.D == 64 ? dispatch16<kBF16, 64>(a, sl2) : dispatch16<kBF16, 128>(a, sl2);
     case kFP16:
-      return a.D == 64 ? dispatch16<kFP16, 64>(a, sl2) : dispatch16<kFP16, 128>(a, sl2);
+      return a.D == 32 ? dispatch16<kFP16, 32>(a, sl2)
+           : a.D == 64 ? dispatch16<kFP16, 64>(a, sl2) : dispatch16<kFP16, 128>(a, sl2);
     default:
-      return a.D == 64 ? dispatch32<64>(a, sl2) : dispatch32<128>(a, sl2);
+      return a.D == 32 ? dispatch32<32>(a, sl2) : a.D == 64 ? dispatch32<64>(a, sl2) : dispatch32<128>(a, sl2);
   }
 }

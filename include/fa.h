@@ -53,11 +53,13 @@ typedef enum {
                           ((N + 256) * D * element size must stay below 2^31 for
                           N = Nq and N = Nk: one head is addressed with 32-bit
                           offsets) */
-  FA_ERR_HEAD_DIM = 3, /* D not in {64, 128} */
+  FA_ERR_HEAD_DIM = 3, /* D not in {32, 64, 128} */
   FA_ERR_DTYPE = 4,    /* unknown dtype code */
   FA_ERR_ALIGN = 5,    /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
   FA_ERR_ALIAS = 6,    /* o or lse overlaps an input, or o overlaps lse */
-  FA_ERR_HIP = 7       /* the HIP runtime reported an error at launch */
+  FA_ERR_HIP = 7,      /* the HIP runtime reported an error at launch */
+  FA_ERR_SCALE = 8     /* softmax_scale not a finite number > 0 (or so small that
+                          softmax_scale * log2(e) is not a normal float) */
 } fa_status;
 
 /*
@@ -68,7 +70,7 @@ typedef enum {
  *   v    device pointer, [B, H, Nk, D] contiguous row-major, `dtype`
  *   o    device pointer, [B, H, Nq, D] contiguous row-major, `dtype` (output)
  *   lse  device pointer, [B, H, Nq] contiguous fp32 (output, natural log)
- *   B, H, Nq, Nk, D   sizes; D in {64, 128}.  B*H*Nq == 0 is a valid no-op
+ *   B, H, Nq, Nk, D   sizes; D in {32, 64, 128}.  B*H*Nq == 0 is a valid no-op
  *        (pointers may then be NULL); otherwise Nk >= 1.
  *   causal  0: every key is kept; non-zero: key j kept for query i iff j <= i
  *   dtype   an fa_dtype code
@@ -81,6 +83,22 @@ typedef enum {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
            int causal, int dtype, void* stream);
+
+/*
+ * fa_fwd_scaled -- fa_fwd with an explicit softmax scale: s_ij =
+ * softmax_scale * (q_i . k_j).  The pages call the library kernel with a
+ * softmax_scale argument ("Flash Attention vs Standard Attention",
+ * Implementation), set there to 1/sqrt(D); any finite softmax_scale > 0 is
+ * accepted (the kernels take the row max of the raw dot products, which
+ * commutes with a positive scale).  Scores whose scaled value overflows
+ * fp32 behave like Inf inputs.  Every other argument, the layouts, the
+ * ownership and the errors are those of fa_fwd; an invalid softmax_scale
+ * returns FA_ERR_SCALE before any HIP call.  fa_fwd(...) is
+ * fa_fwd_scaled(..., 1/sqrt(D), ...).
+ */
+int fa_fwd_scaled(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                  double softmax_scale, int causal, int dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_str(int status);

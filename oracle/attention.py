@@ -9,7 +9,9 @@ values:
 * scale = 1 / sqrt(D)  (every page divides the scores by sqrt of the head
   dimension: "Build a FlashAttention Kernel from Scratch", Step 3;
   "Building a FlashAttention-2 Forward Kernel in Pure NumPy", Step 2;
-  "Python Attention Mechanisms Explained", The Core Idea)
+  "Python Attention Mechanisms Explained", The Core Idea), unless an
+  explicit ``scale`` is given (the softmax_scale argument of the library call
+  on "Flash Attention vs Standard Attention", Implementation)
 * the key set of query i is A_i = {j : 0 <= j < Nk, and j <= i if causal}.
   The causal mask keeps the diagonal (the first page's comment on its Step 3
   mask says lower triangle including the diagonal; the printed call drops
@@ -72,15 +74,20 @@ def _rows_block(qi, kh, vh, row_idx, causal, scale):
     return o, lse
 
 
-def attention_forward(q, k, v, causal: bool, row_chunk: int = 256):
+def _scale(D, scale):
+    return 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+
+def attention_forward(q, k, v, causal: bool, row_chunk: int = 256, scale=None):
     """Exact attention over whole tensors.
 
     q: (B, H, Nq, D); k, v: (B, H, Nk, D); any real dtype (widened to float64).
+    scale: the factor applied to q.k (default 1/sqrt(D)).
     Returns (O float64 (B, H, Nq, D), LSE float64 (B, H, Nq)).
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     B, H, Nq, Nk, D = _check(q, k, v)
-    scale = 1.0 / math.sqrt(D)
+    scale = _scale(D, scale)
     O = np.empty((B, H, Nq, D))
     L = np.empty((B, H, Nq))
     for b in range(B):
@@ -94,7 +101,7 @@ def attention_forward(q, k, v, causal: bool, row_chunk: int = 256):
     return O, L
 
 
-def attention_rows(q, k, v, causal: bool, rows):
+def attention_rows(q, k, v, causal: bool, rows, scale=None):
     """Exact attention for selected query rows only.
 
     rows: iterable of (b, h, i).  Inputs may be torch tensors or arrays; only
@@ -102,7 +109,7 @@ def attention_rows(q, k, v, causal: bool, rows):
     """
     rows = [tuple(int(x) for x in r) for r in rows]
     D = q.shape[-1]
-    scale = 1.0 / math.sqrt(D)
+    scale = _scale(D, scale)
     O = np.empty((len(rows), D))
     L = np.empty(len(rows))
     by_head = {}
@@ -125,12 +132,12 @@ def attention_rows(q, k, v, causal: bool, rows):
     return O, L
 
 
-def scores_row(q, k, b: int, h: int, i: int, causal: bool):
+def scores_row(q, k, b: int, h: int, i: int, causal: bool, scale=None):
     """Scaled, masked float64 scores of one query row (masked keys -> -inf)."""
     D = q.shape[-1]
     qi = _as_f64(q[b, h, i])
     kh = _as_f64(k[b, h])
-    s = (kh @ qi) * (1.0 / math.sqrt(D))
+    s = (kh @ qi) * _scale(D, scale)
     if causal:
         s = np.where(np.arange(kh.shape[0]) <= i, s, -np.inf)
     return s

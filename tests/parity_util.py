@@ -23,7 +23,7 @@ def to_gpu(ts):
     return tuple(t.to("cuda:0").contiguous() for t in ts)
 
 
-def run_gpu(q, k, v, causal, poison=True):
+def run_gpu(q, k, v, causal, poison=True, softmax_scale=None):
     import torch
 
     import exact_tiled_attention_15_amd as fa
@@ -34,17 +34,17 @@ def run_gpu(q, k, v, causal, poison=True):
     if poison:
         out.fill_(float("nan"))
         lse.fill_(float("nan"))
-    fa.forward(q, k, v, causal, out=out, lse=lse)
+    fa.forward(q, k, v, causal, out=out, lse=lse, softmax_scale=softmax_scale)
     torch.cuda.synchronize()
     return out, lse
 
 
-def compare_full(w: workloads.Workload, inputs_cpu, o_gpu, lse_gpu, tag=""):
+def compare_full(w: workloads.Workload, inputs_cpu, o_gpu, lse_gpu, tag="", scale=None):
     o = o_gpu.float().cpu().double().numpy()
     l = lse_gpu.cpu().double().numpy()
     assert np.isfinite(o).all(), f"{tag}: non-finite O"
     assert np.isfinite(l).all(), f"{tag}: non-finite LSE"
-    O, L = oracle.attention_forward(*inputs_cpu, w.causal)
+    O, L = oracle.attention_forward(*inputs_cpu, w.causal, scale=scale)
     eo = float(np.max(np.abs(o - O)))
     el = float(np.max(np.abs(l - L)))
     to, tl = TOL[w.dtype]

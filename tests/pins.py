@@ -42,11 +42,11 @@ def _inputs(seed, B, H, Nq, Nk, D):
             r.standard_normal((B, H, Nk, D)))
 
 
-def brute_force(q, k, v, causal):
+def brute_force(q, k, v, causal, scale=None):
     """Per-element loop straight from the definition, with exact sums."""
     B, H, Nq, D = q.shape
     Nk = k.shape[2]
-    scale = 1.0 / math.sqrt(D)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
     O = np.zeros((B, H, Nq, D))
     L = np.zeros((B, H, Nq))
     for b in range(B):
@@ -83,6 +83,27 @@ def check_brute_force(impl):
                     tag = f"brute Nq={Nq} Nk={Nk} D={D} causal={causal}"
                     _close(O, Ob, 1e-12, tag + " O")
                     _close(L, Lb, 1e-12, tag + " LSE")
+
+
+def check_explicit_scale(impl_scaled):
+    """``impl_scaled(q, k, v, causal, scale)``: an explicit softmax scale
+    multiplies q.k (brute force), which is the same as scaling Q by
+    scale * sqrt(D) at the default scale."""
+    for causal in (False, True):
+        for (Nq, Nk, D) in ((3, 5, 4), (9, 2, 8), (5, 9, 1)):
+            q, k, v = _inputs(3000 + Nq + Nk + D, 1, 2, Nq, Nk, D)
+            for scale in (0.05, 0.7, 2.0):
+                O, L = impl_scaled(q, k, v, causal, scale)
+                Ob, Lb = brute_force(q, k, v, causal, scale)
+                tag = f"scale={scale} Nq={Nq} Nk={Nk} D={D} causal={causal}"
+                _close(O, Ob, 1e-12, tag + " O")
+                _close(L, Lb, 1e-12, tag + " LSE")
+        q, k, v = _inputs(3100, 2, 2, 17, 23, 16)
+        t = 0.37
+        O1, L1 = impl_scaled(q, k, v, causal, t / math.sqrt(16))
+        O2, L2 = impl_scaled(q * t, k, v, causal, 1.0 / math.sqrt(16))
+        _close(O1, O2, 1e-12, "scale t/sqrt(D) == Q scaled by t: O")
+        _close(L1, L2, 1e-12, "scale t/sqrt(D) == Q scaled by t: LSE")
 
 
 def check_golden(impl):

@@ -41,7 +41,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     for code, tag in [(0, "FA_OK"), (1, "FA_ERR_NULL"), (2, "FA_ERR_SHAPE"), (3, "FA_ERR_HEAD_DIM"),
-                      (4, "FA_ERR_DTYPE"), (5, "FA_ERR_ALIGN"), (6, "FA_ERR_ALIAS"), (7, "FA_ERR_HIP")]:
+                      (4, "FA_ERR_DTYPE"), (5, "FA_ERR_ALIGN"), (6, "FA_ERR_ALIAS"), (7, "FA_ERR_HIP"),
+                      (8, "FA_ERR_SCALE")]:
         assert fa.fa_status_str(code).startswith(tag)
     assert "unknown" in fa.fa_status_str(99)
 
@@ -53,7 +54,7 @@ def call(q=Q, k=K, v=V, o=O, lse=L, B=2, H=4, Nq=128, Nk=128, D=64, causal=1, dt
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(o=0), 1), (dict(lse=0), 1),
     (dict(B=-1), 2), (dict(H=-3), 2), (dict(Nq=-1), 2), (dict(Nk=0), 2), (dict(Nk=-5), 2),
-    (dict(D=32), 3), (dict(D=0), 3), (dict(D=256), 3), (dict(D=-64), 2),
+    (dict(D=16), 3), (dict(D=0), 3), (dict(D=256), 3), (dict(D=96), 3), (dict(D=-64), 2),
     (dict(dtype=3), 4), (dict(dtype=-1), 4),
     (dict(q=Q + 8), 5), (dict(k=K + 4), 5), (dict(v=V + 2), 5), (dict(o=O + 1), 5), (dict(lse=L + 2), 5),
     (dict(o=Q), 6), (dict(o=K + 64), 6), (dict(lse=V + 1024), 6), (dict(lse=O + 16), 6),
@@ -66,6 +67,26 @@ def call(q=Q, k=K, v=V, o=O, lse=L, B=2, H=4, Nq=128, Nk=128, D=64, causal=1, dt
 ])
 def test_validation_codes(kw, code):
     assert call(**kw) == code
+
+
+def call_scaled(scale, q=Q, k=K, v=V, o=O, lse=L, B=2, H=4, Nq=128, Nk=128, D=64, causal=0, dtype=2):
+    return fa.fa_fwd_scaled(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, float("nan"), float("inf"), -float("inf"), 1e-300, 1e300])
+def test_scaled_rejects_bad_scale(scale):
+    assert call_scaled(scale) == 8
+    # an empty call still validates the scale
+    assert call_scaled(scale, B=0, q=0, k=0, v=0, o=0, lse=0) == 8
+
+
+def test_scaled_validates_like_fa_fwd():
+    # the other checks come first and are the same as fa_fwd's
+    assert call_scaled(0.1, q=0) == 1
+    assert call_scaled(0.1, D=256) == 3
+    assert call_scaled(0.1, dtype=9) == 4
+    assert call_scaled(float("nan"), q=0) == 1
+    assert call_scaled(0.125, B=0, q=0, k=0, v=0, o=0, lse=0) == 0
 
 
 def test_empty_is_noop():

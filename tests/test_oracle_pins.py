@@ -80,3 +80,19 @@ def test_online_reference_matches_page_grid_dtype_free():
         for x, y in ((a, b), (a, c)):
             assert np.max(np.abs(x[0] - y[0])) <= 1e-12
             assert np.max(np.abs(x[1] - y[1])) <= 1e-12
+
+
+def test_oracle_explicit_scale():
+    pins.check_explicit_scale(lambda q, k, v, causal, scale: oracle.attention_forward(q, k, v, causal, scale=scale))
+    # attention_rows and scores_row honour the same scale
+    r = np.random.default_rng(8)
+    q = r.standard_normal((1, 2, 11, 8))
+    k = r.standard_normal((1, 2, 13, 8))
+    v = r.standard_normal((1, 2, 13, 8))
+    O, L = oracle.attention_forward(q, k, v, True, scale=0.3)
+    Or, Lr = oracle.attention_rows(q, k, v, True, [(0, 1, 7)], scale=0.3)
+    assert np.max(np.abs(Or[0] - O[0, 1, 7])) <= 1e-13 and abs(Lr[0] - L[0, 1, 7]) <= 1e-13
+    s = oracle.scores_row(q, k, 0, 1, 7, True, scale=0.3)
+    from scipy.special import logsumexp
+
+    assert abs(logsumexp(s) - L[0, 1, 7]) <= 1e-12

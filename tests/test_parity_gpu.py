@@ -39,7 +39,7 @@ def test_parity_p1_worked_example_inputs():
 
 SMALL = [(dt, D, causal, Nq, Nk)
          for dt in ("bf16", "fp16", "fp32")
-         for D in (64, 128)
+         for D in (32, 64, 128)
          for causal in (False, True)
          for (Nq, Nk) in ((300, 300), (257, 517), (130, 70))]
 
@@ -75,6 +75,31 @@ def test_parity_reference_moves(dt, D, causal):
     compare_full(w, cpu, o, l, "moves")
 
 
+@pytest.mark.parametrize("dt,D,causal,scale", [
+    ("bf16", 128, True, 0.03), ("bf16", 64, False, 0.5), ("fp16", 32, True, 1.0),
+    ("fp16", 128, False, 0.2), ("fp32", 32, False, 0.4), ("fp32", 128, True, 0.05),
+    ("bf16", 32, False, 1.0 / 32**0.5)])
+def test_parity_explicit_scale(dt, D, causal, scale):
+    # fa_fwd_scaled: s = scale * q.k, against the oracle at the same scale
+    # (larger scales give peakier rows, small ones nearly uniform weights).
+    w = workloads.Workload(f"scaled_{dt}_d{D}_{'c' if causal else 'n'}_{scale:.3g}", 2, 2, 333, 401, D, dt,
+                           causal, 5150 + D)
+    cpu, gpu = _case(w)
+    o, l = run_gpu(*gpu, w.causal, softmax_scale=scale)
+    compare_full(w, cpu, o, l, "scaled", scale=scale)
+
+
+def test_default_scale_matches_explicit():
+    # fa_fwd and fa_fwd_scaled(1/sqrt(D)) run the same kernel with the same
+    # fp32 factor: identical bits.
+    for dt, D in (("bf16", 128), ("fp16", 32), ("fp32", 64)):
+        w = workloads.Workload(f"dflt_{dt}_d{D}", 1, 2, 200, 260, D, dt, True, 61 + D)
+        cpu, gpu = _case(w)
+        o1, l1 = run_gpu(*gpu, True)
+        o2, l2 = run_gpu(*gpu, True, softmax_scale=1.0 / D**0.5)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 @pytest.mark.parametrize("name", ["c3_bf16_causal_b4h16n4096d128",
                                   "c4_bf16_causal_b1h32n16384d128_q4",
                                   "c5_fp16_cross_b8h32q512k8192d64",
@@ -89,7 +114,7 @@ def test_parity_full_size_sampled(name):
     assert bool((o.float().abs().amax(dim=(2, 3)) <= vmax + TOL[w.dtype][0]).all())
 
 
-@pytest.mark.parametrize("dt,D", [("bf16", 128), ("fp16", 64), ("fp32", 64)])
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("fp16", 64), ("fp32", 64), ("bf16", 32), ("fp32", 32)])
 def test_edge_shapes(dt, D):
     for (Nq, Nk, causal) in ((1, 1, False), (1, 1, True), (1, 4099, False), (3, 1, True),
                              (200, 5, True), (5, 200, True), (129, 129, True), (64, 64, False)):

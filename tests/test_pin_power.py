@@ -99,3 +99,15 @@ def test_unmutated_definition_passes():
     impl = lambda q, k, v, c: _definition(q, k, v, c)
     for check in pins.ALL_CHECKS:
         check(impl)
+
+
+def test_ignored_explicit_scale_is_caught():
+    # an implementation that drops the explicit scale (always 1/sqrt(D))
+    impl = lambda q, k, v, c, scale: _definition(q, k, v, c)
+    with pytest.raises(AssertionError):
+        pins.check_explicit_scale(impl)
+    # applying the scale to the exponent base instead of the scores
+    impl2 = lambda q, k, v, c, scale: _definition(q, k, v, c, scale_fn=lambda D: scale / math.sqrt(D))
+    with pytest.raises(AssertionError):
+        pins.check_explicit_scale(impl2)
+    pins.check_explicit_scale(lambda q, k, v, c, scale: _definition(q, k, v, c, scale_fn=lambda D: scale))
