@@ -52,19 +52,22 @@ def kernel_tag(w: workloads.Workload) -> str:
     return f"fa_fwd_16_{w.dtype}_d{w.D}_{'causal' if w.causal else 'noncausal'}"
 
 
-KERNEL_SOURCE = os.path.join(ROOT, "exact_tiled_attention_15_amd", "csrc", "fa_kernels.hip")
+CSRC = os.path.join(ROOT, "exact_tiled_attention_15_amd", "csrc")
+# the device code of the forward kernels: shared helpers, then the kernels
+KERNEL_SOURCES = (os.path.join(CSRC, "fa_device.h"), os.path.join(CSRC, "fa_kernels.hip"))
 
 
-def kernel_code_sha256(path: str = KERNEL_SOURCE) -> str:
-    """SHA-256 of the kernel source with // comments and blank lines removed:
+def kernel_code_sha256(paths=KERNEL_SOURCES) -> str:
+    """SHA-256 of the kernel sources with // comments and blank lines removed:
     it names the code the counters were taken on, and survives comment edits."""
     import hashlib
 
     lines = []
-    for line in open(path, encoding="utf-8"):
-        code = line.split("//", 1)[0].rstrip()
-        if code:
-            lines.append(code)
+    for path in paths:
+        for line in open(path, encoding="utf-8"):
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                lines.append(code)
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 

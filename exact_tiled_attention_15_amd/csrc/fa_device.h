@@ -1,0 +1,213 @@
+// Device helpers shared by the gfx950 attention kernels (forward and
+// backward): MFMA wrappers, 16-bit packing, buffer resources, the swizzled
+// LDS tile layout with its direct-to-LDS loads and operand reads.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef unsigned short u16;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kFP16 = 1, kBF16 = 2;  // fa_dtype codes (0 is fp32)
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kMinit = -1.0e30f;  // finite start for the running max (no inf-inf)
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (DT == kBF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+// Round two fp32 values to the 16-bit type (nearest even) and pack them,
+// the first in the low half (one v_cvt_pk_{bf16,f16}_f32).
+template <int DT>
+__device__ __forceinline__ unsigned pack2(float lo, float hi) {
+  const f32x2 x = {lo, hi};
+  if constexpr (DT == kBF16) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(x, bf16x2));
+  } else {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(x, f16x2));
+  }
+}
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// Lanes l and l^32 hold the two halves of one query row; these combine a
+// per-lane value with its partner's (one ds_bpermute).  The gfx950
+// permlane32 swap builtin is not used: this compiler returns the same
+// register for both of its results.
+__device__ __forceinline__ float pair_max(float x) { return fmaxf(x, xor32(x)); }
+__device__ __forceinline__ float pair_sum(float x) { return x + xor32(x); }
+
+// Workgroup -> (batch*head, Q tile).  Q tiles are issued heaviest first
+// (for causal attention the last Q tile sees the most keys), and all Q tiles
+// of one head get the same block index modulo the head count, so that when
+// that count is a multiple of 8 they land on the same XCD and share its L2
+// for K/V.
+__device__ __forceinline__ void tile_of_block(int nqt, int BH, int& bh, int& qt) {
+  const int bid = blockIdx.x;
+  bh = bid % BH;
+  qt = nqt - 1 - bid / BH;
+}
+
+// ---------------------------------------------------------------------------
+// 16-bit kernel (bf16 / fp16), D in {32, 64, 128}, 64-key tiles.
+// ---------------------------------------------------------------------------
+// Buffer resources: 32-bit byte offsets from a per-head base, with the
+// hardware range check (loads past num_records return 0, stores past it are
+// dropped), which handles the ragged Nq / Nk tails.
+constexpr int kBufFlags = 0x00020000;  // gfx9 buffer descriptor word 3 (32-bit data format)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufFlags);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((vector_size(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// LDS tile layout for a BC x D tile of 16-bit values (K or V), in bytes.
+// The gfx950 LDS serves 256 bytes per clock (64 banks of 4 bytes), so rows
+// are taken in groups of 16 and 16-byte chunk c of the 16 rows shares one
+// 256-byte line, at row slot (R % 16) XOR 4 (c % 4):
+//   off(R, c) = (R / 16) * 32 D + 256 c + 16 ((R % 16) ^ (4 (c % 4))).
+// A K-operand read (16 lanes = 16 rows x one chunk) and a transposing
+// V-operand read (32 lanes = 4 rows x 4 chunks) then each cover one whole
+// 256-byte line, and every read address is one of two per-lane bases plus
+// a compile-time offset.
+
+// Global byte offset (within a tile) of the 16 bytes that lane `lane` of
+// the G-th 1 KB direct-to-LDS load must fetch so that LDS byte 1024 G +
+// 16 lane ends up holding the chunk that the layout above puts there.
+template <int D>
+__device__ __forceinline__ int dma_src_off(int G, int lane) {
+  const int o = G * 1024 + 16 * lane;
+  const int rem = o % (32 * D);
+  const int c = rem / 256;
+  const int R = (o / (32 * D)) * 16 + (((rem % 256) / 16) ^ ((c & 3) << 2));
+  return R * (2 * D) + c * 16;
+}
+
+// Per-wave constants of the 16-bit kernels.  The row/column fields are
+// those of the forward kernel (rows = queries, streamed columns = keys).
+struct Wave16 {
+  int lane, hf, l32, wave;
+  int wq0;    // first query row of the wave
+  int wkend;  // keys [0, wkend) are needed by the wave
+  int wklim;  // smallest last-visible key over the wave's rows
+  int klim;   // last key this lane's row may see
+  // LDS byte offsets of this lane's K-operand reads (even / odd kk) and of
+  // its transposing V-operand reads (q = 0 / 1), each plain (lo) and plus
+  // 64 KB (hi); see ks_operand.
+  int kb_lo[2], kb_hi[2];
+  int vb_lo[2], vb_hi[2];
+};
+
+constexpr int kStages = 4;  // LDS ring depth: three tiles in flight while one is consumed
+
+// Wait until at most `later` of this wave's direct-to-LDS loads and LGKM
+// of its LDS operations are still in flight (each counter completes in
+// issue order), then meet the other waves.  s_waitcnt takes an immediate,
+// hence the switch (`later` is wave-uniform, even and at most 12).
+template <int LGKM = 0>
+__device__ __forceinline__ void wait_tile_and_barrier(int later) {
+  static_assert(LGKM >= 0 && LGKM < 16, "lgkmcnt field");
+  constexpr int kBase = 0x070 | (LGKM << 8);  // expcnt: no wait; lgkmcnt(LGKM); vmcnt in the low bits
+  asm volatile("" ::: "memory");
+  switch (later) {
+    case 12: __builtin_amdgcn_s_waitcnt(kBase | 12); break;
+    case 10: __builtin_amdgcn_s_waitcnt(kBase | 10); break;
+    case 8: __builtin_amdgcn_s_waitcnt(kBase | 8); break;
+    case 6: __builtin_amdgcn_s_waitcnt(kBase | 6); break;
+    case 4: __builtin_amdgcn_s_waitcnt(kBase | 4); break;
+    case 2: __builtin_amdgcn_s_waitcnt(kBase | 2); break;
+    default: __builtin_amdgcn_s_waitcnt(kBase); break;
+  }
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Number of 1 KB direct-to-LDS loads (both tensors together) that wave
+// `wave` of NW issues per 64-row tile: the 1 KB pieces G = wave, wave + NW,
+// ... of each tensor's tile.
+template <int D, int NW>
+__device__ __forceinline__ int loads_per_tile(int wave) {
+  constexpr int NG = 64 * D * 2 / 1024;
+  return 2 * ((NG - wave + NW - 1) / NW);
+}
+
+// Direct-to-LDS loads of 64-row tile t of two [N, D] tensors (K and V in
+// the forward pass) into `dst` (first tensor) and `dst + 64 D 2` (second):
+// this wave's 1 KB pieces G = wave, wave + NW, ... of each.
+template <int D, int NW>
+__device__ __forceinline__ void issue_tile16(const u16* Kh, const u16* Vh, int kbytes, int t,
+                                             unsigned char* dst, const Wave16& w) {
+  constexpr int TILEB = 64 * D * 2;
+  constexpr int NG = TILEB / 1024;
+  const auto rk = make_rsrc(Kh, kbytes);
+  const auto rv = make_rsrc(Vh, kbytes);
+#pragma unroll
+  for (int I = 0; I < (NG + NW - 1) / NW; ++I) {
+    const int G = w.wave + NW * I;
+    if (G < NG) {
+      const int go = dma_src_off<D>(G, w.lane);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst + G * 1024), 16, go, t * TILEB, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst + TILEB + G * 1024), 16, go, t * TILEB, 0, 0);
+    }
+  }
+}
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+// LDS operand reads.  A ring stage may lie above 64 KB, past the reach of
+// the ds_read immediate offset, so each lane's offsets exist twice, plain
+// (lo) and plus 64 KB (hi), both kept opaque to the compiler; a read takes
+// the copy that matches its stage's 64 KB window (`lds_bias`, a link-time
+// constant), so that it is one base register plus an immediate below 64 KB,
+// and its pointer still derives from the stage array, so the compiler still
+// knows which array it reads (and that the loads in flight write others).
+__device__ __forceinline__ unsigned lds_bias(const unsigned char* p) {
+  return (unsigned)(uintptr_t)(const lds_u8*)p & 0xFFFF0000u;
+}
+
+// K operand of score MFMA i (block n = i / (D/16), step kk = i % (D/16)):
+// row 32n + l32, chunk 2kk + hf of the tile.
+template <int D>
+__device__ __forceinline__ u32x4 ks_operand(const unsigned char* ks, const Wave16& w, int i) {
+  const int n = i / (D / 16), kk = i % (D / 16);
+  const unsigned bias = lds_bias(ks);
+  const int base = bias ? w.kb_hi[kk & 1] : w.kb_lo[kk & 1];
+  return *(const lds_u32x4*)((const lds_u8*)ks + (base + (n * 64 * D + (kk >> 1) * 1024 - (int)bias)));
+}
+
+// V^T operand of PV MFMA i (output block dt = i / 4, keys 32n + 16hh with
+// n = (i / 2) % 2, hh = i % 2), from two transposing 64-bit reads.
+template <int D>
+__device__ __forceinline__ u32x4 vt_operand(const unsigned char* vs, const Wave16& w, int i) {
+  const int dt = i >> 2, n = (i >> 1) & 1, hh = i & 1;
+  const unsigned bias = lds_bias(vs);
+  const int off = (2 * n + hh) * (32 * D) + dt * 1024 - (int)bias;
+  const int b0 = bias ? w.vb_hi[0] : w.vb_lo[0], b1 = bias ? w.vb_hi[1] : w.vb_lo[1];
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((const lds_u8*)vs + (b0 + off)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((const lds_u8*)vs + (b1 + off)));
+  const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+}
+
+}  // namespace

@@ -5,5 +5,6 @@ import this package.  The product path never calls it: it shares no code
 with the HIP library and imports nothing from it.
 """
 from .attention import attention_forward, attention_rows, scores_row
+from .backward import attention_backward
 
-__all__ = ["attention_forward", "attention_rows", "scores_row"]
+__all__ = ["attention_forward", "attention_rows", "scores_row", "attention_backward"]
