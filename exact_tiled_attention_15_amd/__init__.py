@@ -12,7 +12,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_scaled", "fa_status_str", "forward", "load_library", "LIB_PATH",
+__all__ = ["fa_fwd", "fa_fwd_scaled", "fa_bwd", "fa_bwd_workspace_size", "backward", "fa_status_str", "forward", "load_library", "LIB_PATH",
            "FA_DTYPE_FP32", "FA_DTYPE_FP16", "FA_DTYPE_BF16", "FA_OK", "FaError",
            "EXPORTED_SYMBOLS"]
 
@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_DTYPE_FP32, FA_DTYPE_FP16, FA_DTYPE_BF16 = 0, 1, 2
 FA_OK = 0
-EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_scaled", "fa_status_str")
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_scaled", "fa_bwd", "fa_bwd_workspace_size", "fa_status_str")
 
 _lib = None
 
@@ -48,6 +48,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fa_fwd_scaled.restype = ctypes.c_int
     lib.fa_fwd_scaled.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + \
         [ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_bwd_workspace_size.restype = ctypes.c_int64
+    lib.fa_bwd_workspace_size.argtypes = [ctypes.c_int64] * 3
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 6 + \
+        [ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [ctypes.c_int]
     if path is None:
@@ -70,6 +75,18 @@ def fa_fwd_scaled(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: 
     """Call the C ``fa_fwd_scaled`` with raw device addresses; returns the status code."""
     return load_library().fa_fwd_scaled(q, k, v, o, lse, B, H, Nq, Nk, D, float(softmax_scale),
                                         int(causal), int(dtype), stream)
+
+
+def fa_bwd_workspace_size(B: int, H: int, Nq: int) -> int:
+    return int(load_library().fa_bwd_workspace_size(B, H, Nq))
+
+
+def fa_bwd(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int,
+           workspace: int, workspace_bytes: int, B: int, H: int, Nq: int, Nk: int, D: int,
+           softmax_scale: float, causal: int, dtype: int, stream: int | None) -> int:
+    """Call the C ``fa_bwd`` with raw device addresses; returns the status code."""
+    return load_library().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
+                                 B, H, Nq, Nk, D, float(softmax_scale), int(causal), int(dtype), stream)
 
 
 def _dtype_code(t) -> int:
@@ -129,3 +146,54 @@ def forward(q, k, v, causal: bool = False, out=None, lse=None, stream=None, soft
     if rc != FA_OK:
         raise FaError(rc)
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, causal: bool = False, softmax_scale=None, dq=None, dk=None,
+             dv=None, workspace=None, stream=None):
+    """Exact attention backward on the GPU.
+
+    q, k, v, causal and softmax_scale as given to ``forward``; o and lse as it
+    returned them; dout: the gradient of o (like q).  16-bit dtypes only.
+    Returns (dq, dk, dv) in the input dtype.  Output tensors and the
+    workspace (a uint8 device tensor of at least ``fa_bwd_workspace_size``
+    bytes) may be given preallocated.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("dout", dout)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, D) or tuple(v.shape) != (B, H, Nk, D):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    for name, t in (("o", o), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be like q")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 (B, H, Nq) tensor")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor like {name[1:]}")
+    need = fa_bwd_workspace_size(B, H, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    scale = 1.0 / D**0.5 if softmax_scale is None else float(softmax_scale)
+    if stream is None:
+        with torch.cuda.device(q.device):
+            stream = torch.cuda.current_stream().cuda_stream
+    with torch.cuda.device(q.device):
+        rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                    workspace.numel() * workspace.element_size(), B, H, Nq, Nk, D, scale, bool(causal),
+                    _dtype_code(q), stream)
+    if rc != FA_OK:
+        raise FaError(rc)
+    return dq, dk, dv

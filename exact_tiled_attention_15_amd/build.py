@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = [os.path.join(CSRC, "fa_kernels.hip"), os.path.join(CSRC, "fa_api.cpp")]
+SOURCES = [os.path.join(CSRC, "fa_kernels.hip"), os.path.join(CSRC, "fa_bwd.hip"),
+           os.path.join(CSRC, "fa_api.cpp")]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for all device code.

@@ -103,6 +103,77 @@ extern "C" int fa_fwd_scaled(const void* q, const void* k, const void* v, void* 
   return fwd(q, k, v, o, lse, B, H, Nq, Nk, D, &softmax_scale, causal, dtype, stream);
 }
 
+extern "C" int64_t fa_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq) {
+  int64_t BH, rows, bytes;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, Nq, &rows) || !mul_ok(rows, 8, &bytes)) return -1;
+  return bytes;
+}
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                      int64_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                      double softmax_scale, int causal, int dtype, void* stream) {
+  if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;  // 16-bit inputs only
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || D < 0) return FA_ERR_SHAPE;
+  if (D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (!scale_ok(softmax_scale)) return FA_ERR_SCALE;
+  int64_t BH, qel, kel;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, Nq, &qel) || !mul_ok(qel, D, &qel) || !mul_ok(BH, Nk, &kel) ||
+      !mul_ok(kel, D, &kel))
+    return FA_ERR_SHAPE;
+  if (BH == 0 || (Nq == 0 && Nk == 0)) return FA_OK;  // nothing to write
+  if (Nk == 0) return FA_ERR_SHAPE;  // query rows with no key have no softmax
+  // Nq == 0 < Nk is valid: dK = dV = 0.
+  if (Nq > INT32_MAX / 2 || Nk > INT32_MAX / 2 || BH > INT32_MAX) return FA_ERR_SHAPE;
+  const int64_t esz = 2;
+  if ((Nq + 256) * D * esz > INT32_MAX || (Nk + 256) * D * esz > INT32_MAX) return FA_ERR_SHAPE;
+  int64_t gq, gk;
+  if (!mul_ok(BH, (Nq + 255) / 256, &gq) || gq > INT32_MAX || !mul_ok(BH, (Nk + 127) / 128, &gk) ||
+      gk > INT32_MAX || BH * Nq * (D / 8) / 256 >= INT32_MAX)
+    return FA_ERR_SHAPE;
+  const int64_t ws_need = fa_bwd_workspace_size(B, H, Nq);
+  if (ws_need < 0) return FA_ERR_SHAPE;
+  // the query-side buffers have zero size when Nq == 0 and may then be NULL
+  if (!k || !v || !dk || !dv) return FA_ERR_NULL;
+  if (Nq > 0 && (!q || !o || !lse || !dout || !dq || !workspace)) return FA_ERR_NULL;
+  if (workspace_bytes < ws_need) return FA_ERR_WORKSPACE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
+       (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)workspace) & 15u)
+    return FA_ERR_ALIGN;
+  if ((uintptr_t)lse & 3u) return FA_ERR_ALIGN;
+  const int64_t qbytes = qel * esz, kbytes = kel * esz, lbytes = BH * Nq * 4;
+  const void* ins[6] = {q, k, v, o, lse, dout};
+  const int64_t in_bytes[6] = {qbytes, kbytes, kbytes, qbytes, lbytes, qbytes};
+  void* outs[4] = {dq, dk, dv, workspace};
+  const int64_t out_bytes[4] = {qbytes, kbytes, kbytes, ws_need};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return FA_ERR_ALIAS;
+  }
+  FaBwdLaunch a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.workspace = workspace;
+  a.BH = BH;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.D = (int)D;
+  a.causal = causal != 0;
+  a.dtype = dtype;
+  a.scale = softmax_scale;
+  a.stream = stream;
+  return fa_launch_bwd(a) == 0 ? FA_OK : FA_ERR_HIP;
+}
+
 extern "C" const char* fa_status_str(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";
@@ -114,6 +185,7 @@ extern "C" const char* fa_status_str(int status) {
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or the other output";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch error";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: softmax_scale must be a finite number > 0";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace smaller than fa_bwd_workspace_size()";
     default: return "unknown fa_status code";
   }
 }

@@ -210,4 +210,33 @@ __device__ __forceinline__ u32x4 vt_operand(const unsigned char* vs, const Wave1
   return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
 }
 
+// Lane offsets of the operand reads (set once per wave; w.lane, w.hf, w.l32
+// must be set).  Row operand (ks_operand): row 32n + l32, chunk
+// c = 2kk + hf, so the slot XOR (4 (c % 4)) depends on the parity of kk.
+// Transposed operand (vt_operand): 16-lane group g reads rows
+// 32n + 16hh + 8q + 4hf + i/4 at columns 32dt + 16g + 4(i%4), i = lane % 16,
+// i.e. chunk 4dt + 2g + (i%4)/2 and half (i%2) of it.
+template <int D>
+__device__ __forceinline__ void init_operand_offsets(Wave16& w) {
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int c = 2 * par + w.hf;
+    w.kb_lo[par] = (w.l32 >> 4) * (32 * D) + c * 256 + (((w.l32 & 15) ^ (c << 2)) << 4);
+    w.kb_hi[par] = w.kb_lo[par] + 65536;
+    asm volatile("" : "+v"(w.kb_lo[par]));
+    asm volatile("" : "+v"(w.kb_hi[par]));
+  }
+  {
+    const int vi = w.l32 & 15, vg = w.l32 >> 4;
+    const int c = 2 * vg + ((vi & 3) >> 1);  // chunk within the 4-chunk (64-column) block
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      w.vb_lo[q] = c * 256 + (((8 * q + 4 * w.hf + (vi >> 2)) ^ (c << 2)) << 4) + 8 * (vi & 1);
+      w.vb_hi[q] = w.vb_lo[q] + 65536;
+      asm volatile("" : "+v"(w.vb_lo[q]));
+      asm volatile("" : "+v"(w.vb_hi[q]));
+    }
+  }
+}
+
 }  // namespace

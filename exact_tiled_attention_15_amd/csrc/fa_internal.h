@@ -23,3 +23,28 @@ struct FaLaunch {
 // Enqueues the forward pass.  Arguments are already validated.  Returns 0 on
 // success, otherwise the HIP error code of the launch.
 int fa_launch_fwd(const FaLaunch& a);
+
+struct FaBwdLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* workspace;  // 2 * BH * Nq floats: lse * log2(e), then delta
+  int64_t BH;
+  int64_t Nq;
+  int64_t Nk;
+  int D;
+  int causal;
+  int dtype;  // FA_DTYPE_FP16 or FA_DTYPE_BF16
+  double scale;
+  void* stream;
+};
+
+// Enqueues the backward pass (three kernels).  Arguments are already
+// validated.  Returns 0 on success, otherwise the HIP error code.
+int fa_launch_bwd(const FaBwdLaunch& a);

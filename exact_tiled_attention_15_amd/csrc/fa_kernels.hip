@@ -200,30 +200,7 @@ __global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict
   w.wkend = CAUSAL ? min(kend, w.wq0 + 32) : kend;
   w.klim = CAUSAL ? min(myq, Nk - 1) : Nk - 1;
   w.wklim = CAUSAL ? min(w.wq0, Nk - 1) : Nk - 1;
-  // K operand (S^T = K Q^T): row 32n + l32, chunk c = 2kk + hf, so the
-  // slot XOR (4 (c % 4)) depends on the parity of kk.  V operand (O^T =
-  // V^T P^T, transposing reads): 16-lane group g reads rows
-  // 32n + 16hh + 8q + 4hf + i/4 at columns 32dt + 16g + 4(i%4), i = lane % 16,
-  // i.e. chunk 4dt + 2g + (i%4)/2 and half (i%2) of it.
-#pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    const int c = 2 * par + w.hf;
-    w.kb_lo[par] = (w.l32 >> 4) * (32 * D) + c * 256 + (((w.l32 & 15) ^ (c << 2)) << 4);
-    w.kb_hi[par] = w.kb_lo[par] + 65536;
-    asm volatile("" : "+v"(w.kb_lo[par]));
-    asm volatile("" : "+v"(w.kb_hi[par]));
-  }
-  {
-    const int vi = w.l32 & 15, vg = w.l32 >> 4;
-    const int c = 2 * vg + ((vi & 3) >> 1);  // chunk within the 4-chunk (64-column) block
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      w.vb_lo[q] = c * 256 + (((8 * q + 4 * w.hf + (vi >> 2)) ^ (c << 2)) << 4) + 8 * (vi & 1);
-      w.vb_hi[q] = w.vb_lo[q] + 65536;
-      asm volatile("" : "+v"(w.vb_lo[q]));
-      asm volatile("" : "+v"(w.vb_hi[q]));
-    }
-  }
+  init_operand_offsets<D>(w);
 
   // Q fragment (B operand of S^T): lane holds Q[myq][16*kk + 8*hf .. +7];
   // rows past Nq read as zero.  Issued before the K/V loads: loads complete

@@ -58,8 +58,9 @@ typedef enum {
   FA_ERR_ALIGN = 5,    /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
   FA_ERR_ALIAS = 6,    /* o or lse overlaps an input, or o overlaps lse */
   FA_ERR_HIP = 7,      /* the HIP runtime reported an error at launch */
-  FA_ERR_SCALE = 8     /* softmax_scale not a finite number > 0 (or so small that
+  FA_ERR_SCALE = 8,    /* softmax_scale not a finite number > 0 (or so small that
                           softmax_scale * log2(e) is not a normal float) */
+  FA_ERR_WORKSPACE = 9 /* workspace_bytes below fa_bwd_workspace_size() */
 } fa_status;
 
 /*
@@ -99,6 +100,53 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_scaled(const void* q, const void* k, const void* v, void* o, float* lse,
                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
                   double softmax_scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs: two fp32
+ * values per query row (8 * B * H * Nq); -1 if that overflows or a size is
+ * negative.
+ */
+int64_t fa_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq);
+
+/*
+ * fa_bwd -- exact attention backward: the gradients of sum(dout * O) with
+ * respect to q, k and v, where O = attention(q, k, v) as fa_fwd_scaled
+ * defines it.  "Building a FlashAttention-2 Forward Kernel in Pure NumPy"
+ * (Extending It) names this step: the forward's softmax statistics are kept
+ * and every score tile is recomputed while the gradients stream tile by
+ * tile.  Here the statistic is lse, so P = exp(s - LSE) exactly, and
+ *
+ *     dV = P^T dO,  dS = P * (dO V^T - delta),  delta_i = dO_i . O_i,
+ *     dQ = scale * dS K,  dK = scale * dS^T Q.
+ *
+ *   q, k, v   the forward's inputs (device, layouts as fa_fwd)
+ *   o, lse    the forward's outputs for these inputs and this scale, exactly
+ *             as fa_fwd / fa_fwd_scaled wrote them
+ *   dout      device pointer, [B, H, Nq, D], `dtype`: the gradient of O
+ *   dq        device pointer, [B, H, Nq, D], `dtype` (output)
+ *   dk, dv    device pointers, [B, H, Nk, D], `dtype` (outputs)
+ *   workspace device memory of at least fa_bwd_workspace_size(B, H, Nq)
+ *             bytes, 16-byte aligned, owned by the caller; its contents on
+ *             entry do not matter and are scratch after the call
+ *   softmax_scale  the forward's scale (1/sqrt(D) for fa_fwd); finite, > 0
+ *   causal, dtype, stream   as fa_fwd; dtype must be FA_DTYPE_FP16 or
+ *             FA_DTYPE_BF16 (FA_ERR_DTYPE otherwise)
+ *
+ * Accumulation is fp32; dq, dk, dv are rounded to `dtype` (nearest even).
+ * B*H == 0, or Nq == Nk == 0, is a no-op; Nq == 0 < Nk writes dK = dV = 0;
+ * Nk == 0 < Nq is FA_ERR_SHAPE.  Keys that no query sees (causal, Nk > Nq)
+ * get dK = dV = 0.  Pointers must be non-NULL and 16-byte aligned (lse
+ * 4-byte aligned) unless the call is a no-op; when Nq == 0 the query-side
+ * buffers (q, o, lse, dout, dq, workspace) are empty and may be NULL.  No
+ * output or the workspace may
+ * overlap an input or another output (FA_ERR_ALIAS).  Validation happens
+ * before any HIP call; the library allocates nothing and keeps no pointer.
+ * The result is deterministic (no atomics).
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, void* workspace,
+           int64_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+           double softmax_scale, int causal, int dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_str(int status);

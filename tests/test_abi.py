@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings():
     for code, tag in [(0, "FA_OK"), (1, "FA_ERR_NULL"), (2, "FA_ERR_SHAPE"), (3, "FA_ERR_HEAD_DIM"),
                       (4, "FA_ERR_DTYPE"), (5, "FA_ERR_ALIGN"), (6, "FA_ERR_ALIAS"), (7, "FA_ERR_HIP"),
-                      (8, "FA_ERR_SCALE")]:
+                      (8, "FA_ERR_SCALE"), (9, "FA_ERR_WORKSPACE")]:
         assert fa.fa_status_str(code).startswith(tag)
     assert "unknown" in fa.fa_status_str(99)
 
@@ -106,3 +106,45 @@ def test_python_binding_rejects_cpu_tensors():
 def test_no_cpu_fallback_when_library_missing(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         fa.load_library(str(tmp_path / "libfa.so"))
+
+
+# fa_bwd: q, k, v, o, lse, dout inputs; dq, dk, dv outputs; workspace.
+DO, DQ, DK, DV, WS = (6 << 40), (7 << 40), (8 << 40), (9 << 40), (10 << 40)
+
+
+def call_bwd(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, ws=WS, ws_bytes=1 << 30, B=2, H=4,
+             Nq=128, Nk=128, D=64, scale=0.125, causal=1, dtype=2):
+    return fa.fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, ws_bytes, B, H, Nq, Nk, D, scale, causal,
+                     dtype, None)
+
+
+def test_bwd_workspace_size():
+    assert fa.fa_bwd_workspace_size(2, 4, 128) == 8 * 2 * 4 * 128
+    assert fa.fa_bwd_workspace_size(0, 4, 128) == 0
+    assert fa.fa_bwd_workspace_size(-1, 4, 128) == -1
+    assert fa.fa_bwd_workspace_size(1 << 40, 1 << 20, 1 << 10) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), 4), (dict(dtype=7), 4), (dict(D=16), 3), (dict(D=256), 3),
+    (dict(scale=0.0), 8), (dict(scale=float("nan")), 8), (dict(scale=-1.0), 8),
+    (dict(Nk=0), 2), (dict(B=-1), 2), (dict(Nq=1 << 40), 2),
+    (dict(q=0), 1), (dict(o=0), 1), (dict(lse=0), 1), (dict(dout=0), 1), (dict(dq=0), 1), (dict(dk=0), 1),
+    (dict(dv=0), 1), (dict(ws=0), 1),
+    (dict(ws_bytes=8 * 2 * 4 * 128 - 1), 9),
+    (dict(dout=DO + 8), 5), (dict(dq=DQ + 4), 5), (dict(ws=WS + 4), 5), (dict(lse=L + 2), 5),
+    (dict(dq=Q + 64), 6), (dict(dk=V), 6), (dict(dv=DO), 6), (dict(ws=L), 6), (dict(dk=DV - 64), 6),
+    (dict(ws=DQ + 1024), 6), (dict(dq=O), 6),
+])
+def test_bwd_validation_codes(kw, code):
+    assert call_bwd(**kw) == code
+
+
+def test_bwd_noop_cases():
+    assert call_bwd(B=0, q=0, k=0, v=0, o=0, lse=0, dout=0, dq=0, dk=0, dv=0, ws=0, ws_bytes=0) == 0
+    assert call_bwd(Nq=0, Nk=0, q=0, dq=0) == 0
+    # Nq == 0 < Nk: the query-side buffers may be NULL, the key side may not
+    assert call_bwd(Nq=0, q=0, o=0, lse=0, dout=0, dq=0, ws=0, dk=0) == 1
+    assert call_bwd(Nq=0, q=0, o=0, lse=0, dout=0, dq=0, ws=0, v=0) == 1
+    # an exact-size workspace passes the size check (reaches the alias check here)
+    assert call_bwd(ws_bytes=8 * 2 * 4 * 128, ws=DQ + 64) == 6

@@ -33,7 +33,9 @@ __all__ = [
     "round_to_dtype",
     "make_inputs",
     "make_p1_legacy_inputs",
+    "make_dout",
     "conv_flops",
+    "conv_flops_bwd",
 ]
 
 
@@ -128,6 +130,14 @@ def make_inputs(w: Workload, seed: int | None = None):
     return tuple(round_to_dtype(x, w.dtype) for x in (q, k, v))
 
 
+def make_dout(w: Workload, seed: int | None = None):
+    """The upstream gradient dO for a backward workload: float64 N(0,1) of
+    Q's shape from its own generator (seed + 1000, drawn after nothing else),
+    rounded to the storage dtype like Q, K, V."""
+    rng = np.random.default_rng((w.seed if seed is None else seed) + 1000)
+    return round_to_dtype(rng.standard_normal(w.q_shape), w.dtype)
+
+
 def make_p1_legacy_inputs():
     """The worked example of "Build a FlashAttention Kernel from Scratch with
     Python and NumPy" (Step 2): legacy ``np.random.seed(0)`` and ``randn`` in
@@ -147,3 +157,9 @@ def conv_flops(B: int, H: int, Nq: int, Nk: int, D: int, causal: bool) -> float:
     """FLOP convention of the metric: 4*B*H*Nq*Nk*D, halved when causal."""
     f = 4.0 * B * H * Nq * Nk * D
     return f / 2.0 if causal else f
+
+
+def conv_flops_bwd(B: int, H: int, Nq: int, Nk: int, D: int, causal: bool) -> float:
+    """Backward FLOP convention: five products of the forward's size (S
+    recomputed, dP = dO V^T, dV, dQ, dK), 10*B*H*Nq*Nk*D, halved when causal."""
+    return 2.5 * conv_flops(B, H, Nq, Nk, D, causal)
