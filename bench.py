@@ -1,14 +1,19 @@
-"""Benchmark of the exact tiled attention forward on one MI355X.
+"""Benchmark of exact tiled attention on one MI355X.
 
-A step is one fa_fwd call over the whole batch of the workload (all of the
-hot path: Q-tile load, K/V streaming, both MFMA contractions, online softmax,
-causal skipping, epilogue), inputs already resident in HBM.
+Default (--op fwd): a step is one fa_fwd call over the whole batch of the
+workload (all of the hot path: Q-tile load, K/V streaming, both MFMA
+contractions, online softmax, causal skipping, epilogue), inputs already
+resident in HBM.  Throughput is the metric's convention: FLOPs =
+4*B*H*Nq*Nk*D, halved when causal, per second, in TFLOP/s.
+
+--op bwd: a step is one fa_bwd call (delta/LSE preprocessing, dQ kernel,
+dK/dV kernel) on the forward's O and LSE; FLOPs = 2.5x the forward
+convention (five products of the forward's size).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--all]
+                    [--op fwd|bwd] [--no-cpu-baseline] [--all]
 
-Prints one JSON line (rank 0).  Throughput is the metric's convention:
-FLOPs = 4*B*H*Nq*Nk*D, halved when causal, per second, in TFLOP/s.
+Prints one JSON line per workload.
 """
 from __future__ import annotations
 
@@ -26,6 +31,7 @@ if ROOT not in sys.path:
 import workloads  # noqa: E402
 
 METRIC = "attention fwd TFLOP/s and % of dense MFMA peak, bf16 causal N=4096 D=128"
+METRIC_BWD = "attention bwd TFLOP/s (2.5x the forward FLOP convention) and % of dense MFMA peak"
 # Published MI355X dense peaks (TFLOP/s) by compute dtype.
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
 
@@ -40,13 +46,16 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--all", action="store_true", help="one line per measured workload (c1..c5)")
+    p.add_argument("--op", choices=("fwd", "bwd"), default="fwd")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="after timing, run 3 plain device copies of this many MiB (a reference "
                         "kernel of known traffic for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     return p.parse_args()
 
 
-def kernel_tag(w: workloads.Workload) -> str:
+def kernel_tag(w: workloads.Workload, op: str = "fwd") -> str:
+    if op == "bwd":
+        return f"fa_bwd_16_{w.dtype}_d{w.D}_{'causal' if w.causal else 'noncausal'}"
     if w.dtype == "fp32":
         return f"fa_fwd_32_d{w.D}_{'causal' if w.causal else 'noncausal'}"
     return f"fa_fwd_16_{w.dtype}_d{w.D}_{'causal' if w.causal else 'noncausal'}"
@@ -55,6 +64,7 @@ def kernel_tag(w: workloads.Workload) -> str:
 CSRC = os.path.join(ROOT, "exact_tiled_attention_15_amd", "csrc")
 # the device code of the forward kernels: shared helpers, then the kernels
 KERNEL_SOURCES = (os.path.join(CSRC, "fa_device.h"), os.path.join(CSRC, "fa_kernels.hip"))
+KERNEL_SOURCES_BWD = (os.path.join(CSRC, "fa_device.h"), os.path.join(CSRC, "fa_bwd.hip"))
 
 
 def kernel_code_sha256(paths=KERNEL_SOURCES) -> str:
@@ -71,11 +81,11 @@ def kernel_code_sha256(paths=KERNEL_SOURCES) -> str:
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
-def measured_traffic(w: workloads.Workload):
+def measured_traffic(w: workloads.Workload, op: str = "fwd"):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     summary of this kernel and workload, or None when there is none or the
     kernel code has changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"{kernel_tag(w)}__{w.name}__hbm_traffic_and_counters.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag(w, op)}__{w.name}__hbm_traffic_and_counters.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -83,7 +93,8 @@ def measured_traffic(w: workloads.Workload):
         if ":" in line and line.split(":")[0] in ("kernel_code_sha256", "traffic_bytes_per_launch"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_code_sha256") != kernel_code_sha256() or "traffic_bytes_per_launch" not in fields:
+    code = kernel_code_sha256(KERNEL_SOURCES_BWD if op == "bwd" else KERNEL_SOURCES)
+    if fields.get("kernel_code_sha256") != code or "traffic_bytes_per_launch" not in fields:
         return None
     return int(fields["traffic_bytes_per_launch"])
 
@@ -100,14 +111,13 @@ def blas_threads() -> int:
     return os.cpu_count() or 1
 
 
-def cpu_baseline(w: workloads.Workload, target_s: float):
+def cpu_baseline(w: workloads.Workload, target_s: float, op: str = "fwd"):
     """The float64 oracle, as it stands, on whole (b, h) heads of the same
     workload, head after head until about ``target_s`` seconds have passed."""
-    import numpy as np
-
     import oracle
 
     q, k, v = workloads.make_inputs(w)
+    do = workloads.make_dout(w) if op == "bwd" else None
     heads = 0
     t_total = 0.0
     BH = w.B * w.H
@@ -116,10 +126,14 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
         sl = (slice(b, b + 1), slice(h, h + 1))
         qh, kh, vh = (x[sl].double().numpy() for x in (q, k, v))
         t0 = time.perf_counter()
-        oracle.attention_forward(qh, kh, vh, w.causal)
+        if op == "bwd":
+            oracle.attention_backward(qh, kh, vh, do[sl].double().numpy(), w.causal)
+        else:
+            oracle.attention_forward(qh, kh, vh, w.causal)
         t_total += time.perf_counter() - t0
         heads += 1
-    flops = workloads.conv_flops(1, heads, w.Nq, w.Nk, w.D, w.causal)
+    conv = workloads.conv_flops_bwd if op == "bwd" else workloads.conv_flops
+    flops = conv(1, heads, w.Nq, w.Nk, w.D, w.causal)
     return {
         "value": round(flops / t_total / 1e12, 6),
         "unit": "TFLOP/s",
@@ -129,7 +143,7 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
     }
 
 
-def bench_one(w: workloads.Workload, steps: int, warmup: int):
+def bench_one(w: workloads.Workload, steps: int, warmup: int, op: str = "fwd"):
     import torch
 
     import exact_tiled_attention_15_amd as fa
@@ -143,11 +157,29 @@ def bench_one(w: workloads.Workload, steps: int, warmup: int):
     sptr = stream.cuda_stream
     code = fa._dtype_code(q)
 
-    def step():
+    def fwd_step():
         rc = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                        w.B, w.H, w.Nq, w.Nk, w.D, int(w.causal), code, sptr)
         if rc != 0:
             raise fa.FaError(rc)
+
+    step = fwd_step
+    if op == "bwd":
+        fwd_step()  # the backward consumes the forward's O and LSE
+        do = workloads.make_dout(w).to(dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws_bytes = fa.fa_bwd_workspace_size(w.B, w.H, w.Nq)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        scale = 1.0 / w.D**0.5
+
+        def bwd_step():
+            rc = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+                           ws_bytes, w.B, w.H, w.Nq, w.Nk, w.D, scale, int(w.causal), code, sptr)
+            if rc != 0:
+                raise fa.FaError(rc)
+
+        step = bwd_step
 
     for _ in range(warmup):
         step()
@@ -174,7 +206,8 @@ def bench_one(w: workloads.Workload, steps: int, warmup: int):
         b.record(stream)
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in evs]
-    flops = workloads.conv_flops(w.B, w.H, w.Nq, w.Nk, w.D, w.causal)
+    conv = workloads.conv_flops_bwd if op == "bwd" else workloads.conv_flops
+    flops = conv(w.B, w.H, w.Nq, w.Nk, w.D, w.causal)
     tflops = flops / (ms_region * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     return {
@@ -188,7 +221,7 @@ def bench_one(w: workloads.Workload, steps: int, warmup: int):
     }
 
 
-def line_for(w, r, steps, warmup, cpu):
+def line_for(w, r, steps, warmup, cpu, op="fwd"):
     props = {}
     try:
         import torch
@@ -199,7 +232,7 @@ def line_for(w, r, steps, warmup, cpu):
     except Exception:
         pass
     return {
-        "metric": METRIC,
+        "metric": METRIC_BWD if op == "bwd" else METRIC,
         "value": round(r["tflops"], 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -215,10 +248,10 @@ def line_for(w, r, steps, warmup, cpu):
                    "causal": w.causal, "seed": w.seed, "q_scale": w.q_scale,
                    "flops_per_step": r["flops"], "parallelism": "single GPU",
                    "median_launch_ms": round(r["median_launch_ms"], 5),
-                   "min_launch_ms": round(r["min_launch_ms"], 5), **props},
+                   "min_launch_ms": round(r["min_launch_ms"], 5), "op": op, **props},
         "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 3), "peak": r["peak"],
                      "unit": "TFLOP/s", "frac": round(r["tflops"] / r["peak"], 4),
-                     "traffic": measured_traffic(w)},
+                     "traffic": measured_traffic(w, op)},
         "cpu_baseline": cpu,
     }
 
@@ -232,13 +265,15 @@ def main():
         sys.exit(2)
     names = ([n for n in workloads.WORKLOADS if n[:2] in ("c1", "c2", "c3", "c4", "c5") and "t_" not in n[:4]]
              if a.all else [a.workload])
+    if a.op == "bwd":  # the backward kernels take 16-bit inputs
+        names = [n for n in names if workloads.WORKLOADS[n].dtype != "fp32"]
     for n in names:
         w = workloads.WORKLOADS[n]
-        r = bench_one(w, a.steps, a.warmup)
+        r = bench_one(w, a.steps, a.warmup, a.op)
         cpu = None
         if not a.no_cpu_baseline and n == names[0]:
-            cpu = cpu_baseline(w, a.cpu_seconds)
-        print(json.dumps(line_for(w, r, a.steps, a.warmup, cpu)), flush=True)
+            cpu = cpu_baseline(w, a.cpu_seconds, a.op)
+        print(json.dumps(line_for(w, r, a.steps, a.warmup, cpu, a.op)), flush=True)
     if a.copy_calib_mib > 0:
         import torch
 

@@ -12,7 +12,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_scaled", "fa_bwd", "fa_bwd_workspace_size", "backward", "fa_status_str", "forward", "load_library", "LIB_PATH",
+__all__ = ["fa_fwd", "fa_fwd_scaled", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "forward_splitkv",
+           "fa_bwd", "fa_bwd_workspace_size", "backward", "fa_status_str", "forward", "load_library", "LIB_PATH",
            "FA_DTYPE_FP32", "FA_DTYPE_FP16", "FA_DTYPE_BF16", "FA_OK", "FaError",
            "EXPORTED_SYMBOLS"]
 
@@ -20,7 +21,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_DTYPE_FP32, FA_DTYPE_FP16, FA_DTYPE_BF16 = 0, 1, 2
 FA_OK = 0
-EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_scaled", "fa_bwd", "fa_bwd_workspace_size", "fa_status_str")
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_scaled", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_bwd",
+                    "fa_bwd_workspace_size", "fa_status_str")
 
 _lib = None
 
@@ -48,6 +50,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fa_fwd_scaled.restype = ctypes.c_int
     lib.fa_fwd_scaled.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + \
         [ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_fwd_splitkv_workspace_size.restype = ctypes.c_int64
+    lib.fa_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int64] * 6
+    lib.fa_fwd_splitkv.restype = ctypes.c_int
+    lib.fa_fwd_splitkv.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 6 + \
+        [ctypes.c_double, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.fa_bwd_workspace_size.restype = ctypes.c_int64
     lib.fa_bwd_workspace_size.argtypes = [ctypes.c_int64] * 3
     lib.fa_bwd.restype = ctypes.c_int
@@ -75,6 +82,18 @@ def fa_fwd_scaled(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: 
     """Call the C ``fa_fwd_scaled`` with raw device addresses; returns the status code."""
     return load_library().fa_fwd_scaled(q, k, v, o, lse, B, H, Nq, Nk, D, float(softmax_scale),
                                         int(causal), int(dtype), stream)
+
+
+def fa_fwd_splitkv_workspace_size(B: int, H: int, Nq: int, Nk: int, D: int, num_splits: int) -> int:
+    return int(load_library().fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D, num_splits))
+
+
+def fa_fwd_splitkv(q: int, k: int, v: int, o: int, lse: int, workspace: int, workspace_bytes: int, B: int,
+                   H: int, Nq: int, Nk: int, D: int, softmax_scale: float, num_splits: int, causal: int,
+                   dtype: int, stream: int | None) -> int:
+    """Call the C ``fa_fwd_splitkv`` with raw device addresses; returns the status code."""
+    return load_library().fa_fwd_splitkv(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, D,
+                                         float(softmax_scale), int(num_splits), int(causal), int(dtype), stream)
 
 
 def fa_bwd_workspace_size(B: int, H: int, Nq: int) -> int:
@@ -197,3 +216,38 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, softmax_scale=None, dq
     if rc != FA_OK:
         raise FaError(rc)
     return dq, dk, dv
+
+
+def forward_splitkv(q, k, v, causal: bool = False, num_splits: int = 0, softmax_scale=None, out=None, lse=None,
+                    workspace=None, stream=None):
+    """``forward`` computed with the keys split into ranges (decoding shape:
+    few query rows, many keys).  16-bit dtypes only.  ``num_splits`` 0 picks
+    the count automatically; ``workspace`` (uint8 device tensor of at least
+    ``fa_fwd_splitkv_workspace_size`` bytes) may be given preallocated."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous (B, H, N, D) GPU tensor")
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, D) or tuple(v.shape) != (B, H, Nk, D):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    need = fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D, num_splits)
+    if need < 0:
+        raise ValueError("invalid sizes or num_splits")
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    scale = 1.0 / D**0.5 if softmax_scale is None else float(softmax_scale)
+    if stream is None:
+        with torch.cuda.device(q.device):
+            stream = torch.cuda.current_stream().cuda_stream
+    with torch.cuda.device(q.device):
+        rc = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            workspace.data_ptr(), workspace.numel() * workspace.element_size(), B, H, Nq, Nk,
+                            D, scale, num_splits, bool(causal), _dtype_code(q), stream)
+    if rc != FA_OK:
+        raise FaError(rc)
+    return out, lse

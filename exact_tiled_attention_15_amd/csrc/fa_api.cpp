@@ -86,10 +86,96 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_
   a.dtype = dtype;
   a.scale = scale ? *scale : 1.0 / sqrt((double)D);
   a.stream = stream;
+  a.workspace = nullptr;
   return fa_launch_fwd(a) == 0 ? FA_OK : FA_ERR_HIP;
 }
 
+constexpr int64_t kMaxSplits = 1024;
+
+// Key ranges of the split-KV forward.  Automatic count: enough workgroups
+// for two per CU of a 256-CU device, every range at least 256 keys.  Range
+// length: ceil(Nk / splits) rounded up to whole 64-key tiles; `n` is the
+// number of non-empty ranges it gives.
+void split_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t splits, int64_t* len, int64_t* n) {
+  if (splits <= 0) {
+    const int64_t wgs = BH * ((Nq + 255) / 256);
+    splits = wgs > 0 ? (512 + wgs - 1) / wgs : 1;
+    const int64_t most = (Nk + 255) / 256;
+    if (splits > most) splits = most;
+  }
+  if (splits > kMaxSplits) splits = kMaxSplits;
+  if (splits < 1) splits = 1;
+  int64_t l = (Nk + splits - 1) / splits;
+  l = (l + 63) / 64 * 64;
+  if (l < 64) l = 64;
+  *len = l;
+  *n = Nk > 0 ? (Nk + l - 1) / l : 1;
+}
+
 }  // namespace
+
+extern "C" int64_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                                                 int64_t num_splits) {
+  int64_t BH, rows, per;
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || D < 1 || num_splits < 0 || num_splits > kMaxSplits) return -1;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, Nq, &rows) || !mul_ok(rows, D + 1, &per) || !mul_ok(per, 4, &per))
+    return -1;
+  int64_t len, n;
+  split_plan(BH, Nq, Nk, num_splits, &len, &n);
+  if (n <= 1) return 0;  // one range: the plain forward, no workspace
+  int64_t bytes;
+  if (!mul_ok(per, n, &bytes)) return -1;
+  return bytes;
+}
+
+extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                              void* workspace, int64_t workspace_bytes, int64_t B, int64_t H, int64_t Nq,
+                              int64_t Nk, int64_t D, double softmax_scale, int64_t num_splits, int causal,
+                              int dtype, void* stream) {
+  if (dtype == FA_DTYPE_FP32) return FA_ERR_DTYPE;  // the split path runs the 16-bit kernel
+  bool empty = false;
+  const int st = validate(q, k, v, o, lse, B, H, Nq, Nk, D, dtype, &empty);
+  if (st != FA_OK) return st;
+  if (!scale_ok(softmax_scale)) return FA_ERR_SCALE;
+  if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_SHAPE;
+  if (empty) return FA_OK;
+  const int64_t BH = B * H, rows = BH * Nq;
+  int64_t len, n;
+  split_plan(BH, Nq, Nk, num_splits, &len, &n);
+  FaLaunch a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.BH = BH;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.D = (int)D;
+  a.causal = causal != 0;
+  a.dtype = dtype;
+  a.scale = softmax_scale;
+  a.stream = stream;
+  a.workspace = nullptr;
+  if (n <= 1) return fa_launch_fwd(a) == 0 ? FA_OK : FA_ERR_HIP;
+  // fp32 partials of one (range, head) are addressed with 32-bit offsets
+  if ((Nq + 256) * (D * 4) > INT32_MAX) return FA_ERR_SHAPE;
+  int64_t grid;
+  if (!mul_ok(BH * ((Nq + 255) / 256), n, &grid) || grid > INT32_MAX || rows * (D / 4) / 256 >= INT32_MAX)
+    return FA_ERR_SHAPE;
+  const int64_t need = fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D, num_splits);
+  if (need < 0) return FA_ERR_SHAPE;
+  if (!workspace) return FA_ERR_NULL;
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if ((uintptr_t)workspace & 15u) return FA_ERR_ALIGN;
+  const int64_t esz = 2, qbytes = rows * D * esz, kbytes = BH * Nk * D * esz, lbytes = rows * 4;
+  if (overlaps(workspace, need, q, qbytes) || overlaps(workspace, need, k, kbytes) ||
+      overlaps(workspace, need, v, kbytes) || overlaps(workspace, need, o, qbytes) ||
+      overlaps(workspace, need, lse, lbytes))
+    return FA_ERR_ALIAS;
+  a.workspace = workspace;
+  return fa_launch_fwd_splitkv(a, (int)n, (int)len) == 0 ? FA_OK : FA_ERR_HIP;
+}
 
 extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                       int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal, int dtype,
@@ -185,7 +271,7 @@ extern "C" const char* fa_status_str(int status) {
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or the other output";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch error";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: softmax_scale must be a finite number > 0";
-    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace smaller than fa_bwd_workspace_size()";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace smaller than the *_workspace_size() call returns";
     default: return "unknown fa_status code";
   }
 }

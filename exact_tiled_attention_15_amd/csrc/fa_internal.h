@@ -18,11 +18,17 @@ struct FaLaunch {
   int dtype;  // fa_dtype
   double scale;  // softmax scale applied to q.k (validated: finite, > 0)
   void* stream;
+  void* workspace;  // split-KV partials (fa_launch_fwd_splitkv only)
 };
 
 // Enqueues the forward pass.  Arguments are already validated.  Returns 0 on
 // success, otherwise the HIP error code of the launch.
 int fa_launch_fwd(const FaLaunch& a);
+
+// Split-KV forward (16-bit dtypes): nsplit key ranges of split_len keys
+// (nsplit = ceil(Nk / split_len)) write fp32 partials to a.workspace
+// (nsplit * BH * Nq * (D + 1) floats), then a merge kernel writes o and lse.
+int fa_launch_fwd_splitkv(const FaLaunch& a, int nsplit, int split_len);
 
 struct FaBwdLaunch {
   const void* q;

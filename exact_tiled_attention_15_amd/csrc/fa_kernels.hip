@@ -161,13 +161,19 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
   }
 }
 
-template <int DT, int D, bool CAUSAL>
+// SPLIT: the grid also runs over key ranges of `split_len` keys; the
+// workgroup of range s attends to keys [s split_len, (s+1) split_len) only
+// and writes its normalised fp32 partial O_s and LSE_s (rows with no key in
+// the range: O_s = 0, LSE_s = -inf) to Po / Pl, laid out [s][B*H][Nq][D] and
+// [s][B*H][Nq]; merge_splits combines them.
+template <int DT, int D, bool CAUSAL, bool SPLIT = false>
 __global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict__ Qg,
                                                            const u16* __restrict__ Kg,
                                                            const u16* __restrict__ Vg,
                                                            u16* __restrict__ Og,
                                                            float* __restrict__ Lg, int BH, int Nq,
-                                                           int Nk, int nqt, float sl2) {
+                                                           int Nk, int nqt, float sl2, int split_len,
+                                                           float* __restrict__ Po, float* __restrict__ Pl) {
   constexpr int BC = 64;
   constexpr int ROWB = D * 2;             // bytes per row
   constexpr int TILEB = BC * ROWB;        // bytes per K (or V) tile
@@ -186,20 +192,33 @@ __global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict
   w.wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   w.hf = w.lane >> 5;
   w.l32 = w.lane & 31;
-  int bh, qt;
-  tile_of_block(nqt, BH, bh, qt);
+  int bh, qt, split = 0;
+  if constexpr (SPLIT) {
+    const int per = BH * nqt;
+    split = blockIdx.x / per;
+    const int rem = blockIdx.x - split * per;
+    bh = rem % BH;
+    qt = nqt - 1 - rem / BH;
+  } else {
+    tile_of_block(nqt, BH, bh, qt);
+  }
   const int q0 = qt * kBR16;
-  const u16* Kh = Kg + (size_t)bh * Nk * D;
-  const u16* Vh = Vg + (size_t)bh * Nk * D;
-  const int kbytes = Nk * ROWB;
+  // This workgroup's keys: [kb, kb + nk) of the head (all of them unless
+  // SPLIT); key indices below are relative to kb.
+  const int kb = SPLIT ? split * split_len : 0;
+  const int nk = SPLIT ? min(split_len, Nk - kb) : Nk;
+  const u16* Kh = Kg + ((size_t)bh * Nk + kb) * D;
+  const u16* Vh = Vg + ((size_t)bh * Nk + kb) * D;
+  const int kbytes = nk * ROWB;
 
-  const int kend = CAUSAL ? min(Nk, min(q0 + kBR16, Nq)) : Nk;  // keys [0, kend) are needed
-  const int nt = (kend + BC - 1) / BC;
+  const int kend = CAUSAL ? min(nk, min(q0 + kBR16, Nq) - kb) : nk;  // keys [0, kend) are needed
+  const int nt = kend > 0 ? (kend + BC - 1) / BC : 0;
   w.wq0 = q0 + 32 * w.wave;
   const int myq = w.wq0 + w.l32;
-  w.wkend = CAUSAL ? min(kend, w.wq0 + 32) : kend;
-  w.klim = CAUSAL ? min(myq, Nk - 1) : Nk - 1;
-  w.wklim = CAUSAL ? min(w.wq0, Nk - 1) : Nk - 1;
+  // A wave whose rows all lie past Nq computes nothing.
+  w.wkend = w.wq0 >= Nq ? 0 : CAUSAL ? min(kend, w.wq0 + 32 - kb) : kend;
+  w.klim = CAUSAL ? min(myq - kb, nk - 1) : nk - 1;
+  w.wklim = CAUSAL ? min(w.wq0 - kb, nk - 1) : nk - 1;
   init_operand_offsets<D>(w);
 
   // Q fragment (B operand of S^T): lane holds Q[myq][16*kk + 8*hf .. +7];
@@ -214,7 +233,7 @@ __global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict
                                                      q0 * ROWB, 0);
   }
   // Tiles 0..2 into stages 0..2.
-  issue_tile16<D, kWaves16>(Kh, Vh, kbytes, 0, stage0, w);
+  if (!SPLIT || nt > 0) issue_tile16<D, kWaves16>(Kh, Vh, kbytes, 0, stage0, w);
   if (nt > 1) issue_tile16<D, kWaves16>(Kh, Vh, kbytes, 1, stage1, w);
   if (nt > 2) issue_tile16<D, kWaves16>(Kh, Vh, kbytes, 2, stage2, w);
 
@@ -232,9 +251,41 @@ __global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict
     if (j + 3 < nt) tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 3, nt, stage3, stage2, w, qf, oacc, mref, l, sl2);
   }
 
-  // Epilogue: combine the two half-row sums, normalise, round to 16 bits,
-  // store (rows past Nq are dropped by the buffer range check).
   const float lt = pair_sum(l);
+  if constexpr (SPLIT) {
+    // fp32 partial of this key range (rows past Nq dropped by the range check).
+    // Stores of 8 bytes, from two address registers so that they are not
+    // merged into 16-byte stores: this compiler lets a VALU instruction
+    // overwrite the data registers of a 16-byte store right after issuing it,
+    // and on gfx950 the store then wrote corrupted data (seen on the first
+    // dword, in the last four lanes of each 16).
+    const bool none = !(lt > 0.f);
+    const float inv = none ? 0.f : 1.0f / lt;
+    const size_t slot = (size_t)split * BH + bh;
+    const auto rP = make_rsrc(Po + slot * Nq * D, Nq * D * 4);
+    const int off0 = (32 * w.wave + w.l32) * D * 4 + 4 * w.hf * 4;
+    int off1 = off0 + 8;
+    asm volatile("" : "+v"(off1));
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x2 v0 = {oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv};
+        const f32x2 v1 = {oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv};
+        const int col = (32 * dt + 8 * g) * 4;
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v0), rP, off0 + col, q0 * D * 4, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v1), rP, off1 + col, q0 * D * 4, 0);
+      }
+    if (w.hf == 0) {
+      const auto rL = make_rsrc(Pl + slot * Nq, Nq * 4);
+      const float lse = none ? -INFINITY : (mref + __log2f(lt)) * kLn2;
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse), rL, (32 * w.wave + w.l32) * 4,
+                                            q0 * 4, 0);
+    }
+    return;
+  }
+  // Epilogue: normalise by the combined half-row sums, round to 16 bits,
+  // store (rows past Nq are dropped by the buffer range check).
   const float inv = 1.0f / lt;
   const auto rO = make_rsrc(Og + (size_t)bh * Nq * D, Nq * ROWB);
 #pragma unroll
@@ -419,11 +470,72 @@ int launch(KernelT kern, const FaLaunch& a, int rows_per_block, int threads, flo
   return (int)hipGetLastError();
 }
 
+template <int DT, int D, bool CAUSAL, bool SPLIT>
+void launch16(const FaLaunch& a, float sl2, int nsplit, int split_len, float* Po, float* Pl) {
+  const int nqt = (int)((a.Nq + kBR16 - 1) / kBR16);
+  const dim3 grid((unsigned)(a.BH * nqt * nsplit)), block(kThreads16);
+  hipLaunchKernelGGL((fa_fwd_16<DT, D, CAUSAL, SPLIT>), grid, block, 0, (hipStream_t)a.stream, (const u16*)a.q,
+                     (const u16*)a.k, (const u16*)a.v, (u16*)a.o, a.lse, (int)a.BH, (int)a.Nq, (int)a.Nk, nqt,
+                     sl2, split_len, Po, Pl);
+}
+
 template <int DT, int D>
 int dispatch16(const FaLaunch& a, float sl2) {
   if (a.causal)
-    return launch<decltype(&fa_fwd_16<DT, D, true>), u16>(&fa_fwd_16<DT, D, true>, a, kBR16, kThreads16, sl2);
-  return launch<decltype(&fa_fwd_16<DT, D, false>), u16>(&fa_fwd_16<DT, D, false>, a, kBR16, kThreads16, sl2);
+    launch16<DT, D, true, false>(a, sl2, 1, 0, nullptr, nullptr);
+  else
+    launch16<DT, D, false, false>(a, sl2, 1, 0, nullptr, nullptr);
+  return (int)hipGetLastError();
+}
+
+// Merge of the key-range partials: the numerically stable associative
+// update that folds partial results into one output row ("Building a
+// FlashAttention-2 Forward Kernel in Pure NumPy", Architecture Overview),
+// exact through the partials' log-sum-exps:
+//   LSE = ln sum_s exp(LSE_s),  O = sum_s exp(LSE_s - LSE) O_s.
+// D/4 lanes per row, four columns each.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void merge_splits(const float* __restrict__ Po, const float* __restrict__ Pl,
+                                                    u16* __restrict__ Og, float* __restrict__ Lg, int64_t rows,
+                                                    int nsplit) {
+  constexpr int LPR = D / 4;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = t / LPR;
+  const int c = (int)(t % LPR);
+  if (row >= rows) return;
+  float m = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, Pl[s * rows + row]);
+  float tot = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nsplit; ++s) {
+    const float ls = Pl[s * rows + row];
+    if (ls == -INFINITY) continue;  // no key of this range reaches the row
+    const float wgt = __expf(ls - m);
+    tot += wgt;
+    const f32x4 o = *(const f32x4*)(Po + (s * rows + row) * D + 4 * c);
+    acc += wgt * o;
+  }
+  const float inv = 1.0f / tot;
+  u32x2 v;
+  v[0] = pack2<DT>(acc[0] * inv, acc[1] * inv);
+  v[1] = pack2<DT>(acc[2] * inv, acc[3] * inv);
+  *(u32x2*)(Og + row * D + 4 * c) = v;
+  if (c == 0) Lg[row] = m + __logf(tot);
+}
+
+template <int DT, int D>
+int dispatch16_split(const FaLaunch& a, float sl2, int nsplit, int split_len) {
+  const int64_t rows = a.BH * a.Nq;
+  float* Po = (float*)a.workspace;
+  float* Pl = Po + (size_t)nsplit * rows * D;
+  if (a.causal)
+    launch16<DT, D, true, true>(a, sl2, nsplit, split_len, Po, Pl);
+  else
+    launch16<DT, D, false, true>(a, sl2, nsplit, split_len, Po, Pl);
+  const int64_t threads = rows * (D / 4);
+  hipLaunchKernelGGL((merge_splits<DT, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     (hipStream_t)a.stream, (const float*)Po, (const float*)Pl, (u16*)a.o, a.lse, rows, nsplit);
+  return (int)hipGetLastError();
 }
 
 template <int D>
@@ -433,6 +545,21 @@ int dispatch32(const FaLaunch& a, float sl2) {
 }
 
 }  // namespace
+
+int fa_launch_fwd_splitkv(const FaLaunch& a, int nsplit, int split_len) {
+  const float sl2 = (float)(a.scale * 1.4426950408889634074);
+  (void)hipGetLastError();  // clear a stale error so that the check below is ours
+  switch (a.dtype) {
+    case kBF16:
+      return a.D == 32 ? dispatch16_split<kBF16, 32>(a, sl2, nsplit, split_len)
+           : a.D == 64 ? dispatch16_split<kBF16, 64>(a, sl2, nsplit, split_len)
+                       : dispatch16_split<kBF16, 128>(a, sl2, nsplit, split_len);
+    default:
+      return a.D == 32 ? dispatch16_split<kFP16, 32>(a, sl2, nsplit, split_len)
+           : a.D == 64 ? dispatch16_split<kFP16, 64>(a, sl2, nsplit, split_len)
+                       : dispatch16_split<kFP16, 128>(a, sl2, nsplit, split_len);
+  }
+}
 
 int fa_launch_fwd(const FaLaunch& a) {
   // scale * log2(e), computed in double and rounded once.

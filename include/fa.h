@@ -60,7 +60,7 @@ typedef enum {
   FA_ERR_HIP = 7,      /* the HIP runtime reported an error at launch */
   FA_ERR_SCALE = 8,    /* softmax_scale not a finite number > 0 (or so small that
                           softmax_scale * log2(e) is not a normal float) */
-  FA_ERR_WORKSPACE = 9 /* workspace_bytes below fa_bwd_workspace_size() */
+  FA_ERR_WORKSPACE = 9 /* workspace_bytes below the matching *_workspace_size() */
 } fa_status;
 
 /*
@@ -100,6 +100,48 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_scaled(const void* q, const void* k, const void* v, void* o, float* lse,
                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
                   double softmax_scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_fwd_splitkv_workspace_size -- bytes of device workspace fa_fwd_splitkv
+ * needs for these sizes and num_splits (0 = automatic, as fa_fwd_splitkv
+ * chooses): (D + 1) fp32 values per query row and key range, or 0 when the
+ * call runs as one range.  -1 for negative or overflowing sizes or
+ * num_splits outside [0, 1024].
+ */
+int64_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                                      int64_t num_splits);
+
+/*
+ * fa_fwd_splitkv -- the same result as fa_fwd_scaled, computed with the keys
+ * of every head split into ranges that separate workgroups process in
+ * parallel: the shape of decoding with a KV cache ("Python Attention
+ * Mechanisms Explained", Causal Masking and Incremental Decoding: a few new
+ * query rows against many cached keys), where one workgroup per head and
+ * query tile would leave most of the GPU idle.  Each range writes an exact
+ * partial (O_s, LSE_s) in fp32 to the workspace; a second kernel combines
+ * them with the associative update that folds partial results into one
+ * output row ("Building a FlashAttention-2 Forward Kernel in Pure NumPy",
+ * Architecture Overview):
+ *
+ *     LSE = ln sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s.
+ *
+ *   num_splits  number of key ranges, 0 for automatic (enough workgroups to
+ *               fill the GPU, at least 256 keys a range); at most 1024.  The
+ *               range length is rounded up to whole 64-key tiles, so fewer
+ *               ranges may result; with one range this is fa_fwd_scaled.
+ *   workspace   device memory of fa_fwd_splitkv_workspace_size(...) bytes
+ *               (may be NULL when that is 0), 16-byte aligned, owned by the
+ *               caller; scratch after the call.
+ *
+ * Every other argument, layout and error is that of fa_fwd_scaled, except
+ * that dtype must be FA_DTYPE_FP16 or FA_DTYPE_BF16 (FA_ERR_DTYPE otherwise);
+ * FA_ERR_WORKSPACE for a short workspace; FA_ERR_ALIAS if it overlaps an
+ * input or output.
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   void* workspace, int64_t workspace_bytes, int64_t B, int64_t H, int64_t Nq,
+                   int64_t Nk, int64_t D, double softmax_scale, int64_t num_splits, int causal,
+                   int dtype, void* stream);
 
 /*
  * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs: two fp32

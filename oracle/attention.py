@@ -36,7 +36,7 @@ import math
 
 import numpy as np
 
-__all__ = ["attention_forward", "attention_rows", "scores_row"]
+__all__ = ["attention_forward", "attention_rows", "scores_row", "attention_partial", "merge_partials"]
 
 
 def _as_f64(x) -> np.ndarray:
@@ -141,3 +141,49 @@ def scores_row(q, k, b: int, h: int, i: int, causal: bool, scale=None):
     if causal:
         s = np.where(np.arange(kh.shape[0]) <= i, s, -np.inf)
     return s
+
+
+def attention_partial(q, k, v, causal: bool, k0: int, k1: int, scale=None):
+    """Exact attention of every query row against keys [k0, k1) only (the
+    causal mask still compares absolute indices).  Rows that see no key of
+    the range get O = 0 and LSE = -inf (the empty sum).  Returns float64
+    (O (B, H, Nq, D), LSE (B, H, Nq))."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, H, Nq, Nk, D = _check(q, k, v)
+    if not 0 <= k0 < k1 <= Nk:
+        raise ValueError(f"key range [{k0}, {k1}) outside [0, {Nk})")
+    scale = _scale(D, scale)
+    O = np.zeros((B, H, Nq, D))
+    L = np.full((B, H, Nq), -np.inf)
+    keys = np.arange(k0, k1)
+    for b in range(B):
+        for h in range(H):
+            s = (q[b, h] @ k[b, h, k0:k1].T) * scale
+            if causal:
+                s = np.where(keys[None, :] <= np.arange(Nq)[:, None], s, -np.inf)
+            seen = np.isfinite(s).any(axis=1)
+            if not seen.any():
+                continue
+            sr = s[seen]
+            m = sr.max(axis=1)
+            e = np.exp(sr - m[:, None])
+            l = e.sum(axis=1)
+            O[b, h, seen] = (e @ v[b, h, k0:k1]) / l[:, None]
+            L[b, h, seen] = m + np.log(l)
+    return O, L
+
+
+def merge_partials(parts):
+    """Combine exact partials (O_s, LSE_s) over disjoint key ranges into the
+    result over their union, by the numerically stable associative update
+    that folds partial results into one output row ("Building a
+    FlashAttention-2 Forward Kernel in Pure NumPy", Architecture Overview):
+    LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s (empty partials,
+    LSE_s = -inf, weigh nothing)."""
+    Ls = np.stack([np.asarray(L, dtype=np.float64) for _, L in parts])
+    Os = np.stack([np.asarray(O, dtype=np.float64) for O, _ in parts])
+    m = Ls.max(axis=0)
+    w = np.exp(Ls - m[None])
+    tot = w.sum(axis=0)
+    O = (w[..., None] * Os).sum(axis=0) / tot[..., None]
+    return O, m + np.log(tot)

@@ -148,3 +148,37 @@ def test_bwd_noop_cases():
     assert call_bwd(Nq=0, q=0, o=0, lse=0, dout=0, dq=0, ws=0, v=0) == 1
     # an exact-size workspace passes the size check (reaches the alias check here)
     assert call_bwd(ws_bytes=8 * 2 * 4 * 128, ws=DQ + 64) == 6
+
+
+def call_split(q=Q, k=K, v=V, o=O, lse=L, ws=WS, ws_bytes=1 << 30, B=1, H=4, Nq=4, Nk=8192, D=128,
+               scale=0.1, splits=0, causal=0, dtype=2):
+    return fa.fa_fwd_splitkv(q, k, v, o, lse, ws, ws_bytes, B, H, Nq, Nk, D, scale, splits, causal, dtype, None)
+
+
+def test_splitkv_workspace_size():
+    # explicit count: (D + 1) floats per row and range
+    assert fa.fa_fwd_splitkv_workspace_size(1, 4, 4, 8192, 128, 8) == 8 * 4 * 4 * 129 * 4
+    # range length rounds up to 64-key tiles: 1000 keys in 3 ranges -> 384 keys a range -> 3 ranges
+    assert fa.fa_fwd_splitkv_workspace_size(1, 1, 2, 1000, 64, 3) == 3 * 2 * 65 * 4
+    # 100 keys in 7 ranges -> 64-key ranges -> only 2 ranges
+    assert fa.fa_fwd_splitkv_workspace_size(1, 1, 2, 100, 64, 7) == 2 * 2 * 65 * 4
+    # one range: the plain forward, no workspace
+    assert fa.fa_fwd_splitkv_workspace_size(1, 4, 4, 8192, 128, 1) == 0
+    assert fa.fa_fwd_splitkv_workspace_size(1, 4, 4, 60, 128, 0) == 0
+    # automatic count: 4 heads x 1 query tile -> 128 ranges wanted, capped by 8192/256 = 32
+    assert fa.fa_fwd_splitkv_workspace_size(1, 4, 4, 8192, 128, 0) == 32 * 4 * 4 * 129 * 4
+    assert fa.fa_fwd_splitkv_workspace_size(1, 4, 4, 8192, 128, -1) == -1
+    assert fa.fa_fwd_splitkv_workspace_size(1, 4, 4, 8192, 128, 1025) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), 4), (dict(D=16), 3), (dict(scale=0.0), 8), (dict(splits=-1), 2), (dict(splits=5000), 2),
+    (dict(q=0), 1), (dict(ws=0), 1), (dict(ws_bytes=32 * 4 * 4 * 129 * 4 - 1), 9), (dict(ws=WS + 8), 5),
+    (dict(ws=K + 4096), 6), (dict(ws=L - 64), 6), (dict(o=Q), 6), (dict(Nk=0), 2),
+])
+def test_splitkv_validation_codes(kw, code):
+    assert call_split(**kw) == code
+
+
+def test_splitkv_noop():
+    assert call_split(B=0, q=0, k=0, v=0, o=0, lse=0, ws=0, ws_bytes=0) == 0

@@ -1,0 +1,79 @@
+"""The gfx950 device code, compiled to assembly on the CPU, checked for a
+store-data hazard: a VMEM store of more than 8 bytes whose data registers
+the very next VALU instruction overwrites.  This compiler does not separate
+the two, and on the MI355X such a store wrote corrupted data (the split-KV
+partials, before they were stored 8 bytes at a time)."""
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "exact_tiled_attention_15_amd", "csrc")
+SOURCES = ["fa_kernels.hip", "fa_bwd.hip"]
+
+WIDE_STORE = re.compile(r"^(buffer|global|flat)_store_dwordx[34]\b")
+
+
+def _hipcc():
+    for c in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if c and os.path.exists(c):
+            return c
+    return None
+
+
+def _asm(src, out):
+    import exact_tiled_attention_15_amd.build as b
+
+    cmd = [_hipcc(), "-O3", "-std=c++17", f"--offload-arch={b.ARCH}", "-fno-honor-nans", "--cuda-device-only",
+           "-S", *b.DEVICE_FLAGS, "-I", os.path.join(ROOT, "include"), os.path.join(CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return open(out).read()
+
+
+def _data_regs(line):
+    """VGPR range of a wide store's data operand."""
+    ops = re.findall(r"v\[(\d+):(\d+)\]|v(\d+)", line.split(None, 1)[1])
+    d = ops[0] if line.startswith("buffer") else ops[1]
+    return (int(d[0]), int(d[1])) if d[0] else (int(d[2]), int(d[2]))
+
+
+def hazards(asm_text):
+    lines = [l.strip() for l in asm_text.split("\n")]
+    found = []
+    for i, s in enumerate(lines):
+        if not WIDE_STORE.match(s):
+            continue
+        lo, hi = _data_regs(s)
+        for n in lines[i + 1:i + 4]:
+            if not n or n.startswith(";"):
+                continue
+            m = re.match(r"v_\w+\s+v(\d+)\b", n)
+            if m and lo <= int(m.group(1)) <= hi:
+                found.append((s, n))
+            break
+    return found
+
+
+def test_scanner_catches_the_pattern():
+    bad = "\tbuffer_store_dwordx4 v[2:5], v20, s[0:3], s4 offen\n\tv_mul_f32_e32 v2, v19, v6\n"
+    ok = "\tbuffer_store_dwordx4 v[2:5], v20, s[0:3], s4 offen\n\ts_nop 0\n\tv_mul_f32_e32 v2, v19, v6\n"
+    ok2 = "\tbuffer_store_dwordx2 v[2:3], v20, s[0:3], s4 offen\n\tv_mul_f32_e32 v2, v19, v6\n"
+    g = "\tglobal_store_dwordx4 v[8:9], v[2:5], off\n\tv_add_f32_e32 v3, v1, v1\n"
+    assert len(hazards(bad)) == 1 and not hazards(ok) and not hazards(ok2) and len(hazards(g)) == 1
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
+def test_device_code_has_no_wide_store_data_hazard():
+    with tempfile.TemporaryDirectory() as d:
+        with ThreadPoolExecutor(len(SOURCES)) as ex:
+            texts = list(ex.map(lambda s: _asm(s, os.path.join(d, s + ".s")), SOURCES))
+    for src, text in zip(SOURCES, texts):
+        assert "v_mfma" in text, f"{src}: no device code?"
+        h = hazards(text)
+        assert not h, f"{src}: {len(h)} wide stores with their data overwritten next: {h[:3]}"

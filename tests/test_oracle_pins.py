@@ -96,3 +96,38 @@ def test_oracle_explicit_scale():
     from scipy.special import logsumexp
 
     assert abs(logsumexp(s) - L[0, 1, 7]) <= 1e-12
+
+
+def test_partials_merge_to_the_full_result():
+    # The associative update: exact partials over disjoint key ranges merge
+    # into the exact result over all keys (any split, causal ranges that some
+    # rows cannot see included), and one range is the whole computation.
+    r = np.random.default_rng(12)
+    q = r.standard_normal((2, 2, 13, 8)) * 2.0
+    k = r.standard_normal((2, 2, 37, 8))
+    v = r.standard_normal((2, 2, 37, 8))
+    for causal in (False, True):
+        O, L = oracle.attention_forward(q, k, v, causal)
+        for cuts in ([0, 37], [0, 5, 37], [0, 1, 2, 20, 36, 37], [0, 12, 13, 14, 37]):
+            parts = [oracle.attention_partial(q, k, v, causal, a, b) for a, b in zip(cuts, cuts[1:])]
+            Om, Lm = oracle.merge_partials(parts)
+            assert np.max(np.abs(Om - O)) <= 1e-12 and np.max(np.abs(Lm - L)) <= 1e-12
+        # a range past every row's last key (causal) is empty
+        if causal:
+            Oe, Le = oracle.attention_partial(q, k, v, True, 13, 37)
+            assert np.all(Le == -np.inf) and np.all(Oe == 0.0)
+    # one range equals the partial over all keys
+    Op, Lp = oracle.attention_partial(q, k, v, False, 0, 37)
+    O, L = oracle.attention_forward(q, k, v, False)
+    assert np.max(np.abs(Op - O)) <= 1e-13 and np.max(np.abs(Lp - L)) <= 1e-13
+
+
+def test_partial_against_brute_force_on_the_range():
+    # a non-causal partial is the plain definition on the sliced keys
+    r = np.random.default_rng(13)
+    q = r.standard_normal((1, 2, 4, 3))
+    k = r.standard_normal((1, 2, 9, 3))
+    v = r.standard_normal((1, 2, 9, 3))
+    Op, Lp = oracle.attention_partial(q, k, v, False, 2, 7)
+    Ob, Lb = pins.brute_force(q, k[:, :, 2:7], v[:, :, 2:7], False)
+    assert np.max(np.abs(Op - Ob)) <= 1e-12 and np.max(np.abs(Lp - Lb)) <= 1e-12

@@ -93,6 +93,11 @@ WORKLOADS: Dict[str, Workload] = {
            note="ragged, Nq != Nk, non-causal"),
         _w("c3t_bf16_causal_b1h3n1000d128", 1, 3, 1000, 1000, 128, "bf16", True, 6,
            note="bf16 D=128 causal with a ragged tail"),
+        # decoding against a KV cache (split-KV path; HBM-bound)
+        _w("d1_bf16_decode_b8h32q1k32768d128", 8, 32, 1, 32768, 128, "bf16", False, 7,
+           note="one new query row per sequence against a 32K-key cache"),
+        _w("d2_bf16_decode_b1h32q16k65536d128", 1, 32, 16, 65536, 128, "bf16", False, 8,
+           note="16 query rows (a draft block) against a 64K-key cache, one sequence"),
     ]
 }
 
