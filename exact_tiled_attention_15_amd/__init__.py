@@ -12,7 +12,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_scaled", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "forward_splitkv",
+__all__ = ["fa_fwd", "fa_fwd_scaled", "fa_fwd_varlen", "forward_varlen", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "forward_splitkv",
            "fa_bwd", "fa_bwd_workspace_size", "backward", "fa_status_str", "forward", "load_library", "LIB_PATH",
            "FA_DTYPE_FP32", "FA_DTYPE_FP16", "FA_DTYPE_BF16", "FA_OK", "FaError",
            "EXPORTED_SYMBOLS"]
@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_DTYPE_FP32, FA_DTYPE_FP16, FA_DTYPE_BF16 = 0, 1, 2
 FA_OK = 0
-EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_scaled", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_bwd",
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_scaled", "fa_fwd_varlen", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_bwd",
                     "fa_bwd_workspace_size", "fa_status_str")
 
 _lib = None
@@ -49,6 +49,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.fa_fwd_scaled.restype = ctypes.c_int
     lib.fa_fwd_scaled.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + \
+        [ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_fwd_varlen.restype = ctypes.c_int
+    lib.fa_fwd_varlen.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int64] * 6 + \
         [ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.fa_fwd_splitkv_workspace_size.restype = ctypes.c_int64
     lib.fa_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int64] * 6
@@ -82,6 +85,14 @@ def fa_fwd_scaled(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: 
     """Call the C ``fa_fwd_scaled`` with raw device addresses; returns the status code."""
     return load_library().fa_fwd_scaled(q, k, v, o, lse, B, H, Nq, Nk, D, float(softmax_scale),
                                         int(causal), int(dtype), stream)
+
+
+def fa_fwd_varlen(q: int, k: int, v: int, o: int, lse: int, cu_q: int, cu_k: int, B: int, H: int, total_q: int,
+                  total_k: int, max_seqlen_q: int, D: int, softmax_scale: float, causal: int, dtype: int,
+                  stream: int | None) -> int:
+    """Call the C ``fa_fwd_varlen`` with raw device addresses; returns the status code."""
+    return load_library().fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, B, H, total_q, total_k, max_seqlen_q, D,
+                                        float(softmax_scale), int(causal), int(dtype), stream)
 
 
 def fa_fwd_splitkv_workspace_size(B: int, H: int, Nq: int, Nk: int, D: int, num_splits: int) -> int:
@@ -248,6 +259,44 @@ def forward_splitkv(q, k, v, causal: bool = False, num_splits: int = 0, softmax_
         rc = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                             workspace.data_ptr(), workspace.numel() * workspace.element_size(), B, H, Nq, Nk,
                             D, scale, num_splits, bool(causal), _dtype_code(q), stream)
+    if rc != FA_OK:
+        raise FaError(rc)
+    return out, lse
+
+
+def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool = False,
+                   softmax_scale=None, out=None, lse=None, stream=None):
+    """Attention over packed variable-length sequences (16-bit dtypes).
+
+    q: (H, total_q, D), k/v: (H, total_k, D) contiguous GPU tensors (head-major
+    packing); cu_seqlens_q / cu_seqlens_k: int32 GPU tensors of B + 1
+    offsets; max_seqlen_q: the longest sequence's query count.  Returns
+    (O (H, total_q, D), LSE (H, total_q) float32).
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2]:
+        raise ValueError(f"expected q (H, total_q, D), k and v (H, total_k, D); got {tuple(q.shape)} {tuple(k.shape)}")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if cu_seqlens_q.shape != cu_seqlens_k.shape or cu_seqlens_q.dim() != 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be (B + 1,)")
+    H, total_q, D = q.shape
+    total_k = k.shape[1]
+    B = cu_seqlens_q.shape[0] - 1
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    scale = 1.0 / D**0.5 if softmax_scale is None else float(softmax_scale)
+    if stream is None:
+        with torch.cuda.device(q.device):
+            stream = torch.cuda.current_stream().cuda_stream
+    with torch.cuda.device(q.device):
+        rc = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                           cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, total_q, total_k,
+                           int(max_seqlen_q), D, scale, bool(causal), _dtype_code(q), stream)
     if rc != FA_OK:
         raise FaError(rc)
     return out, lse

@@ -189,6 +189,59 @@ extern "C" int fa_fwd_scaled(const void* q, const void* k, const void* v, void* 
   return fwd(q, k, v, o, lse, B, H, Nq, Nk, D, &softmax_scale, causal, dtype, stream);
 }
 
+extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int64_t B, int64_t H,
+                             int64_t total_q, int64_t total_k, int64_t max_seqlen_q, int64_t D,
+                             double softmax_scale, int causal, int dtype, void* stream) {
+  if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;  // the 16-bit kernel
+  if (B < 0 || H < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || D < 0) return FA_ERR_SHAPE;
+  if (D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (!scale_ok(softmax_scale)) return FA_ERR_SCALE;
+  int64_t BH, qel, kel;
+  if (!mul_ok(B, H, &BH) || !mul_ok(H, total_q, &qel) || !mul_ok(qel, D, &qel) || !mul_ok(H, total_k, &kel) ||
+      !mul_ok(kel, D, &kel))
+    return FA_ERR_SHAPE;
+  if (BH == 0 || total_q == 0 || max_seqlen_q == 0) return FA_OK;  // no query row to compute
+  if (max_seqlen_q > total_q || total_q > INT32_MAX / 2 || total_k > INT32_MAX / 2 || BH > INT32_MAX)
+    return FA_ERR_SHAPE;
+  const int64_t esz = 2;
+  // one head's packed rows are addressed with 32-bit offsets
+  if ((total_q + 256) * D * esz > INT32_MAX || (total_k + 256) * D * esz > INT32_MAX) return FA_ERR_SHAPE;
+  int64_t grid;
+  if (!mul_ok(BH, (max_seqlen_q + 255) / 256, &grid) || grid > INT32_MAX) return FA_ERR_SHAPE;
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULL;
+  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) ||
+      (((uintptr_t)lse | (uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) & 3u))
+    return FA_ERR_ALIGN;
+  const int64_t qbytes = qel * esz, kbytes = kel * esz, lbytes = H * total_q * 4, cbytes = (B + 1) * 4;
+  const void* ins[5] = {q, k, v, cu_seqlens_q, cu_seqlens_k};
+  const int64_t in_bytes[5] = {qbytes, kbytes, kbytes, cbytes, cbytes};
+  for (int j = 0; j < 5; ++j)
+    if (overlaps(o, qbytes, ins[j], in_bytes[j]) || overlaps(lse, lbytes, ins[j], in_bytes[j])) return FA_ERR_ALIAS;
+  if (overlaps(o, qbytes, lse, lbytes)) return FA_ERR_ALIAS;
+  FaLaunch a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.BH = BH;
+  a.Nq = max_seqlen_q;
+  a.Nk = 0;
+  a.D = (int)D;
+  a.causal = causal != 0;
+  a.dtype = dtype;
+  a.scale = softmax_scale;
+  a.stream = stream;
+  a.workspace = nullptr;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.H = H;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  return fa_launch_fwd_varlen(a) == 0 ? FA_OK : FA_ERR_HIP;
+}
+
 extern "C" int64_t fa_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq) {
   int64_t BH, rows, bytes;
   if (!mul_ok(B, H, &BH) || !mul_ok(BH, Nq, &rows) || !mul_ok(rows, 8, &bytes)) return -1;

@@ -19,6 +19,13 @@ struct FaLaunch {
   double scale;  // softmax scale applied to q.k (validated: finite, > 0)
   void* stream;
   void* workspace;  // split-KV partials (fa_launch_fwd_splitkv only)
+  // packed variable-length batches (fa_launch_fwd_varlen only): BH = B*H,
+  // Nq = longest sequence's query count, offsets on the device
+  const int* cu_q = nullptr;
+  const int* cu_k = nullptr;
+  int64_t H = 0;
+  int64_t total_q = 0;
+  int64_t total_k = 0;
 };
 
 // Enqueues the forward pass.  Arguments are already validated.  Returns 0 on
@@ -29,6 +36,10 @@ int fa_launch_fwd(const FaLaunch& a);
 // (nsplit = ceil(Nk / split_len)) write fp32 partials to a.workspace
 // (nsplit * BH * Nq * (D + 1) floats), then a merge kernel writes o and lse.
 int fa_launch_fwd_splitkv(const FaLaunch& a, int nsplit, int split_len);
+
+// Packed variable-length forward (16-bit dtypes): q, o [H, total_q, D];
+// k, v [H, total_k, D]; lse [H, total_q]; per-sequence offsets cu_q, cu_k.
+int fa_launch_fwd_varlen(const FaLaunch& a);
 
 struct FaBwdLaunch {
   const void* q;

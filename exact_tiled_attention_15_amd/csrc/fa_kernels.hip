@@ -166,14 +166,21 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
 // and writes its normalised fp32 partial O_s and LSE_s (rows with no key in
 // the range: O_s = 0, LSE_s = -inf) to Po / Pl, laid out [s][B*H][Nq][D] and
 // [s][B*H][Nq]; merge_splits combines them.
-template <int DT, int D, bool CAUSAL, bool SPLIT = false>
+// VARLEN: packed sequences of different lengths.  q, o are [H, tq, D], k, v
+// [H, tk, D] and lse [H, tq]; sequence b owns query rows [cuq[b], cuq[b+1])
+// and key rows [cuk[b], cuk[b+1]) (offsets clamped into [0, tq] / [0, tk]);
+// BH = B*H, Nq = the longest sequence's query count (sets nqt).  Rows of a
+// sequence without keys get O = 0 and LSE = -inf.
+template <int DT, int D, bool CAUSAL, bool SPLIT = false, bool VARLEN = false>
 __global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict__ Qg,
                                                            const u16* __restrict__ Kg,
                                                            const u16* __restrict__ Vg,
                                                            u16* __restrict__ Og,
                                                            float* __restrict__ Lg, int BH, int Nq,
                                                            int Nk, int nqt, float sl2, int split_len,
-                                                           float* __restrict__ Po, float* __restrict__ Pl) {
+                                                           float* __restrict__ Po, float* __restrict__ Pl,
+                                                           const int* __restrict__ cuq, const int* __restrict__ cuk,
+                                                           int H, int tq, int tk) {
   constexpr int BC = 64;
   constexpr int ROWB = D * 2;             // bytes per row
   constexpr int TILEB = BC * ROWB;        // bytes per K (or V) tile
@@ -203,20 +210,45 @@ __global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict
     tile_of_block(nqt, BH, bh, qt);
   }
   const int q0 = qt * kBR16;
+  // This head's rows: nq queries at Qh / Oh / Lh, NK keys at Kg + koff.
+  const u16* Qh;
+  u16* Oh;
+  float* Lh;
+  size_t koff;
+  int nq, NK;
+  if constexpr (VARLEN) {
+    const int b = bh / H, h = bh - b * H;
+    const int qs = min(max(cuq[b], 0), tq), qe = min(max(cuq[b + 1], qs), tq);
+    const int ks = min(max(cuk[b], 0), tk), ke = min(max(cuk[b + 1], ks), tk);
+    nq = qe - qs;
+    NK = ke - ks;
+    if (q0 >= nq) return;  // past this sequence's rows: the whole workgroup
+    Qh = Qg + ((size_t)h * tq + qs) * D;
+    Oh = Og + ((size_t)h * tq + qs) * D;
+    Lh = Lg + (size_t)h * tq + qs;
+    koff = ((size_t)h * tk + ks) * D;
+  } else {
+    nq = Nq;
+    NK = Nk;
+    Qh = Qg + (size_t)bh * Nq * D;
+    Oh = Og + (size_t)bh * Nq * D;
+    Lh = Lg + (size_t)bh * Nq;
+    koff = (size_t)bh * Nk * D;
+  }
   // This workgroup's keys: [kb, kb + nk) of the head (all of them unless
   // SPLIT); key indices below are relative to kb.
   const int kb = SPLIT ? split * split_len : 0;
-  const int nk = SPLIT ? min(split_len, Nk - kb) : Nk;
-  const u16* Kh = Kg + ((size_t)bh * Nk + kb) * D;
-  const u16* Vh = Vg + ((size_t)bh * Nk + kb) * D;
+  const int nk = SPLIT ? min(split_len, NK - kb) : NK;
+  const u16* Kh = Kg + koff + (size_t)kb * D;
+  const u16* Vh = Vg + koff + (size_t)kb * D;
   const int kbytes = nk * ROWB;
 
-  const int kend = CAUSAL ? min(nk, min(q0 + kBR16, Nq) - kb) : nk;  // keys [0, kend) are needed
+  const int kend = CAUSAL ? min(nk, min(q0 + kBR16, nq) - kb) : nk;  // keys [0, kend) are needed
   const int nt = kend > 0 ? (kend + BC - 1) / BC : 0;
   w.wq0 = q0 + 32 * w.wave;
   const int myq = w.wq0 + w.l32;
   // A wave whose rows all lie past Nq computes nothing.
-  w.wkend = w.wq0 >= Nq ? 0 : CAUSAL ? min(kend, w.wq0 + 32 - kb) : kend;
+  w.wkend = w.wq0 >= nq ? 0 : CAUSAL ? min(kend, w.wq0 + 32 - kb) : kend;
   w.klim = CAUSAL ? min(myq - kb, nk - 1) : nk - 1;
   w.wklim = CAUSAL ? min(w.wq0 - kb, nk - 1) : nk - 1;
   init_operand_offsets<D>(w);
@@ -226,14 +258,14 @@ __global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict
   // in order, so waiting for a K/V tile also covers Q.
   u32x4 qf[NKK];
   {
-    const auto rQ = make_rsrc(Qg + (size_t)bh * Nq * D, Nq * ROWB);
+    const auto rQ = make_rsrc(Qh, nq * ROWB);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
       qf[kk] = __builtin_amdgcn_raw_buffer_load_b128(rQ, (32 * w.wave + w.l32) * ROWB + (16 * kk + 8 * w.hf) * 2,
                                                      q0 * ROWB, 0);
   }
   // Tiles 0..2 into stages 0..2.
-  if (!SPLIT || nt > 0) issue_tile16<D, kWaves16>(Kh, Vh, kbytes, 0, stage0, w);
+  if ((!SPLIT && !VARLEN) || nt > 0) issue_tile16<D, kWaves16>(Kh, Vh, kbytes, 0, stage0, w);
   if (nt > 1) issue_tile16<D, kWaves16>(Kh, Vh, kbytes, 1, stage1, w);
   if (nt > 2) issue_tile16<D, kWaves16>(Kh, Vh, kbytes, 2, stage2, w);
 
@@ -262,7 +294,7 @@ __global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict
     const bool none = !(lt > 0.f);
     const float inv = none ? 0.f : 1.0f / lt;
     const size_t slot = (size_t)split * BH + bh;
-    const auto rP = make_rsrc(Po + slot * Nq * D, Nq * D * 4);
+    const auto rP = make_rsrc(Po + slot * Nq * D, nq * D * 4);
     const int off0 = (32 * w.wave + w.l32) * D * 4 + 4 * w.hf * 4;
     int off1 = off0 + 8;
     asm volatile("" : "+v"(off1));
@@ -277,7 +309,7 @@ __global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v1), rP, off1 + col, q0 * D * 4, 0);
       }
     if (w.hf == 0) {
-      const auto rL = make_rsrc(Pl + slot * Nq, Nq * 4);
+      const auto rL = make_rsrc(Pl + slot * Nq, nq * 4);
       const float lse = none ? -INFINITY : (mref + __log2f(lt)) * kLn2;
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse), rL, (32 * w.wave + w.l32) * 4,
                                             q0 * 4, 0);
@@ -286,8 +318,9 @@ __global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict
   }
   // Epilogue: normalise by the combined half-row sums, round to 16 bits,
   // store (rows past Nq are dropped by the buffer range check).
-  const float inv = 1.0f / lt;
-  const auto rO = make_rsrc(Og + (size_t)bh * Nq * D, Nq * ROWB);
+  const bool none = VARLEN && !(lt > 0.f);  // a sequence without keys
+  const float inv = none ? 0.f : 1.0f / lt;
+  const auto rO = make_rsrc(Oh, nq * ROWB);
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -299,9 +332,10 @@ __global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict
                                             q0 * ROWB, 0);
     }
   if (w.hf == 0) {
-    const auto rL = make_rsrc(Lg + (size_t)bh * Nq, Nq * 4);
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, (mref + __log2f(lt)) * kLn2), rL,
-                                          (32 * w.wave + w.l32) * 4, q0 * 4, 0);
+    const auto rL = make_rsrc(Lh, nq * 4);
+    const float lse = none ? -INFINITY : (mref + __log2f(lt)) * kLn2;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse), rL, (32 * w.wave + w.l32) * 4,
+                                          q0 * 4, 0);
   }
 }
 
@@ -470,13 +504,14 @@ int launch(KernelT kern, const FaLaunch& a, int rows_per_block, int threads, flo
   return (int)hipGetLastError();
 }
 
-template <int DT, int D, bool CAUSAL, bool SPLIT>
+template <int DT, int D, bool CAUSAL, bool SPLIT, bool VARLEN = false>
 void launch16(const FaLaunch& a, float sl2, int nsplit, int split_len, float* Po, float* Pl) {
   const int nqt = (int)((a.Nq + kBR16 - 1) / kBR16);
   const dim3 grid((unsigned)(a.BH * nqt * nsplit)), block(kThreads16);
-  hipLaunchKernelGGL((fa_fwd_16<DT, D, CAUSAL, SPLIT>), grid, block, 0, (hipStream_t)a.stream, (const u16*)a.q,
-                     (const u16*)a.k, (const u16*)a.v, (u16*)a.o, a.lse, (int)a.BH, (int)a.Nq, (int)a.Nk, nqt,
-                     sl2, split_len, Po, Pl);
+  hipLaunchKernelGGL((fa_fwd_16<DT, D, CAUSAL, SPLIT, VARLEN>), grid, block, 0, (hipStream_t)a.stream,
+                     (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (u16*)a.o, a.lse, (int)a.BH, (int)a.Nq,
+                     (int)a.Nk, nqt, sl2, split_len, Po, Pl, a.cu_q, a.cu_k, (int)a.H, (int)a.total_q,
+                     (int)a.total_k);
 }
 
 template <int DT, int D>
@@ -545,6 +580,28 @@ int dispatch32(const FaLaunch& a, float sl2) {
 }
 
 }  // namespace
+
+template <int DT, int D>
+int dispatch16_varlen(const FaLaunch& a, float sl2) {
+  if (a.causal)
+    launch16<DT, D, true, false, true>(a, sl2, 1, 0, nullptr, nullptr);
+  else
+    launch16<DT, D, false, false, true>(a, sl2, 1, 0, nullptr, nullptr);
+  return (int)hipGetLastError();
+}
+
+int fa_launch_fwd_varlen(const FaLaunch& a) {
+  const float sl2 = (float)(a.scale * 1.4426950408889634074);
+  (void)hipGetLastError();  // clear a stale error so that the check below is ours
+  switch (a.dtype) {
+    case kBF16:
+      return a.D == 32 ? dispatch16_varlen<kBF16, 32>(a, sl2)
+           : a.D == 64 ? dispatch16_varlen<kBF16, 64>(a, sl2) : dispatch16_varlen<kBF16, 128>(a, sl2);
+    default:
+      return a.D == 32 ? dispatch16_varlen<kFP16, 32>(a, sl2)
+           : a.D == 64 ? dispatch16_varlen<kFP16, 64>(a, sl2) : dispatch16_varlen<kFP16, 128>(a, sl2);
+  }
+}
 
 int fa_launch_fwd_splitkv(const FaLaunch& a, int nsplit, int split_len) {
   const float sl2 = (float)(a.scale * 1.4426950408889634074);

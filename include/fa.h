@@ -144,6 +144,39 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int dtype, void* stream);
 
 /*
+ * fa_fwd_varlen -- fa_fwd_scaled over a batch of B packed sequences of
+ * different lengths, with no padding: the variable-length batches the pages
+ * describe ("Flash Attention vs Standard Attention", Frequently Asked
+ * Questions: un-padded sequences processed without padding to the longest
+ * one; "Python Attention Mechanisms Explained", Practical Tips for Python
+ * Developers: padded positions are skipped).  Sequence b has the query rows [cu_seqlens_q[b],
+ * cu_seqlens_q[b+1]) and the key rows [cu_seqlens_k[b], cu_seqlens_k[b+1]);
+ * it attends to its own keys only, with the causal mask (if any) aligned at
+ * its own first row and key.
+ *
+ *   q, o  device, [H, total_q, D] contiguous, `dtype` (head-major packing:
+ *         each (head, sequence) is one contiguous block of rows)
+ *   k, v  device, [H, total_k, D] contiguous, `dtype`
+ *   lse   device, [H, total_q] fp32 (output, natural log)
+ *   cu_seqlens_q, cu_seqlens_k   device int32 arrays of B + 1 offsets,
+ *         non-decreasing from 0 to total_q / total_k.  They are read on the
+ *         device only (no copy, no synchronisation); offsets outside
+ *         [0, total] are clamped there, so bad offsets give wrong rows but
+ *         no access outside the buffers.
+ *   max_seqlen_q  at least the longest sequence's query count (it sizes the
+ *         grid; query rows past it are not written)
+ *   dtype must be FA_DTYPE_FP16 or FA_DTYPE_BF16 (FA_ERR_DTYPE otherwise).
+ *
+ * A sequence with queries but no keys gets O = 0 and LSE = -inf (the empty
+ * sum).  B*H == 0, total_q == 0 or max_seqlen_q == 0 is a no-op.  Other
+ * errors as fa_fwd_scaled; FA_ERR_SHAPE also for max_seqlen_q > total_q.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int64_t B, int64_t H,
+                  int64_t total_q, int64_t total_k, int64_t max_seqlen_q, int64_t D,
+                  double softmax_scale, int causal, int dtype, void* stream);
+
+/*
  * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs: two fp32
  * values per query row (8 * B * H * Nq); -1 if that overflows or a size is
  * negative.

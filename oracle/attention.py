@@ -36,7 +36,8 @@ import math
 
 import numpy as np
 
-__all__ = ["attention_forward", "attention_rows", "scores_row", "attention_partial", "merge_partials"]
+__all__ = ["attention_forward", "attention_rows", "scores_row", "attention_partial", "merge_partials",
+           "attention_varlen"]
 
 
 def _as_f64(x) -> np.ndarray:
@@ -187,3 +188,27 @@ def merge_partials(parts):
     tot = w.sum(axis=0)
     O = (w[..., None] * Os).sum(axis=0) / tot[..., None]
     return O, m + np.log(tot)
+
+
+def attention_varlen(q, k, v, cu_q, cu_k, causal: bool, scale=None):
+    """Exact attention over packed variable-length sequences, un-padded
+    ("Flash Attention vs Standard Attention", Frequently Asked Questions).
+
+    q: (H, total_q, D), k, v: (H, total_k, D) (head-major packing); cu_q,
+    cu_k: B + 1 offsets.  Sequence b's rows [cu_q[b], cu_q[b+1]) attend to
+    its keys [cu_k[b], cu_k[b+1]) only, with the causal mask aligned at the
+    sequence's first row and key.  A sequence with queries and no keys gets
+    O = 0 and LSE = -inf.  Returns float64 (O (H, total_q, D), LSE (H, total_q)).
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    H, total_q, D = q.shape
+    O = np.zeros((H, total_q, D))
+    L = np.full((H, total_q), -np.inf)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if q1 == q0 or k1 == k0:
+            continue
+        o, lse = attention_forward(q[None, :, q0:q1], k[None, :, k0:k1], v[None, :, k0:k1], causal, scale=scale)
+        O[:, q0:q1] = o[0]
+        L[:, q0:q1] = lse[0]
+    return O, L

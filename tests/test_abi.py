@@ -182,3 +182,27 @@ def test_splitkv_validation_codes(kw, code):
 
 def test_splitkv_noop():
     assert call_split(B=0, q=0, k=0, v=0, o=0, lse=0, ws=0, ws_bytes=0) == 0
+
+
+CQ, CK = (11 << 40), (12 << 40)
+
+
+def call_varlen(q=Q, k=K, v=V, o=O, lse=L, cu_q=CQ, cu_k=CK, B=3, H=4, total_q=500, total_k=700, max_q=300,
+                D=64, scale=0.125, causal=1, dtype=2):
+    return fa.fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, B, H, total_q, total_k, max_q, D, scale, causal, dtype,
+                            None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), 4), (dict(D=256), 3), (dict(scale=-1.0), 8), (dict(B=-1), 2), (dict(max_q=501), 2),
+    (dict(total_q=1 << 40), 2), (dict(cu_q=0), 1), (dict(cu_k=0), 1), (dict(lse=0), 1),
+    (dict(cu_q=CQ + 2), 5), (dict(q=Q + 8), 5), (dict(o=Q + 64), 6), (dict(lse=CK), 6), (dict(o=CQ - 16), 6),
+])
+def test_varlen_validation_codes(kw, code):
+    assert call_varlen(**kw) == code
+
+
+def test_varlen_noops():
+    assert call_varlen(B=0, q=0, k=0, v=0, o=0, lse=0, cu_q=0, cu_k=0) == 0
+    assert call_varlen(total_q=0, max_q=0, q=0, o=0, lse=0) == 0
+    assert call_varlen(max_q=0) == 0

@@ -131,3 +131,44 @@ def test_partial_against_brute_force_on_the_range():
     Op, Lp = oracle.attention_partial(q, k, v, False, 2, 7)
     Ob, Lb = pins.brute_force(q, k[:, :, 2:7], v[:, :, 2:7], False)
     assert np.max(np.abs(Op - Ob)) <= 1e-12 and np.max(np.abs(Lp - Lb)) <= 1e-12
+
+
+def test_varlen_oracle_against_brute_force_and_padding():
+    # Each packed sequence is the plain definition on its own slices (brute
+    # force), and the whole batch equals dense attention over the padded
+    # batch with the padded keys masked out, on the real rows ("use padding
+    # with an attention mask"), which the varlen path skips.
+    from scipy.special import logsumexp, softmax
+
+    r = np.random.default_rng(21)
+    lens_q = [3, 0, 5, 1, 4]
+    lens_k = [4, 3, 5, 2, 0]
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)])
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)])
+    H, D = 2, 4
+    q = r.standard_normal((H, cu_q[-1], D))
+    k = r.standard_normal((H, cu_k[-1], D))
+    v = r.standard_normal((H, cu_k[-1], D))
+    for causal in (False, True):
+        O, L = oracle.attention_varlen(q, k, v, cu_q, cu_k, causal)
+        for b in range(len(lens_q)):
+            q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+            if q1 == q0:
+                continue
+            if k1 == k0:
+                assert np.all(O[:, q0:q1] == 0) and np.all(L[:, q0:q1] == -np.inf)
+                continue
+            Ob, Lb = pins.brute_force(q[None, :, q0:q1], k[None, :, k0:k1], v[None, :, k0:k1], causal)
+            assert np.max(np.abs(O[:, q0:q1] - Ob[0])) <= 1e-12
+            assert np.max(np.abs(L[:, q0:q1] - Lb[0])) <= 1e-12
+            # padded to the longest key count, padded keys masked
+            mk = max(lens_k)
+            kp = np.concatenate([k[:, k0:k1], 7.0 * np.ones((H, mk - (k1 - k0), D))], axis=1)
+            vp = np.concatenate([v[:, k0:k1], 9.0 * np.ones((H, mk - (k1 - k0), D))], axis=1)
+            s = np.einsum("hid,hjd->hij", q[:, q0:q1], kp) / np.sqrt(D)
+            keep = np.arange(mk)[None, :] < (k1 - k0)
+            if causal:
+                keep = keep & (np.arange(mk)[None, :] <= np.arange(q1 - q0)[:, None])
+            s = np.where(keep, s, -np.inf)
+            assert np.max(np.abs(np.matmul(softmax(s, -1), vp) - O[:, q0:q1])) <= 1e-12
+            assert np.max(np.abs(logsumexp(s, -1) - L[:, q0:q1])) <= 1e-12

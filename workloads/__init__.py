@@ -36,6 +36,11 @@ __all__ = [
     "make_dout",
     "conv_flops",
     "conv_flops_bwd",
+    "algorithmic_bytes",
+    "VarlenWorkload",
+    "VARLEN_WORKLOADS",
+    "make_varlen_inputs",
+    "varlen_flops",
 ]
 
 
@@ -168,3 +173,72 @@ def conv_flops_bwd(B: int, H: int, Nq: int, Nk: int, D: int, causal: bool) -> fl
     """Backward FLOP convention: five products of the forward's size (S
     recomputed, dP = dO V^T, dV, dQ, dK), 10*B*H*Nq*Nk*D, halved when causal."""
     return 2.5 * conv_flops(B, H, Nq, Nk, D, causal)
+
+
+def algorithmic_bytes(w: Workload) -> int:
+    """Compulsory HBM bytes of one forward call: Q, K, V read once, O and
+    LSE (fp32) written once."""
+    esz = 4 if w.dtype == "fp32" else 2
+    return (2 * w.B * w.H * w.Nq * w.D + 2 * w.B * w.H * w.Nk * w.D) * esz + 4 * w.B * w.H * w.Nq
+
+
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    """Packed variable-length batch: sequence b has lens_q[b] query rows and
+    lens_k[b] keys; q is [H, sum(lens_q), D], k and v [H, sum(lens_k), D]."""
+    name: str
+    H: int
+    D: int
+    dtype: str
+    causal: bool
+    seed: int
+    lens_q: Tuple[int, ...]
+    lens_k: Tuple[int, ...]
+
+    @property
+    def B(self) -> int:
+        return len(self.lens_q)
+
+    @property
+    def cu_q(self):
+        return np.concatenate([[0], np.cumsum(self.lens_q)]).astype(np.int32)
+
+    @property
+    def cu_k(self):
+        return np.concatenate([[0], np.cumsum(self.lens_k)]).astype(np.int32)
+
+
+def _mixed_lengths(seed: int, n: int, lo: int, hi: int):
+    """n sequence lengths, log-uniform in [lo, hi] (a training batch packed
+    without padding: many short sequences, a few long ones)."""
+    r = np.random.default_rng(seed)
+    return tuple(int(x) for x in np.exp(r.uniform(np.log(lo), np.log(hi), n)).round())
+
+
+_V1 = _mixed_lengths(9, 16, 256, 8192)
+VARLEN_WORKLOADS: Dict[str, VarlenWorkload] = {
+    w.name: w
+    for w in [
+        VarlenWorkload("v1_bf16_causal_varlen_b16h16d128", 16, 128, "bf16", True, 9, _V1, _V1),
+    ]
+}
+
+
+def make_varlen_inputs(w: VarlenWorkload, seed: int | None = None):
+    """(q, k, v) as contiguous torch CPU tensors of the storage dtype, drawn
+    like make_inputs (Q, then K, then V, float64 N(0,1), rounded), plus the
+    int32 offset arrays (cu_q, cu_k)."""
+    import torch
+
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    tq, tk = int(sum(w.lens_q)), int(sum(w.lens_k))
+    q = rng.standard_normal((w.H, tq, w.D))
+    k = rng.standard_normal((w.H, tk, w.D))
+    v = rng.standard_normal((w.H, tk, w.D))
+    ts = tuple(round_to_dtype(x, w.dtype) for x in (q, k, v))
+    return ts + (torch.from_numpy(w.cu_q), torch.from_numpy(w.cu_k))
+
+
+def varlen_flops(w: VarlenWorkload) -> float:
+    """The FLOP convention per sequence (4*H*Nq*Nk*D, halved when causal), summed."""
+    return float(sum(conv_flops(1, w.H, nq, nk, w.D, w.causal) for nq, nk in zip(w.lens_q, w.lens_k)))
