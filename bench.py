@@ -10,8 +10,17 @@ resident in HBM.  Throughput is the metric's convention: FLOPs =
 dK/dV kernel) on the forward's O and LSE; FLOPs = 2.5x the forward
 convention (five products of the forward's size).
 
+--op decode: a step is one fa_fwd_splitkv call (key-range partials, then
+the merge) on a decoding workload (few query rows, long KV cache); the
+path is bound by HBM, so the value is algorithmic bytes (Q, K, V read once,
+O and LSE written once) per second in GB/s against 8 TB/s.
+
+--op varlen: a step is one fa_fwd_varlen call over a packed batch of
+sequences of mixed lengths; FLOPs = the forward convention summed over the
+sequences.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--op fwd|bwd] [--no-cpu-baseline] [--all]
+                    [--op fwd|bwd|decode|varlen] [--no-cpu-baseline] [--all]
 
 Prints one JSON line per workload.
 """
@@ -32,6 +41,9 @@ import workloads  # noqa: E402
 
 METRIC = "attention fwd TFLOP/s and % of dense MFMA peak, bf16 causal N=4096 D=128"
 METRIC_BWD = "attention bwd TFLOP/s (2.5x the forward FLOP convention) and % of dense MFMA peak"
+METRIC_DECODE = "attention decode (split-KV) algorithmic HBM GB/s and % of 8 TB/s"
+METRIC_VARLEN = "attention fwd over packed variable-length sequences, TFLOP/s and % of dense MFMA peak"
+HBM_PEAK_GBS = 8000.0
 # Published MI355X dense peaks (TFLOP/s) by compute dtype.
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
 
@@ -46,14 +58,18 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--all", action="store_true", help="one line per measured workload (c1..c5)")
-    p.add_argument("--op", choices=("fwd", "bwd"), default="fwd")
+    p.add_argument("--op", choices=("fwd", "bwd", "decode", "varlen"), default="fwd")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="after timing, run 3 plain device copies of this many MiB (a reference "
                         "kernel of known traffic for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     return p.parse_args()
 
 
-def kernel_tag(w: workloads.Workload, op: str = "fwd") -> str:
+def kernel_tag(w, op: str = "fwd") -> str:
+    if op == "varlen":
+        return f"fa_fwd_varlen_{w.dtype}_d{w.D}_{'causal' if w.causal else 'noncausal'}"
+    if op == "decode":
+        return f"fa_fwd_splitkv_{w.dtype}_d{w.D}"
     if op == "bwd":
         return f"fa_bwd_16_{w.dtype}_d{w.D}_{'causal' if w.causal else 'noncausal'}"
     if w.dtype == "fp32":
@@ -93,7 +109,7 @@ def measured_traffic(w: workloads.Workload, op: str = "fwd"):
         if ":" in line and line.split(":")[0] in ("kernel_code_sha256", "traffic_bytes_per_launch"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    code = kernel_code_sha256(KERNEL_SOURCES_BWD if op == "bwd" else KERNEL_SOURCES)
+    code = kernel_code_sha256(KERNEL_SOURCES_BWD if op == "bwd" else KERNEL_SOURCES)  # decode: forward file
     if fields.get("kernel_code_sha256") != code or "traffic_bytes_per_launch" not in fields:
         return None
     return int(fields["traffic_bytes_per_launch"])
@@ -132,6 +148,15 @@ def cpu_baseline(w: workloads.Workload, target_s: float, op: str = "fwd"):
             oracle.attention_forward(qh, kh, vh, w.causal)
         t_total += time.perf_counter() - t0
         heads += 1
+    if op == "decode":
+        wh = w.replace(B=1, H=heads)
+        return {
+            "value": round(workloads.algorithmic_bytes(wh) / t_total / 1e9, 4),
+            "unit": "GB/s",
+            "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"{heads} of {BH} (b,h) heads of {w.name}, float64, {t_total:.1f} s",
+        }
     conv = workloads.conv_flops_bwd if op == "bwd" else workloads.conv_flops
     flops = conv(1, heads, w.Nq, w.Nk, w.D, w.causal)
     return {
@@ -180,6 +205,19 @@ def bench_one(w: workloads.Workload, steps: int, warmup: int, op: str = "fwd"):
                 raise fa.FaError(rc)
 
         step = bwd_step
+    elif op == "decode":
+        ws_bytes = fa.fa_fwd_splitkv_workspace_size(w.B, w.H, w.Nq, w.Nk, w.D, 0)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        scale = 1.0 / w.D**0.5
+
+        def decode_step():
+            rc = fa.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                   ws.data_ptr(), ws_bytes, w.B, w.H, w.Nq, w.Nk, w.D, scale, 0, int(w.causal),
+                                   code, sptr)
+            if rc != 0:
+                raise fa.FaError(rc)
+
+        step = decode_step
 
     for _ in range(warmup):
         step()
@@ -210,6 +248,18 @@ def bench_one(w: workloads.Workload, steps: int, warmup: int, op: str = "fwd"):
     flops = conv(w.B, w.H, w.Nq, w.Nk, w.D, w.causal)
     tflops = flops / (ms_region * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
+    if op == "decode":
+        nbytes = workloads.algorithmic_bytes(w)
+        return {
+            "ms_per_step": ms_region,
+            "wall_s": wall,
+            "median_launch_ms": statistics.median(per),
+            "min_launch_ms": min(per),
+            "gbs": nbytes / (ms_region * 1e-3) / 1e9,
+            "bytes": nbytes,
+            "flops": flops,
+            "splits_workspace_bytes": ws_bytes,
+        }
     return {
         "ms_per_step": ms_region,
         "wall_s": wall,
@@ -218,6 +268,88 @@ def bench_one(w: workloads.Workload, steps: int, warmup: int, op: str = "fwd"):
         "tflops": tflops,
         "peak": peak,
         "flops": flops,
+    }
+
+
+def bench_varlen(w: workloads.VarlenWorkload, steps: int, warmup: int):
+    import torch
+
+    import exact_tiled_attention_15_amd as fa
+
+    fa.load_library()
+    dev = torch.device("cuda:0")
+    q, k, v, cu_q, cu_k = (t.to(dev) for t in workloads.make_varlen_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    code = fa._dtype_code(q)
+    H, tq, D = q.shape
+    tk = k.shape[1]
+    mq = max(w.lens_q)
+    scale = 1.0 / D**0.5
+
+    def step():
+        rc = fa.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                              cu_q.data_ptr(), cu_k.data_ptr(), w.B, H, tq, tk, mq, D, scale, int(w.causal), code,
+                              sptr)
+        if rc != 0:
+            raise fa.FaError(rc)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = workloads.varlen_flops(w)
+    return {"ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12, "flops": flops, "peak": PEAK_TFLOPS[w.dtype]}
+
+
+def cpu_baseline_varlen(w: workloads.VarlenWorkload, target_s: float):
+    """The float64 varlen oracle on whole sequences (all heads), sequence
+    after sequence until about ``target_s`` seconds have passed."""
+    import oracle
+
+    q, k, v, cu_q, cu_k = workloads.make_varlen_inputs(w)
+    t_total, n, flops = 0.0, 0, 0.0
+    while n < w.B and t_total < target_s:
+        q0, q1, k0, k1 = (int(x) for x in (cu_q[n], cu_q[n + 1], cu_k[n], cu_k[n + 1]))
+        t0 = time.perf_counter()
+        oracle.attention_varlen(q[:, q0:q1].double().numpy(), k[:, k0:k1].double().numpy(),
+                                v[:, k0:k1].double().numpy(), [0, q1 - q0], [0, k1 - k0], w.causal)
+        t_total += time.perf_counter() - t0
+        flops += workloads.conv_flops(1, w.H, q1 - q0, k1 - k0, w.D, w.causal)
+        n += 1
+    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{n} of {w.B} sequences of {w.name}, all heads, float64, {t_total:.1f} s"}
+
+
+def line_varlen(w, r, steps, warmup, cpu):
+    return {
+        "metric": METRIC_VARLEN,
+        "value": round(r["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "D": w.D, "causal": w.causal, "seed": w.seed,
+                   "total_q": int(sum(w.lens_q)), "total_k": int(sum(w.lens_k)), "lens_q": list(w.lens_q),
+                   "flops_per_step": r["flops"], "parallelism": "single GPU", "op": "varlen"},
+        "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 3), "peak": r["peak"], "unit": "TFLOP/s",
+                     "frac": round(r["tflops"] / r["peak"], 4), "traffic": measured_traffic(w, "varlen")},
+        "cpu_baseline": cpu,
     }
 
 
@@ -231,6 +363,29 @@ def line_for(w, r, steps, warmup, cpu, op="fwd"):
                  "gcn_arch": getattr(p, "gcnArchName", "")}
     except Exception:
         pass
+    if op == "decode":
+        return {
+            "metric": METRIC_DECODE,
+            "value": round(r["gbs"], 1),
+            "unit": "GB/s",
+            "n_gpus": 1,
+            "steps": steps,
+            "warmup": warmup,
+            "ms_per_step": round(r["ms_per_step"], 5),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": w.dtype,
+            "data": "synthetic",
+            "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "D": w.D,
+                       "causal": w.causal, "seed": w.seed, "bytes_per_step": r["bytes"],
+                       "splits_workspace_bytes": r["splits_workspace_bytes"], "parallelism": "single GPU",
+                       "median_launch_ms": round(r["median_launch_ms"], 5),
+                       "min_launch_ms": round(r["min_launch_ms"], 5), "op": op, **props},
+            "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(r["gbs"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w, op)},
+            "cpu_baseline": cpu,
+        }
     return {
         "metric": METRIC_BWD if op == "bwd" else METRIC,
         "value": round(r["tflops"], 3),
@@ -263,10 +418,22 @@ def main():
               "shards over (batch, head) with no communication, so there is no multi-GPU "
               "step to time here.", file=sys.stderr)
         sys.exit(2)
+    if a.op == "varlen":
+        names = (list(workloads.VARLEN_WORKLOADS) if a.all or a.workload == workloads.HEADLINE else [a.workload])
+        for i, n in enumerate(names):
+            w = workloads.VARLEN_WORKLOADS[n]
+            r = bench_varlen(w, a.steps, a.warmup)
+            cpu = None if a.no_cpu_baseline or i else cpu_baseline_varlen(w, a.cpu_seconds)
+            print(json.dumps(line_varlen(w, r, a.steps, a.warmup, cpu)), flush=True)
+        copy_calibration(a.copy_calib_mib)
+        return
     names = ([n for n in workloads.WORKLOADS if n[:2] in ("c1", "c2", "c3", "c4", "c5") and "t_" not in n[:4]]
              if a.all else [a.workload])
     if a.op == "bwd":  # the backward kernels take 16-bit inputs
         names = [n for n in names if workloads.WORKLOADS[n].dtype != "fp32"]
+    if a.op == "decode":
+        names = ([n for n in workloads.WORKLOADS if n.startswith("d")] if a.all or a.workload == workloads.HEADLINE
+                 else [a.workload])
     for n in names:
         w = workloads.WORKLOADS[n]
         r = bench_one(w, a.steps, a.warmup, a.op)
@@ -274,16 +441,23 @@ def main():
         if not a.no_cpu_baseline and n == names[0]:
             cpu = cpu_baseline(w, a.cpu_seconds, a.op)
         print(json.dumps(line_for(w, r, a.steps, a.warmup, cpu, a.op)), flush=True)
-    if a.copy_calib_mib > 0:
-        import torch
+    copy_calibration(a.copy_calib_mib)
 
-        n = a.copy_calib_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"copy calibration: 3 x {a.copy_calib_mib} MiB device copies", file=sys.stderr)
+
+def copy_calibration(mib: int):
+    """Three plain device copies of `mib` MiB: a reference kernel of known
+    traffic for the rocprofv3 FETCH_SIZE / WRITE_SIZE counters."""
+    if mib <= 0:
+        return
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copy calibration: 3 x {mib} MiB device copies", file=sys.stderr)
 
 
 if __name__ == "__main__":
