@@ -133,7 +133,8 @@ def forward(q, k, v, causal: bool = False, out=None, lse=None, stream=None, soft
     """Exact attention forward on the GPU.
 
     q: (B, H, Nq, D), k/v: (B, H, Nk, D), contiguous device tensors of one
-    dtype (float32, float16 or bfloat16), D in {32, 64, 128}.  Returns
+    dtype (float32, float16 or bfloat16), D in {32, 64, 128, 256} (256: 16-bit
+    dtypes only).  Returns
     (O (B, H, Nq, D) in the input dtype, LSE (B, H, Nq) float32).  ``out`` and
     ``lse`` may be given preallocated; ``stream`` defaults to torch's current
     stream; ``softmax_scale`` (default 1/sqrt(D)) multiplies q.k.

@@ -26,7 +26,10 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int dtype, bool* empty) {
   if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || D < 0) return FA_ERR_SHAPE;
-  if (D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (D != 32 && D != 64 && D != 128 && D != 256) return FA_ERR_HEAD_DIM;
+  // fp32 at D = 256 would spill registers (its Q fragment, O and staged K/V
+  // exceed one wave's 512); that head dimension runs the 16-bit kernel only.
+  if (D == 256 && dtype == FA_DTYPE_FP32) return FA_ERR_HEAD_DIM;
   int64_t BH, rows, qel, kel;
   if (!mul_ok(B, H, &BH) || !mul_ok(BH, Nq, &rows) || !mul_ok(rows, D, &qel)) return FA_ERR_SHAPE;
   *empty = (rows == 0);
@@ -195,7 +198,7 @@ extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* 
                              double softmax_scale, int causal, int dtype, void* stream) {
   if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;  // the 16-bit kernel
   if (B < 0 || H < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || D < 0) return FA_ERR_SHAPE;
-  if (D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (D != 32 && D != 64 && D != 128 && D != 256) return FA_ERR_HEAD_DIM;
   if (!scale_ok(softmax_scale)) return FA_ERR_SCALE;
   int64_t BH, qel, kel;
   if (!mul_ok(B, H, &BH) || !mul_ok(H, total_q, &qel) || !mul_ok(qel, D, &qel) || !mul_ok(H, total_k, &kel) ||
@@ -318,7 +321,7 @@ extern "C" const char* fa_status_str(int status) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative, empty-key or too large shape";
-    case FA_ERR_HEAD_DIM: return "FA_ERR_HEAD_DIM: head dimension must be 32, 64 or 128";
+    case FA_ERR_HEAD_DIM: return "FA_ERR_HEAD_DIM: head dimension must be 32, 64, 128 or 256 (backward: 32, 64 or 128)";
     case FA_ERR_DTYPE: return "FA_ERR_DTYPE: unknown dtype code";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: q/k/v/o must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or the other output";

@@ -43,15 +43,24 @@ namespace {
 constexpr int kThreads = 256;                     // 4 waves of 64 (fp32 kernel)
 constexpr int kBR = 128;                          // query rows per workgroup (fp32 kernel)
 
-// 16-bit kernel shape: a workgroup of kWaves16 waves owns 32 query rows per
-// wave, streams 64-key K/V tiles through a 4-stage LDS ring (three tiles
-// in flight while one is consumed).
+// 16-bit kernel shape: a workgroup of waves16<D>() waves owns 32 query rows
+// per wave and streams 64-key K/V tiles through an LDS ring of stages16<D>()
+// stages.  D <= 128: 8 waves (256 rows, two waves per SIMD) and 4 stages
+// (three tiles in flight while one is consumed).  D = 256: the Q fragment
+// and fp32 O of 32 rows take more than half of a SIMD's registers, and a
+// 64-key K+V stage takes 64 KB, so 4 waves (128 rows, one wave per SIMD) and
+// 2 stages (one tile in flight).
 #ifndef FA_WAVES16
 #define FA_WAVES16 8
 #endif
-constexpr int kWaves16 = FA_WAVES16;  // waves per workgroup
-constexpr int kThreads16 = 64 * kWaves16;
-constexpr int kBR16 = 32 * kWaves16;  // query rows per workgroup
+template <int D>
+constexpr int waves16() {
+  return D == 256 ? 4 : FA_WAVES16;
+}
+template <int D>
+constexpr int stages16() {
+  return D == 256 ? 2 : 4;
+}
 
 // One K/V tile of the 16-bit kernel (stage `src`).  Tile j is complete in
 // LDS since the previous tile's barrier (each barrier waits for the tile
@@ -63,11 +72,15 @@ constexpr int kBR16 = 32 * kWaves16;  // query rows per workgroup
 // online-softmax update and O^T += V^T P^T.  `src` and `dst` are distinct
 // __shared__ arrays, so the compiler knows the loads in flight never alias
 // the operand reads.
+// With a 2-stage ring (D = 256) the order is simpler: wait for tile j itself
+// (every wave has then also finished tile j-1), start tile j+1 into `dst`
+// (tile j-1's stage), then read and compute.
 template <int DT, int D, bool CAUSAL>
 __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes, int j, int nt,
                                        const unsigned char* src, unsigned char* dst,
                                        const Wave16& w, const u32x4 (&qf)[D / 16],
                                        f32x16 (&oacc)[D / 32], float& mref, float& l, float sl2) {
+  constexpr int NW = waves16<D>(), ST = stages16<D>();
   constexpr int BC = 64;
   constexpr int TILEB = BC * D * 2;
   constexpr int NKK = D / 16, NDT = D / 32;
@@ -84,14 +97,23 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
   const unsigned char* ks = src;
   const unsigned char* vs = src + TILEB;
   u32x4 ka[NQK];
-  if (mine) {
+  if constexpr (ST == 4) {
+    if (mine) {
 #pragma unroll
-    for (int i = 0; i < kPre; ++i) ka[i] = ks_operand<D>(ks, w, i);
+      for (int i = 0; i < kPre; ++i) ka[i] = ks_operand<D>(ks, w, i);
+    }
+    // Loads complete in order: only tile j+2's may still be in flight; the
+    // kPre reads just issued may be too (older LDS reads have completed).
+    wait_tile_and_barrier<kPre>(j + 2 < nt ? loads_per_tile<D, NW>(w.wave) : 0);
+    if (j + 3 < nt) issue_tile16<D, NW>(Kh, Vh, kbytes, j + 3, dst, w);
+  } else {
+    wait_tile_and_barrier(0);
+    if (j + 1 < nt) issue_tile16<D, NW>(Kh, Vh, kbytes, j + 1, dst, w);
+    if (mine) {
+#pragma unroll
+      for (int i = 0; i < kPre; ++i) ka[i] = ks_operand<D>(ks, w, i);
+    }
   }
-  // Loads complete in order: only tile j+2's may still be in flight; the
-  // kPre reads just issued may be too (older LDS reads have completed).
-  wait_tile_and_barrier<kPre>(j + 2 < nt ? loads_per_tile<D, kWaves16>(w.wave) : 0);
-  if (j + kStages - 1 < nt) issue_tile16<D, kWaves16>(Kh, Vh, kbytes, j + kStages - 1, dst, w);
 
   if (mine) {
     f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -172,7 +194,7 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
 // BH = B*H, Nq = the longest sequence's query count (sets nqt).  Rows of a
 // sequence without keys get O = 0 and LSE = -inf.
 template <int DT, int D, bool CAUSAL, bool SPLIT = false, bool VARLEN = false>
-__global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict__ Qg,
+__global__ __launch_bounds__(64 * waves16<D>(), 1) void fa_fwd_16(const u16* __restrict__ Qg,
                                                            const u16* __restrict__ Kg,
                                                            const u16* __restrict__ Vg,
                                                            u16* __restrict__ Og,
@@ -186,12 +208,15 @@ __global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict
   constexpr int TILEB = BC * ROWB;        // bytes per K (or V) tile
   constexpr int NKK = D / 16;             // MFMA steps over the head dimension
   constexpr int NDT = D / 32;             // 32-wide output column tiles
+  constexpr int NW = waves16<D>(), ST = stages16<D>();
+  constexpr int BR = 32 * NW;              // query rows per workgroup
 
-  // The LDS ring: tile j lives in stage j % 4 (a K tile followed by a V tile).
+  // The LDS ring: tile j lives in stage j % ST (a K tile followed by a V
+  // tile); stages 2 and 3 exist only in the 4-stage ring.
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * TILEB];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage2[2 * TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage3[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage2[ST == 4 ? 2 * TILEB : 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage3[ST == 4 ? 2 * TILEB : 1024];
 
   Wave16 w;
   const int tid = threadIdx.x;
@@ -209,7 +234,7 @@ __global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict
   } else {
     tile_of_block(nqt, BH, bh, qt);
   }
-  const int q0 = qt * kBR16;
+  const int q0 = qt * BR;
   // This head's rows: nq queries at Qh / Oh / Lh, NK keys at Kg + koff.
   const u16* Qh;
   u16* Oh;
@@ -243,7 +268,7 @@ __global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict
   const u16* Vh = Vg + koff + (size_t)kb * D;
   const int kbytes = nk * ROWB;
 
-  const int kend = CAUSAL ? min(nk, min(q0 + kBR16, nq) - kb) : nk;  // keys [0, kend) are needed
+  const int kend = CAUSAL ? min(nk, min(q0 + BR, nq) - kb) : nk;  // keys [0, kend) are needed
   const int nt = kend > 0 ? (kend + BC - 1) / BC : 0;
   w.wq0 = q0 + 32 * w.wave;
   const int myq = w.wq0 + w.l32;
@@ -264,23 +289,32 @@ __global__ __launch_bounds__(kThreads16, 1) void fa_fwd_16(const u16* __restrict
       qf[kk] = __builtin_amdgcn_raw_buffer_load_b128(rQ, (32 * w.wave + w.l32) * ROWB + (16 * kk + 8 * w.hf) * 2,
                                                      q0 * ROWB, 0);
   }
-  // Tiles 0..2 into stages 0..2.
-  if ((!SPLIT && !VARLEN) || nt > 0) issue_tile16<D, kWaves16>(Kh, Vh, kbytes, 0, stage0, w);
-  if (nt > 1) issue_tile16<D, kWaves16>(Kh, Vh, kbytes, 1, stage1, w);
-  if (nt > 2) issue_tile16<D, kWaves16>(Kh, Vh, kbytes, 2, stage2, w);
+  // Tiles 0..2 into stages 0..2 (tile 0 only with two stages).
+  if ((!SPLIT && !VARLEN) || nt > 0) issue_tile16<D, NW>(Kh, Vh, kbytes, 0, stage0, w);
+  if constexpr (ST == 4) {
+    if (nt > 1) issue_tile16<D, NW>(Kh, Vh, kbytes, 1, stage1, w);
+    if (nt > 2) issue_tile16<D, NW>(Kh, Vh, kbytes, 2, stage2, w);
+  }
 
   float mref = kMinit, l = 0.f;
   f32x16 oacc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
 
-  // Tile 0 must be complete before tile16(0) reads its first K operands.
-  wait_tile_and_barrier(nt > 2 ? loads_per_tile<D, kWaves16>(w.wave) : 0);
-  for (int j = 0; j < nt; j += kStages) {
-    tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j, nt, stage0, stage3, w, qf, oacc, mref, l, sl2);
-    if (j + 1 < nt) tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 1, nt, stage1, stage0, w, qf, oacc, mref, l, sl2);
-    if (j + 2 < nt) tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 2, nt, stage2, stage1, w, qf, oacc, mref, l, sl2);
-    if (j + 3 < nt) tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 3, nt, stage3, stage2, w, qf, oacc, mref, l, sl2);
+  if constexpr (ST == 4) {
+    // Tile 0 must be complete before tile16(0) reads its first K operands.
+    wait_tile_and_barrier(nt > 2 ? loads_per_tile<D, NW>(w.wave) : 0);
+    for (int j = 0; j < nt; j += 4) {
+      tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j, nt, stage0, stage3, w, qf, oacc, mref, l, sl2);
+      if (j + 1 < nt) tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 1, nt, stage1, stage0, w, qf, oacc, mref, l, sl2);
+      if (j + 2 < nt) tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 2, nt, stage2, stage1, w, qf, oacc, mref, l, sl2);
+      if (j + 3 < nt) tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 3, nt, stage3, stage2, w, qf, oacc, mref, l, sl2);
+    }
+  } else {
+    for (int j = 0; j < nt; j += 2) {
+      tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j, nt, stage0, stage1, w, qf, oacc, mref, l, sl2);
+      if (j + 1 < nt) tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 1, nt, stage1, stage0, w, qf, oacc, mref, l, sl2);
+    }
   }
 
   const float lt = pair_sum(l);
@@ -506,8 +540,9 @@ int launch(KernelT kern, const FaLaunch& a, int rows_per_block, int threads, flo
 
 template <int DT, int D, bool CAUSAL, bool SPLIT, bool VARLEN = false>
 void launch16(const FaLaunch& a, float sl2, int nsplit, int split_len, float* Po, float* Pl) {
-  const int nqt = (int)((a.Nq + kBR16 - 1) / kBR16);
-  const dim3 grid((unsigned)(a.BH * nqt * nsplit)), block(kThreads16);
+  constexpr int BR = 32 * waves16<D>();
+  const int nqt = (int)((a.Nq + BR - 1) / BR);
+  const dim3 grid((unsigned)(a.BH * nqt * nsplit)), block(64 * waves16<D>());
   hipLaunchKernelGGL((fa_fwd_16<DT, D, CAUSAL, SPLIT, VARLEN>), grid, block, 0, (hipStream_t)a.stream,
                      (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (u16*)a.o, a.lse, (int)a.BH, (int)a.Nq,
                      (int)a.Nk, nqt, sl2, split_len, Po, Pl, a.cu_q, a.cu_k, (int)a.H, (int)a.total_q,
@@ -596,10 +631,12 @@ int fa_launch_fwd_varlen(const FaLaunch& a) {
   switch (a.dtype) {
     case kBF16:
       return a.D == 32 ? dispatch16_varlen<kBF16, 32>(a, sl2)
-           : a.D == 64 ? dispatch16_varlen<kBF16, 64>(a, sl2) : dispatch16_varlen<kBF16, 128>(a, sl2);
+           : a.D == 64 ? dispatch16_varlen<kBF16, 64>(a, sl2)
+           : a.D == 128 ? dispatch16_varlen<kBF16, 128>(a, sl2) : dispatch16_varlen<kBF16, 256>(a, sl2);
     default:
       return a.D == 32 ? dispatch16_varlen<kFP16, 32>(a, sl2)
-           : a.D == 64 ? dispatch16_varlen<kFP16, 64>(a, sl2) : dispatch16_varlen<kFP16, 128>(a, sl2);
+           : a.D == 64 ? dispatch16_varlen<kFP16, 64>(a, sl2)
+           : a.D == 128 ? dispatch16_varlen<kFP16, 128>(a, sl2) : dispatch16_varlen<kFP16, 256>(a, sl2);
   }
 }
 
@@ -610,11 +647,13 @@ int fa_launch_fwd_splitkv(const FaLaunch& a, int nsplit, int split_len) {
     case kBF16:
       return a.D == 32 ? dispatch16_split<kBF16, 32>(a, sl2, nsplit, split_len)
            : a.D == 64 ? dispatch16_split<kBF16, 64>(a, sl2, nsplit, split_len)
-                       : dispatch16_split<kBF16, 128>(a, sl2, nsplit, split_len);
+           : a.D == 128 ? dispatch16_split<kBF16, 128>(a, sl2, nsplit, split_len)
+                        : dispatch16_split<kBF16, 256>(a, sl2, nsplit, split_len);
     default:
       return a.D == 32 ? dispatch16_split<kFP16, 32>(a, sl2, nsplit, split_len)
            : a.D == 64 ? dispatch16_split<kFP16, 64>(a, sl2, nsplit, split_len)
-                       : dispatch16_split<kFP16, 128>(a, sl2, nsplit, split_len);
+           : a.D == 128 ? dispatch16_split<kFP16, 128>(a, sl2, nsplit, split_len)
+                        : dispatch16_split<kFP16, 256>(a, sl2, nsplit, split_len);
   }
 }
 
@@ -625,10 +664,12 @@ int fa_launch_fwd(const FaLaunch& a) {
   switch (a.dtype) {
     case kBF16:
       return a.D == 32 ? dispatch16<kBF16, 32>(a, sl2)
-           : a.D == 64 ? dispatch16<kBF16, 64>(a, sl2) : dispatch16<kBF16, 128>(a, sl2);
+           : a.D == 64 ? dispatch16<kBF16, 64>(a, sl2)
+           : a.D == 128 ? dispatch16<kBF16, 128>(a, sl2) : dispatch16<kBF16, 256>(a, sl2);
     case kFP16:
       return a.D == 32 ? dispatch16<kFP16, 32>(a, sl2)
-           : a.D == 64 ? dispatch16<kFP16, 64>(a, sl2) : dispatch16<kFP16, 128>(a, sl2);
+           : a.D == 64 ? dispatch16<kFP16, 64>(a, sl2)
+           : a.D == 128 ? dispatch16<kFP16, 128>(a, sl2) : dispatch16<kFP16, 256>(a, sl2);
     default:
       return a.D == 32 ? dispatch32<32>(a, sl2) : a.D == 64 ? dispatch32<64>(a, sl2) : dispatch32<128>(a, sl2);
   }

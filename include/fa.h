@@ -53,7 +53,8 @@ typedef enum {
                           ((N + 256) * D * element size must stay below 2^31 for
                           N = Nq and N = Nk: one head is addressed with 32-bit
                           offsets) */
-  FA_ERR_HEAD_DIM = 3, /* D not in {32, 64, 128} */
+  FA_ERR_HEAD_DIM = 3, /* D not in {32, 64, 128, 256}; D = 256 with FA_DTYPE_FP32;
+                          D = 256 in fa_bwd */
   FA_ERR_DTYPE = 4,    /* unknown dtype code */
   FA_ERR_ALIGN = 5,    /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
   FA_ERR_ALIAS = 6,    /* o or lse overlaps an input, or o overlaps lse */
@@ -71,7 +72,7 @@ typedef enum {
  *   v    device pointer, [B, H, Nk, D] contiguous row-major, `dtype`
  *   o    device pointer, [B, H, Nq, D] contiguous row-major, `dtype` (output)
  *   lse  device pointer, [B, H, Nq] contiguous fp32 (output, natural log)
- *   B, H, Nq, Nk, D   sizes; D in {32, 64, 128}.  B*H*Nq == 0 is a valid no-op
+ *   B, H, Nq, Nk, D   sizes; D in {32, 64, 128, 256} (256: fp16 and bf16 only).  B*H*Nq == 0 is a valid no-op
  *        (pointers may then be NULL); otherwise Nk >= 1.
  *   causal  0: every key is kept; non-zero: key j kept for query i iff j <= i
  *   dtype   an fa_dtype code

@@ -54,7 +54,8 @@ def call(q=Q, k=K, v=V, o=O, lse=L, B=2, H=4, Nq=128, Nk=128, D=64, causal=1, dt
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(o=0), 1), (dict(lse=0), 1),
     (dict(B=-1), 2), (dict(H=-3), 2), (dict(Nq=-1), 2), (dict(Nk=0), 2), (dict(Nk=-5), 2),
-    (dict(D=16), 3), (dict(D=0), 3), (dict(D=256), 3), (dict(D=96), 3), (dict(D=-64), 2),
+    (dict(D=16), 3), (dict(D=0), 3), (dict(D=512), 3), (dict(D=96), 3), (dict(D=-64), 2),
+    (dict(D=256, dtype=0), 3),
     (dict(dtype=3), 4), (dict(dtype=-1), 4),
     (dict(q=Q + 8), 5), (dict(k=K + 4), 5), (dict(v=V + 2), 5), (dict(o=O + 1), 5), (dict(lse=L + 2), 5),
     (dict(o=Q), 6), (dict(o=K + 64), 6), (dict(lse=V + 1024), 6), (dict(lse=O + 16), 6),
@@ -83,7 +84,8 @@ def test_scaled_rejects_bad_scale(scale):
 def test_scaled_validates_like_fa_fwd():
     # the other checks come first and are the same as fa_fwd's
     assert call_scaled(0.1, q=0) == 1
-    assert call_scaled(0.1, D=256) == 3
+    assert call_scaled(0.1, D=512) == 3
+    assert call_scaled(0.1, D=256, dtype=0) == 3
     assert call_scaled(0.1, dtype=9) == 4
     assert call_scaled(float("nan"), q=0) == 1
     assert call_scaled(0.125, B=0, q=0, k=0, v=0, o=0, lse=0) == 0
@@ -194,7 +196,7 @@ def call_varlen(q=Q, k=K, v=V, o=O, lse=L, cu_q=CQ, cu_k=CK, B=3, H=4, total_q=5
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=0), 4), (dict(D=256), 3), (dict(scale=-1.0), 8), (dict(B=-1), 2), (dict(max_q=501), 2),
+    (dict(dtype=0), 4), (dict(D=512), 3), (dict(scale=-1.0), 8), (dict(B=-1), 2), (dict(max_q=501), 2),
     (dict(total_q=1 << 40), 2), (dict(cu_q=0), 1), (dict(cu_k=0), 1), (dict(lse=0), 1),
     (dict(cu_q=CQ + 2), 5), (dict(q=Q + 8), 5), (dict(o=Q + 64), 6), (dict(lse=CK), 6), (dict(o=CQ - 16), 6),
 ])

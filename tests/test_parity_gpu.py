@@ -53,8 +53,27 @@ def test_parity_small_grid(dt, D, causal, Nq, Nk):
     compare_full(w, cpu, o, l, "grid")
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq,Nk", [(300, 300), (257, 517), (130, 70), (1, 200)])
+def test_parity_d256(dt, causal, Nq, Nk):
+    # head dimension 256: 4 waves per workgroup and a 2-stage ring
+    w = workloads.Workload(f"d256_{dt}_{'c' if causal else 'n'}_{Nq}x{Nk}", 2, 2, Nq, Nk, 256, dt, causal,
+                           2560 + Nq + Nk)
+    cpu, gpu = _case(w)
+    o, l = run_gpu(*gpu, w.causal)
+    compare_full(w, cpu, o, l, "d256")
+
+
+def test_parity_d256_scaled_and_moves():
+    w = workloads.Workload("d256_scaled", 1, 2, 333, 401, 256, "bf16", True, 256)
+    cpu, gpu = _case(w)
+    o, l = run_gpu(*gpu, True, softmax_scale=0.04)
+    compare_full(w, cpu, o, l, "d256-scaled", scale=0.04)
+
+
 @pytest.mark.parametrize("dt,D,causal", [("bf16", 128, True), ("bf16", 128, False), ("fp16", 64, True),
-                                         ("fp16", 128, False), ("fp32", 64, True)])
+                                         ("fp16", 128, False), ("fp32", 64, True), ("bf16", 256, True)])
 def test_parity_reference_moves(dt, D, causal):
     # Keys whose norm grows along the sequence (K row j scaled by
     # 1 + a j/Nk, Q by a): each row's running max climbs tile after tile, so
@@ -103,6 +122,7 @@ def test_default_scale_matches_explicit():
 @pytest.mark.parametrize("name", ["c3_bf16_causal_b4h16n4096d128",
                                   "c4_bf16_causal_b1h32n16384d128_q4",
                                   "c5_fp16_cross_b8h32q512k8192d64",
+                                  "x1_bf16_causal_b4h8n4096d256",
                                   "c5t_fp16_cross_b8h32q511k8191d64"])
 def test_parity_full_size_sampled(name):
     w = W[name]

@@ -20,6 +20,7 @@ for i, (dt, D, causal, Nq, Nk) in enumerate([
         for causal in (False, True)
         for (Nq, Nk) in ((1, 4097), (16, 3000), (33, 700), (300, 1500))]):
     CASES.append((dt, D, causal, Nq, Nk, (0, 3, 7, 40)[i % 4]))
+CASES += [("bf16", 256, False, 1, 5000, 0), ("fp16", 256, True, 40, 900, 3)]
 
 
 def _run(w, splits, scale=None):

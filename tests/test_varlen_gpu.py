@@ -56,7 +56,7 @@ LENS = [
 
 
 @pytest.mark.parametrize("dt", ["bf16", "fp16"])
-@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("li", range(len(LENS)))
 def test_varlen_parity(dt, D, causal, li):
