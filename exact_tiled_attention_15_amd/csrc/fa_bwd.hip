@@ -259,47 +259,157 @@ __device__ __forceinline__ void kv_tile(const u16* Qh, const u16* dOh, int qbyte
   wait_tile_and_barrier(j + 2 < nt ? kv_loads_per_tile<D>(w.wave) : 0);
   if (j + kStages - 1 < nt) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t + kStages - 1, dst, w);
   if (CAUSAL && q0 + 63 < wk0) return;  // every query of the tile precedes the wave's keys
-  const bool need_mask = CAUSAL && q0 < wk0 + 31;
-  const int mykey = wk0 + w.l32;
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    f32x16 s = {}, dp = {};
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) s = mfma_32x32x16<DT>(ks_operand<D>(qs, w, n * NKK + kk), kf[kk], s);
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) dp = mfma_32x32x16<DT>(ks_operand<D>(dos, w, n * NKK + kk), vf[kk], dp);
-    // Lane l holds key mykey and queries q0 + 32n + 8g + 4hf + e (r = 4g + e).
-    float p[16], ds[16];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int qo = 32 * n + 8 * g + 4 * w.hf;
-      const f32x4 l4 = *(const f32x4*)(st + qo * 4);
-      const f32x4 d4 = *(const f32x4*)(st + 256 + qo * 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g + e;
-        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l4[e]));
-        if (need_mask && q0 + qo + e < mykey) pr = 0.f;
-        p[r] = pr;
-        ds[r] = pr * (dp[r] - d4[e]);
+  if constexpr (D == 128) {
+    // Queries of the tile below `qlim` (relative to q0) precede this lane's key
+    // and are masked (causal diagonal tiles only; elsewhere no query is).
+    const int qlim = (CAUSAL && q0 < wk0 + 31) ? wk0 + w.l32 - q0 : 0;
+    // One wave per SIMD, so the wave overlaps its own work, in an order fixed
+    // by scheduling fences: block 1's S and dP MFMAs each carry one score of
+    // block 0's softmax arithmetic, block 0's dV and dK MFMAs each carry one of
+    // block 1's, and every LDS operand is read a few MFMAs ahead.
+    constexpr int NS = 2 * NKK;  // S and dP MFMAs of a 32-query block (interleaved)
+    constexpr int NG = 4 * NDT;  // dV and dK MFMAs of a block (interleaved)
+    // Lane l holds key wk0 + l % 32 and queries q0 + 32n + 8g + 4hf + e (r = 4g + e).
+    f32x16 s[2], dp[2];
+    u32x4 pf[2][2], dsf[2][2];
+    float pv[2][16], dsv[2][16];
+    // operand i of the score MFMAs of block n: even i -> Q row operand for S,
+    // odd i -> dO row operand for dP, both at head-dimension step i / 2
+    auto score_operand = [&](int n, int i) -> u32x4 {
+      return (i & 1) ? ks_operand<D>(dos, w, n * NKK + (i >> 1)) : ks_operand<D>(qs, w, n * NKK + (i >> 1));
+    };
+    auto score_mfma = [&](int n, int i, u32x4 a) {
+      if (i & 1)
+        dp[n] = mfma_32x32x16<DT>(a, vf[i >> 1], dp[n]);
+      else
+        s[n] = mfma_32x32x16<DT>(a, kf[i >> 1], s[n]);
+    };
+    // operand i of the gradient MFMAs of block n: even i -> dO^T for dV,
+    // odd i -> Q^T for dK, at (dt, hh) = ((i / 2) / 2, (i / 2) % 2)
+    auto grad_operand = [&](int n, int i) -> u32x4 {
+      const int u = i >> 1, idx = 4 * (u >> 1) + 2 * n + (u & 1);
+      return (i & 1) ? vt_operand<D>(qs, w, idx) : vt_operand<D>(dos, w, idx);
+    };
+    auto grad_mfma = [&](int n, int i, u32x4 a) {
+      const int u = i >> 1;
+      if (i & 1)
+        dk[u >> 1] = mfma_32x32x16<DT>(a, dsf[n][u & 1], dk[u >> 1]);
+      else
+        dv[u >> 1] = mfma_32x32x16<DT>(a, pf[n][u & 1], dv[u >> 1]);
+    };
+    // softmax-gradient arithmetic of score r of block n (and the packing of a
+    // finished pair)
+    f32x4 l4[2][4], d4[2][4];
+    auto score_math = [&](int n, int r) {
+      const int g = r >> 2, e = r & 3, qo = 32 * n + 8 * g + 4 * w.hf;
+      float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[n][r], sl2, -l4[n][g][e]));
+      pr = qo + e < qlim ? 0.f : pr;
+      pv[n][r] = pr;
+      dsv[n][r] = pr * (dp[n][r] - d4[n][g][e]);
+      if (r & 1) {
+        const int hh = r >> 3, i = (r & 7) >> 1;
+        pf[n][hh][i] = pack2<DT>(pv[n][r - 1], pv[n][r]);
+        dsf[n][hh][i] = pack2<DT>(dsv[n][r - 1], dsv[n][r]);
       }
+    };
+    auto load_stats = [&](int n) {
+  #pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qo = 32 * n + 8 * g + 4 * w.hf;
+        l4[n][g] = *(const f32x4*)(st + qo * 4);
+        d4[n][g] = *(const f32x4*)(st + 256 + qo * 4);
+      }
+    };
+    constexpr int PRE = 8;  // operand read-ahead, in MFMAs
+    u32x4 op[NS > NG ? NS : NG];
+    s[0] = dp[0] = s[1] = dp[1] = f32x16{};
+    // block 0: score MFMAs
+  #pragma unroll
+    for (int i = 0; i < PRE; ++i) op[i] = score_operand(0, i);
+    load_stats(0);
+  #pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (i + PRE < NS) op[i + PRE] = score_operand(0, i + PRE);
+      score_mfma(0, i, op[i]);
     }
-    u32x4 pf[2], dsf[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pf[hh][i] = pack2<DT>(p[8 * hh + 2 * i], p[8 * hh + 2 * i + 1]);
-        dsf[hh][i] = pack2<DT>(ds[8 * hh + 2 * i], ds[8 * hh + 2 * i + 1]);
+    // block 1: score MFMAs, each with one score of block 0's arithmetic
+  #pragma unroll
+    for (int i = 0; i < PRE; ++i) op[i] = score_operand(1, i);
+    load_stats(1);
+    __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (i + PRE < NS) op[i + PRE] = score_operand(1, i + PRE);
+      score_mfma(1, i, op[i]);
+  #pragma unroll
+      for (int r = i * 16 / NS; r < (i + 1) * 16 / NS; ++r) score_math(0, r);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // block 0: gradient MFMAs, each with one score of block 1's arithmetic
+  #pragma unroll
+    for (int i = 0; i < PRE; ++i) op[i] = grad_operand(0, i);
+    __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      if (i + PRE < NG) op[i + PRE] = grad_operand(0, i + PRE);
+      grad_mfma(0, i, op[i]);
+  #pragma unroll
+      for (int r = i * 16 / NG; r < (i + 1) * 16 / NG; ++r) score_math(1, r);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // block 1: gradient MFMAs
+  #pragma unroll
+    for (int i = 0; i < PRE; ++i) op[i] = grad_operand(1, i);
+  #pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      if (i + PRE < NG) op[i + PRE] = grad_operand(1, i + PRE);
+      grad_mfma(1, i, op[i]);
+    }
+  } else {
+    // D <= 64: the compiler's own schedule measured faster than the fenced
+    // one below D = 128.
+    const bool need_mask = CAUSAL && q0 < wk0 + 31;
+    const int mykey = wk0 + w.l32;
+  #pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      f32x16 s = {}, dp = {};
+  #pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) s = mfma_32x32x16<DT>(ks_operand<D>(qs, w, n * NKK + kk), kf[kk], s);
+  #pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) dp = mfma_32x32x16<DT>(ks_operand<D>(dos, w, n * NKK + kk), vf[kk], dp);
+      // Lane l holds key mykey and queries q0 + 32n + 8g + 4hf + e (r = 4g + e).
+      float p[16], ds[16];
+  #pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qo = 32 * n + 8 * g + 4 * w.hf;
+        const f32x4 l4 = *(const f32x4*)(st + qo * 4);
+        const f32x4 d4 = *(const f32x4*)(st + 256 + qo * 4);
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l4[e]));
+          if (need_mask && q0 + qo + e < mykey) pr = 0.f;
+          p[r] = pr;
+          ds[r] = pr * (dp[r] - d4[e]);
+        }
       }
-    // dV^T += dO^T P and dK^T += Q^T dS over this block's 32 queries.
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        dv[dt] = mfma_32x32x16<DT>(vt_operand<D>(dos, w, 4 * dt + 2 * n + hh), pf[hh], dv[dt]);
-        dk[dt] = mfma_32x32x16<DT>(vt_operand<D>(qs, w, 4 * dt + 2 * n + hh), dsf[hh], dk[dt]);
-      }
+      u32x4 pf[2], dsf[2];
+  #pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pf[hh][i] = pack2<DT>(p[8 * hh + 2 * i], p[8 * hh + 2 * i + 1]);
+          dsf[hh][i] = pack2<DT>(ds[8 * hh + 2 * i], ds[8 * hh + 2 * i + 1]);
+        }
+      // dV^T += dO^T P and dK^T += Q^T dS over this block's 32 queries.
+  #pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+  #pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          dv[dt] = mfma_32x32x16<DT>(vt_operand<D>(dos, w, 4 * dt + 2 * n + hh), pf[hh], dv[dt]);
+          dk[dt] = mfma_32x32x16<DT>(vt_operand<D>(qs, w, 4 * dt + 2 * n + hh), dsf[hh], dk[dt]);
+        }
+    }
   }
 }
 
