@@ -211,7 +211,7 @@ extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* 
   // one head's packed rows are addressed with 32-bit offsets
   if ((total_q + 256) * D * esz > INT32_MAX || (total_k + 256) * D * esz > INT32_MAX) return FA_ERR_SHAPE;
   int64_t grid;
-  if (!mul_ok(BH, (max_seqlen_q + 255) / 256, &grid) || grid > INT32_MAX) return FA_ERR_SHAPE;
+  if (!mul_ok((BH + 7) / 8 * 8, (max_seqlen_q + 127) / 128, &grid) || grid > INT32_MAX) return FA_ERR_SHAPE;
   if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULL;
   if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) ||
       (((uintptr_t)lse | (uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) & 3u))

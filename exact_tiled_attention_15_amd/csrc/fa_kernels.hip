@@ -225,7 +225,17 @@ __global__ __launch_bounds__(64 * waves16<D>(), 1) void fa_fwd_16(const u16* __r
   w.hf = w.lane >> 5;
   w.l32 = w.lane & 31;
   int bh, qt, split = 0;
-  if constexpr (SPLIT) {
+  if constexpr (VARLEN) {
+    // Workgroups go to the 8 XCDs round-robin by block id.  Each XCD sweeps
+    // all Q tiles of one head (heaviest first) before the next head, so that
+    // the tiles running together on its 32 CUs share that head's K/V in the
+    // XCD's L2 (with one head per Q tile at a time, the K/V of the long
+    // sequences of a packed batch overflowed it).
+    const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3;
+    bh = xcd + 8 * (i / nqt);
+    qt = nqt - 1 - i % nqt;
+    if (bh >= BH) return;
+  } else if constexpr (SPLIT) {
     const int per = BH * nqt;
     split = blockIdx.x / per;
     const int rem = blockIdx.x - split * per;
@@ -542,7 +552,9 @@ template <int DT, int D, bool CAUSAL, bool SPLIT, bool VARLEN = false>
 void launch16(const FaLaunch& a, float sl2, int nsplit, int split_len, float* Po, float* Pl) {
   constexpr int BR = 32 * waves16<D>();
   const int nqt = (int)((a.Nq + BR - 1) / BR);
-  const dim3 grid((unsigned)(a.BH * nqt * nsplit)), block(64 * waves16<D>());
+  // VARLEN maps block ids per XCD (8 of them): round B*H up to a multiple of 8
+  const int64_t heads = VARLEN ? (a.BH + 7) / 8 * 8 : a.BH;
+  const dim3 grid((unsigned)(heads * nqt * nsplit)), block(64 * waves16<D>());
   hipLaunchKernelGGL((fa_fwd_16<DT, D, CAUSAL, SPLIT, VARLEN>), grid, block, 0, (hipStream_t)a.stream,
                      (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (u16*)a.o, a.lse, (int)a.BH, (int)a.Nq,
                      (int)a.Nk, nqt, sl2, split_len, Po, Pl, a.cu_q, a.cu_k, (int)a.H, (int)a.total_q,
