@@ -176,3 +176,34 @@ def test_gpu_invariants(dt):
     vc = c.expand_as(v).contiguous()
     o, _ = run_gpu(q, k, vc, False)
     assert float((o.float() - c.float()).abs().max()) <= TOL[dt][0]
+
+
+@pytest.mark.parametrize("path", ["fwd", "splitkv"])
+def test_max_size_closed_forms(path):
+    # Nk just below the 32-bit per-head offset limit ((Nk + 256) D 2 < 2^31 at
+    # D = 128): the oracle would need tens of GB of float64, so use the closed
+    # forms that hold at any size: Q = 0 gives uniform weights, O = mean of V
+    # over the keys and LSE = ln Nk.
+    import exact_tiled_attention_15_amd as fa
+
+    Nk = (2**31 - 1) // 256 - 256 - 1000
+    Nq = 100 if path == "fwd" else 8
+    D = 128
+    log(f"case max-size {path}: Nq={Nq} Nk={Nk} D={D} bf16, Q = 0")
+    gen = torch.Generator(device="cuda:0").manual_seed(31)
+    q = torch.zeros(1, 1, Nq, D, device="cuda:0", dtype=torch.bfloat16)
+    k = torch.randn(1, 1, Nk, D, device="cuda:0", dtype=torch.bfloat16, generator=gen)
+    v = torch.randn(1, 1, Nk, D, device="cuda:0", dtype=torch.bfloat16, generator=gen)
+    if path == "fwd":
+        o, l = fa.forward(q, k, v, False)
+    else:
+        o, l = fa.forward_splitkv(q, k, v, False)
+    torch.cuda.synchronize()
+    mean = v[0, 0].double().mean(dim=0)
+    eo = float((o[0, 0].double() - mean).abs().max())
+    el = float((l.double() - np.log(Nk)).abs().max())
+    log(f"  max|O - mean V|={eo:.3e} max|LSE - ln Nk|={el:.3e}")
+    assert bool(torch.isfinite(o).all())
+    assert eo <= TOL["bf16"][0] and el <= TOL["bf16"][1]
+    del k, v
+    torch.cuda.empty_cache()
