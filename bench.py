@@ -78,20 +78,24 @@ def kernel_tag(w, op: str = "fwd") -> str:
 
 
 CSRC = os.path.join(ROOT, "exact_tiled_attention_15_amd", "csrc")
-# the device code of the forward kernels: shared helpers, then the kernels
-KERNEL_SOURCES = (os.path.join(CSRC, "fa_device.h"), os.path.join(CSRC, "fa_kernels.hip"))
-KERNEL_SOURCES_BWD = (os.path.join(CSRC, "fa_device.h"), os.path.join(CSRC, "fa_bwd.hip"))
+# The code of a kernel: the shared device helpers, its source file, and the
+# build script that holds the compile flags of its unit.
+_BUILD = os.path.join(os.path.dirname(CSRC), "build.py")
+KERNEL_SOURCES = (os.path.join(CSRC, "fa_device.h"), os.path.join(CSRC, "fa_kernels.hip"), _BUILD)
+KERNEL_SOURCES_BWD = (os.path.join(CSRC, "fa_device.h"), os.path.join(CSRC, "fa_bwd.hip"), _BUILD)
 
 
 def kernel_code_sha256(paths=KERNEL_SOURCES) -> str:
-    """SHA-256 of the kernel sources with // comments and blank lines removed:
-    it names the code the counters were taken on, and survives comment edits."""
+    """SHA-256 of the kernel sources with comments (// in C++, # in Python)
+    and blank lines removed: it names the code the counters were taken on,
+    and survives comment edits."""
     import hashlib
 
     lines = []
     for path in paths:
+        mark = "#" if path.endswith(".py") else "//"
         for line in open(path, encoding="utf-8"):
-            code = line.split("//", 1)[0].rstrip()
+            code = line.split(mark, 1)[0].rstrip()
             if code:
                 lines.append(code)
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()

@@ -8,6 +8,7 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -21,8 +22,23 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # The kernels never need NaN-preserving max/min (no input-quieting
 # v_max x, x before each v_max of an MFMA result).
-FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}", "-fno-honor-nans",
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fno-honor-nans",
          "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
+# MFMA destinations and accumulators in VGPRs instead of AGPRs.
+VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+
+# Compile units: (object name, source, extra flags).  The two kernel sources
+# are each compiled twice; a macro picks which head dimensions a unit holds,
+# so that only the kernels that gain from VGPR-form MFMAs get that flag (the
+# forward at D = 256 and the backward at D = 32 and 64; the forward at D = 64
+# and the backward at D = 128 lose with it).
+UNITS = [
+    ("fwd", os.path.join(CSRC, "fa_kernels.hip"), []),
+    ("fwd_d256", os.path.join(CSRC, "fa_kernels.hip"), ["-DFA_FWD_D256", *VGPR_MFMA]),
+    ("bwd", os.path.join(CSRC, "fa_bwd.hip"), []),
+    ("bwd_small_d", os.path.join(CSRC, "fa_bwd.hip"), ["-DFA_BWD_SMALL_D", *VGPR_MFMA]),
+    ("api", os.path.join(CSRC, "fa_api.cpp"), []),
+]
 
 
 def hipcc() -> str:
@@ -32,20 +48,39 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the HIP library cannot be built")
 
 
-def build_library(verbose: bool = False, asm_dir: str | None = None) -> str:
-    cmd = [hipcc(), *FLAGS, *DEVICE_FLAGS, *SOURCES, "-o", LIB + ".tmp"]
-    if asm_dir:
-        os.makedirs(asm_dir, exist_ok=True)
-        cmd += ["-save-temps=obj", "-o", LIB + ".tmp"]
+def _run(cmd, cwd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, cwd=asm_dir or PKG, capture_output=True, text=True)
-    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
-                    if "packed-fp32-ops" not in l)
+    res = subprocess.run(cmd, cwd=cwd, capture_output=True, text=True)
+    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
     if verbose and out.strip():
         print(out)
+
+
+def build_library(verbose: bool = False, asm_dir: str | None = None) -> str:
+    """Compile every unit to an object (in parallel), then link libfa.so.
+
+    With asm_dir, the intermediate files (device assembly included) of each
+    unit are kept there, named after the unit.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
+    with tempfile.TemporaryDirectory() as tmp:
+        objdir = asm_dir or tmp
+        if asm_dir:
+            os.makedirs(asm_dir, exist_ok=True)
+        objs = [os.path.join(objdir, name + ".o") for name, _, _ in UNITS]
+        cmds = []
+        for (name, src, extra), obj in zip(UNITS, objs):
+            cmd = [hipcc(), *FLAGS, *DEVICE_FLAGS, *extra, "-c", src, "-o", obj]
+            if asm_dir:
+                cmd.append("-save-temps=obj")
+            cmds.append(cmd)
+        with ThreadPoolExecutor(len(cmds)) as ex:
+            list(ex.map(lambda c: _run(c, objdir, verbose), cmds))
+        _run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", LIB + ".tmp"], objdir, verbose)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

@@ -27,6 +27,14 @@
 //    dV^T += dO^T P and dK^T += Q^T dS (dO and Q read transposed).
 // S and dP are recomputed in both kernels: seven tile products instead of
 // the five a single kernel with atomic dQ updates would need.
+//
+// The library compiles this file twice.  Without FA_BWD_SMALL_D it defines
+// fa_launch_bwd and the D = 128 kernels; with FA_BWD_SMALL_D only the D = 32
+// and 64 launcher (fa_launch_bwd_small_d), compiled with the MFMA
+// accumulators in VGPRs: in the AGPR form the compiler copied the dK/dV
+// accumulators and every S / dP value between the two register files
+// (about 960 copies in the D = 64 dK/dV kernel), while at D = 128 the VGPR
+// form runs out of registers.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -510,20 +518,24 @@ int dispatch_bwd(const FaBwdLaunch& a, float sl2, float scale) {
   return a.causal ? launch_bwd<DT, D, true>(a, sl2, scale) : launch_bwd<DT, D, false>(a, sl2, scale);
 }
 
-template <int DT>
-int dispatch_bwd_d(const FaBwdLaunch& a, float sl2, float scale) {
-  switch (a.D) {
-    case 32: return dispatch_bwd<DT, 32>(a, sl2, scale);
-    case 64: return dispatch_bwd<DT, 64>(a, sl2, scale);
-    default: return dispatch_bwd<DT, 128>(a, sl2, scale);
-  }
+}  // namespace
+
+#ifdef FA_BWD_SMALL_D
+
+int fa_launch_bwd_small_d(const FaBwdLaunch& a, float sl2, float scale) {
+  if (a.dtype == kBF16)
+    return a.D == 32 ? dispatch_bwd<kBF16, 32>(a, sl2, scale) : dispatch_bwd<kBF16, 64>(a, sl2, scale);
+  return a.D == 32 ? dispatch_bwd<kFP16, 32>(a, sl2, scale) : dispatch_bwd<kFP16, 64>(a, sl2, scale);
 }
 
-}  // namespace
+#else
 
 int fa_launch_bwd(const FaBwdLaunch& a) {
   const float sl2 = (float)(a.scale * 1.4426950408889634074);
   const float scale = (float)a.scale;
   (void)hipGetLastError();  // clear a stale error so that the check below is ours
-  return a.dtype == kBF16 ? dispatch_bwd_d<kBF16>(a, sl2, scale) : dispatch_bwd_d<kFP16>(a, sl2, scale);
+  if (a.D < 128) return fa_launch_bwd_small_d(a, sl2, scale);
+  return a.dtype == kBF16 ? dispatch_bwd<kBF16, 128>(a, sl2, scale) : dispatch_bwd<kFP16, 128>(a, sl2, scale);
 }
+
+#endif  // FA_BWD_SMALL_D

@@ -41,6 +41,12 @@ int fa_launch_fwd_splitkv(const FaLaunch& a, int nsplit, int split_len);
 // k, v [H, total_k, D]; lse [H, total_q]; per-sequence offsets cu_q, cu_k.
 int fa_launch_fwd_varlen(const FaLaunch& a);
 
+// The D = 256 launchers of the three forward entry points above (a unit of
+// their own; sl2 = scale * log2(e)).
+int fa_launch_fwd_d256(const FaLaunch& a, float sl2);
+int fa_launch_fwd_splitkv_d256(const FaLaunch& a, float sl2, int nsplit, int split_len);
+int fa_launch_fwd_varlen_d256(const FaLaunch& a, float sl2);
+
 struct FaBwdLaunch {
   const void* q;
   const void* k;
@@ -65,3 +71,7 @@ struct FaBwdLaunch {
 // Enqueues the backward pass (three kernels).  Arguments are already
 // validated.  Returns 0 on success, otherwise the HIP error code.
 int fa_launch_bwd(const FaBwdLaunch& a);
+
+// The D = 32 and D = 64 backward launcher (a unit of its own; sl2 = scale *
+// log2(e)), called by fa_launch_bwd.
+int fa_launch_bwd_small_d(const FaBwdLaunch& a, float sl2, float scale);

@@ -32,6 +32,13 @@
 // Softmax runs in the log2 domain: t = s * scale * log2(e) (scale = 1/sqrt(D)
 // unless given), p = exp2(t - m) on v_exp_f32; LSE = (m + log2 l) * ln 2 at
 // the end.
+//
+// The library compiles this file twice.  Without FA_FWD_D256 it defines the
+// fa_launch_fwd* entry points and every kernel up to D = 128; with
+// FA_FWD_D256 it defines only the D = 256 launchers (fa_launch_fwd*_d256),
+// compiled with the MFMA accumulators in VGPRs (in the AGPR form the loop
+// carried O of 32 rows x 256 columns was copied between the two register
+// files on every tile), which the D <= 128 kernels do not want.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -626,8 +633,6 @@ int dispatch32(const FaLaunch& a, float sl2) {
   return launch<decltype(&fa_fwd_32<D, false>), float>(&fa_fwd_32<D, false>, a, kBR, kThreads, sl2);
 }
 
-}  // namespace
-
 template <int DT, int D>
 int dispatch16_varlen(const FaLaunch& a, float sl2) {
   if (a.causal)
@@ -637,35 +642,52 @@ int dispatch16_varlen(const FaLaunch& a, float sl2) {
   return (int)hipGetLastError();
 }
 
+}  // namespace
+
+#ifdef FA_FWD_D256
+
+int fa_launch_fwd_d256(const FaLaunch& a, float sl2) {
+  return a.dtype == kBF16 ? dispatch16<kBF16, 256>(a, sl2) : dispatch16<kFP16, 256>(a, sl2);
+}
+
+int fa_launch_fwd_splitkv_d256(const FaLaunch& a, float sl2, int nsplit, int split_len) {
+  return a.dtype == kBF16 ? dispatch16_split<kBF16, 256>(a, sl2, nsplit, split_len)
+                          : dispatch16_split<kFP16, 256>(a, sl2, nsplit, split_len);
+}
+
+int fa_launch_fwd_varlen_d256(const FaLaunch& a, float sl2) {
+  return a.dtype == kBF16 ? dispatch16_varlen<kBF16, 256>(a, sl2) : dispatch16_varlen<kFP16, 256>(a, sl2);
+}
+
+#else
+
 int fa_launch_fwd_varlen(const FaLaunch& a) {
   const float sl2 = (float)(a.scale * 1.4426950408889634074);
   (void)hipGetLastError();  // clear a stale error so that the check below is ours
+  if (a.D == 256) return fa_launch_fwd_varlen_d256(a, sl2);
   switch (a.dtype) {
     case kBF16:
       return a.D == 32 ? dispatch16_varlen<kBF16, 32>(a, sl2)
-           : a.D == 64 ? dispatch16_varlen<kBF16, 64>(a, sl2)
-           : a.D == 128 ? dispatch16_varlen<kBF16, 128>(a, sl2) : dispatch16_varlen<kBF16, 256>(a, sl2);
+           : a.D == 64 ? dispatch16_varlen<kBF16, 64>(a, sl2) : dispatch16_varlen<kBF16, 128>(a, sl2);
     default:
       return a.D == 32 ? dispatch16_varlen<kFP16, 32>(a, sl2)
-           : a.D == 64 ? dispatch16_varlen<kFP16, 64>(a, sl2)
-           : a.D == 128 ? dispatch16_varlen<kFP16, 128>(a, sl2) : dispatch16_varlen<kFP16, 256>(a, sl2);
+           : a.D == 64 ? dispatch16_varlen<kFP16, 64>(a, sl2) : dispatch16_varlen<kFP16, 128>(a, sl2);
   }
 }
 
 int fa_launch_fwd_splitkv(const FaLaunch& a, int nsplit, int split_len) {
   const float sl2 = (float)(a.scale * 1.4426950408889634074);
   (void)hipGetLastError();  // clear a stale error so that the check below is ours
+  if (a.D == 256) return fa_launch_fwd_splitkv_d256(a, sl2, nsplit, split_len);
   switch (a.dtype) {
     case kBF16:
       return a.D == 32 ? dispatch16_split<kBF16, 32>(a, sl2, nsplit, split_len)
            : a.D == 64 ? dispatch16_split<kBF16, 64>(a, sl2, nsplit, split_len)
-           : a.D == 128 ? dispatch16_split<kBF16, 128>(a, sl2, nsplit, split_len)
-                        : dispatch16_split<kBF16, 256>(a, sl2, nsplit, split_len);
+                       : dispatch16_split<kBF16, 128>(a, sl2, nsplit, split_len);
     default:
       return a.D == 32 ? dispatch16_split<kFP16, 32>(a, sl2, nsplit, split_len)
            : a.D == 64 ? dispatch16_split<kFP16, 64>(a, sl2, nsplit, split_len)
-           : a.D == 128 ? dispatch16_split<kFP16, 128>(a, sl2, nsplit, split_len)
-                        : dispatch16_split<kFP16, 256>(a, sl2, nsplit, split_len);
+                       : dispatch16_split<kFP16, 128>(a, sl2, nsplit, split_len);
   }
 }
 
@@ -673,16 +695,17 @@ int fa_launch_fwd(const FaLaunch& a) {
   // scale * log2(e), computed in double and rounded once.
   const float sl2 = (float)(a.scale * 1.4426950408889634074);
   (void)hipGetLastError();  // clear a stale error so that the check below is ours
+  if (a.D == 256) return fa_launch_fwd_d256(a, sl2);
   switch (a.dtype) {
     case kBF16:
       return a.D == 32 ? dispatch16<kBF16, 32>(a, sl2)
-           : a.D == 64 ? dispatch16<kBF16, 64>(a, sl2)
-           : a.D == 128 ? dispatch16<kBF16, 128>(a, sl2) : dispatch16<kBF16, 256>(a, sl2);
+           : a.D == 64 ? dispatch16<kBF16, 64>(a, sl2) : dispatch16<kBF16, 128>(a, sl2);
     case kFP16:
       return a.D == 32 ? dispatch16<kFP16, 32>(a, sl2)
-           : a.D == 64 ? dispatch16<kFP16, 64>(a, sl2)
-           : a.D == 128 ? dispatch16<kFP16, 128>(a, sl2) : dispatch16<kFP16, 256>(a, sl2);
+           : a.D == 64 ? dispatch16<kFP16, 64>(a, sl2) : dispatch16<kFP16, 128>(a, sl2);
     default:
       return a.D == 32 ? dispatch32<32>(a, sl2) : a.D == 64 ? dispatch32<64>(a, sl2) : dispatch32<128>(a, sl2);
   }
 }
+
+#endif  // FA_FWD_D256

@@ -14,7 +14,6 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "exact_tiled_attention_15_amd", "csrc")
-SOURCES = ["fa_kernels.hip", "fa_bwd.hip"]
 
 WIDE_STORE = re.compile(r"^(buffer|global|flat)_store_dwordx[34]\b")
 
@@ -26,11 +25,19 @@ def _hipcc():
     return None
 
 
-def _asm(src, out):
+def _device_units():
+    """The library's device compile units: (name, source, extra flags)."""
     import exact_tiled_attention_15_amd.build as b
 
+    return [u for u in b.UNITS if u[1].endswith(".hip")]
+
+
+def _asm(unit, out):
+    import exact_tiled_attention_15_amd.build as b
+
+    _, src, extra = unit
     cmd = [_hipcc(), "-O3", "-std=c++17", f"--offload-arch={b.ARCH}", "-fno-honor-nans", "--cuda-device-only",
-           "-S", *b.DEVICE_FLAGS, "-I", os.path.join(ROOT, "include"), os.path.join(CSRC, src), "-o", out]
+           "-S", *b.DEVICE_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), src, "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     return open(out).read()
@@ -70,10 +77,12 @@ def test_scanner_catches_the_pattern():
 
 @pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
 def test_device_code_has_no_wide_store_data_hazard():
+    units = _device_units()
+    assert len(units) >= 4
     with tempfile.TemporaryDirectory() as d:
-        with ThreadPoolExecutor(len(SOURCES)) as ex:
-            texts = list(ex.map(lambda s: _asm(s, os.path.join(d, s + ".s")), SOURCES))
-    for src, text in zip(SOURCES, texts):
-        assert "v_mfma" in text, f"{src}: no device code?"
+        with ThreadPoolExecutor(len(units)) as ex:
+            texts = list(ex.map(lambda u: _asm(u, os.path.join(d, u[0] + ".s")), units))
+    for (name, _, _), text in zip(units, texts):
+        assert "v_mfma" in text, f"{name}: no device code?"
         h = hazards(text)
-        assert not h, f"{src}: {len(h)} wide stores with their data overwritten next: {h[:3]}"
+        assert not h, f"{name}: {len(h)} wide stores with their data overwritten next: {h[:3]}"
