@@ -257,7 +257,7 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
                       double softmax_scale, int causal, int dtype, void* stream) {
   if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;  // 16-bit inputs only
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || D < 0) return FA_ERR_SHAPE;
-  if (D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (D != 32 && D != 64 && D != 128 && D != 256) return FA_ERR_HEAD_DIM;
   if (!scale_ok(softmax_scale)) return FA_ERR_SCALE;
   int64_t BH, qel, kel;
   if (!mul_ok(B, H, &BH) || !mul_ok(BH, Nq, &qel) || !mul_ok(qel, D, &qel) || !mul_ok(BH, Nk, &kel) ||
@@ -270,7 +270,8 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   const int64_t esz = 2;
   if ((Nq + 256) * D * esz > INT32_MAX || (Nk + 256) * D * esz > INT32_MAX) return FA_ERR_SHAPE;
   int64_t gq, gk;
-  if (!mul_ok(BH, (Nq + 255) / 256, &gq) || gq > INT32_MAX || !mul_ok(BH, (Nk + 127) / 128, &gk) ||
+  // dQ workgroups take 256 query rows (128 at D = 256), dK/dV ones 128 keys
+  if (!mul_ok(BH, (Nq + 127) / 128, &gq) || gq > INT32_MAX || !mul_ok(BH, (Nk + 127) / 128, &gk) ||
       gk > INT32_MAX || BH * Nq * (D / 8) / 256 >= INT32_MAX)
     return FA_ERR_SHAPE;
   const int64_t ws_need = fa_bwd_workspace_size(B, H, Nq);
@@ -321,7 +322,7 @@ extern "C" const char* fa_status_str(int status) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative, empty-key or too large shape";
-    case FA_ERR_HEAD_DIM: return "FA_ERR_HEAD_DIM: head dimension must be 32, 64, 128 or 256 (backward: 32, 64 or 128)";
+    case FA_ERR_HEAD_DIM: return "FA_ERR_HEAD_DIM: head dimension must be 32, 64, 128 or 256 (256: 16-bit types only)";
     case FA_ERR_DTYPE: return "FA_ERR_DTYPE: unknown dtype code";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: q/k/v/o must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or the other output";

@@ -1,5 +1,5 @@
 // Exact tiled attention backward pass for gfx950 (CDNA4, MI355X), 16-bit
-// inputs (bf16 / fp16), D in {32, 64, 128}.
+// inputs (bf16 / fp16), D in {32, 64, 128, 256}.
 //
 // "Building a FlashAttention-2 Forward Kernel in Pure NumPy" (Extending It)
 // describes the backward pass as recomputation: keep the forward's softmax
@@ -27,6 +27,9 @@
 //    dV^T += dO^T P and dK^T += Q^T dS (dO and Q read transposed).
 // S and dP are recomputed in both kernels: seven tile products instead of
 // the five a single kernel with atomic dQ updates would need.
+// At D = 256 bwd_dq has 4 waves (one per SIMD), bwd_dkdv runs as two kernels
+// (dV, then dK: one gradient's accumulators per wave), and both rings have 2
+// stages (a stage of two 64-row tiles takes 64 KB).
 //
 // The library compiles this file twice.  Without FA_BWD_SMALL_D it defines
 // fa_launch_bwd and the D = 128 kernels; with FA_BWD_SMALL_D only the D = 32
@@ -44,8 +47,22 @@
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634074f;
-constexpr int kWavesQ = 8;   // bwd_dq: waves per workgroup (32 query rows each)
 constexpr int kWavesKV = 4;  // bwd_dkdv: waves per workgroup (32 keys each)
+
+// bwd_dq: waves per workgroup (32 query rows each).  Up to D = 128, 8 (two
+// per SIMD); at D = 256 the Q and dO fragments and the fp32 dQ of 32 rows take
+// more than half of a SIMD's registers, so 4 (one per SIMD).
+template <int D>
+constexpr int dq_waves() {
+  return D == 256 ? 4 : 8;
+}
+// Stages of both kernels' LDS rings: 4 up to D = 128 (three tiles in flight);
+// at D = 256 a stage (64 rows of two tensors) takes 64 KB, so 2 (one tile in
+// flight: each tile waits for itself, then the next one starts).
+template <int D>
+constexpr int bwd_stages() {
+  return D == 256 ? 2 : 4;
+}
 
 template <int DT>
 __device__ __forceinline__ float lo16(unsigned x) {
@@ -122,14 +139,14 @@ __device__ __forceinline__ void dq_tile(const u16* Kh, const u16* Vh, int kbytes
                                         const unsigned char* src, unsigned char* dst, const Wave16& w,
                                         const u32x4 (&qf)[D / 16], const u32x4 (&dof)[D / 16],
                                         f32x16 (&acc)[D / 32], float lse2, float delta, float sl2) {
-  constexpr int BC = 64, TILEB = BC * D * 2, NKK = D / 16, NDT = D / 32;
+  constexpr int BC = 64, TILEB = BC * D * 2, NKK = D / 16, NDT = D / 32, NW = dq_waves<D>(), ST = bwd_stages<D>();
   const int k0 = j * BC;
   const unsigned char* ks = src;
   const unsigned char* vs = src + TILEB;
-  // Tile j is complete since the previous barrier; wait for tile j+1 and
-  // refill the stage of tile j-1.
-  wait_tile_and_barrier(j + 2 < nt ? loads_per_tile<D, kWavesQ>(w.wave) : 0);
-  if (j + kStages - 1 < nt) issue_tile16<D, kWavesQ>(Kh, Vh, kbytes, j + kStages - 1, dst, w);
+  // 4 stages: tile j is complete since the previous barrier; wait for tile
+  // j+1.  2 stages: wait for tile j itself.  Then refill the stage of tile j-1.
+  wait_tile_and_barrier(ST == 4 && j + 2 < nt ? loads_per_tile<D, NW>(w.wave) : 0);
+  if (j + ST - 1 < nt) issue_tile16<D, NW>(Kh, Vh, kbytes, j + ST - 1, dst, w);
   if (k0 >= w.wkend) return;
   const bool need_mask = k0 + BC - 1 > w.wklim;  // causal diagonal or past Nk
   const int lim = w.klim - (k0 + 4 * w.hf);
@@ -163,16 +180,16 @@ __device__ __forceinline__ void dq_tile(const u16* Kh, const u16* Vh, int kbytes
 }
 
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * kWavesQ, 1) void bwd_dq(const u16* __restrict__ Qg, const u16* __restrict__ Kg,
+__global__ __launch_bounds__(64 * dq_waves<D>(), 1) void bwd_dq(const u16* __restrict__ Qg, const u16* __restrict__ Kg,
                                                           const u16* __restrict__ Vg, const u16* __restrict__ dOg,
                                                           const float* __restrict__ lse2g,
                                                           const float* __restrict__ deltag, u16* __restrict__ dQg,
                                                           int BH, int Nq, int Nk, int nqt, float sl2, float scale) {
-  constexpr int BC = 64, ROWB = D * 2, TILEB = BC * ROWB, BR = 32 * kWavesQ;
+  constexpr int BC = 64, ROWB = D * 2, TILEB = BC * ROWB, NW = dq_waves<D>(), BR = 32 * NW, ST = bwd_stages<D>();
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * TILEB];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage2[2 * TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage3[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage2[ST == 4 ? 2 * TILEB : 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage3[ST == 4 ? 2 * TILEB : 1024];
 
   Wave16 w;
   const int tid = threadIdx.x;
@@ -203,19 +220,30 @@ __global__ __launch_bounds__(64 * kWavesQ, 1) void bwd_dq(const u16* __restrict_
   const float lse2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, myq * 4, 0, 0));
   const float delta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, myq * 4, 0, 0));
 
-  issue_tile16<D, kWavesQ>(Kh, Vh, kbytes, 0, stage0, w);
-  if (nt > 1) issue_tile16<D, kWavesQ>(Kh, Vh, kbytes, 1, stage1, w);
-  if (nt > 2) issue_tile16<D, kWavesQ>(Kh, Vh, kbytes, 2, stage2, w);
+  issue_tile16<D, NW>(Kh, Vh, kbytes, 0, stage0, w);
   f32x16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
-  // Tile 0 complete before the first tile's reads.
-  wait_tile_and_barrier(nt > 2 ? loads_per_tile<D, kWavesQ>(w.wave) : 0);
-  for (int j = 0; j < nt; j += kStages) {
-    dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j, nt, stage0, stage3, w, qf, dof, acc, lse2, delta, sl2);
-    if (j + 1 < nt) dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 1, nt, stage1, stage0, w, qf, dof, acc, lse2, delta, sl2);
-    if (j + 2 < nt) dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 2, nt, stage2, stage1, w, qf, dof, acc, lse2, delta, sl2);
-    if (j + 3 < nt) dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 3, nt, stage3, stage2, w, qf, dof, acc, lse2, delta, sl2);
+  if constexpr (ST == 4) {
+    if (nt > 1) issue_tile16<D, NW>(Kh, Vh, kbytes, 1, stage1, w);
+    if (nt > 2) issue_tile16<D, NW>(Kh, Vh, kbytes, 2, stage2, w);
+    // Tile 0 complete before the first tile's reads.
+    wait_tile_and_barrier(nt > 2 ? loads_per_tile<D, NW>(w.wave) : 0);
+    for (int j = 0; j < nt; j += 4) {
+      dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j, nt, stage0, stage3, w, qf, dof, acc, lse2, delta, sl2);
+      if (j + 1 < nt)
+        dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 1, nt, stage1, stage0, w, qf, dof, acc, lse2, delta, sl2);
+      if (j + 2 < nt)
+        dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 2, nt, stage2, stage1, w, qf, dof, acc, lse2, delta, sl2);
+      if (j + 3 < nt)
+        dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 3, nt, stage3, stage2, w, qf, dof, acc, lse2, delta, sl2);
+    }
+  } else {
+    for (int j = 0; j < nt; j += 2) {
+      dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j, nt, stage0, stage1, w, qf, dof, acc, lse2, delta, sl2);
+      if (j + 1 < nt)
+        dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 1, nt, stage1, stage0, w, qf, dof, acc, lse2, delta, sl2);
+    }
   }
   const auto rq = make_rsrc(dQg + (size_t)bh * Nq * D, Nq * ROWB);
   store_rows16<DT, D>(acc, scale, rq, (32 * w.wave + w.l32) * ROWB, q0 * ROWB, w.hf);
@@ -252,21 +280,26 @@ __device__ __forceinline__ void issue_kv_tile(const u16* Qh, const u16* dOh, int
   }
 }
 
-template <int DT, int D, bool CAUSAL>
+// GRADS: 3 = dK and dV, 1 = dK only, 2 = dV only (D = 256, where the fp32 dK
+// and dV of 32 keys plus the K and V fragments do not fit one wave's
+// registers, so one kernel runs per gradient).
+template <int DT, int D, bool CAUSAL, int GRADS>
 __device__ __forceinline__ void kv_tile(const u16* Qh, const u16* dOh, int qbytes, const float* l2h,
                                         const float* dlh, int Nq, int t0, int j, int nt, const unsigned char* src,
                                         unsigned char* dst, const Wave16& w, int wk0, const u32x4 (&kf)[D / 16],
                                         const u32x4 (&vf)[D / 16], f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32],
                                         float sl2) {
-  constexpr int TILEB = 64 * D * 2, NKK = D / 16, NDT = D / 32;
+  constexpr int TILEB = 64 * D * 2, NKK = D / 16, NDT = D / 32, ST = bwd_stages<D>();
   const int t = t0 + j;
   const int q0 = 64 * t;
   const unsigned char* qs = src;
   const unsigned char* dos = src + TILEB;
   const unsigned char* st = src + 2 * TILEB;
-  wait_tile_and_barrier(j + 2 < nt ? kv_loads_per_tile<D>(w.wave) : 0);
-  if (j + kStages - 1 < nt) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t + kStages - 1, dst, w);
+  // As in dq_tile: 4 stages wait for tile j+1, 2 stages for tile j.
+  wait_tile_and_barrier(ST == 4 && j + 2 < nt ? kv_loads_per_tile<D>(w.wave) : 0);
+  if (j + ST - 1 < nt) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t + ST - 1, dst, w);
   if (CAUSAL && q0 + 63 < wk0) return;  // every query of the tile precedes the wave's keys
+  static_assert(GRADS == 3 || D == 256, "one gradient per kernel only at D = 256");
   if constexpr (D == 128) {
     // Queries of the tile below `qlim` (relative to q0) precede this lane's key
     // and are masked (causal diagonal tiles only; elsewhere no query is).
@@ -374,8 +407,9 @@ __device__ __forceinline__ void kv_tile(const u16* Qh, const u16* dOh, int qbyte
       grad_mfma(1, i, op[i]);
     }
   } else {
-    // D <= 64: the compiler's own schedule measured faster than the fenced
-    // one below D = 128.
+    // D <= 64 and D = 256: the compiler's own schedule (below D = 128 it
+    // measured faster than the fenced one).
+    constexpr bool kDK = GRADS & 1, kDV = GRADS & 2;
     const bool need_mask = CAUSAL && q0 < wk0 + 31;
     const int mykey = wk0 + w.l32;
   #pragma unroll
@@ -383,8 +417,10 @@ __device__ __forceinline__ void kv_tile(const u16* Qh, const u16* dOh, int qbyte
       f32x16 s = {}, dp = {};
   #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) s = mfma_32x32x16<DT>(ks_operand<D>(qs, w, n * NKK + kk), kf[kk], s);
+      if constexpr (kDK) {
   #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) dp = mfma_32x32x16<DT>(ks_operand<D>(dos, w, n * NKK + kk), vf[kk], dp);
+        for (int kk = 0; kk < NKK; ++kk) dp = mfma_32x32x16<DT>(ks_operand<D>(dos, w, n * NKK + kk), vf[kk], dp);
+      }
       // Lane l holds key mykey and queries q0 + 32n + 8g + 4hf + e (r = 4g + e).
       float p[16], ds[16];
   #pragma unroll
@@ -398,7 +434,7 @@ __device__ __forceinline__ void kv_tile(const u16* Qh, const u16* dOh, int qbyte
           float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l4[e]));
           if (need_mask && q0 + qo + e < mykey) pr = 0.f;
           p[r] = pr;
-          ds[r] = pr * (dp[r] - d4[e]);
+          ds[r] = kDK ? pr * (dp[r] - d4[e]) : 0.f;
         }
       }
       u32x4 pf[2], dsf[2];
@@ -414,25 +450,25 @@ __device__ __forceinline__ void kv_tile(const u16* Qh, const u16* dOh, int qbyte
       for (int dt = 0; dt < NDT; ++dt)
   #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          dv[dt] = mfma_32x32x16<DT>(vt_operand<D>(dos, w, 4 * dt + 2 * n + hh), pf[hh], dv[dt]);
-          dk[dt] = mfma_32x32x16<DT>(vt_operand<D>(qs, w, 4 * dt + 2 * n + hh), dsf[hh], dk[dt]);
+          if constexpr (kDV) dv[dt] = mfma_32x32x16<DT>(vt_operand<D>(dos, w, 4 * dt + 2 * n + hh), pf[hh], dv[dt]);
+          if constexpr (kDK) dk[dt] = mfma_32x32x16<DT>(vt_operand<D>(qs, w, 4 * dt + 2 * n + hh), dsf[hh], dk[dt]);
         }
     }
   }
 }
 
-template <int DT, int D, bool CAUSAL>
+template <int DT, int D, bool CAUSAL, int GRADS>
 __global__ __launch_bounds__(64 * kWavesKV, 1) void bwd_dkdv(const u16* __restrict__ Qg, const u16* __restrict__ Kg,
                                                              const u16* __restrict__ Vg, const u16* __restrict__ dOg,
                                                              const float* __restrict__ lse2g,
                                                              const float* __restrict__ deltag, u16* __restrict__ dKg,
                                                              u16* __restrict__ dVg, int BH, int Nq, int Nk,
                                                              float sl2, float scale) {
-  constexpr int ROWB = D * 2, SB = kv_stage_bytes<D>(), BK = 32 * kWavesKV;
+  constexpr int ROWB = D * 2, SB = kv_stage_bytes<D>(), BK = 32 * kWavesKV, ST = bwd_stages<D>();
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[SB];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[SB];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage2[SB];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage3[SB];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage2[ST == 4 ? SB : 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage3[ST == 4 ? SB : 1024];
 
   Wave16 w;
   const int tid = threadIdx.x;
@@ -458,30 +494,42 @@ __global__ __launch_bounds__(64 * kWavesKV, 1) void bwd_dkdv(const u16* __restri
 
   u32x4 kf[D / 16], vf[D / 16];
   load_frag<D>(kf, Kg + (size_t)bh * Nk * D, Nk, wk0, w);
-  load_frag<D>(vf, Vg + (size_t)bh * Nk * D, Nk, wk0, w);
+  if constexpr (GRADS & 1) load_frag<D>(vf, Vg + (size_t)bh * Nk * D, Nk, wk0, w);
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) dk[dt] = dv[dt] = f32x16{};
 
   if (nt > 0) {
     issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t0, stage0, w);
-    if (nt > 1) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t0 + 1, stage1, w);
-    if (nt > 2) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t0 + 2, stage2, w);
-    wait_tile_and_barrier(nt > 2 ? kv_loads_per_tile<D>(w.wave) : 0);
-    for (int j = 0; j < nt; j += kStages) {
-      kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, Nq, t0, j, nt, stage0, stage3, w, wk0, kf, vf, dk, dv, sl2);
-      if (j + 1 < nt)
-        kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, Nq, t0, j + 1, nt, stage1, stage0, w, wk0, kf, vf, dk, dv, sl2);
-      if (j + 2 < nt)
-        kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, Nq, t0, j + 2, nt, stage2, stage1, w, wk0, kf, vf, dk, dv, sl2);
-      if (j + 3 < nt)
-        kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, Nq, t0, j + 3, nt, stage3, stage2, w, wk0, kf, vf, dk, dv, sl2);
+    if constexpr (ST == 2) {
+      for (int j = 0; j < nt; j += 2) {
+        kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, Nq, t0, j, nt, stage0, stage1, w, wk0, kf, vf, dk, dv, sl2);
+        if (j + 1 < nt)
+          kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, Nq, t0, j + 1, nt, stage1, stage0, w, wk0, kf, vf, dk, dv,
+                                 sl2);
+      }
+    } else {
+      if (nt > 1) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t0 + 1, stage1, w);
+      if (nt > 2) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t0 + 2, stage2, w);
+      wait_tile_and_barrier(nt > 2 ? kv_loads_per_tile<D>(w.wave) : 0);
+      for (int j = 0; j < nt; j += 4) {
+        kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, Nq, t0, j, nt, stage0, stage3, w, wk0, kf, vf, dk, dv, sl2);
+        if (j + 1 < nt)
+          kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, Nq, t0, j + 1, nt, stage1, stage0, w, wk0, kf, vf, dk, dv,
+                                 sl2);
+        if (j + 2 < nt)
+          kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, Nq, t0, j + 2, nt, stage2, stage1, w, wk0, kf, vf, dk, dv,
+                                 sl2);
+        if (j + 3 < nt)
+          kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, Nq, t0, j + 3, nt, stage3, stage2, w, wk0, kf, vf, dk, dv,
+                                 sl2);
+      }
     }
   }
   const auto rk = make_rsrc(dKg + (size_t)bh * Nk * D, Nk * ROWB);
   const auto rv = make_rsrc(dVg + (size_t)bh * Nk * D, Nk * ROWB);
-  store_rows16<DT, D>(dk, scale, rk, (32 * w.wave + w.l32) * ROWB, kb0 * ROWB, w.hf);
-  store_rows16<DT, D>(dv, 1.0f, rv, (32 * w.wave + w.l32) * ROWB, kb0 * ROWB, w.hf);
+  if constexpr (GRADS & 1) store_rows16<DT, D>(dk, scale, rk, (32 * w.wave + w.l32) * ROWB, kb0 * ROWB, w.hf);
+  if constexpr (GRADS & 2) store_rows16<DT, D>(dv, 1.0f, rv, (32 * w.wave + w.l32) * ROWB, kb0 * ROWB, w.hf);
 }
 
 template <int DT, int D, bool CAUSAL>
@@ -497,8 +545,9 @@ int launch_bwd(const FaBwdLaunch& a, float sl2, float scale) {
                        delta, rows);
   }
   if (rows > 0) {
-    const int nqt = (int)((a.Nq + 32 * kWavesQ - 1) / (32 * kWavesQ));
-    const dim3 grid((unsigned)(a.BH * nqt)), block(64 * kWavesQ);
+    constexpr int NWQ = dq_waves<D>();
+    const int nqt = (int)((a.Nq + 32 * NWQ - 1) / (32 * NWQ));
+    const dim3 grid((unsigned)(a.BH * nqt)), block(64 * NWQ);
     hipLaunchKernelGGL((bwd_dq<DT, D, CAUSAL>), grid, block, 0, st, (const u16*)a.q, (const u16*)a.k,
                        (const u16*)a.v, (const u16*)a.dout, (const float*)lse2, (const float*)delta, (u16*)a.dq,
                        (int)a.BH, (int)a.Nq, (int)a.Nk, nqt, sl2, scale);
@@ -506,9 +555,17 @@ int launch_bwd(const FaBwdLaunch& a, float sl2, float scale) {
   {
     const int nkt = (int)((a.Nk + 32 * kWavesKV - 1) / (32 * kWavesKV));
     const dim3 grid((unsigned)(a.BH * nkt)), block(64 * kWavesKV);
-    hipLaunchKernelGGL((bwd_dkdv<DT, D, CAUSAL>), grid, block, 0, st, (const u16*)a.q, (const u16*)a.k,
-                       (const u16*)a.v, (const u16*)a.dout, (const float*)lse2, (const float*)delta, (u16*)a.dk,
-                       (u16*)a.dv, (int)a.BH, (int)a.Nq, (int)a.Nk, sl2, scale);
+    auto run = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, block, 0, st, (const u16*)a.q, (const u16*)a.k, (const u16*)a.v,
+                         (const u16*)a.dout, (const float*)lse2, (const float*)delta, (u16*)a.dk, (u16*)a.dv,
+                         (int)a.BH, (int)a.Nq, (int)a.Nk, sl2, scale);
+    };
+    if constexpr (D == 256) {  // one kernel per gradient: dV, then dK
+      run(bwd_dkdv<DT, D, CAUSAL, 2>);
+      run(bwd_dkdv<DT, D, CAUSAL, 1>);
+    } else {
+      run(bwd_dkdv<DT, D, CAUSAL, 3>);
+    }
   }
   return (int)hipGetLastError();
 }
@@ -535,6 +592,8 @@ int fa_launch_bwd(const FaBwdLaunch& a) {
   const float scale = (float)a.scale;
   (void)hipGetLastError();  // clear a stale error so that the check below is ours
   if (a.D < 128) return fa_launch_bwd_small_d(a, sl2, scale);
+  if (a.D == 256)
+    return a.dtype == kBF16 ? dispatch_bwd<kBF16, 256>(a, sl2, scale) : dispatch_bwd<kFP16, 256>(a, sl2, scale);
   return a.dtype == kBF16 ? dispatch_bwd<kBF16, 128>(a, sl2, scale) : dispatch_bwd<kFP16, 128>(a, sl2, scale);
 }
 

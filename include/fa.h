@@ -53,8 +53,7 @@ typedef enum {
                           ((N + 256) * D * element size must stay below 2^31 for
                           N = Nq and N = Nk: one head is addressed with 32-bit
                           offsets) */
-  FA_ERR_HEAD_DIM = 3, /* D not in {32, 64, 128, 256}; D = 256 with FA_DTYPE_FP32;
-                          D = 256 in fa_bwd */
+  FA_ERR_HEAD_DIM = 3, /* D not in {32, 64, 128, 256}; D = 256 with FA_DTYPE_FP32 */
   FA_ERR_DTYPE = 4,    /* unknown dtype code */
   FA_ERR_ALIGN = 5,    /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
   FA_ERR_ALIAS = 6,    /* o or lse overlaps an input, or o overlaps lse */
@@ -207,6 +206,7 @@ int64_t fa_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq);
  *   softmax_scale  the forward's scale (1/sqrt(D) for fa_fwd); finite, > 0
  *   causal, dtype, stream   as fa_fwd; dtype must be FA_DTYPE_FP16 or
  *             FA_DTYPE_BF16 (FA_ERR_DTYPE otherwise)
+ *   B, H, Nq, Nk, D   sizes as fa_fwd; D in {32, 64, 128, 256}
  *
  * Accumulation is fp32; dq, dk, dv are rounded to `dtype` (nearest even).
  * B*H == 0, or Nq == Nk == 0, is a no-op; Nq == 0 < Nk writes dK = dV = 0;

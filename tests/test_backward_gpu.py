@@ -58,7 +58,7 @@ def _compare(w, cpu, dout, grads, scale=None, tag=""):
 
 GRID = [(dt, D, causal, Nq, Nk)
         for dt in ("bf16", "fp16")
-        for D in (32, 64, 128)
+        for D in (32, 64, 128, 256)
         for causal in (False, True)
         for (Nq, Nk) in ((300, 300), (257, 517), (130, 70))]
 
@@ -73,7 +73,7 @@ def test_backward_parity_grid(dt, D, causal, Nq, Nk):
 
 
 @pytest.mark.parametrize("dt,D,causal,scale", [("bf16", 128, True, 0.05), ("fp16", 64, False, 0.4),
-                                               ("bf16", 32, True, 1.0)])
+                                               ("bf16", 32, True, 1.0), ("fp16", 256, True, 0.3)])
 def test_backward_explicit_scale(dt, D, causal, scale):
     w = workloads.Workload(f"bwd_scaled_{dt}_d{D}", 1, 2, 200, 333, D, dt, causal, 71 + D)
     log(f"case {w.name} scale={scale}")
@@ -120,7 +120,8 @@ def test_backward_deterministic():
         assert torch.equal(a, b), "run-to-run backward results differ"
 
 
-@pytest.mark.parametrize("name", ["c3_bf16_causal_b4h16n4096d128", "c5_fp16_cross_b8h32q512k8192d64"])
+@pytest.mark.parametrize("name", ["c3_bf16_causal_b4h16n4096d128", "c5_fp16_cross_b8h32q512k8192d64",
+                                  "x1_bf16_causal_b4h8n4096d256"])
 def test_backward_full_size_sampled_heads(name):
     # the measured shapes, checked on whole (b, h) heads the oracle can afford
     w = workloads.WORKLOADS[name]
