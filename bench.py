@@ -70,6 +70,8 @@ def kernel_tag(w, op: str = "fwd") -> str:
         return f"fa_fwd_varlen_{w.dtype}_d{w.D}_{'causal' if w.causal else 'noncausal'}"
     if op == "decode":
         return f"fa_fwd_splitkv_{w.dtype}_d{w.D}"
+    if op == "bwd" and w.dtype == "fp32":
+        return f"fa_bwd_32_d{w.D}_{'causal' if w.causal else 'noncausal'}"
     if op == "bwd":
         return f"fa_bwd_16_{w.dtype}_d{w.D}_{'causal' if w.causal else 'noncausal'}"
     if w.dtype == "fp32":
@@ -83,6 +85,15 @@ CSRC = os.path.join(ROOT, "exact_tiled_attention_15_amd", "csrc")
 _BUILD = os.path.join(os.path.dirname(CSRC), "build.py")
 KERNEL_SOURCES = (os.path.join(CSRC, "fa_device.h"), os.path.join(CSRC, "fa_kernels.hip"), _BUILD)
 KERNEL_SOURCES_BWD = (os.path.join(CSRC, "fa_device.h"), os.path.join(CSRC, "fa_bwd.hip"), _BUILD)
+KERNEL_SOURCES_BWD32 = (os.path.join(CSRC, "fa_device.h"), os.path.join(CSRC, "fa_bwd32.hip"), _BUILD)
+
+
+def kernel_sources(w: workloads.Workload, op: str = "fwd"):
+    """The source files whose code an op's kernels on this workload run
+    (decode and varlen run the forward file's kernels)."""
+    if op == "bwd":
+        return KERNEL_SOURCES_BWD32 if w.dtype == "fp32" else KERNEL_SOURCES_BWD
+    return KERNEL_SOURCES
 
 
 def kernel_code_sha256(paths=KERNEL_SOURCES) -> str:
@@ -113,7 +124,7 @@ def measured_traffic(w: workloads.Workload, op: str = "fwd"):
         if ":" in line and line.split(":")[0] in ("kernel_code_sha256", "traffic_bytes_per_launch"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    code = kernel_code_sha256(KERNEL_SOURCES_BWD if op == "bwd" else KERNEL_SOURCES)  # decode: forward file
+    code = kernel_code_sha256(kernel_sources(w, op))
     if fields.get("kernel_code_sha256") != code or "traffic_bytes_per_launch" not in fields:
         return None
     return int(fields["traffic_bytes_per_launch"])
@@ -433,8 +444,6 @@ def main():
         return
     names = ([n for n in workloads.WORKLOADS if n[:2] in ("c1", "c2", "c3", "c4", "c5") and "t_" not in n[:4]]
              if a.all else [a.workload])
-    if a.op == "bwd":  # the backward kernels take 16-bit inputs
-        names = [n for n in names if workloads.WORKLOADS[n].dtype != "fp32"]
     if a.op == "decode":
         names = ([n for n in workloads.WORKLOADS if n.startswith("d")] if a.all or a.workload == workloads.HEADLINE
                  else [a.workload])

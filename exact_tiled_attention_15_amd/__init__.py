@@ -184,7 +184,8 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, softmax_scale=None, dq
     """Exact attention backward on the GPU.
 
     q, k, v, causal and softmax_scale as given to ``forward``; o and lse as it
-    returned them; dout: the gradient of o (like q).  16-bit dtypes only.
+    returned them; dout: the gradient of o (like q).  float32 (D <= 128),
+    float16 or bfloat16.
     Returns (dq, dk, dv) in the input dtype.  Output tensors and the
     workspace (a uint8 device tensor of at least ``fa_bwd_workspace_size``
     bytes) may be given preallocated.

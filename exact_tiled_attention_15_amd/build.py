@@ -37,6 +37,7 @@ UNITS = [
     ("fwd_d256", os.path.join(CSRC, "fa_kernels.hip"), ["-DFA_FWD_D256", *VGPR_MFMA]),
     ("bwd", os.path.join(CSRC, "fa_bwd.hip"), []),
     ("bwd_small_d", os.path.join(CSRC, "fa_bwd.hip"), ["-DFA_BWD_SMALL_D", *VGPR_MFMA]),
+    ("bwd32", os.path.join(CSRC, "fa_bwd32.hip"), []),
     ("api", os.path.join(CSRC, "fa_api.cpp"), []),
 ]
 

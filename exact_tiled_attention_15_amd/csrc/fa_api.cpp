@@ -255,9 +255,10 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
                       const void* dout, void* dq, void* dk, void* dv, void* workspace,
                       int64_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
                       double softmax_scale, int causal, int dtype, void* stream) {
-  if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;  // 16-bit inputs only
+  if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || D < 0) return FA_ERR_SHAPE;
   if (D != 32 && D != 64 && D != 128 && D != 256) return FA_ERR_HEAD_DIM;
+  if (D == 256 && dtype == FA_DTYPE_FP32) return FA_ERR_HEAD_DIM;
   if (!scale_ok(softmax_scale)) return FA_ERR_SCALE;
   int64_t BH, qel, kel;
   if (!mul_ok(B, H, &BH) || !mul_ok(BH, Nq, &qel) || !mul_ok(qel, D, &qel) || !mul_ok(BH, Nk, &kel) ||
@@ -267,12 +268,13 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   if (Nk == 0) return FA_ERR_SHAPE;  // query rows with no key have no softmax
   // Nq == 0 < Nk is valid: dK = dV = 0.
   if (Nq > INT32_MAX / 2 || Nk > INT32_MAX / 2 || BH > INT32_MAX) return FA_ERR_SHAPE;
-  const int64_t esz = 2;
+  const int64_t esz = dtype == FA_DTYPE_FP32 ? 4 : 2;
   if ((Nq + 256) * D * esz > INT32_MAX || (Nk + 256) * D * esz > INT32_MAX) return FA_ERR_SHAPE;
   int64_t gq, gk;
-  // dQ workgroups take 256 query rows (128 at D = 256), dK/dV ones 128 keys
+  // dQ workgroups take 256 query rows (128 at D = 256 and for fp32), dK/dV
+  // ones 128 keys; the statistics kernel takes D/8 (fp32: D/4) lanes a row
   if (!mul_ok(BH, (Nq + 127) / 128, &gq) || gq > INT32_MAX || !mul_ok(BH, (Nk + 127) / 128, &gk) ||
-      gk > INT32_MAX || BH * Nq * (D / 8) / 256 >= INT32_MAX)
+      gk > INT32_MAX || BH * Nq * (D / 4) / 256 >= INT32_MAX)
     return FA_ERR_SHAPE;
   const int64_t ws_need = fa_bwd_workspace_size(B, H, Nq);
   if (ws_need < 0) return FA_ERR_SHAPE;

@@ -591,6 +591,7 @@ int fa_launch_bwd(const FaBwdLaunch& a) {
   const float sl2 = (float)(a.scale * 1.4426950408889634074);
   const float scale = (float)a.scale;
   (void)hipGetLastError();  // clear a stale error so that the check below is ours
+  if (a.dtype != kBF16 && a.dtype != kFP16) return fa_launch_bwd32(a, sl2, scale);
   if (a.D < 128) return fa_launch_bwd_small_d(a, sl2, scale);
   if (a.D == 256)
     return a.dtype == kBF16 ? dispatch_bwd<kBF16, 256>(a, sl2, scale) : dispatch_bwd<kFP16, 256>(a, sl2, scale);

@@ -1,0 +1,359 @@
+// Exact attention backward for gfx950, fp32 inputs, D in {32, 64, 128}.
+//
+// The same recomputation as the 16-bit backward ("Building a FlashAttention-2
+// Forward Kernel in Pure NumPy", Extending It): the forward's LSE is kept,
+// every probability is recomputed as P = exp(s - LSE), and with
+// delta_i = sum_d dO[i,d] O[i,d]
+//
+//   dP = dO V^T,  dS = P * (dP - delta),  dV = P^T dO,
+//   dQ = scale dS K,  dK = scale dS^T Q,
+//
+// here with P and dS kept in fp32 (no rounding between the products) and
+// v_mfma_f32_32x32x2_f32, the operand layout of the fp32 forward kernel:
+// tiles are staged through registers into a double-buffered LDS stage with
+// rows padded to D+4 floats, and a lane holds half of a row fragment (the
+// MFMA step c pairs column c of the low half-wave with column D/2 + c of
+// the high one).  Three kernels, no atomics, deterministic:
+//  * bwd32_prep: delta and LSE * log2(e) per query row (the workspace);
+//  * bwd32_dq: 4 waves x 32 query rows; K/V tiles of 64 keys (32 at D = 128);
+//    per tile S^T = K Q^T and dP^T = V dO^T with the wave's Q and dO rows in
+//    registers, P and dS, then dQ^T += K^T dS^T;
+//  * bwd32_dkdv: 4 waves x 32 keys; Q/dO tiles of 64 rows (32 at D = 128)
+//    with their LSE and delta; per tile S = Q K^T and dP = dO V^T with the
+//    wave's K and V rows in registers (keys along the MFMA N dimension), then
+//    dV^T += dO^T P and dK^T += Q^T dS.
+// The products are recomputed in both big kernels (seven tile products).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr float kLog2e32 = 1.4426950408889634074f;
+constexpr int kThreads32 = 256;  // 4 waves
+
+__device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// delta = sum_d dO[d] O[d] and lse2 = LSE log2(e) per query row; D/4 lanes
+// per row, 16 bytes each.
+template <int D>
+__global__ __launch_bounds__(256) void bwd32_prep(const float* __restrict__ O, const float* __restrict__ dO,
+                                                  const float* __restrict__ lse, float* __restrict__ lse2,
+                                                  float* __restrict__ delta, int64_t rows) {
+  constexpr int LPR = D / 4;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = t / LPR;
+  const int c = (int)(t % LPR);
+  float acc = 0.f;
+  if (row < rows) {
+    const f32x4 a = *(const f32x4*)(O + row * D + 4 * c);
+    const f32x4 b = *(const f32x4*)(dO + row * D + 4 * c);
+    acc = a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < rows && c == 0) {
+    delta[row] = acc;
+    lse2[row] = lse[row] * kLog2e32;
+  }
+}
+
+// Half row fragment of row `row` of a [rows, D] tensor: lane half hf holds
+// columns [D/2 hf, D/2 hf + D/2); rows past `rows` read as zero.
+template <int D>
+__device__ __forceinline__ void load_half_row(f32x4 (&f)[D / 8], const float* base, int rows, int row, int hf) {
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c)
+    f[c] = row < rows ? *(const f32x4*)(base + (size_t)row * D + (D / 2) * hf + 4 * c) : f32x4{0, 0, 0, 0};
+}
+
+// 32x32 product over the head dimension: rows 32 n + l32 of the LDS tile
+// `rows_lds` (A operand) against the lane's half row fragment (B operand).
+template <int D, int STR>
+__device__ __forceinline__ f32x16 rows_times_frag(const float* rows_lds, int n, int l32, int hf,
+                                                  const f32x4 (&f)[D / 8]) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const f32x4 a = *(const f32x4*)(rows_lds + (32 * n + l32) * STR + (D / 2) * hf + 4 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = mfma32(a[e], f[c][e], acc);
+  }
+  return acc;
+}
+
+// acc[dt] += T^T X over the 32 rows of block n of the LDS tile `t_lds`, where
+// the lane holds X for row 32 n + 8 (r/4) + 4 hf + r%4 in x[r] (the layout of
+// an S-like accumulator); MFMA step r pairs those rows across the half-waves.
+template <int D, int STR>
+__device__ __forceinline__ void acc_transposed(f32x16 (&acc)[D / 32], const float* t_lds, int n, int l32, int hf,
+                                               const f32x16& x) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 32 * n + 8 * (r >> 2) + 4 * hf + (r & 3);
+      acc[dt] = mfma32(t_lds[row * STR + 32 * dt + l32], x[r], acc[dt]);
+    }
+}
+
+// Store the transposed accumulators of row `row` (lane l32 of the wave's 32:
+// columns 32 dt + 8 g + 4 hf + e), multiplied by `mul`.
+template <int D>
+__device__ __forceinline__ void store_row32(const f32x16 (&acc)[D / 32], float mul, float* out, int hf) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *(f32x4*)(out + 32 * dt + 8 * g + 4 * hf) = f32x4{acc[dt][4 * g] * mul, acc[dt][4 * g + 1] * mul,
+                                                         acc[dt][4 * g + 2] * mul, acc[dt][4 * g + 3] * mul};
+}
+
+// ---------------------------------------------------------------------------
+// dQ: 4 waves x 32 query rows per workgroup.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads32, 1) void bwd32_dq(const float* __restrict__ Qg, const float* __restrict__ Kg,
+                                                          const float* __restrict__ Vg, const float* __restrict__ dOg,
+                                                          const float* __restrict__ lse2g,
+                                                          const float* __restrict__ deltag, float* __restrict__ dQg,
+                                                          int BH, int Nq, int Nk, int nqt, float sl2, float scale) {
+  constexpr int BR = 128, BC = D <= 64 ? 64 : 32, NSUB = BC / 32, STR = D + 4, ST = BC * STR, NDT = D / 32;
+  constexpr int CPT = BC * D / 4 / kThreads32;  // 16-byte chunks per thread per tensor
+  static_assert(CPT >= 1, "tile shape");
+  __shared__ __attribute__((aligned(16))) float smem[2 * 2 * ST];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hf = lane >> 5, l32 = lane & 31;
+  int bh, qt;
+  tile_of_block(nqt, BH, bh, qt);
+  const int q0 = qt * BR;
+  const float* K = Kg + (size_t)bh * Nk * D;
+  const float* V = Vg + (size_t)bh * Nk * D;
+  const int kend = CAUSAL ? min(Nk, min(q0 + BR, Nq)) : Nk;
+  const int nt = (kend + BC - 1) / BC;
+  const int wq0 = q0 + 32 * wave;
+  const int myq = wq0 + l32;
+  const int wkend = CAUSAL ? min(kend, wq0 + 32) : kend;
+
+  f32x4 qf[D / 8], df[D / 8];
+  load_half_row<D>(qf, Qg + (size_t)bh * Nq * D, Nq, myq, hf);
+  load_half_row<D>(df, dOg + (size_t)bh * Nq * D, Nq, myq, hf);
+  // rows past Nq: zero Q, dO and statistics, so dS = 0 (and they are not stored)
+  const float lse2 = myq < Nq ? lse2g[(size_t)bh * Nq + myq] : 0.f;
+  const float delta = myq < Nq ? deltag[(size_t)bh * Nq + myq] : 0.f;
+
+  f32x4 kr[CPT], vr[CPT];
+  auto load_tile = [&](int j) {
+    const int k0 = j * BC;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + kThreads32 * i;
+      const int key = c / (D / 4), col = (c % (D / 4)) * 4;
+      const bool ok = k0 + key < Nk;
+      kr[i] = ok ? *(const f32x4*)(K + (size_t)(k0 + key) * D + col) : f32x4{0, 0, 0, 0};
+      vr[i] = ok ? *(const f32x4*)(V + (size_t)(k0 + key) * D + col) : f32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_tile = [&](int stage) {
+    float* ks = smem + stage * 2 * ST;
+    float* vs = ks + ST;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + kThreads32 * i;
+      const int key = c / (D / 4), col = (c % (D / 4)) * 4;
+      *(f32x4*)(ks + key * STR + col) = kr[i];
+      *(f32x4*)(vs + key * STR + col) = vr[i];
+    }
+  };
+
+  f32x16 acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
+
+  if (nt > 0) load_tile(0);
+  for (int j = 0; j < nt; ++j) {
+    // stage j&1 was last read in step j-2, which every wave finished before
+    // step j-1's barrier
+    const int stage = j & 1;
+    store_tile(stage);
+    __syncthreads();
+    if (j + 1 < nt) load_tile(j + 1);
+    const int k0 = j * BC;
+    if (k0 >= wkend) continue;
+    const float* ks = smem + stage * 2 * ST;
+    const float* vs = ks + ST;
+    const bool need_mask = k0 + BC > Nk || (CAUSAL && k0 + BC - 1 > wq0);
+#pragma unroll
+    for (int n = 0; n < NSUB; ++n) {
+      // lane: query myq, keys k0 + 32 n + 8 (r/4) + 4 hf + r%4
+      const f32x16 s = rows_times_frag<D, STR>(ks, n, l32, hf, qf);
+      const f32x16 dp = rows_times_frag<D, STR>(vs, n, l32, hf, df);
+      f32x16 ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -lse2));
+        if (need_mask) {
+          const int key = k0 + 32 * n + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (key >= Nk || (CAUSAL && key > myq)) p = 0.f;
+        }
+        ds[r] = p * (dp[r] - delta);
+      }
+      acc_transposed<D, STR>(acc, ks, n, l32, hf, ds);  // dQ^T += K^T dS^T
+    }
+  }
+  if (myq < Nq) store_row32<D>(acc, scale, dQg + ((size_t)bh * Nq + myq) * D, hf);
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV: 4 waves x 32 keys per workgroup.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads32, 1) void bwd32_dkdv(const float* __restrict__ Qg, const float* __restrict__ Kg,
+                                                            const float* __restrict__ Vg,
+                                                            const float* __restrict__ dOg,
+                                                            const float* __restrict__ lse2g,
+                                                            const float* __restrict__ deltag, float* __restrict__ dKg,
+                                                            float* __restrict__ dVg, int BH, int Nq, int Nk,
+                                                            float sl2, float scale) {
+  constexpr int BK = 128, BQ = D <= 64 ? 64 : 32, NSUB = BQ / 32, STR = D + 4, ST = BQ * STR, NDT = D / 32;
+  constexpr int SS = 2 * ST + 2 * BQ;  // floats per stage: Q tile, dO tile, lse2, delta
+  constexpr int CPT = BQ * D / 4 / kThreads32;
+  static_assert(CPT >= 1, "tile shape");
+  __shared__ __attribute__((aligned(16))) float smem[2 * SS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hf = lane >> 5, l32 = lane & 31;
+  // Key blocks in ascending order: under the causal mask the first keys are
+  // seen by the most queries, so the heaviest workgroups start first.
+  const int bh = blockIdx.x % BH, kt = blockIdx.x / BH;
+  const int kb0 = kt * BK;
+  const int wk0 = kb0 + 32 * wave;
+  const int mykey = wk0 + l32;
+  const float* Q = Qg + (size_t)bh * Nq * D;
+  const float* dO = dOg + (size_t)bh * Nq * D;
+  const float* l2h = lse2g + (size_t)bh * Nq;
+  const float* dlh = deltag + (size_t)bh * Nq;
+  const int t0 = CAUSAL ? kb0 / BQ : 0;  // first query tile that sees a key of the block
+  const int nt = max((Nq + BQ - 1) / BQ - t0, 0);
+
+  f32x4 kf[D / 8], vf[D / 8];
+  load_half_row<D>(kf, Kg + (size_t)bh * Nk * D, Nk, mykey, hf);
+  load_half_row<D>(vf, Vg + (size_t)bh * Nk * D, Nk, mykey, hf);
+
+  // Query rows past Nq are staged as zero Q, dO and statistics: their P is
+  // exp2(0) = 1 but dO = 0 and dS = P (0 - 0) = 0, so they add nothing.
+  f32x4 qr[CPT], dr[CPT];
+  float sr = 0.f;
+  auto load_tile = [&](int t) {
+    const int qb = t * BQ;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + kThreads32 * i;
+      const int row = c / (D / 4), col = (c % (D / 4)) * 4;
+      const bool ok = qb + row < Nq;
+      qr[i] = ok ? *(const f32x4*)(Q + (size_t)(qb + row) * D + col) : f32x4{0, 0, 0, 0};
+      dr[i] = ok ? *(const f32x4*)(dO + (size_t)(qb + row) * D + col) : f32x4{0, 0, 0, 0};
+    }
+    if (tid < 2 * BQ) {
+      const int row = tid % BQ;
+      const float* src = tid < BQ ? l2h : dlh;
+      sr = qb + row < Nq ? src[qb + row] : 0.f;
+    }
+  };
+  auto store_tile = [&](int stage) {
+    float* qs = smem + stage * SS;
+    float* ds = qs + ST;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + kThreads32 * i;
+      const int row = c / (D / 4), col = (c % (D / 4)) * 4;
+      *(f32x4*)(qs + row * STR + col) = qr[i];
+      *(f32x4*)(ds + row * STR + col) = dr[i];
+    }
+    if (tid < 2 * BQ) qs[2 * ST + tid] = sr;  // lse2 then delta
+  };
+
+  f32x16 dk[NDT], dv[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) dk[dt] = dv[dt] = f32x16{};
+
+  if (nt > 0) load_tile(t0);
+  for (int j = 0; j < nt; ++j) {
+    const int stage = j & 1;
+    store_tile(stage);
+    __syncthreads();
+    if (j + 1 < nt) load_tile(t0 + j + 1);
+    const int q0 = (t0 + j) * BQ;
+    if (CAUSAL && q0 + BQ - 1 < wk0) continue;  // every query of the tile precedes the wave's keys
+    const float* qs = smem + stage * SS;
+    const float* dos = qs + ST;
+    const float* l2s = qs + 2 * ST;
+    const float* dls = l2s + BQ;
+    const bool need_mask = CAUSAL && q0 < wk0 + 31;
+#pragma unroll
+    for (int n = 0; n < NSUB; ++n) {
+      // lane: key mykey, queries q0 + 32 n + 8 (r/4) + 4 hf + r%4
+      const f32x16 s = rows_times_frag<D, STR>(qs, n, l32, hf, kf);
+      const f32x16 dp = rows_times_frag<D, STR>(dos, n, l32, hf, vf);
+      f32x16 p, ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * n + 8 * (r >> 2) + 4 * hf + (r & 3);
+        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l2s[row]));
+        if (need_mask && q0 + row < mykey) pr = 0.f;
+        p[r] = pr;
+        ds[r] = pr * (dp[r] - dls[row]);
+      }
+      acc_transposed<D, STR>(dv, dos, n, l32, hf, p);  // dV^T += dO^T P
+      acc_transposed<D, STR>(dk, qs, n, l32, hf, ds);  // dK^T += Q^T dS
+    }
+  }
+  if (mykey < Nk) {
+    store_row32<D>(dk, scale, dKg + ((size_t)bh * Nk + mykey) * D, hf);
+    store_row32<D>(dv, 1.0f, dVg + ((size_t)bh * Nk + mykey) * D, hf);
+  }
+}
+
+template <int D, bool CAUSAL>
+int launch_bwd32(const FaBwdLaunch& a, float sl2, float scale) {
+  const hipStream_t st = (hipStream_t)a.stream;
+  const int64_t rows = a.BH * a.Nq;
+  float* lse2 = (float*)a.workspace;
+  float* delta = lse2 + rows;
+  if (rows > 0) {
+    const int64_t threads = rows * (D / 4);
+    hipLaunchKernelGGL((bwd32_prep<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                       (const float*)a.o, (const float*)a.dout, a.lse, lse2, delta, rows);
+    const int nqt = (int)((a.Nq + 127) / 128);
+    hipLaunchKernelGGL((bwd32_dq<D, CAUSAL>), dim3((unsigned)(a.BH * nqt)), dim3(kThreads32), 0, st,
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout,
+                       (const float*)lse2, (const float*)delta, (float*)a.dq, (int)a.BH, (int)a.Nq, (int)a.Nk, nqt,
+                       sl2, scale);
+  }
+  const int nkt = (int)((a.Nk + 127) / 128);
+  hipLaunchKernelGGL((bwd32_dkdv<D, CAUSAL>), dim3((unsigned)(a.BH * nkt)), dim3(kThreads32), 0, st,
+                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout,
+                     (const float*)lse2, (const float*)delta, (float*)a.dk, (float*)a.dv, (int)a.BH, (int)a.Nq,
+                     (int)a.Nk, sl2, scale);
+  return (int)hipGetLastError();
+}
+
+template <int D>
+int dispatch_bwd32(const FaBwdLaunch& a, float sl2, float scale) {
+  return a.causal ? launch_bwd32<D, true>(a, sl2, scale) : launch_bwd32<D, false>(a, sl2, scale);
+}
+
+}  // namespace
+
+int fa_launch_bwd32(const FaBwdLaunch& a, float sl2, float scale) {
+  switch (a.D) {
+    case 32: return dispatch_bwd32<32>(a, sl2, scale);
+    case 64: return dispatch_bwd32<64>(a, sl2, scale);
+    default: return dispatch_bwd32<128>(a, sl2, scale);
+  }
+}

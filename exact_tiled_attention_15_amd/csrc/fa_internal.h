@@ -63,7 +63,7 @@ struct FaBwdLaunch {
   int64_t Nk;
   int D;
   int causal;
-  int dtype;  // FA_DTYPE_FP16 or FA_DTYPE_BF16
+  int dtype;  // fa_dtype
   double scale;
   void* stream;
 };
@@ -75,3 +75,7 @@ int fa_launch_bwd(const FaBwdLaunch& a);
 // The D = 32 and D = 64 backward launcher (a unit of its own; sl2 = scale *
 // log2(e)), called by fa_launch_bwd.
 int fa_launch_bwd_small_d(const FaBwdLaunch& a, float sl2, float scale);
+
+// The fp32 backward launcher (D in {32, 64, 128}; its own unit), called by
+// fa_launch_bwd.
+int fa_launch_bwd32(const FaBwdLaunch& a, float sl2, float scale);

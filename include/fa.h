@@ -204,11 +204,13 @@ int64_t fa_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq);
  *             bytes, 16-byte aligned, owned by the caller; its contents on
  *             entry do not matter and are scratch after the call
  *   softmax_scale  the forward's scale (1/sqrt(D) for fa_fwd); finite, > 0
- *   causal, dtype, stream   as fa_fwd; dtype must be FA_DTYPE_FP16 or
- *             FA_DTYPE_BF16 (FA_ERR_DTYPE otherwise)
- *   B, H, Nq, Nk, D   sizes as fa_fwd; D in {32, 64, 128, 256}
+ *   causal, dtype, stream   as fa_fwd
+ *   B, H, Nq, Nk, D   sizes as fa_fwd; D in {32, 64, 128, 256} (256: fp16
+ *             and bf16 only)
  *
- * Accumulation is fp32; dq, dk, dv are rounded to `dtype` (nearest even).
+ * Accumulation is fp32.  16-bit dtypes: P and dS enter the products rounded
+ * to `dtype`, and dq, dk, dv are rounded to it (nearest even); fp32: no
+ * rounding between the products.
  * B*H == 0, or Nq == Nk == 0, is a no-op; Nq == 0 < Nk writes dK = dV = 0;
  * Nk == 0 < Nq is FA_ERR_SHAPE.  Keys that no query sees (causal, Nk > Nq)
  * get dK = dV = 0.  Pointers must be non-NULL and 16-byte aligned (lse

@@ -128,7 +128,7 @@ def test_bwd_workspace_size():
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=0), 4), (dict(dtype=7), 4), (dict(D=16), 3), (dict(D=512), 3),
+    (dict(dtype=7), 4), (dict(dtype=-1), 4), (dict(D=16), 3), (dict(D=512), 3), (dict(D=256, dtype=0), 3),
     (dict(scale=0.0), 8), (dict(scale=float("nan")), 8), (dict(scale=-1.0), 8),
     (dict(Nk=0), 2), (dict(B=-1), 2), (dict(Nq=1 << 40), 2),
     (dict(q=0), 1), (dict(o=0), 1), (dict(lse=0), 1), (dict(dout=0), 1), (dict(dq=0), 1), (dict(dk=0), 1),

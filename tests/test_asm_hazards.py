@@ -43,11 +43,24 @@ def _asm(unit, out):
     return open(out).read()
 
 
+REG = re.compile(r"\b([va])\[(\d+):(\d+)\]|\b([va])(\d+)\b")
+
+
+def _regs(text):
+    """(register file, first, last) of each v/a register operand in `text`."""
+    out = []
+    for m in REG.finditer(text):
+        if m.group(1):
+            out.append((m.group(1), int(m.group(2)), int(m.group(3))))
+        else:
+            out.append((m.group(4), int(m.group(5)), int(m.group(5))))
+    return out
+
+
 def _data_regs(line):
-    """VGPR range of a wide store's data operand."""
-    ops = re.findall(r"v\[(\d+):(\d+)\]|v(\d+)", line.split(None, 1)[1])
-    d = ops[0] if line.startswith("buffer") else ops[1]
-    return (int(d[0]), int(d[1])) if d[0] else (int(d[2]), int(d[2]))
+    """Register range of a wide store's data operand (VGPRs or AGPRs)."""
+    ops = _regs(line.split(None, 1)[1])
+    return ops[0] if line.startswith("buffer") else ops[1]
 
 
 def hazards(asm_text):
@@ -56,13 +69,14 @@ def hazards(asm_text):
     for i, s in enumerate(lines):
         if not WIDE_STORE.match(s):
             continue
-        lo, hi = _data_regs(s)
+        f, lo, hi = _data_regs(s)
         for n in lines[i + 1:i + 4]:
             if not n or n.startswith(";"):
                 continue
-            m = re.match(r"v_\w+\s+v(\d+)\b", n)
-            if m and lo <= int(m.group(1)) <= hi:
-                found.append((s, n))
+            if n.startswith("v_"):  # a vector instruction: its first operand is the destination
+                dst = _regs(n.split(None, 1)[1].split(",", 1)[0]) if " " in n else []
+                if dst and dst[0][0] == f and dst[0][1] <= hi and lo <= dst[0][2]:
+                    found.append((s, n))
             break
     return found
 
@@ -72,7 +86,11 @@ def test_scanner_catches_the_pattern():
     ok = "\tbuffer_store_dwordx4 v[2:5], v20, s[0:3], s4 offen\n\ts_nop 0\n\tv_mul_f32_e32 v2, v19, v6\n"
     ok2 = "\tbuffer_store_dwordx2 v[2:3], v20, s[0:3], s4 offen\n\tv_mul_f32_e32 v2, v19, v6\n"
     g = "\tglobal_store_dwordx4 v[8:9], v[2:5], off\n\tv_add_f32_e32 v3, v1, v1\n"
+    ga = "\tglobal_store_dwordx4 v[0:1], a[8:11], off offset:64\n\tv_accvgpr_write_b32 a9, v4\n"
+    ga_ok = "\tglobal_store_dwordx4 v[0:1], a[8:11], off offset:64\n\tv_add_f32_e32 v9, v1, v1\n"
+    wide = "\tbuffer_store_dwordx4 v[2:5], v20, s[0:3], s4 offen\n\tv_mov_b64_e32 v[4:5], v[8:9]\n"
     assert len(hazards(bad)) == 1 and not hazards(ok) and not hazards(ok2) and len(hazards(g)) == 1
+    assert len(hazards(ga)) == 1 and not hazards(ga_ok) and len(hazards(wide)) == 1
 
 
 @pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")

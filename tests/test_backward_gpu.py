@@ -2,14 +2,18 @@
 float64 backward oracle on the same seeded inputs.  The GPU backward takes
 the GPU forward's O and LSE, as a training step would.
 
-Tolerance: the gradients have no fixed scale (dV entries shrink like 1/N
+Tolerance (16-bit inputs): the gradients have no fixed scale (dV entries shrink like 1/N
 for spread-out softmax rows), so the error of each gradient tensor is taken
 relative to its largest magnitude: max|G_gpu - G| <= 2e-2 * max|G|, the
 forward's 16-bit bound on O (whose entries are O(1)) applied to the
 gradient's own scale, plus an absolute 1e-4 for gradients that vanish
 exactly (a row with a single key has dQ = dK = 0 up to rounding).  Its budget: P and dS enter the MFMAs rounded to 16
 bits (relative 2^-9 for bf16), delta comes from the 16-bit O, and the
-results are rounded to 16 bits."""
+results are rounded to 16 bits.  fp32 inputs: nothing is rounded below
+fp32 and every product accumulates in fp32 (relative error of order
+2^-24 sqrt(N) per dot product, ~1e-6 here), and the forward's O and LSE it
+starts from are within 1e-4 / 1e-5 of exact; 1e-4 of max|G| (plus 1e-6
+absolute) bounds the result with room."""
 import numpy as np
 import pytest
 
@@ -22,9 +26,13 @@ pytestmark = pytest.mark.gpu
 
 REL_TOL = 2e-2
 ABS_FLOOR = 1e-4
+REL_TOL_FP32 = 1e-4
+ABS_FLOOR_FP32 = 1e-6
 
 
-def _bound(m):
+def _bound(m, dtype="bf16"):
+    if dtype == "fp32":
+        return REL_TOL_FP32 * m + ABS_FLOOR_FP32
     return REL_TOL * m + ABS_FLOOR
 
 
@@ -52,13 +60,13 @@ def _compare(w, cpu, dout, grads, scale=None, tag=""):
         e = float(np.max(np.abs(g - r)))
         m = float(np.max(np.abs(r)))
         errs.append((name, e, m))
-        assert e <= _bound(m), f"{tag} {name}: max err {e:.3e} > {REL_TOL} * {m:.3e} + {ABS_FLOOR}"
+        assert e <= _bound(m, w.dtype), f"{tag} {name}: max err {e:.3e} > bound {_bound(m, w.dtype):.3e}"
     log(f"  {tag} {w.name}: " + " ".join(f"{n} err {e:.2e} max {m:.2e}" for n, e, m in errs))
 
 
 GRID = [(dt, D, causal, Nq, Nk)
-        for dt in ("bf16", "fp16")
-        for D in (32, 64, 128, 256)
+        for dt in ("bf16", "fp16", "fp32")
+        for D in (32, 64, 128, 256) if not (dt == "fp32" and D == 256)
         for causal in (False, True)
         for (Nq, Nk) in ((300, 300), (257, 517), (130, 70))]
 
@@ -73,7 +81,8 @@ def test_backward_parity_grid(dt, D, causal, Nq, Nk):
 
 
 @pytest.mark.parametrize("dt,D,causal,scale", [("bf16", 128, True, 0.05), ("fp16", 64, False, 0.4),
-                                               ("bf16", 32, True, 1.0), ("fp16", 256, True, 0.3)])
+                                               ("bf16", 32, True, 1.0), ("fp16", 256, True, 0.3),
+                                               ("fp32", 128, True, 0.2)])
 def test_backward_explicit_scale(dt, D, causal, scale):
     w = workloads.Workload(f"bwd_scaled_{dt}_d{D}", 1, 2, 200, 333, D, dt, causal, 71 + D)
     log(f"case {w.name} scale={scale}")
@@ -81,10 +90,14 @@ def test_backward_explicit_scale(dt, D, causal, scale):
     _compare(w, cpu, dout, grads, scale=scale, tag="scaled")
 
 
-@pytest.mark.parametrize("Nq,Nk,causal", [(1, 1, True), (1, 300, False), (5, 200, True), (200, 5, True),
-                                          (64, 64, False), (65, 129, True), (0, 70, False)])
-def test_backward_edge_shapes(Nq, Nk, causal):
-    w = workloads.Workload(f"bwd_edge_{Nq}x{Nk}", 1, 2, Nq, Nk, 64, "bf16", causal, Nq * 3 + Nk)
+EDGE = [("bf16", Nq, Nk, c) for (Nq, Nk, c) in ((1, 1, True), (1, 300, False), (5, 200, True), (200, 5, True),
+                                                 (64, 64, False), (65, 129, True), (0, 70, False))]
+EDGE += [("fp32", Nq, Nk, c) for (Nq, Nk, c) in ((1, 1, True), (5, 200, True), (200, 5, True), (0, 70, False))]
+
+
+@pytest.mark.parametrize("dt,Nq,Nk,causal", EDGE)
+def test_backward_edge_shapes(dt, Nq, Nk, causal):
+    w = workloads.Workload(f"bwd_edge_{dt}_{Nq}x{Nk}", 1, 2, Nq, Nk, 64, dt, causal, Nq * 3 + Nk)
     log(f"case {w.name} causal={causal}")
     if Nq == 0:
         import exact_tiled_attention_15_amd as fa
@@ -103,17 +116,28 @@ def test_backward_edge_shapes(Nq, Nk, causal):
     _compare(w, cpu, dout, grads, tag="edge")
 
 
-def test_backward_unseen_keys_are_zero():
+@pytest.mark.parametrize("name", ["c1_fp32_causal_b2h4n128d64", "c2_fp32_b1h8n1024d64"])
+def test_backward_fp32_workloads(name):
+    # the fp32 workloads at their full sizes, every element compared
+    w = workloads.WORKLOADS[name]
+    log(f"case {w.name} (backward)")
+    cpu, dout, grads = _run(w)
+    _compare(w, cpu, dout, grads, tag="fp32")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_backward_unseen_keys_are_zero(dt):
     # causal, Nk > Nq: keys past the last query get exactly zero gradients
-    w = workloads.Workload("bwd_unseen", 1, 2, 100, 400, 128, "bf16", True, 17)
+    w = workloads.Workload(f"bwd_unseen_{dt}", 1, 2, 100, 400, 128, dt, True, 17)
     cpu, dout, (dq, dk, dv) = _run(w)
     assert float(dk[:, :, 100:].abs().max()) == 0.0
     assert float(dv[:, :, 100:].abs().max()) == 0.0
     _compare(w, cpu, dout, (dq, dk, dv), tag="unseen")
 
 
-def test_backward_deterministic():
-    w = workloads.Workload("bwd_det", 1, 4, 700, 700, 128, "bf16", True, 23)
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_backward_deterministic(dt):
+    w = workloads.Workload(f"bwd_det_{dt}", 1, 4, 700, 700, 128, dt, True, 23)
     cpu, dout, g1 = _run(w)
     _, _, g2 = _run(w, cpu=cpu, dout=dout)
     for a, b in zip(g1, g2):
@@ -138,4 +162,4 @@ def test_backward_full_size_sampled_heads(name):
             e = float(np.max(np.abs(gg - r)))
             m = float(np.max(np.abs(r)))
             log(f"  head {bh} {name_}: err {e:.2e} / max {m:.2e}")
-            assert e <= _bound(m)
+            assert e <= _bound(m, w.dtype)
