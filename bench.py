@@ -80,12 +80,11 @@ def kernel_tag(w, op: str = "fwd") -> str:
 
 
 CSRC = os.path.join(ROOT, "exact_tiled_attention_15_amd", "csrc")
-# The code of a kernel: the shared device helpers, its source file, and the
-# build script that holds the compile flags of its unit.
-_BUILD = os.path.join(os.path.dirname(CSRC), "build.py")
-KERNEL_SOURCES = (os.path.join(CSRC, "fa_device.h"), os.path.join(CSRC, "fa_kernels.hip"), _BUILD)
-KERNEL_SOURCES_BWD = (os.path.join(CSRC, "fa_device.h"), os.path.join(CSRC, "fa_bwd.hip"), _BUILD)
-KERNEL_SOURCES_BWD32 = (os.path.join(CSRC, "fa_device.h"), os.path.join(CSRC, "fa_bwd32.hip"), _BUILD)
+# The code of a kernel: the shared device helpers and its source file, with
+# the compile flags of the build units that compile that file.
+KERNEL_SOURCES = (os.path.join(CSRC, "fa_device.h"), os.path.join(CSRC, "fa_kernels.hip"))
+KERNEL_SOURCES_BWD = (os.path.join(CSRC, "fa_device.h"), os.path.join(CSRC, "fa_bwd.hip"))
+KERNEL_SOURCES_BWD32 = (os.path.join(CSRC, "fa_device.h"), os.path.join(CSRC, "fa_bwd32.hip"))
 
 
 def kernel_sources(w: workloads.Workload, op: str = "fwd"):
@@ -97,18 +96,24 @@ def kernel_sources(w: workloads.Workload, op: str = "fwd"):
 
 
 def kernel_code_sha256(paths=KERNEL_SOURCES) -> str:
-    """SHA-256 of the kernel sources with comments (// in C++, # in Python)
-    and blank lines removed: it names the code the counters were taken on,
-    and survives comment edits."""
+    """SHA-256 of the kernel sources with // comments and blank lines removed,
+    followed by the compile flags (no paths) of every build unit that
+    compiles one of them: it names the code the counters were taken on, and
+    survives comment edits."""
     import hashlib
+
+    import exact_tiled_attention_15_amd.build as build
 
     lines = []
     for path in paths:
-        mark = "#" if path.endswith(".py") else "//"
         for line in open(path, encoding="utf-8"):
-            code = line.split(mark, 1)[0].rstrip()
+            code = line.split("//", 1)[0].rstrip()
             if code:
                 lines.append(code)
+        for name, src, extra in build.UNITS:
+            if os.path.basename(src) == os.path.basename(path):
+                flags = [f for f in build.FLAGS + build.DEVICE_FLAGS + extra if not os.path.isabs(f)]
+                lines.append(f"unit {name}: {' '.join(flags)}")
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
