@@ -234,7 +234,7 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, softmax_scale=None, dq
 def forward_splitkv(q, k, v, causal: bool = False, num_splits: int = 0, softmax_scale=None, out=None, lse=None,
                     workspace=None, stream=None):
     """``forward`` computed with the keys split into ranges (decoding shape:
-    few query rows, many keys).  16-bit dtypes only.  ``num_splits`` 0 picks
+    few query rows, many keys).  Dtypes and head dimensions as ``forward``.  ``num_splits`` 0 picks
     the count automatically; ``workspace`` (uint8 device tensor of at least
     ``fa_fwd_splitkv_workspace_size`` bytes) may be given preallocated."""
     import torch
@@ -268,7 +268,8 @@ def forward_splitkv(q, k, v, causal: bool = False, num_splits: int = 0, softmax_
 
 def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool = False,
                    softmax_scale=None, out=None, lse=None, stream=None):
-    """Attention over packed variable-length sequences (16-bit dtypes).
+    """Attention over packed variable-length sequences (dtypes and head
+    dimensions as ``forward``).
 
     q: (H, total_q, D), k/v: (H, total_k, D) contiguous GPU tensors (head-major
     packing); cu_seqlens_q / cu_seqlens_k: int32 GPU tensors of B + 1

@@ -135,7 +135,6 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
                               void* workspace, int64_t workspace_bytes, int64_t B, int64_t H, int64_t Nq,
                               int64_t Nk, int64_t D, double softmax_scale, int64_t num_splits, int causal,
                               int dtype, void* stream) {
-  if (dtype == FA_DTYPE_FP32) return FA_ERR_DTYPE;  // the split path runs the 16-bit kernel
   bool empty = false;
   const int st = validate(q, k, v, o, lse, B, H, Nq, Nk, D, dtype, &empty);
   if (st != FA_OK) return st;
@@ -163,15 +162,16 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
   if (n <= 1) return fa_launch_fwd(a) == 0 ? FA_OK : FA_ERR_HIP;
   // fp32 partials of one (range, head) are addressed with 32-bit offsets
   if ((Nq + 256) * (D * 4) > INT32_MAX) return FA_ERR_SHAPE;
-  int64_t grid;
-  if (!mul_ok(BH * ((Nq + 255) / 256), n, &grid) || grid > INT32_MAX || rows * (D / 4) / 256 >= INT32_MAX)
+  int64_t grid;  // Q tiles of 256 rows (16-bit) or 128 (fp32)
+  if (!mul_ok(BH * ((Nq + 127) / 128), n, &grid) || grid > INT32_MAX || rows * (D / 4) / 256 >= INT32_MAX)
     return FA_ERR_SHAPE;
   const int64_t need = fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D, num_splits);
   if (need < 0) return FA_ERR_SHAPE;
   if (!workspace) return FA_ERR_NULL;
   if (workspace_bytes < need) return FA_ERR_WORKSPACE;
   if ((uintptr_t)workspace & 15u) return FA_ERR_ALIGN;
-  const int64_t esz = 2, qbytes = rows * D * esz, kbytes = BH * Nk * D * esz, lbytes = rows * 4;
+  const int64_t esz = dtype == FA_DTYPE_FP32 ? 4 : 2;
+  const int64_t qbytes = rows * D * esz, kbytes = BH * Nk * D * esz, lbytes = rows * 4;
   if (overlaps(workspace, need, q, qbytes) || overlaps(workspace, need, k, kbytes) ||
       overlaps(workspace, need, v, kbytes) || overlaps(workspace, need, o, qbytes) ||
       overlaps(workspace, need, lse, lbytes))
@@ -196,9 +196,10 @@ extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* 
                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int64_t B, int64_t H,
                              int64_t total_q, int64_t total_k, int64_t max_seqlen_q, int64_t D,
                              double softmax_scale, int causal, int dtype, void* stream) {
-  if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;  // the 16-bit kernel
+  if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (B < 0 || H < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || D < 0) return FA_ERR_SHAPE;
   if (D != 32 && D != 64 && D != 128 && D != 256) return FA_ERR_HEAD_DIM;
+  if (D == 256 && dtype == FA_DTYPE_FP32) return FA_ERR_HEAD_DIM;
   if (!scale_ok(softmax_scale)) return FA_ERR_SCALE;
   int64_t BH, qel, kel;
   if (!mul_ok(B, H, &BH) || !mul_ok(H, total_q, &qel) || !mul_ok(qel, D, &qel) || !mul_ok(H, total_k, &kel) ||
@@ -207,7 +208,7 @@ extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* 
   if (BH == 0 || total_q == 0 || max_seqlen_q == 0) return FA_OK;  // no query row to compute
   if (max_seqlen_q > total_q || total_q > INT32_MAX / 2 || total_k > INT32_MAX / 2 || BH > INT32_MAX)
     return FA_ERR_SHAPE;
-  const int64_t esz = 2;
+  const int64_t esz = dtype == FA_DTYPE_FP32 ? 4 : 2;
   // one head's packed rows are addressed with 32-bit offsets
   if ((total_q + 256) * D * esz > INT32_MAX || (total_k + 256) * D * esz > INT32_MAX) return FA_ERR_SHAPE;
   int64_t grid;

@@ -391,15 +391,20 @@ __global__ __launch_bounds__(64 * waves16<D>(), 1) void fa_fwd_16(const u16* __r
 }
 
 // ---------------------------------------------------------------------------
-// fp32 kernel, D in {32, 64, 128}, v_mfma_f32_32x32x2_f32.
+// fp32 kernel, D in {32, 64, 128}, v_mfma_f32_32x32x2_f32.  SPLIT and
+// VARLEN as in fa_fwd_16 (the same workgroup mapping, key ranges, partial
+// layout and packed layout).
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT = false, bool VARLEN = false>
 __global__ __launch_bounds__(kThreads, 1) void fa_fwd_32(const float* __restrict__ Qg,
                                                          const float* __restrict__ Kg,
                                                          const float* __restrict__ Vg,
                                                          float* __restrict__ Og,
                                                          float* __restrict__ Lg, int BH, int Nq,
-                                                         int Nk, int nqt, float sl2) {
+                                                         int Nk, int nqt, float sl2, int split_len,
+                                                         float* __restrict__ Po, float* __restrict__ Pl,
+                                                         const int* __restrict__ cuq, const int* __restrict__ cuk,
+                                                         int H, int tq, int tk) {
   constexpr int BC = (D <= 64) ? 64 : 32;
   constexpr int NSUB = BC / 32;
   constexpr int STR = D + 4;      // row stride (floats) of K and V in LDS
@@ -413,26 +418,67 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_32(const float* __restrict
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, l32 = lane & 31;
-  int bh, qt;
-  tile_of_block(nqt, BH, bh, qt);
+  int bh, qt, split = 0;
+  if constexpr (VARLEN) {
+    const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3;
+    bh = xcd + 8 * (i / nqt);
+    qt = nqt - 1 - i % nqt;
+    if (bh >= BH) return;
+  } else if constexpr (SPLIT) {
+    const int per = BH * nqt;
+    split = blockIdx.x / per;
+    const int rem = blockIdx.x - split * per;
+    bh = rem % BH;
+    qt = nqt - 1 - rem / BH;
+  } else {
+    tile_of_block(nqt, BH, bh, qt);
+  }
   const int q0 = qt * kBR;
-  const size_t qoff = (size_t)bh * Nq * D, koff = (size_t)bh * Nk * D;
-  const float* Q = Qg + qoff;
-  const float* K = Kg + koff;
-  const float* V = Vg + koff;
+  // This head's rows: nq queries at Q / Oh / Lh, NK keys at Kg + koff.
+  const float* Q;
+  float* Oh;
+  float* Lh;
+  size_t koff;
+  int nq, NK;
+  if constexpr (VARLEN) {
+    const int b = bh / H, h = bh - b * H;
+    const int qs = min(max(cuq[b], 0), tq), qe = min(max(cuq[b + 1], qs), tq);
+    const int ks = min(max(cuk[b], 0), tk), ke = min(max(cuk[b + 1], ks), tk);
+    nq = qe - qs;
+    NK = ke - ks;
+    if (q0 >= nq) return;  // past this sequence's rows: the whole workgroup
+    Q = Qg + ((size_t)h * tq + qs) * D;
+    Oh = Og + ((size_t)h * tq + qs) * D;
+    Lh = Lg + (size_t)h * tq + qs;
+    koff = ((size_t)h * tk + ks) * D;
+  } else {
+    nq = Nq;
+    NK = Nk;
+    Q = Qg + (size_t)bh * Nq * D;
+    Oh = Og + (size_t)bh * Nq * D;
+    Lh = Lg + (size_t)bh * Nq;
+    koff = (size_t)bh * Nk * D;
+  }
+  // This workgroup's keys: [kb, kb + nk) of the head (all of them unless
+  // SPLIT); key indices below are relative to kb.
+  const int kb = SPLIT ? split * split_len : 0;
+  const int nk = SPLIT ? min(split_len, NK - kb) : NK;
+  const float* K = Kg + koff + (size_t)kb * D;
+  const float* V = Vg + koff + (size_t)kb * D;
 
-  const int kend = CAUSAL ? min(Nk, min(q0 + kBR, Nq)) : Nk;
-  const int nt = (kend + BC - 1) / BC;
+  const int kend = CAUSAL ? min(nk, min(q0 + kBR, nq) - kb) : nk;  // keys [0, kend) are needed
+  const int nt = kend > 0 ? (kend + BC - 1) / BC : 0;
   const int wq0 = q0 + 32 * wave;
   const int myq = wq0 + l32;
-  const int wkend = CAUSAL ? min(kend, wq0 + 32) : kend;
+  // A wave whose rows all lie past Nq computes nothing.
+  const int wkend = wq0 >= nq ? 0 : CAUSAL ? min(kend, wq0 + 32 - kb) : kend;
 
   // Q fragment: lane holds Q[myq][HALF*hf + c] for c = 0..HALF-1 (MFMA step c
   // pairs column c of the low half-wave with column HALF + c of the high).
   f32x4 qf[HALF / 4];
 #pragma unroll
   for (int c = 0; c < HALF / 4; ++c)
-    qf[c] = (myq < Nq) ? *(const f32x4*)(Q + (size_t)myq * D + HALF * hf + 4 * c) : f32x4{0, 0, 0, 0};
+    qf[c] = (myq < nq) ? *(const f32x4*)(Q + (size_t)myq * D + HALF * hf + 4 * c) : f32x4{0, 0, 0, 0};
 
   f32x4 kr[CPT], vr[CPT];
   auto load_tile = [&](int j) {
@@ -441,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_32(const float* __restrict
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + kThreads * i;
       const int key = c / (D / 4), col = (c % (D / 4)) * 4;
-      const bool ok = (k0 + key < Nk);
+      const bool ok = (k0 + key < nk);
       kr[i] = ok ? *(const f32x4*)(K + (size_t)(k0 + key) * D + col) : f32x4{0, 0, 0, 0};
       vr[i] = ok ? *(const f32x4*)(V + (size_t)(k0 + key) * D + col) : f32x4{0, 0, 0, 0};
     }
@@ -463,7 +509,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_32(const float* __restrict
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
 
-  load_tile(0);
+  if (nt > 0) load_tile(0);
   for (int j = 0; j < nt; ++j) {
     const int stage = j & 1;
     store_tile(stage);
@@ -485,7 +531,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_32(const float* __restrict
             s[n] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qf[c][e], s[n], 0, 0, 0);
         }
       }
-      const bool need_mask = (k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > wq0));
+      const bool need_mask = (k0 + BC > nk) || (CAUSAL && (k0 + BC - 1 > wq0 - kb));
       float mx = -INFINITY;
 #pragma unroll
       for (int n = 0; n < NSUB; ++n)
@@ -494,7 +540,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_32(const float* __restrict
           float t = s[n][r] * sl2;
           if (need_mask) {
             const int key = k0 + 32 * n + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (key >= Nk || (CAUSAL && key > myq)) t = -INFINITY;
+            if (key >= nk || (CAUSAL && key > myq - kb)) t = -INFINITY;
           }
           s[n][r] = t;
           mx = fmaxf(mx, t);
@@ -531,9 +577,21 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_32(const float* __restrict
   }
 
   const float lt = l + xor32(l);
-  if (myq < Nq) {
-    const float inv = 1.0f / lt;
-    float* O = Og + qoff + (size_t)myq * D;
+  if (myq < nq) {
+    // Rows without a key (an empty key range of SPLIT, a sequence without
+    // keys of VARLEN): O = 0, LSE = -inf.
+    const bool none = (SPLIT || VARLEN) && !(lt > 0.f);
+    const float inv = none ? 0.f : 1.0f / lt;
+    float* O;
+    float* L;
+    if constexpr (SPLIT) {
+      const size_t slot = (size_t)split * BH + bh;
+      O = Po + (slot * Nq + myq) * D;
+      L = Pl + slot * Nq + myq;
+    } else {
+      O = Oh + (size_t)myq * D;
+      L = Lh + myq;
+    }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -542,17 +600,20 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_32(const float* __restrict
         *(f32x4*)(O + d) = f32x4{oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv,
                                  oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv};
       }
-    if (hf == 0) Lg[(size_t)bh * Nq + myq] = (m + __log2f(lt)) * kLn2;
+    if (hf == 0) *L = none ? -INFINITY : (m + __log2f(lt)) * kLn2;
   }
 }
 
-template <typename KernelT, typename T>
-int launch(KernelT kern, const FaLaunch& a, int rows_per_block, int threads, float sl2) {
-  const int nqt = (int)((a.Nq + rows_per_block - 1) / rows_per_block);
-  const dim3 grid((unsigned)(a.BH * nqt)), block(threads);
-  hipLaunchKernelGGL(kern, grid, block, 0, (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k,
-                     (const T*)a.v, (T*)a.o, a.lse, (int)a.BH, (int)a.Nq, (int)a.Nk, nqt, sl2);
-  return (int)hipGetLastError();
+template <int D, bool CAUSAL, bool SPLIT, bool VARLEN = false>
+void launch32(const FaLaunch& a, float sl2, int nsplit, int split_len, float* Po, float* Pl) {
+  const int nqt = (int)((a.Nq + kBR - 1) / kBR);
+  // VARLEN maps block ids per XCD (8 of them): round B*H up to a multiple of 8
+  const int64_t heads = VARLEN ? (a.BH + 7) / 8 * 8 : a.BH;
+  const dim3 grid((unsigned)(heads * nqt * nsplit)), block(kThreads);
+  hipLaunchKernelGGL((fa_fwd_32<D, CAUSAL, SPLIT, VARLEN>), grid, block, 0, (hipStream_t)a.stream,
+                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, (int)a.BH,
+                     (int)a.Nq, (int)a.Nk, nqt, sl2, split_len, Po, Pl, a.cu_q, a.cu_k, (int)a.H, (int)a.total_q,
+                     (int)a.total_k);
 }
 
 template <int DT, int D, bool CAUSAL, bool SPLIT, bool VARLEN = false>
@@ -585,7 +646,7 @@ int dispatch16(const FaLaunch& a, float sl2) {
 // D/4 lanes per row, four columns each.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void merge_splits(const float* __restrict__ Po, const float* __restrict__ Pl,
-                                                    u16* __restrict__ Og, float* __restrict__ Lg, int64_t rows,
+                                                    void* __restrict__ Og, float* __restrict__ Lg, int64_t rows,
                                                     int nsplit) {
   constexpr int LPR = D / 4;
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -605,10 +666,14 @@ __global__ __launch_bounds__(256) void merge_splits(const float* __restrict__ Po
     acc += wgt * o;
   }
   const float inv = 1.0f / tot;
-  u32x2 v;
-  v[0] = pack2<DT>(acc[0] * inv, acc[1] * inv);
-  v[1] = pack2<DT>(acc[2] * inv, acc[3] * inv);
-  *(u32x2*)(Og + row * D + 4 * c) = v;
+  if constexpr (DT == kFP16 || DT == kBF16) {
+    u32x2 v;
+    v[0] = pack2<DT>(acc[0] * inv, acc[1] * inv);
+    v[1] = pack2<DT>(acc[2] * inv, acc[3] * inv);
+    *(u32x2*)((u16*)Og + row * D + 4 * c) = v;
+  } else {
+    *(f32x4*)((float*)Og + row * D + 4 * c) = acc * inv;
+  }
   if (c == 0) Lg[row] = m + __logf(tot);
 }
 
@@ -623,14 +688,41 @@ int dispatch16_split(const FaLaunch& a, float sl2, int nsplit, int split_len) {
     launch16<DT, D, false, true>(a, sl2, nsplit, split_len, Po, Pl);
   const int64_t threads = rows * (D / 4);
   hipLaunchKernelGGL((merge_splits<DT, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                     (hipStream_t)a.stream, (const float*)Po, (const float*)Pl, (u16*)a.o, a.lse, rows, nsplit);
+                     (hipStream_t)a.stream, (const float*)Po, (const float*)Pl, a.o, a.lse, rows, nsplit);
   return (int)hipGetLastError();
 }
 
 template <int D>
 int dispatch32(const FaLaunch& a, float sl2) {
-  if (a.causal) return launch<decltype(&fa_fwd_32<D, true>), float>(&fa_fwd_32<D, true>, a, kBR, kThreads, sl2);
-  return launch<decltype(&fa_fwd_32<D, false>), float>(&fa_fwd_32<D, false>, a, kBR, kThreads, sl2);
+  if (a.causal)
+    launch32<D, true, false>(a, sl2, 1, 0, nullptr, nullptr);
+  else
+    launch32<D, false, false>(a, sl2, 1, 0, nullptr, nullptr);
+  return (int)hipGetLastError();
+}
+
+template <int D>
+int dispatch32_split(const FaLaunch& a, float sl2, int nsplit, int split_len) {
+  const int64_t rows = a.BH * a.Nq;
+  float* Po = (float*)a.workspace;
+  float* Pl = Po + (size_t)nsplit * rows * D;
+  if (a.causal)
+    launch32<D, true, true>(a, sl2, nsplit, split_len, Po, Pl);
+  else
+    launch32<D, false, true>(a, sl2, nsplit, split_len, Po, Pl);
+  const int64_t threads = rows * (D / 4);
+  hipLaunchKernelGGL((merge_splits<0, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     (hipStream_t)a.stream, (const float*)Po, (const float*)Pl, a.o, a.lse, rows, nsplit);
+  return (int)hipGetLastError();
+}
+
+template <int D>
+int dispatch32_varlen(const FaLaunch& a, float sl2) {
+  if (a.causal)
+    launch32<D, true, false, true>(a, sl2, 1, 0, nullptr, nullptr);
+  else
+    launch32<D, false, false, true>(a, sl2, 1, 0, nullptr, nullptr);
+  return (int)hipGetLastError();
 }
 
 template <int DT, int D>
@@ -669,9 +761,12 @@ int fa_launch_fwd_varlen(const FaLaunch& a) {
     case kBF16:
       return a.D == 32 ? dispatch16_varlen<kBF16, 32>(a, sl2)
            : a.D == 64 ? dispatch16_varlen<kBF16, 64>(a, sl2) : dispatch16_varlen<kBF16, 128>(a, sl2);
-    default:
+    case kFP16:
       return a.D == 32 ? dispatch16_varlen<kFP16, 32>(a, sl2)
            : a.D == 64 ? dispatch16_varlen<kFP16, 64>(a, sl2) : dispatch16_varlen<kFP16, 128>(a, sl2);
+    default:
+      return a.D == 32 ? dispatch32_varlen<32>(a, sl2)
+           : a.D == 64 ? dispatch32_varlen<64>(a, sl2) : dispatch32_varlen<128>(a, sl2);
   }
 }
 
@@ -684,10 +779,14 @@ int fa_launch_fwd_splitkv(const FaLaunch& a, int nsplit, int split_len) {
       return a.D == 32 ? dispatch16_split<kBF16, 32>(a, sl2, nsplit, split_len)
            : a.D == 64 ? dispatch16_split<kBF16, 64>(a, sl2, nsplit, split_len)
                        : dispatch16_split<kBF16, 128>(a, sl2, nsplit, split_len);
-    default:
+    case kFP16:
       return a.D == 32 ? dispatch16_split<kFP16, 32>(a, sl2, nsplit, split_len)
            : a.D == 64 ? dispatch16_split<kFP16, 64>(a, sl2, nsplit, split_len)
                        : dispatch16_split<kFP16, 128>(a, sl2, nsplit, split_len);
+    default:
+      return a.D == 32 ? dispatch32_split<32>(a, sl2, nsplit, split_len)
+           : a.D == 64 ? dispatch32_split<64>(a, sl2, nsplit, split_len)
+                       : dispatch32_split<128>(a, sl2, nsplit, split_len);
   }
 }
 

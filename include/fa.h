@@ -133,10 +133,9 @@ int64_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t 
  *               (may be NULL when that is 0), 16-byte aligned, owned by the
  *               caller; scratch after the call.
  *
- * Every other argument, layout and error is that of fa_fwd_scaled, except
- * that dtype must be FA_DTYPE_FP16 or FA_DTYPE_BF16 (FA_ERR_DTYPE otherwise);
- * FA_ERR_WORKSPACE for a short workspace; FA_ERR_ALIAS if it overlaps an
- * input or output.
+ * Every other argument, layout and error is that of fa_fwd_scaled (every
+ * dtype; D = 256 for fp16 and bf16 only), plus FA_ERR_WORKSPACE for a short
+ * workspace and FA_ERR_ALIAS if it overlaps an input or output.
  */
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                    void* workspace, int64_t workspace_bytes, int64_t B, int64_t H, int64_t Nq,
@@ -165,7 +164,8 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
  *         no access outside the buffers.
  *   max_seqlen_q  at least the longest sequence's query count (it sizes the
  *         grid; query rows past it are not written)
- *   dtype must be FA_DTYPE_FP16 or FA_DTYPE_BF16 (FA_ERR_DTYPE otherwise).
+ *   dtype  any fa_dtype (D = 256: fp16 and bf16 only, FA_ERR_HEAD_DIM
+ *         otherwise).
  *
  * A sequence with queries but no keys gets O = 0 and LSE = -inf (the empty
  * sum).  B*H == 0, total_q == 0 or max_seqlen_q == 0 is a no-op.  Other

@@ -174,7 +174,8 @@ def test_splitkv_workspace_size():
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=0), 4), (dict(D=16), 3), (dict(scale=0.0), 8), (dict(splits=-1), 2), (dict(splits=5000), 2),
+    (dict(dtype=7), 4), (dict(D=256, dtype=0), 3), (dict(D=16), 3), (dict(scale=0.0), 8), (dict(splits=-1), 2),
+    (dict(splits=5000), 2),
     (dict(q=0), 1), (dict(ws=0), 1), (dict(ws_bytes=32 * 4 * 4 * 129 * 4 - 1), 9), (dict(ws=WS + 8), 5),
     (dict(ws=K + 4096), 6), (dict(ws=L - 64), 6), (dict(o=Q), 6), (dict(Nk=0), 2),
 ])
@@ -196,7 +197,8 @@ def call_varlen(q=Q, k=K, v=V, o=O, lse=L, cu_q=CQ, cu_k=CK, B=3, H=4, total_q=5
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=0), 4), (dict(D=512), 3), (dict(scale=-1.0), 8), (dict(B=-1), 2), (dict(max_q=501), 2),
+    (dict(dtype=7), 4), (dict(D=256, dtype=0), 3), (dict(D=512), 3), (dict(scale=-1.0), 8), (dict(B=-1), 2),
+    (dict(max_q=501), 2),
     (dict(total_q=1 << 40), 2), (dict(cu_q=0), 1), (dict(cu_k=0), 1), (dict(lse=0), 1),
     (dict(cu_q=CQ + 2), 5), (dict(q=Q + 8), 5), (dict(o=Q + 64), 6), (dict(lse=CK), 6), (dict(o=CQ - 16), 6),
 ])

@@ -21,6 +21,10 @@ for i, (dt, D, causal, Nq, Nk) in enumerate([
         for (Nq, Nk) in ((1, 4097), (16, 3000), (33, 700), (300, 1500))]):
     CASES.append((dt, D, causal, Nq, Nk, (0, 3, 7, 40)[i % 4]))
 CASES += [("bf16", 256, False, 1, 5000, 0), ("fp16", 256, True, 40, 900, 3)]
+# fp32 inputs (the fp32 kernel in split mode, fp32 output from the merge)
+for i, (D, causal, Nq, Nk) in enumerate([(D, causal, Nq, Nk) for D in (32, 64, 128) for causal in (False, True)
+                                          for (Nq, Nk) in ((1, 4097), (33, 700), (300, 1500))]):
+    CASES.append(("fp32", D, causal, Nq, Nk, (0, 3, 7)[i % 3]))
 
 
 def _run(w, splits, scale=None):
@@ -46,12 +50,13 @@ def test_splitkv_parity(dt, D, causal, Nq, Nk, splits):
     compare_full(w, cpu, o, lse, "splitkv")
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_splitkv_partials(causal):
+def test_splitkv_partials(causal, dt):
     # every range's fp32 partial (O_s, LSE_s), empty causal ranges included
     # 500 query rows: under the causal mask range 1 is seen in full by rows
     # >= 383, ranges 2 and 3 in part or not at all
-    w = workloads.Workload(f"split_partials_{'c' if causal else 'n'}", 1, 2, 500, 700, 64, "bf16", causal, 91)
+    w = workloads.Workload(f"split_partials_{dt}_{'c' if causal else 'n'}", 1, 2, 500, 700, 64, dt, causal, 91)
     splits = 5  # 700 keys -> ranges of 192 keys: [0,192) [192,384) [384,576) [576,700)
     cpu, _, o, lse, ws, need = _run(w, splits)
     n, length = 4, 192
@@ -69,7 +74,7 @@ def test_splitkv_partials(causal):
         eo = float(np.max(np.abs(Po[s] - Or)))
         el = float(np.max(np.abs(Pl[s][~empty] - Lr[~empty]))) if (~empty).any() else 0.0
         log(f"  range {s} [{k0},{k1}): max|dO_s|={eo:.2e} max|dLSE_s|={el:.2e} empty rows {int(empty.sum())}")
-        assert eo <= TOL["bf16"][0] and el <= TOL["bf16"][1]
+        assert eo <= TOL[dt][0] and el <= TOL[dt][1]
     compare_full(w, cpu, o, lse, "partials-merged")
 
 

@@ -55,8 +55,10 @@ LENS = [
 ]
 
 
-@pytest.mark.parametrize("dt", ["bf16", "fp16"])
-@pytest.mark.parametrize("D", [32, 64, 128, 256])
+GRID = [(dt, D) for dt in ("bf16", "fp16", "fp32") for D in (32, 64, 128, 256) if not (dt == "fp32" and D == 256)]
+
+
+@pytest.mark.parametrize("dt,D", GRID)
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("li", range(len(LENS)))
 def test_varlen_parity(dt, D, causal, li):
@@ -74,12 +76,13 @@ def test_varlen_explicit_scale_and_large_max():
     _compare("bf16", inputs, o, lse, True, "varlen-scaled", scale=0.2)
 
 
-def test_varlen_equals_dense_for_equal_lengths():
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_varlen_equals_dense_for_equal_lengths(dt):
     # equal lengths: the same tiles as the dense kernel, bit for bit
     import exact_tiled_attention_15_amd as fa
 
     B, H, N, D = 3, 4, 300, 128
-    inputs = _inputs("bf16", H, D, [N] * B, [N] * B, 11)
+    inputs = _inputs(dt, H, D, [N] * B, [N] * B, 11)
     q, k, v = inputs[:3]
     o, lse = _run(*inputs, True)
     dense = [t.reshape(H, B, N, D).permute(1, 0, 2, 3).contiguous().cuda() for t in (q, k, v)]
