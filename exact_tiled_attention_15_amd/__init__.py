@@ -13,7 +13,7 @@ import ctypes
 import os
 
 __all__ = ["fa_fwd", "fa_fwd_scaled", "fa_fwd_varlen", "forward_varlen", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "forward_splitkv",
-           "fa_bwd", "fa_bwd_workspace_size", "backward", "fa_status_str", "forward", "load_library", "LIB_PATH",
+           "fa_bwd", "fa_bwd_workspace_size", "backward", "fa_bwd_varlen", "backward_varlen", "fa_status_str", "forward", "load_library", "LIB_PATH",
            "FA_DTYPE_FP32", "FA_DTYPE_FP16", "FA_DTYPE_BF16", "FA_OK", "FaError",
            "EXPORTED_SYMBOLS"]
 
@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 FA_DTYPE_FP32, FA_DTYPE_FP16, FA_DTYPE_BF16 = 0, 1, 2
 FA_OK = 0
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_scaled", "fa_fwd_varlen", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_bwd",
-                    "fa_bwd_workspace_size", "fa_status_str")
+                    "fa_bwd_workspace_size", "fa_bwd_varlen", "fa_status_str")
 
 _lib = None
 
@@ -62,6 +62,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fa_bwd_workspace_size.argtypes = [ctypes.c_int64] * 3
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 6 + \
+        [ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_bwd_varlen.restype = ctypes.c_int
+    lib.fa_bwd_varlen.argtypes = [ctypes.c_void_p] * 12 + [ctypes.c_int64] * 8 + \
         [ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [ctypes.c_int]
@@ -109,6 +112,16 @@ def fa_fwd_splitkv(q: int, k: int, v: int, o: int, lse: int, workspace: int, wor
 
 def fa_bwd_workspace_size(B: int, H: int, Nq: int) -> int:
     return int(load_library().fa_bwd_workspace_size(B, H, Nq))
+
+
+def fa_bwd_varlen(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int, cu_q: int,
+                  cu_k: int, workspace: int, workspace_bytes: int, B: int, H: int, total_q: int, total_k: int,
+                  max_seqlen_q: int, max_seqlen_k: int, D: int, softmax_scale: float, causal: int, dtype: int,
+                  stream: int | None) -> int:
+    """Call the C ``fa_bwd_varlen`` with raw device addresses; returns the status code."""
+    return load_library().fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, cu_q, cu_k, workspace, workspace_bytes,
+                                        B, H, total_q, total_k, max_seqlen_q, max_seqlen_k, D,
+                                        float(softmax_scale), int(causal), int(dtype), stream)
 
 
 def fa_bwd(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int,
@@ -303,3 +316,60 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causa
     if rc != FA_OK:
         raise FaError(rc)
     return out, lse
+
+
+def backward_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                    causal: bool = False, softmax_scale=None, dq=None, dk=None, dv=None, workspace=None,
+                    stream=None):
+    """Exact attention backward over packed variable-length sequences.
+
+    q, o, dout: (H, total_q, D); k, v: (H, total_k, D); lse: (H, total_q)
+    float32 as ``forward_varlen`` returned it; cu_seqlens_q / cu_seqlens_k:
+    int32 device tensors of B + 1 offsets.  Returns (dq, dk, dv).
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("dout", dout),
+                    ("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    H, total_q, D = q.shape
+    total_k = k.shape[1]
+    if tuple(k.shape) != (H, total_k, D) or tuple(v.shape) != (H, total_k, D):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    for name, t in (("o", o), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be like q")
+    if lse.shape != (H, total_q) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 (H, total_q) tensor")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must hold B + 1 offsets each")
+    B = cu_seqlens_q.numel() - 1
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor like {name[1:]}")
+    need = fa_bwd_workspace_size(1, H, total_q)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    scale = 1.0 / D**0.5 if softmax_scale is None else float(softmax_scale)
+    if stream is None:
+        with torch.cuda.device(q.device):
+            stream = torch.cuda.current_stream().cuda_stream
+    with torch.cuda.device(q.device):
+        rc = fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens_q.data_ptr(),
+                           cu_seqlens_k.data_ptr(), workspace.data_ptr(),
+                           workspace.numel() * workspace.element_size(), B, H, total_q, total_k,
+                           int(max_seqlen_q), int(max_seqlen_k), D, scale, bool(causal), _dtype_code(q), stream)
+    if rc != FA_OK:
+        raise FaError(rc)
+    return dq, dk, dv

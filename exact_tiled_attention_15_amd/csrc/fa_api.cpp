@@ -320,6 +320,82 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   return fa_launch_bwd(a) == 0 ? FA_OK : FA_ERR_HIP;
 }
 
+extern "C" int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, const int32_t* cu_seqlens_q,
+                             const int32_t* cu_seqlens_k, void* workspace, int64_t workspace_bytes, int64_t B,
+                             int64_t H, int64_t total_q, int64_t total_k, int64_t max_seqlen_q,
+                             int64_t max_seqlen_k, int64_t D, double softmax_scale, int causal, int dtype,
+                             void* stream) {
+  if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (B < 0 || H < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || D < 0)
+    return FA_ERR_SHAPE;
+  if (D != 32 && D != 64 && D != 128 && D != 256) return FA_ERR_HEAD_DIM;
+  if (D == 256 && dtype == FA_DTYPE_FP32) return FA_ERR_HEAD_DIM;
+  if (!scale_ok(softmax_scale)) return FA_ERR_SCALE;
+  int64_t BH, qel, kel;
+  if (!mul_ok(B, H, &BH) || !mul_ok(H, total_q, &qel) || !mul_ok(qel, D, &qel) || !mul_ok(H, total_k, &kel) ||
+      !mul_ok(kel, D, &kel))
+    return FA_ERR_SHAPE;
+  if (BH == 0 || (total_q == 0 && total_k == 0)) return FA_OK;  // nothing to write
+  if (max_seqlen_q > total_q || max_seqlen_k > total_k || total_q > INT32_MAX / 2 || total_k > INT32_MAX / 2 ||
+      BH > INT32_MAX)
+    return FA_ERR_SHAPE;
+  const int64_t esz = dtype == FA_DTYPE_FP32 ? 4 : 2;
+  // one sequence's rows are addressed with 32-bit offsets
+  if ((total_q + 256) * D * esz > INT32_MAX || (total_k + 256) * D * esz > INT32_MAX) return FA_ERR_SHAPE;
+  int64_t gq, gk;
+  if (!mul_ok(BH, (max_seqlen_q + 127) / 128, &gq) || gq > INT32_MAX ||
+      !mul_ok(BH, (max_seqlen_k + 127) / 128, &gk) || gk > INT32_MAX || qel / 4 / 256 >= INT32_MAX)
+    return FA_ERR_SHAPE;
+  const int64_t ws_need = fa_bwd_workspace_size(1, H, total_q);
+  if (ws_need < 0) return FA_ERR_SHAPE;
+  // the buffers of an empty side have zero size and may then be NULL
+  if (!cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULL;
+  if (total_k > 0 && (!k || !v || !dk || !dv)) return FA_ERR_NULL;
+  if (total_q > 0 && (!q || !o || !lse || !dout || !dq || !workspace)) return FA_ERR_NULL;
+  if (workspace_bytes < ws_need) return FA_ERR_WORKSPACE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
+       (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)workspace) & 15u)
+    return FA_ERR_ALIGN;
+  if (((uintptr_t)lse | (uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) & 3u) return FA_ERR_ALIGN;
+  const int64_t qbytes = qel * esz, kbytes = kel * esz, lbytes = H * total_q * 4, cbytes = (B + 1) * 4;
+  const void* ins[8] = {q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k};
+  const int64_t in_bytes[8] = {qbytes, kbytes, kbytes, qbytes, lbytes, qbytes, cbytes, cbytes};
+  void* outs[4] = {dq, dk, dv, workspace};
+  const int64_t out_bytes[4] = {qbytes, kbytes, kbytes, ws_need};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 8; ++j)
+      if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return FA_ERR_ALIAS;
+  }
+  FaBwdLaunch a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.workspace = workspace;
+  a.BH = BH;
+  a.Nq = max_seqlen_q;
+  a.Nk = max_seqlen_k;
+  a.D = (int)D;
+  a.causal = causal != 0;
+  a.dtype = dtype;
+  a.scale = softmax_scale;
+  a.stream = stream;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.H = H;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  return fa_launch_bwd(a) == 0 ? FA_OK : FA_ERR_HIP;
+}
+
 extern "C" const char* fa_status_str(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";

@@ -179,12 +179,16 @@ __device__ __forceinline__ void dq_tile(const u16* Kh, const u16* Vh, int kbytes
   }
 }
 
-template <int DT, int D, bool CAUSAL>
+// VARLEN: packed sequences (the rows of head_rows); a workgroup past its
+// sequence's queries exits, a sequence without keys gets dQ = 0.
+template <int DT, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(64 * dq_waves<D>(), 1) void bwd_dq(const u16* __restrict__ Qg, const u16* __restrict__ Kg,
                                                           const u16* __restrict__ Vg, const u16* __restrict__ dOg,
                                                           const float* __restrict__ lse2g,
                                                           const float* __restrict__ deltag, u16* __restrict__ dQg,
-                                                          int BH, int Nq, int Nk, int nqt, float sl2, float scale) {
+                                                          int BH, int Nq, int Nk, int nqt, float sl2, float scale,
+                                                          const int* __restrict__ cuq, const int* __restrict__ cuk,
+                                                          int H, int tq, int tk) {
   constexpr int BC = 64, ROWB = D * 2, TILEB = BC * ROWB, NW = dq_waves<D>(), BR = 32 * NW, ST = bwd_stages<D>();
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * TILEB];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * TILEB];
@@ -200,27 +204,31 @@ __global__ __launch_bounds__(64 * dq_waves<D>(), 1) void bwd_dq(const u16* __res
   int bh, qt;
   tile_of_block(nqt, BH, bh, qt);
   const int q0 = qt * BR;
-  const u16* Kh = Kg + (size_t)bh * Nk * D;
-  const u16* Vh = Vg + (size_t)bh * Nk * D;
-  const int kbytes = Nk * ROWB;
-  const int kend = CAUSAL ? min(Nk, min(q0 + BR, Nq)) : Nk;
+  const HeadRows hr = head_rows<VARLEN>(bh, Nq, Nk, D, cuq, cuk, H, tq, tk);
+  const int nq = hr.nq, nk = hr.nk;
+  if (q0 >= nq) return;  // past this sequence's queries: the whole workgroup
+  const u16* Kh = Kg + hr.ko;
+  const u16* Vh = Vg + hr.ko;
+  const int kbytes = nk * ROWB;
+  const int kend = CAUSAL ? min(nk, min(q0 + BR, nq)) : nk;
   const int nt = (kend + BC - 1) / BC;
   w.wq0 = q0 + 32 * w.wave;
   const int myq = w.wq0 + w.l32;
   w.wkend = CAUSAL ? min(kend, w.wq0 + 32) : kend;
-  w.klim = CAUSAL ? min(myq, Nk - 1) : Nk - 1;
-  w.wklim = CAUSAL ? min(w.wq0, Nk - 1) : Nk - 1;
+  w.klim = CAUSAL ? min(myq, nk - 1) : nk - 1;
+  w.wklim = CAUSAL ? min(w.wq0, nk - 1) : nk - 1;
   init_operand_offsets<D>(w);
 
   u32x4 qf[D / 16], dof[D / 16];
-  load_frag<D>(qf, Qg + (size_t)bh * Nq * D, Nq, w.wq0, w);
-  load_frag<D>(dof, dOg + (size_t)bh * Nq * D, Nq, w.wq0, w);
-  const auto rs = make_rsrc(lse2g + (size_t)bh * Nq, Nq * 4);
-  const auto rd = make_rsrc(deltag + (size_t)bh * Nq, Nq * 4);
+  load_frag<D>(qf, Qg + hr.qo, nq, w.wq0, w);
+  load_frag<D>(dof, dOg + hr.qo, nq, w.wq0, w);
+  const auto rs = make_rsrc(lse2g + hr.so, nq * 4);
+  const auto rd = make_rsrc(deltag + hr.so, nq * 4);
   const float lse2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, myq * 4, 0, 0));
   const float delta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, myq * 4, 0, 0));
 
-  issue_tile16<D, NW>(Kh, Vh, kbytes, 0, stage0, w);
+  // (a sequence without keys has no tile: nothing may be left in flight)
+  if (!VARLEN || nt > 0) issue_tile16<D, NW>(Kh, Vh, kbytes, 0, stage0, w);
   f32x16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
@@ -245,7 +253,7 @@ __global__ __launch_bounds__(64 * dq_waves<D>(), 1) void bwd_dq(const u16* __res
         dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 1, nt, stage1, stage0, w, qf, dof, acc, lse2, delta, sl2);
     }
   }
-  const auto rq = make_rsrc(dQg + (size_t)bh * Nq * D, Nq * ROWB);
+  const auto rq = make_rsrc(dQg + hr.qo, nq * ROWB);
   store_rows16<DT, D>(acc, scale, rq, (32 * w.wave + w.l32) * ROWB, q0 * ROWB, w.hf);
 }
 
@@ -457,13 +465,16 @@ __device__ __forceinline__ void kv_tile(const u16* Qh, const u16* dOh, int qbyte
   }
 }
 
-template <int DT, int D, bool CAUSAL, int GRADS>
+// VARLEN: packed sequences (the rows of head_rows); a workgroup past its
+// sequence's keys exits, keys of a sequence without queries get zeros.
+template <int DT, int D, bool CAUSAL, int GRADS, bool VARLEN>
 __global__ __launch_bounds__(64 * kWavesKV, 1) void bwd_dkdv(const u16* __restrict__ Qg, const u16* __restrict__ Kg,
                                                              const u16* __restrict__ Vg, const u16* __restrict__ dOg,
                                                              const float* __restrict__ lse2g,
                                                              const float* __restrict__ deltag, u16* __restrict__ dKg,
                                                              u16* __restrict__ dVg, int BH, int Nq, int Nk,
-                                                             float sl2, float scale) {
+                                                             float sl2, float scale, const int* __restrict__ cuq,
+                                                             const int* __restrict__ cuk, int H, int tq, int tk) {
   constexpr int ROWB = D * 2, SB = kv_stage_bytes<D>(), BK = 32 * kWavesKV, ST = bwd_stages<D>();
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[SB];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[SB];
@@ -482,60 +493,67 @@ __global__ __launch_bounds__(64 * kWavesKV, 1) void bwd_dkdv(const u16* __restri
   const int bh = bid % BH, kt = bid / BH;
   const int kb0 = kt * BK;
   const int wk0 = kb0 + 32 * w.wave;
-  const u16* Qh = Qg + (size_t)bh * Nq * D;
-  const u16* dOh = dOg + (size_t)bh * Nq * D;
-  const float* l2h = lse2g + (size_t)bh * Nq;
-  const float* dlh = deltag + (size_t)bh * Nq;
-  const int qbytes = Nq * ROWB;
+  const HeadRows hr = head_rows<VARLEN>(bh, Nq, Nk, D, cuq, cuk, H, tq, tk);
+  const int nq = hr.nq, nk = hr.nk;
+  if (kb0 >= nk) return;  // past this sequence's keys: the whole workgroup
+  const u16* Qh = Qg + hr.qo;
+  const u16* dOh = dOg + hr.qo;
+  const float* l2h = lse2g + hr.so;
+  const float* dlh = deltag + hr.so;
+  const int qbytes = nq * ROWB;
   const int t0 = CAUSAL ? kb0 / 64 : 0;  // first query tile that sees a key of the block
-  const int nt = max((Nq + 63) / 64 - t0, 0);
+  const int nt = max((nq + 63) / 64 - t0, 0);
   w.wq0 = w.wkend = w.wklim = w.klim = 0;  // forward-only fields
   init_operand_offsets<D>(w);
 
   u32x4 kf[D / 16], vf[D / 16];
-  load_frag<D>(kf, Kg + (size_t)bh * Nk * D, Nk, wk0, w);
-  if constexpr (GRADS & 1) load_frag<D>(vf, Vg + (size_t)bh * Nk * D, Nk, wk0, w);
+  load_frag<D>(kf, Kg + hr.ko, nk, wk0, w);
+  if constexpr (GRADS & 1) load_frag<D>(vf, Vg + hr.ko, nk, wk0, w);
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) dk[dt] = dv[dt] = f32x16{};
 
   if (nt > 0) {
-    issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t0, stage0, w);
+    issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, nq, t0, stage0, w);
     if constexpr (ST == 2) {
       for (int j = 0; j < nt; j += 2) {
-        kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, Nq, t0, j, nt, stage0, stage1, w, wk0, kf, vf, dk, dv, sl2);
+        kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j, nt, stage0, stage1, w, wk0, kf, vf, dk, dv, sl2);
         if (j + 1 < nt)
-          kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, Nq, t0, j + 1, nt, stage1, stage0, w, wk0, kf, vf, dk, dv,
+          kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 1, nt, stage1, stage0, w, wk0, kf, vf, dk, dv,
                                  sl2);
       }
     } else {
-      if (nt > 1) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t0 + 1, stage1, w);
-      if (nt > 2) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t0 + 2, stage2, w);
+      if (nt > 1) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, nq, t0 + 1, stage1, w);
+      if (nt > 2) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, nq, t0 + 2, stage2, w);
       wait_tile_and_barrier(nt > 2 ? kv_loads_per_tile<D>(w.wave) : 0);
       for (int j = 0; j < nt; j += 4) {
-        kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, Nq, t0, j, nt, stage0, stage3, w, wk0, kf, vf, dk, dv, sl2);
+        kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j, nt, stage0, stage3, w, wk0, kf, vf, dk, dv, sl2);
         if (j + 1 < nt)
-          kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, Nq, t0, j + 1, nt, stage1, stage0, w, wk0, kf, vf, dk, dv,
+          kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 1, nt, stage1, stage0, w, wk0, kf, vf, dk, dv,
                                  sl2);
         if (j + 2 < nt)
-          kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, Nq, t0, j + 2, nt, stage2, stage1, w, wk0, kf, vf, dk, dv,
+          kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 2, nt, stage2, stage1, w, wk0, kf, vf, dk, dv,
                                  sl2);
         if (j + 3 < nt)
-          kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, Nq, t0, j + 3, nt, stage3, stage2, w, wk0, kf, vf, dk, dv,
+          kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 3, nt, stage3, stage2, w, wk0, kf, vf, dk, dv,
                                  sl2);
       }
     }
   }
-  const auto rk = make_rsrc(dKg + (size_t)bh * Nk * D, Nk * ROWB);
-  const auto rv = make_rsrc(dVg + (size_t)bh * Nk * D, Nk * ROWB);
+  const auto rk = make_rsrc(dKg + hr.ko, nk * ROWB);
+  const auto rv = make_rsrc(dVg + hr.ko, nk * ROWB);
   if constexpr (GRADS & 1) store_rows16<DT, D>(dk, scale, rk, (32 * w.wave + w.l32) * ROWB, kb0 * ROWB, w.hf);
   if constexpr (GRADS & 2) store_rows16<DT, D>(dv, 1.0f, rv, (32 * w.wave + w.l32) * ROWB, kb0 * ROWB, w.hf);
 }
 
-template <int DT, int D, bool CAUSAL>
+// VARLEN: q, o, dout, dq [H, total_q, D]; k, v, dk, dv [H, total_k, D]; lse
+// and the workspace [H, total_q]; a.Nq / a.Nk are the longest sequence's
+// query / key counts and size the grids.
+template <int DT, int D, bool CAUSAL, bool VARLEN>
 int launch_bwd(const FaBwdLaunch& a, float sl2, float scale) {
   const hipStream_t st = (hipStream_t)a.stream;
-  const int64_t rows = a.BH * a.Nq;
+  const int64_t rows = VARLEN ? a.H * a.total_q : a.BH * a.Nq;  // query rows (statistics)
+  const int H = (int)a.H, tq = (int)a.total_q, tk = (int)a.total_k;
   float* lse2 = (float*)a.workspace;
   float* delta = lse2 + rows;
   if (rows > 0) {
@@ -543,28 +561,27 @@ int launch_bwd(const FaBwdLaunch& a, float sl2, float scale) {
     const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
     hipLaunchKernelGGL((bwd_prep<DT, D>), grid, block, 0, st, (const u16*)a.o, (const u16*)a.dout, a.lse, lse2,
                        delta, rows);
-  }
-  if (rows > 0) {
     constexpr int NWQ = dq_waves<D>();
     const int nqt = (int)((a.Nq + 32 * NWQ - 1) / (32 * NWQ));
-    const dim3 grid((unsigned)(a.BH * nqt)), block(64 * NWQ);
-    hipLaunchKernelGGL((bwd_dq<DT, D, CAUSAL>), grid, block, 0, st, (const u16*)a.q, (const u16*)a.k,
-                       (const u16*)a.v, (const u16*)a.dout, (const float*)lse2, (const float*)delta, (u16*)a.dq,
-                       (int)a.BH, (int)a.Nq, (int)a.Nk, nqt, sl2, scale);
+    if (nqt > 0)
+      hipLaunchKernelGGL((bwd_dq<DT, D, CAUSAL, VARLEN>), dim3((unsigned)(a.BH * nqt)), dim3(64 * NWQ), 0, st,
+                         (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, (const float*)lse2,
+                         (const float*)delta, (u16*)a.dq, (int)a.BH, (int)a.Nq, (int)a.Nk, nqt, sl2, scale, a.cu_q,
+                         a.cu_k, H, tq, tk);
   }
-  {
-    const int nkt = (int)((a.Nk + 32 * kWavesKV - 1) / (32 * kWavesKV));
+  const int nkt = (int)((a.Nk + 32 * kWavesKV - 1) / (32 * kWavesKV));
+  if (nkt > 0) {
     const dim3 grid((unsigned)(a.BH * nkt)), block(64 * kWavesKV);
     auto run = [&](auto kern) {
       hipLaunchKernelGGL(kern, grid, block, 0, st, (const u16*)a.q, (const u16*)a.k, (const u16*)a.v,
                          (const u16*)a.dout, (const float*)lse2, (const float*)delta, (u16*)a.dk, (u16*)a.dv,
-                         (int)a.BH, (int)a.Nq, (int)a.Nk, sl2, scale);
+                         (int)a.BH, (int)a.Nq, (int)a.Nk, sl2, scale, a.cu_q, a.cu_k, H, tq, tk);
     };
     if constexpr (D == 256) {  // one kernel per gradient: dV, then dK
-      run(bwd_dkdv<DT, D, CAUSAL, 2>);
-      run(bwd_dkdv<DT, D, CAUSAL, 1>);
+      run(bwd_dkdv<DT, D, CAUSAL, 2, VARLEN>);
+      run(bwd_dkdv<DT, D, CAUSAL, 1, VARLEN>);
     } else {
-      run(bwd_dkdv<DT, D, CAUSAL, 3>);
+      run(bwd_dkdv<DT, D, CAUSAL, 3, VARLEN>);
     }
   }
   return (int)hipGetLastError();
@@ -572,7 +589,9 @@ int launch_bwd(const FaBwdLaunch& a, float sl2, float scale) {
 
 template <int DT, int D>
 int dispatch_bwd(const FaBwdLaunch& a, float sl2, float scale) {
-  return a.causal ? launch_bwd<DT, D, true>(a, sl2, scale) : launch_bwd<DT, D, false>(a, sl2, scale);
+  if (a.cu_q)
+    return a.causal ? launch_bwd<DT, D, true, true>(a, sl2, scale) : launch_bwd<DT, D, false, true>(a, sl2, scale);
+  return a.causal ? launch_bwd<DT, D, true, false>(a, sl2, scale) : launch_bwd<DT, D, false, false>(a, sl2, scale);
 }
 
 }  // namespace

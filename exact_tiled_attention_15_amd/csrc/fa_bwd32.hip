@@ -116,12 +116,14 @@ __device__ __forceinline__ void store_row32(const f32x16 (&acc)[D / 32], float m
 // ---------------------------------------------------------------------------
 // dQ: 4 waves x 32 query rows per workgroup.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads32, 1) void bwd32_dq(const float* __restrict__ Qg, const float* __restrict__ Kg,
                                                           const float* __restrict__ Vg, const float* __restrict__ dOg,
                                                           const float* __restrict__ lse2g,
                                                           const float* __restrict__ deltag, float* __restrict__ dQg,
-                                                          int BH, int Nq, int Nk, int nqt, float sl2, float scale) {
+                                                          int BH, int Nq, int Nk, int nqt, float sl2, float scale,
+                                                          const int* __restrict__ cuq, const int* __restrict__ cuk,
+                                                          int H, int tq, int tk) {
   constexpr int BR = 128, BC = D <= 64 ? 64 : 32, NSUB = BC / 32, STR = D + 4, ST = BC * STR, NDT = D / 32;
   constexpr int CPT = BC * D / 4 / kThreads32;  // 16-byte chunks per thread per tensor
   static_assert(CPT >= 1, "tile shape");
@@ -132,20 +134,23 @@ __global__ __launch_bounds__(kThreads32, 1) void bwd32_dq(const float* __restric
   int bh, qt;
   tile_of_block(nqt, BH, bh, qt);
   const int q0 = qt * BR;
-  const float* K = Kg + (size_t)bh * Nk * D;
-  const float* V = Vg + (size_t)bh * Nk * D;
-  const int kend = CAUSAL ? min(Nk, min(q0 + BR, Nq)) : Nk;
+  const HeadRows hr = head_rows<VARLEN>(bh, Nq, Nk, D, cuq, cuk, H, tq, tk);
+  const int nq = hr.nq, nk = hr.nk;
+  if (q0 >= nq) return;  // past this sequence's queries: the whole workgroup
+  const float* K = Kg + hr.ko;
+  const float* V = Vg + hr.ko;
+  const int kend = CAUSAL ? min(nk, min(q0 + BR, nq)) : nk;
   const int nt = (kend + BC - 1) / BC;
   const int wq0 = q0 + 32 * wave;
   const int myq = wq0 + l32;
   const int wkend = CAUSAL ? min(kend, wq0 + 32) : kend;
 
   f32x4 qf[D / 8], df[D / 8];
-  load_half_row<D>(qf, Qg + (size_t)bh * Nq * D, Nq, myq, hf);
-  load_half_row<D>(df, dOg + (size_t)bh * Nq * D, Nq, myq, hf);
-  // rows past Nq: zero Q, dO and statistics, so dS = 0 (and they are not stored)
-  const float lse2 = myq < Nq ? lse2g[(size_t)bh * Nq + myq] : 0.f;
-  const float delta = myq < Nq ? deltag[(size_t)bh * Nq + myq] : 0.f;
+  load_half_row<D>(qf, Qg + hr.qo, nq, myq, hf);
+  load_half_row<D>(df, dOg + hr.qo, nq, myq, hf);
+  // rows past nq: zero Q, dO and statistics, so dS = 0 (and they are not stored)
+  const float lse2 = myq < nq ? lse2g[hr.so + myq] : 0.f;
+  const float delta = myq < nq ? deltag[hr.so + myq] : 0.f;
 
   f32x4 kr[CPT], vr[CPT];
   auto load_tile = [&](int j) {
@@ -154,7 +159,7 @@ __global__ __launch_bounds__(kThreads32, 1) void bwd32_dq(const float* __restric
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + kThreads32 * i;
       const int key = c / (D / 4), col = (c % (D / 4)) * 4;
-      const bool ok = k0 + key < Nk;
+      const bool ok = k0 + key < nk;
       kr[i] = ok ? *(const f32x4*)(K + (size_t)(k0 + key) * D + col) : f32x4{0, 0, 0, 0};
       vr[i] = ok ? *(const f32x4*)(V + (size_t)(k0 + key) * D + col) : f32x4{0, 0, 0, 0};
     }
@@ -187,7 +192,7 @@ __global__ __launch_bounds__(kThreads32, 1) void bwd32_dq(const float* __restric
     if (k0 >= wkend) continue;
     const float* ks = smem + stage * 2 * ST;
     const float* vs = ks + ST;
-    const bool need_mask = k0 + BC > Nk || (CAUSAL && k0 + BC - 1 > wq0);
+    const bool need_mask = k0 + BC > nk || (CAUSAL && k0 + BC - 1 > wq0);
 #pragma unroll
     for (int n = 0; n < NSUB; ++n) {
       // lane: query myq, keys k0 + 32 n + 8 (r/4) + 4 hf + r%4
@@ -199,27 +204,28 @@ __global__ __launch_bounds__(kThreads32, 1) void bwd32_dq(const float* __restric
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -lse2));
         if (need_mask) {
           const int key = k0 + 32 * n + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= Nk || (CAUSAL && key > myq)) p = 0.f;
+          if (key >= nk || (CAUSAL && key > myq)) p = 0.f;
         }
         ds[r] = p * (dp[r] - delta);
       }
       acc_transposed<D, STR>(acc, ks, n, l32, hf, ds);  // dQ^T += K^T dS^T
     }
   }
-  if (myq < Nq) store_row32<D>(acc, scale, dQg + ((size_t)bh * Nq + myq) * D, hf);
+  if (myq < nq) store_row32<D>(acc, scale, dQg + hr.qo + (size_t)myq * D, hf);
 }
 
 // ---------------------------------------------------------------------------
 // dK / dV: 4 waves x 32 keys per workgroup.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads32, 1) void bwd32_dkdv(const float* __restrict__ Qg, const float* __restrict__ Kg,
                                                             const float* __restrict__ Vg,
                                                             const float* __restrict__ dOg,
                                                             const float* __restrict__ lse2g,
                                                             const float* __restrict__ deltag, float* __restrict__ dKg,
                                                             float* __restrict__ dVg, int BH, int Nq, int Nk,
-                                                            float sl2, float scale) {
+                                                            float sl2, float scale, const int* __restrict__ cuq,
+                                                            const int* __restrict__ cuk, int H, int tq, int tk) {
   constexpr int BK = 128, BQ = D <= 64 ? 64 : 32, NSUB = BQ / 32, STR = D + 4, ST = BQ * STR, NDT = D / 32;
   constexpr int SS = 2 * ST + 2 * BQ;  // floats per stage: Q tile, dO tile, lse2, delta
   constexpr int CPT = BQ * D / 4 / kThreads32;
@@ -234,18 +240,21 @@ __global__ __launch_bounds__(kThreads32, 1) void bwd32_dkdv(const float* __restr
   const int kb0 = kt * BK;
   const int wk0 = kb0 + 32 * wave;
   const int mykey = wk0 + l32;
-  const float* Q = Qg + (size_t)bh * Nq * D;
-  const float* dO = dOg + (size_t)bh * Nq * D;
-  const float* l2h = lse2g + (size_t)bh * Nq;
-  const float* dlh = deltag + (size_t)bh * Nq;
+  const HeadRows hr = head_rows<VARLEN>(bh, Nq, Nk, D, cuq, cuk, H, tq, tk);
+  const int nq = hr.nq, nk = hr.nk;
+  if (kb0 >= nk) return;  // past this sequence's keys: the whole workgroup
+  const float* Q = Qg + hr.qo;
+  const float* dO = dOg + hr.qo;
+  const float* l2h = lse2g + hr.so;
+  const float* dlh = deltag + hr.so;
   const int t0 = CAUSAL ? kb0 / BQ : 0;  // first query tile that sees a key of the block
-  const int nt = max((Nq + BQ - 1) / BQ - t0, 0);
+  const int nt = max((nq + BQ - 1) / BQ - t0, 0);
 
   f32x4 kf[D / 8], vf[D / 8];
-  load_half_row<D>(kf, Kg + (size_t)bh * Nk * D, Nk, mykey, hf);
-  load_half_row<D>(vf, Vg + (size_t)bh * Nk * D, Nk, mykey, hf);
+  load_half_row<D>(kf, Kg + hr.ko, nk, mykey, hf);
+  load_half_row<D>(vf, Vg + hr.ko, nk, mykey, hf);
 
-  // Query rows past Nq are staged as zero Q, dO and statistics: their P is
+  // Query rows past nq are staged as zero Q, dO and statistics: their P is
   // exp2(0) = 1 but dO = 0 and dS = P (0 - 0) = 0, so they add nothing.
   f32x4 qr[CPT], dr[CPT];
   float sr = 0.f;
@@ -255,14 +264,14 @@ __global__ __launch_bounds__(kThreads32, 1) void bwd32_dkdv(const float* __restr
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + kThreads32 * i;
       const int row = c / (D / 4), col = (c % (D / 4)) * 4;
-      const bool ok = qb + row < Nq;
+      const bool ok = qb + row < nq;
       qr[i] = ok ? *(const f32x4*)(Q + (size_t)(qb + row) * D + col) : f32x4{0, 0, 0, 0};
       dr[i] = ok ? *(const f32x4*)(dO + (size_t)(qb + row) * D + col) : f32x4{0, 0, 0, 0};
     }
     if (tid < 2 * BQ) {
       const int row = tid % BQ;
       const float* src = tid < BQ ? l2h : dlh;
-      sr = qb + row < Nq ? src[qb + row] : 0.f;
+      sr = qb + row < nq ? src[qb + row] : 0.f;
     }
   };
   auto store_tile = [&](int stage) {
@@ -313,16 +322,17 @@ __global__ __launch_bounds__(kThreads32, 1) void bwd32_dkdv(const float* __restr
       acc_transposed<D, STR>(dk, qs, n, l32, hf, ds);  // dK^T += Q^T dS
     }
   }
-  if (mykey < Nk) {
-    store_row32<D>(dk, scale, dKg + ((size_t)bh * Nk + mykey) * D, hf);
-    store_row32<D>(dv, 1.0f, dVg + ((size_t)bh * Nk + mykey) * D, hf);
+  if (mykey < nk) {
+    store_row32<D>(dk, scale, dKg + hr.ko + (size_t)mykey * D, hf);
+    store_row32<D>(dv, 1.0f, dVg + hr.ko + (size_t)mykey * D, hf);
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 int launch_bwd32(const FaBwdLaunch& a, float sl2, float scale) {
   const hipStream_t st = (hipStream_t)a.stream;
-  const int64_t rows = a.BH * a.Nq;
+  const int64_t rows = VARLEN ? a.H * a.total_q : a.BH * a.Nq;  // query rows (statistics)
+  const int H = (int)a.H, tq = (int)a.total_q, tk = (int)a.total_k;
   float* lse2 = (float*)a.workspace;
   float* delta = lse2 + rows;
   if (rows > 0) {
@@ -330,22 +340,26 @@ int launch_bwd32(const FaBwdLaunch& a, float sl2, float scale) {
     hipLaunchKernelGGL((bwd32_prep<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
                        (const float*)a.o, (const float*)a.dout, a.lse, lse2, delta, rows);
     const int nqt = (int)((a.Nq + 127) / 128);
-    hipLaunchKernelGGL((bwd32_dq<D, CAUSAL>), dim3((unsigned)(a.BH * nqt)), dim3(kThreads32), 0, st,
-                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout,
-                       (const float*)lse2, (const float*)delta, (float*)a.dq, (int)a.BH, (int)a.Nq, (int)a.Nk, nqt,
-                       sl2, scale);
+    if (nqt > 0)
+      hipLaunchKernelGGL((bwd32_dq<D, CAUSAL, VARLEN>), dim3((unsigned)(a.BH * nqt)), dim3(kThreads32), 0, st,
+                         (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout,
+                         (const float*)lse2, (const float*)delta, (float*)a.dq, (int)a.BH, (int)a.Nq, (int)a.Nk,
+                         nqt, sl2, scale, a.cu_q, a.cu_k, H, tq, tk);
   }
   const int nkt = (int)((a.Nk + 127) / 128);
-  hipLaunchKernelGGL((bwd32_dkdv<D, CAUSAL>), dim3((unsigned)(a.BH * nkt)), dim3(kThreads32), 0, st,
-                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout,
-                     (const float*)lse2, (const float*)delta, (float*)a.dk, (float*)a.dv, (int)a.BH, (int)a.Nq,
-                     (int)a.Nk, sl2, scale);
+  if (nkt > 0)
+    hipLaunchKernelGGL((bwd32_dkdv<D, CAUSAL, VARLEN>), dim3((unsigned)(a.BH * nkt)), dim3(kThreads32), 0, st,
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout,
+                       (const float*)lse2, (const float*)delta, (float*)a.dk, (float*)a.dv, (int)a.BH, (int)a.Nq,
+                       (int)a.Nk, sl2, scale, a.cu_q, a.cu_k, H, tq, tk);
   return (int)hipGetLastError();
 }
 
 template <int D>
 int dispatch_bwd32(const FaBwdLaunch& a, float sl2, float scale) {
-  return a.causal ? launch_bwd32<D, true>(a, sl2, scale) : launch_bwd32<D, false>(a, sl2, scale);
+  if (a.cu_q)
+    return a.causal ? launch_bwd32<D, true, true>(a, sl2, scale) : launch_bwd32<D, false, true>(a, sl2, scale);
+  return a.causal ? launch_bwd32<D, true, false>(a, sl2, scale) : launch_bwd32<D, false, false>(a, sl2, scale);
 }
 
 }  // namespace

@@ -66,6 +66,40 @@ __device__ __forceinline__ void tile_of_block(int nqt, int BH, int& bh, int& qt)
   qt = nqt - 1 - bid / BH;
 }
 
+// The rows of one (batch, head) that a workgroup works on: nq queries and nk
+// keys, and the offsets of the first query row (elements of q, o, dout, dq),
+// key row (elements of k, v, dk, dv) and query statistic (lse, workspace).
+// Dense tensors: [B*H, Nq, D] and [B*H, Nk, D].  Packed (VARLEN): sequence b
+// owns query rows [cuq[b], cuq[b+1]) and key rows [cuk[b], cuk[b+1]) of
+// [H, tq, D] / [H, tk, D] (offsets clamped into [0, tq] / [0, tk]).
+struct HeadRows {
+  int nq, nk;
+  size_t qo, ko, so;
+};
+
+template <bool VARLEN>
+__device__ __forceinline__ HeadRows head_rows(int bh, int Nq, int Nk, int D, const int* cuq, const int* cuk, int H,
+                                              int tq, int tk) {
+  HeadRows r;
+  if constexpr (VARLEN) {
+    const int b = bh / H, h = bh - b * H;
+    const int qs = min(max(cuq[b], 0), tq), qe = min(max(cuq[b + 1], qs), tq);
+    const int ks = min(max(cuk[b], 0), tk), ke = min(max(cuk[b + 1], ks), tk);
+    r.nq = qe - qs;
+    r.nk = ke - ks;
+    r.qo = ((size_t)h * tq + qs) * D;
+    r.ko = ((size_t)h * tk + ks) * D;
+    r.so = (size_t)h * tq + qs;
+  } else {
+    r.nq = Nq;
+    r.nk = Nk;
+    r.qo = (size_t)bh * Nq * D;
+    r.ko = (size_t)bh * Nk * D;
+    r.so = (size_t)bh * Nq;
+  }
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // 16-bit kernel (bf16 / fp16), D in {32, 64, 128}, 64-key tiles.
 // ---------------------------------------------------------------------------

@@ -66,6 +66,14 @@ struct FaBwdLaunch {
   int dtype;  // fa_dtype
   double scale;
   void* stream;
+  // Packed sequences (fa_bwd_varlen), NULL otherwise: q, o, dout, dq are
+  // [H, total_q, D], k, v, dk, dv [H, total_k, D], lse and the workspace
+  // [H, total_q]; BH = B*H, Nq / Nk the longest sequence's counts.
+  const int* cu_q = nullptr;
+  const int* cu_k = nullptr;
+  int64_t H = 0;
+  int64_t total_q = 0;
+  int64_t total_k = 0;
 };
 
 // Enqueues the backward pass (three kernels).  Arguments are already

@@ -226,6 +226,40 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            int64_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
            double softmax_scale, int causal, int dtype, void* stream);
 
+/*
+ * fa_bwd_varlen -- fa_bwd over packed variable-length sequences: the
+ * gradients of sum(dout * O) where O = fa_fwd_varlen(q, k, v, ...) with the
+ * same offsets, scale and mask ("Frequently Asked Questions" and "Practical
+ * Tips for Python Developers" name packed variable-length batches; each
+ * sequence is an independent attention problem, so its gradients are fa_bwd's
+ * on its own rows).
+ *
+ *   q, o, dout, dq   device, [H, total_q, D] contiguous, `dtype`
+ *   k, v, dk, dv     device, [H, total_k, D] contiguous, `dtype`
+ *   lse              device, [H, total_q] fp32: fa_fwd_varlen's output
+ *   cu_seqlens_q, cu_seqlens_k   device int32 [B + 1] offsets, as
+ *         fa_fwd_varlen (clamped into [0, total] on the device)
+ *   workspace   device memory of at least fa_bwd_workspace_size(1, H,
+ *         total_q) bytes, 16-byte aligned, owned by the caller; scratch
+ *         after the call
+ *   max_seqlen_q, max_seqlen_k   at least the longest sequence's query /
+ *         key count (they size the grids; rows past them are not written)
+ *   D in {32, 64, 128, 256} (256: fp16 and bf16 only); any fa_dtype
+ *
+ * A sequence with queries but no keys gets dq = 0; keys of a sequence
+ * without queries (or that no query sees under the causal mask) get
+ * dk = dv = 0.  Rows outside every sequence are not written.  The buffers of
+ * an empty side (total_q == 0: q, o, lse, dout, dq, workspace; total_k == 0:
+ * k, v, dk, dv) may be NULL.  Errors as fa_bwd; the offsets arrays are inputs
+ * for FA_ERR_ALIAS.  Deterministic (no atomics); the library allocates
+ * nothing and keeps no pointer.
+ */
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, void* dq, void* dk, void* dv, const int32_t* cu_seqlens_q,
+                  const int32_t* cu_seqlens_k, void* workspace, int64_t workspace_bytes, int64_t B,
+                  int64_t H, int64_t total_q, int64_t total_k, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                  int64_t D, double softmax_scale, int causal, int dtype, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_str(int status);
 

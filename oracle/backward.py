@@ -29,7 +29,7 @@ import numpy as np
 
 from .attention import _as_f64, _check
 
-__all__ = ["attention_backward"]
+__all__ = ["attention_backward", "attention_varlen_backward"]
 
 
 def _block_grads(qi, kh, vh, doi, row_idx, causal, scale):
@@ -75,4 +75,32 @@ def attention_backward(q, k, v, do, causal: bool, scale=None, row_chunk: int = 2
                 dQ[b, h, r0:r1] = dq
                 dK[b, h] += dk
                 dV[b, h] += dv
+    return dQ, dK, dV
+
+
+def attention_varlen_backward(q, k, v, do, cu_q, cu_k, causal: bool, scale=None):
+    """Exact gradients of sum(dO * attention_varlen(q, k, v, cu_q, cu_k)).
+
+    Each packed sequence is an independent attention problem (its rows attend
+    to its own keys only), so its gradients are ``attention_backward`` on its
+    own rows; rows of sequences without keys get dQ = 0 (their O is the
+    constant 0), keys of sequences without queries dK = dV = 0.  q, do:
+    (H, total_q, D); k, v: (H, total_k, D); cu_q, cu_k: B + 1 offsets.
+    Returns float64 (dQ, dK, dV) in those shapes.
+    """
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    if do.shape != q.shape:
+        raise ValueError(f"dO shape {do.shape} != q shape {q.shape}")
+    dQ = np.zeros(q.shape)
+    dK = np.zeros(k.shape)
+    dV = np.zeros(v.shape)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if q1 == q0 or k1 == k0:
+            continue
+        g = attention_backward(q[None, :, q0:q1], k[None, :, k0:k1], v[None, :, k0:k1], do[None, :, q0:q1], causal,
+                               scale=scale)
+        dQ[:, q0:q1] = g[0][0]
+        dK[:, k0:k1] = g[1][0]
+        dV[:, k0:k1] = g[2][0]
     return dQ, dK, dV

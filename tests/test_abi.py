@@ -210,3 +210,31 @@ def test_varlen_noops():
     assert call_varlen(B=0, q=0, k=0, v=0, o=0, lse=0, cu_q=0, cu_k=0) == 0
     assert call_varlen(total_q=0, max_q=0, q=0, o=0, lse=0) == 0
     assert call_varlen(max_q=0) == 0
+
+
+def call_bwd_varlen(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, cu_q=CQ, cu_k=CK, ws=WS,
+                    ws_bytes=1 << 30, B=3, H=4, total_q=500, total_k=700, max_q=300, max_k=400, D=64,
+                    scale=0.125, causal=1, dtype=2):
+    return fa.fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, cu_q, cu_k, ws, ws_bytes, B, H, total_q, total_k,
+                            max_q, max_k, D, scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), 4), (dict(D=256, dtype=0), 3), (dict(D=512), 3), (dict(scale=0.0), 8), (dict(B=-1), 2),
+    (dict(max_q=501), 2), (dict(max_k=701), 2), (dict(total_k=1 << 40), 2),
+    (dict(cu_q=0), 1), (dict(cu_k=0), 1), (dict(dq=0), 1), (dict(dk=0), 1), (dict(ws=0), 1),
+    (dict(ws_bytes=8 * 4 * 500 - 1), 9),
+    (dict(cu_k=CK + 2), 5), (dict(dv=DV + 8), 5), (dict(lse=L + 2), 5),
+    (dict(dq=Q + 64), 6), (dict(dk=CQ - 16), 6), (dict(ws=CK), 6), (dict(dv=DK + 64), 6),
+])
+def test_bwd_varlen_validation_codes(kw, code):
+    assert call_bwd_varlen(**kw) == code
+
+
+def test_bwd_varlen_noops_and_empty_sides():
+    assert call_bwd_varlen(B=0, q=0, k=0, v=0, o=0, lse=0, dout=0, dq=0, dk=0, dv=0, cu_q=0, cu_k=0, ws=0,
+                           ws_bytes=0) == 0
+    assert call_bwd_varlen(total_q=0, total_k=0, max_q=0, max_k=0, q=0, k=0) == 0
+    # an empty side's buffers may be NULL; the other side's may not
+    assert call_bwd_varlen(total_q=0, max_q=0, q=0, o=0, lse=0, dout=0, dq=0, ws=0, dk=0) == 1
+    assert call_bwd_varlen(total_k=0, max_k=0, k=0, v=0, dk=0, dv=0, dq=0) == 1

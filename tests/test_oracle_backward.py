@@ -85,3 +85,66 @@ def test_backward_planted_mistake_is_caught(name):
 def test_backward_unmutated_definition_passes():
     for check in pb.ALL_CHECKS:
         check(lambda q, k, v, do, c, s: _mutant(q, k, v, do, c, s))
+
+
+# ---------------------------------------------------------------------------
+# Packed variable-length sequences: oracle.attention_varlen_backward
+# ---------------------------------------------------------------------------
+def _varlen_fd(q, k, v, do, cu_q, cu_k, causal, scale, eps=1e-5):
+    """Central finite differences of sum(dO * O) through the varlen forward
+    oracle (a separate definition: per-sequence slices of the forward)."""
+    def f():
+        O, _ = oracle.attention_varlen(q, k, v, cu_q, cu_k, causal, scale=scale)
+        return float(np.sum(O * do))
+
+    grads = []
+    for x in (q, k, v):
+        g = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            old = x[i]
+            x[i] = old + eps
+            fp = f()
+            x[i] = old - eps
+            fm = f()
+            x[i] = old
+            g[i] = (fp - fm) / (2 * eps)
+        grads.append(g)
+    return grads
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_backward_oracle_finite_differences(causal):
+    # sequence 1 has keys but no queries, sequence 2 queries but no keys
+    lens_q, lens_k = [2, 0, 3, 4], [3, 2, 0, 2]
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int64)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int64)
+    r = np.random.default_rng(31)
+    H, D = 2, 3
+    q = r.standard_normal((H, cu_q[-1], D))
+    k = r.standard_normal((H, cu_k[-1], D))
+    v = r.standard_normal((H, cu_k[-1], D))
+    do = r.standard_normal((H, cu_q[-1], D))
+    for scale in (None, 0.7):
+        got = oracle.attention_varlen_backward(q, k, v, do, cu_q, cu_k, causal, scale=scale)
+        ref = _varlen_fd(q, k, v, do, cu_q, cu_k, causal, scale)
+        for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
+            assert np.max(np.abs(a - b)) <= 1e-7, (name, scale, float(np.max(np.abs(a - b))))
+    dQ, dK, dV = oracle.attention_varlen_backward(q, k, v, do, cu_q, cu_k, causal)
+    assert np.all(dQ[:, cu_q[2]:cu_q[3]] == 0.0)  # queries without keys
+    assert np.all(dK[:, cu_k[1]:cu_k[2]] == 0.0) and np.all(dV[:, cu_k[1]:cu_k[2]] == 0.0)  # keys without queries
+
+
+def test_varlen_backward_oracle_equal_lengths_match_dense():
+    # B equal-length sequences packed head-major are the dense batch
+    r = np.random.default_rng(32)
+    B, H, N, D = 3, 2, 17, 8
+    q, k, v, do = (r.standard_normal((B, H, N, D)) for _ in range(4))
+    pack = lambda t: t.transpose(1, 0, 2, 3).reshape(H, B * N, D)
+    cu = np.arange(B + 1) * N
+    for causal in (False, True):
+        dense = oracle.attention_backward(q, k, v, do, causal)
+        packed = oracle.attention_varlen_backward(pack(q), pack(k), pack(v), pack(do), cu, cu, causal)
+        for a, b in zip(packed, dense):
+            assert np.array_equal(a, pack(b))

@@ -110,3 +110,84 @@ def test_varlen_full_size_sampled():
             eo, el = float(np.max(np.abs(og - O))), float(np.max(np.abs(lg - L)))
             assert eo <= TOL["bf16"][0] and el <= TOL["bf16"][1], (b, h, eo, el)
     log("  sampled rows within tolerance")
+
+
+# ---------------------------------------------------------------------------
+# Backward over packed sequences (fa_bwd_varlen)
+# ---------------------------------------------------------------------------
+# Tolerance as the dense backward's (tests/test_backward_gpu.py): each
+# gradient tensor within REL of its own largest magnitude, plus a floor.
+BWD_TOL = {"bf16": (2e-2, 1e-4), "fp16": (2e-2, 1e-4), "fp32": (1e-4, 1e-6)}
+
+
+def _dout(dt, like, seed):
+    r = np.random.default_rng(seed)
+    return torch.from_numpy(r.standard_normal(tuple(like.shape)).astype(np.float32)).to(like.dtype)
+
+
+def _run_bwd(inputs, causal, dout, scale=None):
+    import exact_tiled_attention_15_amd as fa
+
+    q, k, v, cu_q, cu_k = inputs
+    o, lse = _run(q, k, v, cu_q, cu_k, causal, scale=scale)
+    dev = o.device
+    qg, kg, vg = (t.to(dev).contiguous() for t in (q, k, v))
+    cq, ck = cu_q.to(dev), cu_k.to(dev)
+    max_q = int((cu_q[1:] - cu_q[:-1]).max())
+    max_k = int((cu_k[1:] - cu_k[:-1]).max())
+    grads = [torch.full_like(t, float("nan")) for t in (qg, kg, vg)]
+    fa.backward_varlen(qg, kg, vg, o, lse, dout.to(dev), cq, ck, max_q, max_k, causal, softmax_scale=scale,
+                       dq=grads[0], dk=grads[1], dv=grads[2])
+    torch.cuda.synchronize()
+    return grads
+
+
+def _compare_bwd(dt, inputs, dout, grads, causal, tag, scale=None):
+    q, k, v, cu_q, cu_k = inputs
+    ref = oracle.attention_varlen_backward(q, k, v, dout, cu_q.numpy(), cu_k.numpy(), causal, scale=scale)
+    rel, floor = BWD_TOL[dt]
+    msg = []
+    for name, g, r in zip(("dQ", "dK", "dV"), grads, ref):
+        g = g.float().cpu().double().numpy()
+        assert np.isfinite(g).all(), f"{tag} {name}: rows left unwritten or non-finite"
+        e = float(np.max(np.abs(g - r))) if r.size else 0.0
+        m = float(np.max(np.abs(r))) if r.size else 0.0
+        msg.append(f"{name} err {e:.2e} max {m:.2e}")
+        assert e <= rel * m + floor, f"{tag} {name}: {e:.3e} > {rel} * {m:.3e} + {floor}"
+    log(f"  {tag}: " + " ".join(msg))
+
+
+@pytest.mark.parametrize("dt,D", GRID)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("li", range(len(LENS)))
+def test_varlen_backward_parity(dt, D, causal, li):
+    lens_q, lens_k = LENS[li]
+    log(f"case varlen backward {dt} D={D} causal={causal} lens_q={lens_q} lens_k={lens_k}")
+    inputs = _inputs(dt, 2, D, lens_q, lens_k, 200 + li + D)
+    dout = _dout(dt, inputs[0], 300 + li + D)
+    grads = _run_bwd(inputs, causal, dout)
+    _compare_bwd(dt, inputs, dout, grads, causal, f"varlen-bwd-{li}")
+
+
+def test_varlen_backward_explicit_scale():
+    inputs = _inputs("fp16", 2, 128, [33, 250, 1], [77, 250, 9], 17)
+    dout = _dout("fp16", inputs[0], 18)
+    grads = _run_bwd(inputs, True, dout, scale=0.2)
+    _compare_bwd("fp16", inputs, dout, grads, True, "varlen-bwd-scaled", scale=0.2)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_varlen_backward_equals_dense_for_equal_lengths(dt):
+    # equal lengths: the same tiles as the dense backward, bit for bit
+    import exact_tiled_attention_15_amd as fa
+
+    B, H, N, D = 3, 4, 300, 128
+    inputs = _inputs(dt, H, D, [N] * B, [N] * B, 21)
+    dout = _dout(dt, inputs[0], 22)
+    grads = _run_bwd(inputs, True, dout)
+    q, k, v = inputs[:3]
+    dense = [t.reshape(H, B, N, D).permute(1, 0, 2, 3).contiguous().cuda() for t in (q, k, v, dout)]
+    o, lse = fa.forward(*dense[:3], True)
+    gd = fa.backward(*dense[:3], o, lse, dense[3], True)
+    for g, d in zip(grads, gd):
+        assert torch.equal(g, d.permute(1, 0, 2, 3).reshape(H, B * N, D))
