@@ -190,6 +190,35 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
   }
 }
 
+// Workgroup -> (batch*head, Q tile, key range) of the forward kernels;
+// false for a workgroup with nothing to do.
+// VARLEN: workgroups go to the 8 XCDs round-robin by block id.  Each XCD
+// sweeps all Q tiles of one head (heaviest first) before the next head, so
+// that the tiles running together on its 32 CUs share that head's K/V in the
+// XCD's L2 (with one head per Q tile at a time, the K/V of the long sequences
+// of a packed batch overflowed it).  The grid rounds B*H up to a multiple of
+// 8.
+// SPLIT: range-major, then Q tiles heaviest first over all heads.
+template <bool SPLIT, bool VARLEN>
+__device__ __forceinline__ bool fwd_block(int nqt, int BH, int& bh, int& qt, int& split) {
+  split = 0;
+  if constexpr (VARLEN) {
+    const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3;
+    bh = xcd + 8 * (i / nqt);
+    qt = nqt - 1 - i % nqt;
+    return bh < BH;
+  } else if constexpr (SPLIT) {
+    const int per = BH * nqt;
+    split = blockIdx.x / per;
+    const int rem = blockIdx.x - split * per;
+    bh = rem % BH;
+    qt = nqt - 1 - rem / BH;
+  } else {
+    tile_of_block(nqt, BH, bh, qt);
+  }
+  return true;
+}
+
 // SPLIT: the grid also runs over key ranges of `split_len` keys; the
 // workgroup of range s attends to keys [s split_len, (s+1) split_len) only
 // and writes its normalised fp32 partial O_s and LSE_s (rows with no key in
@@ -231,52 +260,17 @@ __global__ __launch_bounds__(64 * waves16<D>(), 1) void fa_fwd_16(const u16* __r
   w.wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   w.hf = w.lane >> 5;
   w.l32 = w.lane & 31;
-  int bh, qt, split = 0;
-  if constexpr (VARLEN) {
-    // Workgroups go to the 8 XCDs round-robin by block id.  Each XCD sweeps
-    // all Q tiles of one head (heaviest first) before the next head, so that
-    // the tiles running together on its 32 CUs share that head's K/V in the
-    // XCD's L2 (with one head per Q tile at a time, the K/V of the long
-    // sequences of a packed batch overflowed it).
-    const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3;
-    bh = xcd + 8 * (i / nqt);
-    qt = nqt - 1 - i % nqt;
-    if (bh >= BH) return;
-  } else if constexpr (SPLIT) {
-    const int per = BH * nqt;
-    split = blockIdx.x / per;
-    const int rem = blockIdx.x - split * per;
-    bh = rem % BH;
-    qt = nqt - 1 - rem / BH;
-  } else {
-    tile_of_block(nqt, BH, bh, qt);
-  }
+  int bh, qt, split;
+  if (!fwd_block<SPLIT, VARLEN>(nqt, BH, bh, qt, split)) return;
   const int q0 = qt * BR;
-  // This head's rows: nq queries at Qh / Oh / Lh, NK keys at Kg + koff.
-  const u16* Qh;
-  u16* Oh;
-  float* Lh;
-  size_t koff;
-  int nq, NK;
-  if constexpr (VARLEN) {
-    const int b = bh / H, h = bh - b * H;
-    const int qs = min(max(cuq[b], 0), tq), qe = min(max(cuq[b + 1], qs), tq);
-    const int ks = min(max(cuk[b], 0), tk), ke = min(max(cuk[b + 1], ks), tk);
-    nq = qe - qs;
-    NK = ke - ks;
-    if (q0 >= nq) return;  // past this sequence's rows: the whole workgroup
-    Qh = Qg + ((size_t)h * tq + qs) * D;
-    Oh = Og + ((size_t)h * tq + qs) * D;
-    Lh = Lg + (size_t)h * tq + qs;
-    koff = ((size_t)h * tk + ks) * D;
-  } else {
-    nq = Nq;
-    NK = Nk;
-    Qh = Qg + (size_t)bh * Nq * D;
-    Oh = Og + (size_t)bh * Nq * D;
-    Lh = Lg + (size_t)bh * Nq;
-    koff = (size_t)bh * Nk * D;
-  }
+  // This head's rows: nq queries at Qh / Oh / Lh, NK keys at Kg + hr.ko.
+  const HeadRows hr = head_rows<VARLEN>(bh, Nq, Nk, D, cuq, cuk, H, tq, tk);
+  const int nq = hr.nq, NK = hr.nk;
+  if (q0 >= nq) return;  // past this sequence's rows: the whole workgroup
+  const u16* Qh = Qg + hr.qo;
+  u16* Oh = Og + hr.qo;
+  float* Lh = Lg + hr.so;
+  const size_t koff = hr.ko;
   // This workgroup's keys: [kb, kb + nk) of the head (all of them unless
   // SPLIT); key indices below are relative to kb.
   const int kb = SPLIT ? split * split_len : 0;
@@ -418,47 +412,17 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_32(const float* __restrict
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, l32 = lane & 31;
-  int bh, qt, split = 0;
-  if constexpr (VARLEN) {
-    const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3;
-    bh = xcd + 8 * (i / nqt);
-    qt = nqt - 1 - i % nqt;
-    if (bh >= BH) return;
-  } else if constexpr (SPLIT) {
-    const int per = BH * nqt;
-    split = blockIdx.x / per;
-    const int rem = blockIdx.x - split * per;
-    bh = rem % BH;
-    qt = nqt - 1 - rem / BH;
-  } else {
-    tile_of_block(nqt, BH, bh, qt);
-  }
+  int bh, qt, split;
+  if (!fwd_block<SPLIT, VARLEN>(nqt, BH, bh, qt, split)) return;
   const int q0 = qt * kBR;
-  // This head's rows: nq queries at Q / Oh / Lh, NK keys at Kg + koff.
-  const float* Q;
-  float* Oh;
-  float* Lh;
-  size_t koff;
-  int nq, NK;
-  if constexpr (VARLEN) {
-    const int b = bh / H, h = bh - b * H;
-    const int qs = min(max(cuq[b], 0), tq), qe = min(max(cuq[b + 1], qs), tq);
-    const int ks = min(max(cuk[b], 0), tk), ke = min(max(cuk[b + 1], ks), tk);
-    nq = qe - qs;
-    NK = ke - ks;
-    if (q0 >= nq) return;  // past this sequence's rows: the whole workgroup
-    Q = Qg + ((size_t)h * tq + qs) * D;
-    Oh = Og + ((size_t)h * tq + qs) * D;
-    Lh = Lg + (size_t)h * tq + qs;
-    koff = ((size_t)h * tk + ks) * D;
-  } else {
-    nq = Nq;
-    NK = Nk;
-    Q = Qg + (size_t)bh * Nq * D;
-    Oh = Og + (size_t)bh * Nq * D;
-    Lh = Lg + (size_t)bh * Nq;
-    koff = (size_t)bh * Nk * D;
-  }
+  // This head's rows: nq queries at Q / Oh / Lh, NK keys at Kg + hr.ko.
+  const HeadRows hr = head_rows<VARLEN>(bh, Nq, Nk, D, cuq, cuk, H, tq, tk);
+  const int nq = hr.nq, NK = hr.nk;
+  if (q0 >= nq) return;  // past this sequence's rows: the whole workgroup
+  const float* Q = Qg + hr.qo;
+  float* Oh = Og + hr.qo;
+  float* Lh = Lg + hr.so;
+  const size_t koff = hr.ko;
   // This workgroup's keys: [kb, kb + nk) of the head (all of them unless
   // SPLIT); key indices below are relative to kb.
   const int kb = SPLIT ? split * split_len : 0;
