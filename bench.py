@@ -89,9 +89,12 @@ KERNEL_SOURCES_BWD32 = (os.path.join(CSRC, "fa_device.h"), os.path.join(CSRC, "f
 
 def kernel_sources(w: workloads.Workload, op: str = "fwd"):
     """The source files whose code an op's kernels on this workload run
-    (decode and varlen run the forward file's kernels)."""
+    (decode and varlen run the forward file's kernels; decode also depends on
+    the key-range plan of the C ABI source)."""
     if op == "bwd":
         return KERNEL_SOURCES_BWD32 if w.dtype == "fp32" else KERNEL_SOURCES_BWD
+    if op == "decode":
+        return KERNEL_SOURCES + (os.path.join(CSRC, "fa_api.cpp"),)
     return KERNEL_SOURCES
 
 

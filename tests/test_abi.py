@@ -167,7 +167,7 @@ def test_splitkv_workspace_size():
     # one range: the plain forward, no workspace
     assert fa.fa_fwd_splitkv_workspace_size(1, 4, 4, 8192, 128, 1) == 0
     assert fa.fa_fwd_splitkv_workspace_size(1, 4, 4, 60, 128, 0) == 0
-    # automatic count: 4 heads x 1 query tile -> 128 ranges wanted, capped by 8192/256 = 32
+    # automatic count: 4 heads x 1 query tile fill one wave up to 64 ranges; at least 256 keys a range caps it at 32
     assert fa.fa_fwd_splitkv_workspace_size(1, 4, 4, 8192, 128, 0) == 32 * 4 * 4 * 129 * 4
     assert fa.fa_fwd_splitkv_workspace_size(1, 4, 4, 8192, 128, -1) == -1
     assert fa.fa_fwd_splitkv_workspace_size(1, 4, 4, 8192, 128, 1025) == -1
