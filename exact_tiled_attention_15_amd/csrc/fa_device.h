@@ -177,21 +177,22 @@ __device__ __forceinline__ void wait_tile_and_barrier(int later) {
 }
 
 // Number of 1 KB direct-to-LDS loads (both tensors together) that wave
-// `wave` of NW issues per 64-row tile: the 1 KB pieces G = wave, wave + NW,
+// `wave` of NW issues per BC-row tile: the 1 KB pieces G = wave, wave + NW,
 // ... of each tensor's tile.
-template <int D, int NW>
+template <int D, int NW, int BC = 64>
 __device__ __forceinline__ int loads_per_tile(int wave) {
-  constexpr int NG = 64 * D * 2 / 1024;
+  constexpr int NG = BC * D * 2 / 1024;
   return 2 * ((NG - wave + NW - 1) / NW);
 }
 
-// Direct-to-LDS loads of 64-row tile t of two [N, D] tensors (K and V in
-// the forward pass) into `dst` (first tensor) and `dst + 64 D 2` (second):
+// Direct-to-LDS loads of BC-row tile t of two [N, D] tensors (K and V in
+// the forward pass) into `dst` (first tensor) and `dst + BC D 2` (second):
 // this wave's 1 KB pieces G = wave, wave + NW, ... of each.
-template <int D, int NW>
+template <int D, int NW, int BC = 64>
 __device__ __forceinline__ void issue_tile16(const u16* Kh, const u16* Vh, int kbytes, int t,
                                              unsigned char* dst, const Wave16& w) {
-  constexpr int TILEB = 64 * D * 2;
+  static_assert(BC % 16 == 0 && BC * D * 2 % 1024 == 0, "whole 16-row groups and 1 KB pieces");
+  constexpr int TILEB = BC * D * 2;
   constexpr int NG = TILEB / 1024;
   const auto rk = make_rsrc(Kh, kbytes);
   const auto rv = make_rsrc(Vh, kbytes);
@@ -230,11 +231,13 @@ __device__ __forceinline__ u32x4 ks_operand(const unsigned char* ks, const Wave1
   return *(const lds_u32x4*)((const lds_u8*)ks + (base + (n * 64 * D + (kk >> 1) * 1024 - (int)bias)));
 }
 
-// V^T operand of PV MFMA i (output block dt = i / 4, keys 32n + 16hh with
-// n = (i / 2) % 2, hh = i % 2), from two transposing 64-bit reads.
-template <int D>
+// V^T operand of PV MFMA i of a BC-row tile (output block dt = i / (BC/16),
+// keys 16 (i % (BC/16)), i.e. 32n + 16hh), from two transposing 64-bit reads.
+template <int D, int BC = 64>
 __device__ __forceinline__ u32x4 vt_operand(const unsigned char* vs, const Wave16& w, int i) {
-  const int dt = i >> 2, n = (i >> 1) & 1, hh = i & 1;
+  static_assert(BC == 32 || BC == 64, "one or two 32-key blocks");
+  constexpr int KSH = BC == 64 ? 2 : 1;  // log2 of the 16-key steps per tile
+  const int dt = i >> KSH, n = (i >> 1) & (BC / 32 - 1), hh = i & 1;
   const unsigned bias = lds_bias(vs);
   const int off = (2 * n + hh) * (32 * D) + dt * 1024 - (int)bias;
   const int b0 = bias ? w.vb_hi[0] : w.vb_lo[0], b1 = bias ? w.vb_hi[1] : w.vb_lo[1];

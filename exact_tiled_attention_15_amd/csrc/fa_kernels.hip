@@ -51,12 +51,14 @@ constexpr int kThreads = 256;                     // 4 waves of 64 (fp32 kernel)
 constexpr int kBR = 128;                          // query rows per workgroup (fp32 kernel)
 
 // 16-bit kernel shape: a workgroup of waves16<D>() waves owns 32 query rows
-// per wave and streams 64-key K/V tiles through an LDS ring of stages16<D>()
-// stages.  D <= 128: 8 waves (256 rows, two waves per SIMD) and 4 stages
-// (three tiles in flight while one is consumed).  D = 256: the Q fragment
-// and fp32 O of 32 rows take more than half of a SIMD's registers, and a
-// 64-key K+V stage takes 64 KB, so 4 waves (128 rows, one wave per SIMD) and
-// 2 stages (one tile in flight).
+// per wave and streams K/V tiles of bc16<D>() keys through a 4-stage LDS ring
+// (three tiles in flight while one is consumed; each stage holds a K tile and
+// a V tile, 32 KB).  D <= 128: 8 waves (256 rows, two waves per SIMD) and
+// 64-key tiles.  D = 256: the Q fragment and fp32 O of 32 rows take more than
+// half of a SIMD's registers, so 4 waves (128 rows, one wave per SIMD), and
+// 32-key tiles, so that the ring still holds four stages in 128 KB (with two
+// 64-key stages, one tile in flight left the loads' latency exposed).  Either
+// way a tile is 32 MFMAs per wave.
 #ifndef FA_WAVES16
 #define FA_WAVES16 8
 #endif
@@ -64,9 +66,17 @@ template <int D>
 constexpr int waves16() {
   return D == 256 ? 4 : FA_WAVES16;
 }
+// Software pipelining (step16p) pays only where a SIMD runs one wave: at
+// D <= 128 the two waves of a SIMD already overlap one's softmax with the
+// other's MFMAs, and the fixed interleave of step16p measured slower there
+// (6% at D = 128, 22% at D = 64), while at D = 256 it gains 9%.
 template <int D>
-constexpr int stages16() {
-  return D == 256 ? 2 : 4;
+constexpr bool pipe16() {
+  return waves16<D>() == 4;
+}
+template <int D>
+constexpr int bc16() {
+  return D == 256 ? 32 : 64;
 }
 
 // One K/V tile of the 16-bit kernel (stage `src`).  Tile j is complete in
@@ -79,51 +89,42 @@ constexpr int stages16() {
 // online-softmax update and O^T += V^T P^T.  `src` and `dst` are distinct
 // __shared__ arrays, so the compiler knows the loads in flight never alias
 // the operand reads.
-// With a 2-stage ring (D = 256) the order is simpler: wait for tile j itself
-// (every wave has then also finished tile j-1), start tile j+1 into `dst`
-// (tile j-1's stage), then read and compute.
 template <int DT, int D, bool CAUSAL>
 __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes, int j, int nt,
                                        const unsigned char* src, unsigned char* dst,
                                        const Wave16& w, const u32x4 (&qf)[D / 16],
                                        f32x16 (&oacc)[D / 32], float& mref, float& l, float sl2) {
-  constexpr int NW = waves16<D>(), ST = stages16<D>();
-  constexpr int BC = 64;
+  constexpr int NW = waves16<D>(), BC = bc16<D>();
   constexpr int TILEB = BC * D * 2;
   constexpr int NKK = D / 16, NDT = D / 32;
+  constexpr int NB = BC / 32;  // 32-key score blocks per tile
   // mref is raised only when a tile's row max exceeds it by more than kTau
   // (log2 units), so P = exp2(t - mref) stays below 2^kTau; O and l always
   // share mref, so O / l and mref + log2(l) are exact whatever mref is.
   constexpr float kTau = 8.0f;
   // S^T = K Q^T.  The K operands are read kPre MFMAs ahead of their use
-  // (LDS latency, not bandwidth, bounds these reads).
-  constexpr int NQK = 2 * NKK, kPre = NKK;
+  // (LDS latency, not bandwidth, bounds these reads); kPre also bounds the
+  // LDS reads left in flight at the barrier (a 4-bit counter field).
+  constexpr int NQK = NB * NKK, kPre = NKK < 8 ? NKK : 8;
 
   const int k0 = j * BC;
   const bool mine = k0 < w.wkend;
   const unsigned char* ks = src;
   const unsigned char* vs = src + TILEB;
   u32x4 ka[NQK];
-  if constexpr (ST == 4) {
-    if (mine) {
+  if (mine) {
 #pragma unroll
-      for (int i = 0; i < kPre; ++i) ka[i] = ks_operand<D>(ks, w, i);
-    }
-    // Loads complete in order: only tile j+2's may still be in flight; the
-    // kPre reads just issued may be too (older LDS reads have completed).
-    wait_tile_and_barrier<kPre>(j + 2 < nt ? loads_per_tile<D, NW>(w.wave) : 0);
-    if (j + 3 < nt) issue_tile16<D, NW>(Kh, Vh, kbytes, j + 3, dst, w);
-  } else {
-    wait_tile_and_barrier(0);
-    if (j + 1 < nt) issue_tile16<D, NW>(Kh, Vh, kbytes, j + 1, dst, w);
-    if (mine) {
-#pragma unroll
-      for (int i = 0; i < kPre; ++i) ka[i] = ks_operand<D>(ks, w, i);
-    }
+    for (int i = 0; i < kPre; ++i) ka[i] = ks_operand<D>(ks, w, i);
   }
+  // Loads complete in order: only tile j+2's may still be in flight; the
+  // kPre reads just issued may be too (older LDS reads have completed).
+  wait_tile_and_barrier<kPre>(j + 2 < nt ? loads_per_tile<D, NW, BC>(w.wave) : 0);
+  if (j + 3 < nt) issue_tile16<D, NW, BC>(Kh, Vh, kbytes, j + 3, dst, w);
 
   if (mine) {
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+    f32x16 s[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) s[n] = f32x16{};
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       if (i + kPre < NQK) ka[i + kPre] = ks_operand<D>(ks, w, i + kPre);
@@ -131,16 +132,17 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
     }
     // The first V^T operands of the PV are read now, so that the softmax
     // hides their latency (at D = 64 the PV is short, and fewer pay off).
-    constexpr int NPV = 4 * NDT, vPre = D == 128 ? 8 : 4;
+    constexpr int KS = BC / 16;  // 16-key PV steps per output block
+    constexpr int NPV = KS * NDT, vPre = D == 128 ? 8 : 4;
     u32x4 va[NPV];
 #pragma unroll
-    for (int i = 0; i < vPre; ++i) va[i] = vt_operand<D>(vs, w, i);
+    for (int i = 0; i < vPre; ++i) va[i] = vt_operand<D, BC>(vs, w, i);
     __builtin_amdgcn_sched_barrier(0);
     // Mask (diagonal and tail tiles only): key = k0 + 4*hf + off(n, r).
     if (k0 + BC - 1 > w.wklim) {
       const int lim = w.klim - (k0 + 4 * w.hf);
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
+      for (int n = 0; n < NB; ++n)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           s[n][r] = (32 * n + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[n][r];
@@ -148,7 +150,7 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
     // Row max of the raw scores (scale > 0 commutes with max).
     float mx = s[0][0];
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
+    for (int n = 0; n < NB; ++n)
 #pragma unroll
       for (int r = (n == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[n][r]);
     // Half-row max in the scaled log2 domain: a row's max exceeds mref + kTau
@@ -164,12 +166,12 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
       mref = mnew;
     }
     const float nm = -mref;
-    u32x4 pf[2][2];
+    u32x4 pf[NB][2];
     // l sums the fp32 P (its rounding to 16 bits would leave a relative
     // error of up to 2^-9 in the LSE of rows that see few keys).
     float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
+    for (int n = 0; n < NB; ++n)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -184,9 +186,115 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
     // O^T += V^T P^T, V^T operands read vPre MFMAs ahead.
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
-      if (i + vPre < NPV) va[i + vPre] = vt_operand<D>(vs, w, i + vPre);
-      oacc[i >> 2] = mfma_32x32x16<DT>(va[i], pf[(i >> 1) & 1][i & 1], oacc[i >> 2]);
+      if (i + vPre < NPV) va[i + vPre] = vt_operand<D, BC>(vs, w, i + vPre);
+      const int g16 = i % KS;
+      oacc[i / KS] = mfma_32x32x16<DT>(va[i], pf[g16 >> 1][g16 & 1], oacc[i / KS]);
     }
+  }
+}
+
+// Software-pipelined step j of the 16-bit kernel (used at D = 256, where one
+// wave per SIMD leaves no other wave to fill the matrix core while a wave
+// runs its softmax; see pipe16).  On entry `s` holds the raw scores S(j) of
+// tile j, computed by the previous step; the step meets the other waves
+// (tile j+1 is then complete, and every wave is done with stage `dst`, tile
+// j-1's), starts the loads of tile j+3 into `dst`, and then runs the softmax
+// of S(j) with the score MFMAs of tile j+1 (from stage `nxt`) interleaved
+// into it, so that the exponentials execute while the matrix core works,
+// and last O^T += V^T P^T from stage `cur`.  On return `s` holds S(j+1).
+// The sched_barrier after each MFMA and its softmax units fixes that order
+// (left to the scheduler, the step measured 5% slower).
+template <int DT, int D, bool CAUSAL>
+__device__ __forceinline__ void step16p(const u16* Kh, const u16* Vh, int kbytes, int j, int nt,
+                                        const unsigned char* cur, const unsigned char* nxt, unsigned char* dst,
+                                        const Wave16& w, const u32x4 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
+                                        f32x16 (&s)[bc16<D>() / 32], float& mref, float& l, float sl2) {
+  constexpr int NW = waves16<D>(), BC = bc16<D>();
+  constexpr int TILEB = BC * D * 2;
+  constexpr int NKK = D / 16, NDT = D / 32, NB = BC / 32, KS = BC / 16;
+  constexpr int NQK = NB * NKK, NPV = KS * NDT;
+  constexpr int NU = 4 * KS;  // units of softmax work: one pair of P values per lane each
+  static_assert(NQK % NU == 0 || NU % NQK == 0, "units spread evenly over the score MFMAs");
+  constexpr float kTau = 8.0f;  // as in tile16
+  constexpr int kPre = 4, vPre = 4;
+
+  wait_tile_and_barrier(j + 2 < nt ? loads_per_tile<D, NW, BC>(w.wave) : 0);
+  if (j + 3 < nt) issue_tile16<D, NW, BC>(Kh, Vh, kbytes, j + 3, dst, w);
+  const int k0 = j * BC;
+  // The wave's last tile also scores stage `nxt` (stale data when tile j+1
+  // is not needed or does not exist: the result is never used), which keeps
+  // one path through the step.
+  if (k0 < w.wkend) {
+    const unsigned char* vs = cur + TILEB;
+    u32x4 ka[NQK];
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) ka[i] = ks_operand<D>(nxt, w, i);
+    u32x4 va[NPV];
+#pragma unroll
+    for (int i = 0; i < vPre; ++i) va[i] = vt_operand<D, BC>(vs, w, (i % NDT) * KS + i / NDT);
+
+    // Mask (diagonal and tail tiles only): key = k0 + 4*hf + off(n, r).
+    if (k0 + BC - 1 > w.wklim) {
+      const int lim = w.klim - (k0 + 4 * w.hf);
+#pragma unroll
+      for (int n = 0; n < NB; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[n][r] = (32 * n + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[n][r];
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int r = (n == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[n][r]);
+    mx *= sl2;
+    if (__builtin_amdgcn_ballot_w64(mx > mref + kTau)) {
+      const float mnew = fmaxf(mref, pair_max(mx));
+      const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+      mref = mnew;
+    }
+    const float nm = -mref;
+    u32x4 pf[NB][2];
+    float ls0 = 0.f, ls1 = 0.f;
+    f32x16 sn[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) sn[n] = f32x16{};
+    __builtin_amdgcn_sched_barrier(0);
+    // S(j+1) = K Q^T, with the units of the softmax of S(j) spread evenly
+    // behind its MFMAs; unit u: P values 2q, 2q+1 of 16-key step g = u / 4
+    // (block n = g / 2, half hh = g % 2), q = u % 4.
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      if (i + kPre < NQK) ka[i + kPre] = ks_operand<D>(nxt, w, i + kPre);
+      sn[i / NKK] = mfma_32x32x16<DT>(ka[i], qf[i % NKK], sn[i / NKK]);
+      // Units [u0, u1) follow MFMA i.
+      const int u0 = (i * NU) / NQK, u1 = ((i + 1) * NU) / NQK;
+#pragma unroll
+      for (int u = u0; u < u1; ++u) {
+        const int g = u >> 2, n = g >> 1, hh = g & 1, q = u & 3;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[n][8 * hh + 2 * q], sl2, nm));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[n][8 * hh + 2 * q + 1], sl2, nm));
+        pf[n][hh][q] = pack2<DT>(p0, p1);
+        ls0 += p0;
+        ls1 += p1;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l += ls0 + ls1;
+    // O^T += V^T P^T, 16-key step major (consecutive MFMAs use different
+    // accumulators), V^T operands read vPre MFMAs ahead.
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      const int ip = i + vPre;
+      if (ip < NPV) va[ip] = vt_operand<D, BC>(vs, w, (ip % NDT) * KS + ip / NDT);
+      const int g = i / NDT, dt = i % NDT;
+      oacc[dt] = mfma_32x32x16<DT>(va[i], pf[g >> 1][g & 1], oacc[dt]);
+    }
+#pragma unroll
+    for (int n = 0; n < NB; ++n) s[n] = sn[n];
   }
 }
 
@@ -239,20 +347,19 @@ __global__ __launch_bounds__(64 * waves16<D>(), 1) void fa_fwd_16(const u16* __r
                                                            float* __restrict__ Po, float* __restrict__ Pl,
                                                            const int* __restrict__ cuq, const int* __restrict__ cuk,
                                                            int H, int tq, int tk) {
-  constexpr int BC = 64;
+  constexpr int BC = bc16<D>();          // keys per tile
   constexpr int ROWB = D * 2;             // bytes per row
   constexpr int TILEB = BC * ROWB;        // bytes per K (or V) tile
   constexpr int NKK = D / 16;             // MFMA steps over the head dimension
   constexpr int NDT = D / 32;             // 32-wide output column tiles
-  constexpr int NW = waves16<D>(), ST = stages16<D>();
+  constexpr int NW = waves16<D>();
   constexpr int BR = 32 * NW;              // query rows per workgroup
 
-  // The LDS ring: tile j lives in stage j % ST (a K tile followed by a V
-  // tile); stages 2 and 3 exist only in the 4-stage ring.
+  // The LDS ring: tile j lives in stage j % 4 (a K tile followed by a V tile).
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * TILEB];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage2[ST == 4 ? 2 * TILEB : 1024];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage3[ST == 4 ? 2 * TILEB : 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage2[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage3[2 * TILEB];
 
   Wave16 w;
   const int tid = threadIdx.x;
@@ -300,31 +407,40 @@ __global__ __launch_bounds__(64 * waves16<D>(), 1) void fa_fwd_16(const u16* __r
       qf[kk] = __builtin_amdgcn_raw_buffer_load_b128(rQ, (32 * w.wave + w.l32) * ROWB + (16 * kk + 8 * w.hf) * 2,
                                                      q0 * ROWB, 0);
   }
-  // Tiles 0..2 into stages 0..2 (tile 0 only with two stages).
-  if ((!SPLIT && !VARLEN) || nt > 0) issue_tile16<D, NW>(Kh, Vh, kbytes, 0, stage0, w);
-  if constexpr (ST == 4) {
-    if (nt > 1) issue_tile16<D, NW>(Kh, Vh, kbytes, 1, stage1, w);
-    if (nt > 2) issue_tile16<D, NW>(Kh, Vh, kbytes, 2, stage2, w);
-  }
+  // Tiles 0..2 into stages 0..2.
+  if ((!SPLIT && !VARLEN) || nt > 0) issue_tile16<D, NW, BC>(Kh, Vh, kbytes, 0, stage0, w);
+  if (nt > 1) issue_tile16<D, NW, BC>(Kh, Vh, kbytes, 1, stage1, w);
+  if (nt > 2) issue_tile16<D, NW, BC>(Kh, Vh, kbytes, 2, stage2, w);
 
   float mref = kMinit, l = 0.f;
   f32x16 oacc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
 
-  if constexpr (ST == 4) {
-    // Tile 0 must be complete before tile16(0) reads its first K operands.
-    wait_tile_and_barrier(nt > 2 ? loads_per_tile<D, NW>(w.wave) : 0);
+  // Tile 0 must be complete before its first K operands are read.
+  wait_tile_and_barrier(nt > 2 ? loads_per_tile<D, NW, BC>(w.wave) : 0);
+  if constexpr (pipe16<D>()) {
+    // Pipelined: S(0) first, then each step finishes tile j and scores j+1.
+    f32x16 s[BC / 32];
+#pragma unroll
+    for (int n = 0; n < BC / 32; ++n) s[n] = f32x16{};
+    if (0 < w.wkend) {
+#pragma unroll
+      for (int i = 0; i < (BC / 32) * NKK; ++i)
+        s[i / NKK] = mfma_32x32x16<DT>(ks_operand<D>(stage0, w, i), qf[i % NKK], s[i / NKK]);
+    }
+    for (int j = 0; j < nt; j += 4) {
+      step16p<DT, D, CAUSAL>(Kh, Vh, kbytes, j, nt, stage0, stage1, stage3, w, qf, oacc, s, mref, l, sl2);
+      if (j + 1 < nt) step16p<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 1, nt, stage1, stage2, stage0, w, qf, oacc, s, mref, l, sl2);
+      if (j + 2 < nt) step16p<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 2, nt, stage2, stage3, stage1, w, qf, oacc, s, mref, l, sl2);
+      if (j + 3 < nt) step16p<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 3, nt, stage3, stage0, stage2, w, qf, oacc, s, mref, l, sl2);
+    }
+  } else {
     for (int j = 0; j < nt; j += 4) {
       tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j, nt, stage0, stage3, w, qf, oacc, mref, l, sl2);
       if (j + 1 < nt) tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 1, nt, stage1, stage0, w, qf, oacc, mref, l, sl2);
       if (j + 2 < nt) tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 2, nt, stage2, stage1, w, qf, oacc, mref, l, sl2);
       if (j + 3 < nt) tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 3, nt, stage3, stage2, w, qf, oacc, mref, l, sl2);
-    }
-  } else {
-    for (int j = 0; j < nt; j += 2) {
-      tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j, nt, stage0, stage1, w, qf, oacc, mref, l, sl2);
-      if (j + 1 < nt) tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 1, nt, stage1, stage0, w, qf, oacc, mref, l, sl2);
     }
   }
 
