@@ -53,11 +53,28 @@ def test_parity_small_grid(dt, D, causal, Nq, Nk):
     compare_full(w, cpu, o, l, "grid")
 
 
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,Nq,Nk", [(1, 3, 300, 700), (2, 2, 1, 129), (1, 256, 130, 300)])
+def test_parity_fp32_grid_sizes(D, causal, B, H, Nq, Nk):
+    # The fp32 forward picks its workgroup shape from the grid: with at most
+    # as many 128-row workgroups as the 256 CUs (B*H*ceil(Nq/128) <= 256: the
+    # first two shapes) 32-row workgroups split each 128-key tile over their
+    # four waves and merge the waves' partial results at the end; otherwise
+    # (the third shape, 512 workgroups) each wave owns 32 rows of a 128-row
+    # tile.  Both with ragged Q and K tails.
+    w = workloads.Workload(f"fp32grid_d{D}_{'c' if causal else 'n'}_b{B}h{H}_{Nq}x{Nk}", B, H, Nq, Nk, D, "fp32",
+                           causal, 3200 + D + Nq)
+    cpu, gpu = _case(w)
+    o, l = run_gpu(*gpu, w.causal)
+    compare_full(w, cpu, o, l, "fp32-grid")
+
+
 @pytest.mark.parametrize("dt", ["bf16", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("Nq,Nk", [(300, 300), (257, 517), (130, 70), (1, 200)])
 def test_parity_d256(dt, causal, Nq, Nk):
-    # head dimension 256: 4 waves per workgroup and a 2-stage ring
+    # head dimension 256: 4 waves per workgroup, 32-key tiles, pipelined steps
     w = workloads.Workload(f"d256_{dt}_{'c' if causal else 'n'}_{Nq}x{Nk}", 2, 2, Nq, Nk, 256, dt, causal,
                            2560 + Nq + Nk)
     cpu, gpu = _case(w)
