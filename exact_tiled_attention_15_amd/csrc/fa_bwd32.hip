@@ -33,6 +33,7 @@ namespace {
 
 constexpr float kLog2e32 = 1.4426950408889634074f;
 constexpr int kThreads32 = 256;  // 4 waves
+constexpr int64_t kNumCUs32 = 256;  // compute units of the MI355X
 
 __device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -113,10 +114,37 @@ __device__ __forceinline__ void store_row32(const f32x16 (&acc)[D / 32], float m
                                                          acc[dt][4 * g + 2] * mul, acc[dt][4 * g + 3] * mul};
 }
 
+// KS mode of both kernels: the four waves hold partial sums of the same 32
+// rows; add waves 1-3's into wave 0's through LDS word
+// ((w NDT + dt) 16 + r) 64 + lane (`x` holds 4 D/32 16 64 floats).  Every
+// wave must call it (it contains barriers); the result is in wave 0.
+template <int D>
+__device__ __forceinline__ void sum_over_waves(f32x16 (&acc)[D / 32], float* x, int wave, int lane) {
+  constexpr int NDT = D / 32;
+  __syncthreads();
+  if (wave != 0) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[((wave * NDT + dt) * 16 + r) * 64 + lane] = acc[dt][r];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w2 = 1; w2 < 4; ++w2)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] += x[((w2 * NDT + dt) * 16 + r) * 64 + lane];
+  }
+}
+
 // ---------------------------------------------------------------------------
-// dQ: 4 waves x 32 query rows per workgroup.
+// dQ: 4 waves x 32 query rows per workgroup.  KS (grids with at most one
+// 128-row workgroup per CU): 32 query rows per workgroup, 128-key tiles, wave
+// w takes keys [32w, 32w + 32) of each and the waves' partial dQ are summed.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool KS = false>
 __global__ __launch_bounds__(kThreads32, 1) void bwd32_dq(const float* __restrict__ Qg, const float* __restrict__ Kg,
                                                           const float* __restrict__ Vg, const float* __restrict__ dOg,
                                                           const float* __restrict__ lse2g,
@@ -124,10 +152,13 @@ __global__ __launch_bounds__(kThreads32, 1) void bwd32_dq(const float* __restric
                                                           int BH, int Nq, int Nk, int nqt, float sl2, float scale,
                                                           const int* __restrict__ cuq, const int* __restrict__ cuk,
                                                           int H, int tq, int tk) {
-  constexpr int BR = 128, BC = D <= 64 ? 64 : 32, NSUB = BC / 32, STR = D + 4, ST = BC * STR, NDT = D / 32;
+  static_assert(!(KS && VARLEN), "the key split runs on dense inputs only");
+  constexpr int BR = KS ? 32 : 128, BC = KS ? 128 : D <= 64 ? 64 : 32, NSUB = KS ? 1 : BC / 32;
+  constexpr int STR = D + 4, ST = BC * STR, NDT = D / 32;
+  constexpr int NSTG = (KS && D == 128) ? 1 : 2;  // LDS stages (a 128-key D = 128 stage takes 135 KB)
   constexpr int CPT = BC * D / 4 / kThreads32;  // 16-byte chunks per thread per tensor
   static_assert(CPT >= 1, "tile shape");
-  __shared__ __attribute__((aligned(16))) float smem[2 * 2 * ST];
+  __shared__ __attribute__((aligned(16))) float smem[NSTG * 2 * ST];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, l32 = lane & 31;
@@ -141,7 +172,8 @@ __global__ __launch_bounds__(kThreads32, 1) void bwd32_dq(const float* __restric
   const float* V = Vg + hr.ko;
   const int kend = CAUSAL ? min(nk, min(q0 + BR, nq)) : nk;
   const int nt = (kend + BC - 1) / BC;
-  const int wq0 = q0 + 32 * wave;
+  const int wq0 = KS ? q0 : q0 + 32 * wave;
+  const int kw = KS ? 32 * wave : 0;  // this wave's first key within a tile
   const int myq = wq0 + l32;
   const int wkend = CAUSAL ? min(kend, wq0 + 32) : kend;
 
@@ -182,17 +214,19 @@ __global__ __launch_bounds__(kThreads32, 1) void bwd32_dq(const float* __restric
 
   if (nt > 0) load_tile(0);
   for (int j = 0; j < nt; ++j) {
-    // stage j&1 was last read in step j-2, which every wave finished before
-    // step j-1's barrier
-    const int stage = j & 1;
+    // two stages: stage j&1 was last read in step j-2, which every wave
+    // finished before step j-1's barrier; one stage: wait for every wave
+    const int stage = NSTG == 2 ? (j & 1) : 0;
+    if (NSTG == 1 && j > 0) __syncthreads();
     store_tile(stage);
     __syncthreads();
     if (j + 1 < nt) load_tile(j + 1);
-    const int k0 = j * BC;
+    const int k0 = j * BC + kw;  // this wave's first key of the tile
     if (k0 >= wkend) continue;
-    const float* ks = smem + stage * 2 * ST;
+    const float* ks = smem + stage * 2 * ST + kw * STR;
     const float* vs = ks + ST;
-    const bool need_mask = k0 + BC > nk || (CAUSAL && k0 + BC - 1 > wq0);
+    constexpr int BCW = 32 * NSUB;  // keys of the tile this wave attends to
+    const bool need_mask = k0 + BCW > nk || (CAUSAL && k0 + BCW - 1 > wq0);
 #pragma unroll
     for (int n = 0; n < NSUB; ++n) {
       // lane: query myq, keys k0 + 32 n + 8 (r/4) + 4 hf + r%4
@@ -211,13 +245,19 @@ __global__ __launch_bounds__(kThreads32, 1) void bwd32_dq(const float* __restric
       acc_transposed<D, STR>(acc, ks, n, l32, hf, ds);  // dQ^T += K^T dS^T
     }
   }
+  if constexpr (KS) {
+    sum_over_waves<D>(acc, smem, wave, lane);
+    if (wave != 0) return;
+  }
   if (myq < nq) store_row32<D>(acc, scale, dQg + hr.qo + (size_t)myq * D, hf);
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV: 4 waves x 32 keys per workgroup.
+// dK / dV: 4 waves x 32 keys per workgroup.  KS (D <= 64): 32 keys per
+// workgroup, 128-query tiles, wave w takes queries [32w, 32w + 32) of each
+// and the waves' partial dK and dV are summed.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool KS = false>
 __global__ __launch_bounds__(kThreads32, 1) void bwd32_dkdv(const float* __restrict__ Qg, const float* __restrict__ Kg,
                                                             const float* __restrict__ Vg,
                                                             const float* __restrict__ dOg,
@@ -226,11 +266,15 @@ __global__ __launch_bounds__(kThreads32, 1) void bwd32_dkdv(const float* __restr
                                                             float* __restrict__ dVg, int BH, int Nq, int Nk,
                                                             float sl2, float scale, const int* __restrict__ cuq,
                                                             const int* __restrict__ cuk, int H, int tq, int tk) {
-  constexpr int BK = 128, BQ = D <= 64 ? 64 : 32, NSUB = BQ / 32, STR = D + 4, ST = BQ * STR, NDT = D / 32;
+  static_assert(!(KS && (VARLEN || D > 64)), "the query split runs on dense inputs up to D = 64");
+  constexpr int BK = KS ? 32 : 128, BQ = KS ? 128 : D <= 64 ? 64 : 32, NSUB = KS ? 1 : BQ / 32;
+  constexpr int STR = D + 4, ST = BQ * STR, NDT = D / 32;
   constexpr int SS = 2 * ST + 2 * BQ;  // floats per stage: Q tile, dO tile, lse2, delta
+  constexpr int NSTG = (KS && D == 128) ? 1 : 2;  // LDS stages (a 128-row D = 128 stage takes 136 KB)
   constexpr int CPT = BQ * D / 4 / kThreads32;
-  static_assert(CPT >= 1, "tile shape");
-  __shared__ __attribute__((aligned(16))) float smem[2 * SS];
+  static_assert(CPT >= 1 && 2 * BQ <= kThreads32, "tile shape");
+  static_assert(!KS || NSTG * SS >= 2 * 4 * NDT * 16 * 64, "room for the sums over waves");
+  __shared__ __attribute__((aligned(16))) float smem[NSTG * SS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, l32 = lane & 31;
@@ -238,7 +282,8 @@ __global__ __launch_bounds__(kThreads32, 1) void bwd32_dkdv(const float* __restr
   // seen by the most queries, so the heaviest workgroups start first.
   const int bh = blockIdx.x % BH, kt = blockIdx.x / BH;
   const int kb0 = kt * BK;
-  const int wk0 = kb0 + 32 * wave;
+  const int wk0 = KS ? kb0 : kb0 + 32 * wave;
+  const int qw = KS ? 32 * wave : 0;  // this wave's first query within a tile
   const int mykey = wk0 + l32;
   const HeadRows hr = head_rows<VARLEN>(bh, Nq, Nk, D, cuq, cuk, H, tq, tk);
   const int nq = hr.nq, nk = hr.nk;
@@ -293,15 +338,17 @@ __global__ __launch_bounds__(kThreads32, 1) void bwd32_dkdv(const float* __restr
 
   if (nt > 0) load_tile(t0);
   for (int j = 0; j < nt; ++j) {
-    const int stage = j & 1;
+    const int stage = NSTG == 2 ? (j & 1) : 0;
+    if (NSTG == 1 && j > 0) __syncthreads();  // every wave is done with the one stage
     store_tile(stage);
     __syncthreads();
     if (j + 1 < nt) load_tile(t0 + j + 1);
-    const int q0 = (t0 + j) * BQ;
-    if (CAUSAL && q0 + BQ - 1 < wk0) continue;  // every query of the tile precedes the wave's keys
-    const float* qs = smem + stage * SS;
+    const int q0 = (t0 + j) * BQ + qw;  // this wave's first query of the tile
+    constexpr int BQW = 32 * NSUB;      // queries of the tile this wave takes
+    if (CAUSAL && q0 + BQW - 1 < wk0) continue;  // every query of the wave's rows precedes its keys
+    const float* qs = smem + stage * SS + qw * STR;
     const float* dos = qs + ST;
-    const float* l2s = qs + 2 * ST;
+    const float* l2s = smem + stage * SS + 2 * ST + qw;
     const float* dls = l2s + BQ;
     const bool need_mask = CAUSAL && q0 < wk0 + 31;
 #pragma unroll
@@ -322,6 +369,11 @@ __global__ __launch_bounds__(kThreads32, 1) void bwd32_dkdv(const float* __restr
       acc_transposed<D, STR>(dk, qs, n, l32, hf, ds);  // dK^T += Q^T dS
     }
   }
+  if constexpr (KS) {
+    sum_over_waves<D>(dk, smem, wave, lane);
+    sum_over_waves<D>(dv, smem + 4 * NDT * 16 * 64, wave, lane);
+    if (wave != 0) return;
+  }
   if (mykey < nk) {
     store_row32<D>(dk, scale, dKg + hr.ko + (size_t)mykey * D, hf);
     store_row32<D>(dv, 1.0f, dVg + hr.ko + (size_t)mykey * D, hf);
@@ -339,19 +391,39 @@ int launch_bwd32(const FaBwdLaunch& a, float sl2, float scale) {
     const int64_t threads = rows * (D / 4);
     hipLaunchKernelGGL((bwd32_prep<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
                        (const float*)a.o, (const float*)a.dout, a.lse, lse2, delta, rows);
+    // At most one 128-row workgroup per CU: the key-split form (four times
+    // the waves), as in the fp32 forward.
     const int nqt = (int)((a.Nq + 127) / 128);
-    if (nqt > 0)
+    const bool ks = !VARLEN && a.BH * nqt <= kNumCUs32;
+    if (nqt > 0 && ks) {
+      if constexpr (!VARLEN)
+        hipLaunchKernelGGL((bwd32_dq<D, CAUSAL, false, true>), dim3((unsigned)(a.BH * ((a.Nq + 31) / 32))),
+                           dim3(kThreads32), 0, st, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                           (const float*)a.dout, (const float*)lse2, (const float*)delta, (float*)a.dq, (int)a.BH,
+                           (int)a.Nq, (int)a.Nk, (int)((a.Nq + 31) / 32), sl2, scale, a.cu_q, a.cu_k, H, tq, tk);
+    } else if (nqt > 0) {
       hipLaunchKernelGGL((bwd32_dq<D, CAUSAL, VARLEN>), dim3((unsigned)(a.BH * nqt)), dim3(kThreads32), 0, st,
                          (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout,
                          (const float*)lse2, (const float*)delta, (float*)a.dq, (int)a.BH, (int)a.Nq, (int)a.Nk,
                          nqt, sl2, scale, a.cu_q, a.cu_k, H, tq, tk);
+    }
   }
   const int nkt = (int)((a.Nk + 127) / 128);
-  if (nkt > 0)
+  // (not at D = 128: staging 128 query rows of Q and dO next to the K, V
+  // fragments and both gradients spills registers)
+  const bool ks = !VARLEN && D <= 64 && a.BH * nkt <= kNumCUs32;
+  if (nkt > 0 && ks) {
+    if constexpr (!VARLEN && D <= 64)
+      hipLaunchKernelGGL((bwd32_dkdv<D, CAUSAL, false, true>), dim3((unsigned)(a.BH * ((a.Nk + 31) / 32))),
+                         dim3(kThreads32), 0, st, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                         (const float*)a.dout, (const float*)lse2, (const float*)delta, (float*)a.dk, (float*)a.dv,
+                         (int)a.BH, (int)a.Nq, (int)a.Nk, sl2, scale, a.cu_q, a.cu_k, H, tq, tk);
+  } else if (nkt > 0) {
     hipLaunchKernelGGL((bwd32_dkdv<D, CAUSAL, VARLEN>), dim3((unsigned)(a.BH * nkt)), dim3(kThreads32), 0, st,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout,
                        (const float*)lse2, (const float*)delta, (float*)a.dk, (float*)a.dv, (int)a.BH, (int)a.Nq,
                        (int)a.Nk, sl2, scale, a.cu_q, a.cu_k, H, tq, tk);
+  }
   return (int)hipGetLastError();
 }
 

@@ -71,6 +71,24 @@ GRID = [(dt, D, causal, Nq, Nk)
         for (Nq, Nk) in ((300, 300), (257, 517), (130, 70))]
 
 
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,Nq,Nk", [(1, 3, 300, 700), (1, 256, 130, 300), (1, 128, 100, 300),
+                                       (1, 128, 300, 100)])
+def test_backward_fp32_grid_sizes(D, causal, B, H, Nq, Nk):
+    # Each fp32 backward kernel picks its workgroup shape from its own grid:
+    # with at most one 128-row workgroup per CU (B*H*ceil(N/128) <= 256, N =
+    # Nq for dQ, Nk for dK/dV) it runs 32-row workgroups whose four waves
+    # split the streamed keys (dQ) or queries (dK/dV, D <= 64) and sum their
+    # partial gradients at the end.  The shapes cover: both split, neither
+    # split, only dQ split, only dK/dV split; with ragged tails.
+    w = workloads.Workload(f"bwd32grid_d{D}_{'c' if causal else 'n'}_h{H}_{Nq}x{Nk}", B, H, Nq, Nk, D, "fp32",
+                           causal, 900 + D + Nq + Nk)
+    log(f"case {w.name}")
+    cpu, dout, grads = _run(w)
+    _compare(w, cpu, dout, grads, tag="fp32-grid")
+
+
 @pytest.mark.parametrize("dt,D,causal,Nq,Nk", GRID)
 def test_backward_parity_grid(dt, D, causal, Nq, Nk):
     w = workloads.Workload(f"bwd_{dt}_d{D}_{'c' if causal else 'n'}_{Nq}x{Nk}", 2, 3, Nq, Nk, D, dt, causal,
