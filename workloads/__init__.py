@@ -100,7 +100,7 @@ WORKLOADS: Dict[str, Workload] = {
            note="bf16 D=128 causal with a ragged tail"),
         # head dimension 256 (the headline's FLOP count at twice the head size)
         _w("x1_bf16_causal_b4h8n4096d256", 4, 8, 4096, 4096, 256, "bf16", True, 10,
-           note="head dimension 256, causal; 4 waves per workgroup, 2-stage ring"),
+           note="head dimension 256, causal; 4 waves per workgroup, 32-key tiles in a 4-stage ring"),
         # decoding against a KV cache (split-KV path; HBM-bound)
         _w("d1_bf16_decode_b8h32q1k32768d128", 8, 32, 1, 32768, 128, "bf16", False, 7,
            note="one new query row per sequence against a 32K-key cache"),
