@@ -11,9 +11,11 @@
 //
 // Work decomposition: one workgroup per (batch*head, Q tile); each wave owns
 // 32 query rows.  16-bit kernel: 8 waves (256 rows), K/V tiles of 64 keys
-// loaded straight from HBM into a 4-stage LDS ring (one barrier per tile).
+// loaded straight from HBM into a 4-stage LDS ring (one barrier per tile);
+// at D = 256, 4 waves (128 rows), 32-key tiles and software-pipelined steps.
 // fp32 kernel: 4 waves (128 rows), K/V staged through registers into a
-// double-buffered LDS stage.
+// double-buffered LDS stage; on grids with at most one such workgroup per CU,
+// 32-row workgroups whose waves split each 128-key tile and merge at the end.
 //
 // Data layout inside a wave (16-bit types): the score tile is computed
 // transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_{bf16,f16}: K (from LDS)
