@@ -69,14 +69,11 @@ template <int D>
 constexpr int waves16() {
   return D == 256 ? 4 : FA_WAVES16;
 }
-// Software pipelining (step16p) pays only where a SIMD runs one wave: at
-// D <= 128 the two waves of a SIMD already overlap one's softmax with the
+// Software pipelining (step16p) pays only where a SIMD runs one wave, i.e.
+// in the 4-wave form (D = 256, and small grids at D <= 128, see dispatch16):
+// with 8 waves the two waves of a SIMD already overlap one's softmax with the
 // other's MFMAs, and the fixed interleave of step16p measured slower there
 // (6% at D = 128, 22% at D = 64), while at D = 256 it gains 9%.
-template <int D>
-constexpr bool pipe16() {
-  return waves16<D>() == 4;
-}
 template <int D>
 constexpr int bc16() {
   return D == 256 ? 32 : 64;
@@ -92,12 +89,12 @@ constexpr int bc16() {
 // online-softmax update and O^T += V^T P^T.  `src` and `dst` are distinct
 // __shared__ arrays, so the compiler knows the loads in flight never alias
 // the operand reads.
-template <int DT, int D, bool CAUSAL>
+template <int DT, int D, bool CAUSAL, int NW = waves16<D>()>
 __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes, int j, int nt,
                                        const unsigned char* src, unsigned char* dst,
                                        const Wave16& w, const u32x4 (&qf)[D / 16],
                                        f32x16 (&oacc)[D / 32], float& mref, float& l, float sl2) {
-  constexpr int NW = waves16<D>(), BC = bc16<D>();
+  constexpr int BC = bc16<D>();
   constexpr int TILEB = BC * D * 2;
   constexpr int NKK = D / 16, NDT = D / 32;
   constexpr int NB = BC / 32;  // 32-key score blocks per tile
@@ -198,7 +195,7 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
 
 // Software-pipelined step j of the 16-bit kernel (used at D = 256, where one
 // wave per SIMD leaves no other wave to fill the matrix core while a wave
-// runs its softmax; see pipe16).  On entry `s` holds the raw scores S(j) of
+// runs its softmax; see the note above waves16/bc16).  On entry `s` holds the raw scores S(j) of
 // tile j, computed by the previous step; the step meets the other waves
 // (tile j+1 is then complete, and every wave is done with stage `dst`, tile
 // j-1's), starts the loads of tile j+3 into `dst`, and then runs the softmax
@@ -207,12 +204,12 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
 // and last O^T += V^T P^T from stage `cur`.  On return `s` holds S(j+1).
 // The sched_barrier after each MFMA and its softmax units fixes that order
 // (left to the scheduler, the step measured 5% slower).
-template <int DT, int D, bool CAUSAL>
+template <int DT, int D, bool CAUSAL, int NW = waves16<D>()>
 __device__ __forceinline__ void step16p(const u16* Kh, const u16* Vh, int kbytes, int j, int nt,
                                         const unsigned char* cur, const unsigned char* nxt, unsigned char* dst,
                                         const Wave16& w, const u32x4 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
                                         f32x16 (&s)[bc16<D>() / 32], float& mref, float& l, float sl2) {
-  constexpr int NW = waves16<D>(), BC = bc16<D>();
+  constexpr int BC = bc16<D>();
   constexpr int TILEB = BC * D * 2;
   constexpr int NKK = D / 16, NDT = D / 32, NB = BC / 32, KS = BC / 16;
   constexpr int NQK = NB * NKK, NPV = KS * NDT;
@@ -340,8 +337,8 @@ __device__ __forceinline__ bool fwd_block(int nqt, int BH, int& bh, int& qt, int
 // and key rows [cuk[b], cuk[b+1]) (offsets clamped into [0, tq] / [0, tk]);
 // BH = B*H, Nq = the longest sequence's query count (sets nqt).  Rows of a
 // sequence without keys get O = 0 and LSE = -inf.
-template <int DT, int D, bool CAUSAL, bool SPLIT = false, bool VARLEN = false>
-__global__ __launch_bounds__(64 * waves16<D>(), 1) void fa_fwd_16(const u16* __restrict__ Qg,
+template <int DT, int D, bool CAUSAL, bool SPLIT = false, bool VARLEN = false, int NW = waves16<D>()>
+__global__ __launch_bounds__(64 * NW, 1) void fa_fwd_16(const u16* __restrict__ Qg,
                                                            const u16* __restrict__ Kg,
                                                            const u16* __restrict__ Vg,
                                                            u16* __restrict__ Og,
@@ -355,7 +352,7 @@ __global__ __launch_bounds__(64 * waves16<D>(), 1) void fa_fwd_16(const u16* __r
   constexpr int TILEB = BC * ROWB;        // bytes per K (or V) tile
   constexpr int NKK = D / 16;             // MFMA steps over the head dimension
   constexpr int NDT = D / 32;             // 32-wide output column tiles
-  constexpr int NW = waves16<D>();
+  static_assert(NW == waves16<D>() || (NW == 4 && !SPLIT && !VARLEN), "4-wave form: plain forward only");
   constexpr int BR = 32 * NW;              // query rows per workgroup
 
   // The LDS ring: tile j lives in stage j % 4 (a K tile followed by a V tile).
@@ -422,7 +419,7 @@ __global__ __launch_bounds__(64 * waves16<D>(), 1) void fa_fwd_16(const u16* __r
 
   // Tile 0 must be complete before its first K operands are read.
   wait_tile_and_barrier(nt > 2 ? loads_per_tile<D, NW, BC>(w.wave) : 0);
-  if constexpr (pipe16<D>()) {
+  if constexpr (NW == 4) {
     // Pipelined: S(0) first, then each step finishes tile j and scores j+1.
     f32x16 s[BC / 32];
 #pragma unroll
@@ -433,17 +430,17 @@ __global__ __launch_bounds__(64 * waves16<D>(), 1) void fa_fwd_16(const u16* __r
         s[i / NKK] = mfma_32x32x16<DT>(ks_operand<D>(stage0, w, i), qf[i % NKK], s[i / NKK]);
     }
     for (int j = 0; j < nt; j += 4) {
-      step16p<DT, D, CAUSAL>(Kh, Vh, kbytes, j, nt, stage0, stage1, stage3, w, qf, oacc, s, mref, l, sl2);
-      if (j + 1 < nt) step16p<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 1, nt, stage1, stage2, stage0, w, qf, oacc, s, mref, l, sl2);
-      if (j + 2 < nt) step16p<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 2, nt, stage2, stage3, stage1, w, qf, oacc, s, mref, l, sl2);
-      if (j + 3 < nt) step16p<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 3, nt, stage3, stage0, stage2, w, qf, oacc, s, mref, l, sl2);
+      step16p<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j, nt, stage0, stage1, stage3, w, qf, oacc, s, mref, l, sl2);
+      if (j + 1 < nt) step16p<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j + 1, nt, stage1, stage2, stage0, w, qf, oacc, s, mref, l, sl2);
+      if (j + 2 < nt) step16p<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j + 2, nt, stage2, stage3, stage1, w, qf, oacc, s, mref, l, sl2);
+      if (j + 3 < nt) step16p<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j + 3, nt, stage3, stage0, stage2, w, qf, oacc, s, mref, l, sl2);
     }
   } else {
     for (int j = 0; j < nt; j += 4) {
-      tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j, nt, stage0, stage3, w, qf, oacc, mref, l, sl2);
-      if (j + 1 < nt) tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 1, nt, stage1, stage0, w, qf, oacc, mref, l, sl2);
-      if (j + 2 < nt) tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 2, nt, stage2, stage1, w, qf, oacc, mref, l, sl2);
-      if (j + 3 < nt) tile16<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 3, nt, stage3, stage2, w, qf, oacc, mref, l, sl2);
+      tile16<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j, nt, stage0, stage3, w, qf, oacc, mref, l, sl2);
+      if (j + 1 < nt) tile16<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j + 1, nt, stage1, stage0, w, qf, oacc, mref, l, sl2);
+      if (j + 2 < nt) tile16<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j + 2, nt, stage2, stage1, w, qf, oacc, mref, l, sl2);
+      if (j + 3 < nt) tile16<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j + 3, nt, stage3, stage2, w, qf, oacc, mref, l, sl2);
     }
   }
 
@@ -746,14 +743,14 @@ void launch32(const FaLaunch& a, float sl2, int nsplit, int split_len, float* Po
                      (int)a.total_k);
 }
 
-template <int DT, int D, bool CAUSAL, bool SPLIT, bool VARLEN = false>
+template <int DT, int D, bool CAUSAL, bool SPLIT, bool VARLEN = false, int NW = waves16<D>()>
 void launch16(const FaLaunch& a, float sl2, int nsplit, int split_len, float* Po, float* Pl) {
-  constexpr int BR = 32 * waves16<D>();
+  constexpr int BR = 32 * NW;
   const int nqt = (int)((a.Nq + BR - 1) / BR);
   // VARLEN maps block ids per XCD (8 of them): round B*H up to a multiple of 8
   const int64_t heads = VARLEN ? (a.BH + 7) / 8 * 8 : a.BH;
-  const dim3 grid((unsigned)(heads * nqt * nsplit)), block(64 * waves16<D>());
-  hipLaunchKernelGGL((fa_fwd_16<DT, D, CAUSAL, SPLIT, VARLEN>), grid, block, 0, (hipStream_t)a.stream,
+  const dim3 grid((unsigned)(heads * nqt * nsplit)), block(64 * NW);
+  hipLaunchKernelGGL((fa_fwd_16<DT, D, CAUSAL, SPLIT, VARLEN, NW>), grid, block, 0, (hipStream_t)a.stream,
                      (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (u16*)a.o, a.lse, (int)a.BH, (int)a.Nq,
                      (int)a.Nk, nqt, sl2, split_len, Po, Pl, a.cu_q, a.cu_k, (int)a.H, (int)a.total_q,
                      (int)a.total_k);
@@ -761,10 +758,19 @@ void launch16(const FaLaunch& a, float sl2, int nsplit, int split_len, float* Po
 
 template <int DT, int D>
 int dispatch16(const FaLaunch& a, float sl2) {
-  if (a.causal)
+  // Fewer 8-wave workgroups than CUs: the 4-wave form (128 rows, one wave
+  // per SIMD, pipelined steps) doubles the workgroups.
+  constexpr int NW8 = waves16<D>();
+  if (NW8 == 8 && a.BH * ((a.Nq + 32 * NW8 - 1) / (32 * NW8)) < kNumCUs) {
+    if (a.causal)
+      launch16<DT, D, true, false, false, 4>(a, sl2, 1, 0, nullptr, nullptr);
+    else
+      launch16<DT, D, false, false, false, 4>(a, sl2, 1, 0, nullptr, nullptr);
+  } else if (a.causal) {
     launch16<DT, D, true, false>(a, sl2, 1, 0, nullptr, nullptr);
-  else
+  } else {
     launch16<DT, D, false, false>(a, sl2, 1, 0, nullptr, nullptr);
+  }
   return (int)hipGetLastError();
 }
 
