@@ -71,6 +71,23 @@ def test_parity_fp32_grid_sizes(D, causal, B, H, Nq, Nk):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "fp16"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,Nq,Nk", [(1, 3, 300, 700), (1, 256, 130, 300)])
+def test_parity_16bit_grid_sizes(dt, D, causal, B, H, Nq, Nk):
+    # The 16-bit forward picks its workgroup from the grid: with fewer
+    # 256-row (8-wave) workgroups than the 256 CUs (B*H*ceil(Nq/256) < 256,
+    # the first shape) it runs 128-row 4-wave workgroups with pipelined
+    # steps; the second shape (256 workgroups) keeps the 8-wave form.  Both
+    # compared element by element, with ragged Q and K tails.
+    w = workloads.Workload(f"g16_{dt}_d{D}_{'c' if causal else 'n'}_h{H}_{Nq}x{Nk}", B, H, Nq, Nk, D, dt, causal,
+                           1600 + D + Nq)
+    cpu, gpu = _case(w)
+    o, l = run_gpu(*gpu, w.causal)
+    compare_full(w, cpu, o, l, "16bit-grid")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("Nq,Nk", [(300, 300), (257, 517), (130, 70), (1, 200)])
 def test_parity_d256(dt, causal, Nq, Nk):
