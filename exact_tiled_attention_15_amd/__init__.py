@@ -14,13 +14,15 @@ import os
 
 __all__ = ["fa_fwd", "fa_fwd_scaled", "fa_fwd_varlen", "forward_varlen", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "forward_splitkv",
            "fa_bwd", "fa_bwd_workspace_size", "backward", "fa_bwd_varlen", "backward_varlen", "fa_status_str", "forward", "load_library", "LIB_PATH",
-           "FA_DTYPE_FP32", "FA_DTYPE_FP16", "FA_DTYPE_BF16", "FA_OK", "FaError",
+           "FA_DTYPE_FP32", "FA_DTYPE_FP16", "FA_DTYPE_BF16", "FA_OK", "FA_DEFAULT_SCALE", "FaError",
            "EXPORTED_SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_DTYPE_FP32, FA_DTYPE_FP16, FA_DTYPE_BF16 = 0, 1, 2
 FA_OK = 0
+# softmax_scale value that makes the C entry points use 1/sqrt(D)
+FA_DEFAULT_SCALE = 0.0
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_scaled", "fa_fwd_varlen", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_bwd",
                     "fa_bwd_workspace_size", "fa_bwd_varlen", "fa_status_str")
 
@@ -142,6 +144,46 @@ def _dtype_code(t) -> int:
     return codes[t.dtype]
 
 
+def _require(name, t, device, dtype=None, shape=None, dim=None):
+    """Raise unless `t` is a contiguous GPU tensor on `device` (and, when
+    given, of `dtype`, exactly `shape`, or `dim` dimensions).  Every tensor
+    reaches the kernels as a raw device address, so these checks run before
+    any C call."""
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}; every tensor must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dimensions, got shape {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _scale_arg(softmax_scale) -> float:
+    return FA_DEFAULT_SCALE if softmax_scale is None else float(softmax_scale)
+
+
+def _stream(device, stream):
+    import torch
+
+    if stream is not None:
+        return stream
+    with torch.cuda.device(device):
+        return torch.cuda.current_stream().cuda_stream
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
 def forward(q, k, v, causal: bool = False, out=None, lse=None, stream=None, softmax_scale=None):
     """Exact attention forward on the GPU.
 
@@ -150,43 +192,33 @@ def forward(q, k, v, causal: bool = False, out=None, lse=None, stream=None, soft
     dtypes only).  Returns
     (O (B, H, Nq, D) in the input dtype, LSE (B, H, Nq) float32).  ``out`` and
     ``lse`` may be given preallocated; ``stream`` defaults to torch's current
-    stream; ``softmax_scale`` (default 1/sqrt(D)) multiplies q.k.
+    stream; ``softmax_scale`` (default 1/sqrt(D), chosen by the C library)
+    multiplies q.k.
     """
     import torch
 
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-        if t.dim() != 4:
-            raise ValueError(f"{name} must be (B, H, N, D)")
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share one dtype")
+    _require("q", q, q.device if isinstance(q, torch.Tensor) else None, dim=4)
+    dev, dt = q.device, q.dtype
     B, H, Nq, D = q.shape
+    _require("k", k, dev, dt, dim=4)
     Nk = k.shape[2]
-    if tuple(k.shape) != (B, H, Nk, D) or tuple(v.shape) != (B, H, Nk, D):
-        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
-    if q.device != k.device or q.device != v.device:
-        raise ValueError("q, k, v must be on one device")
+    _require("k", k, dev, dt, (B, H, Nk, D))
+    _require("v", v, dev, dt, (B, H, Nk, D))
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
-    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 (B, H, Nq) tensor")
-    if stream is None:
-        with torch.cuda.device(q.device):
-            stream = torch.cuda.current_stream().cuda_stream
-    with torch.cuda.device(q.device):
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    _require("out", out, dev, dt, (B, H, Nq, D))
+    _require("lse", lse, dev, torch.float32, (B, H, Nq))
+    code = _dtype_code(q)
+    stream = _stream(dev, stream)
+    with torch.cuda.device(dev):
         if softmax_scale is None:
             rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                        B, H, Nq, Nk, D, bool(causal), _dtype_code(q), stream)
+                        B, H, Nq, Nk, D, bool(causal), code, stream)
         else:
             rc = fa_fwd_scaled(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                               B, H, Nq, Nk, D, softmax_scale, bool(causal), _dtype_code(q), stream)
+                               B, H, Nq, Nk, D, float(softmax_scale), bool(causal), code, stream)
     if rc != FA_OK:
         raise FaError(rc)
     return out, lse
@@ -200,45 +232,37 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, softmax_scale=None, dq
     returned them; dout: the gradient of o (like q).  float32 (D <= 128),
     float16 or bfloat16.
     Returns (dq, dk, dv) in the input dtype.  Output tensors and the
-    workspace (a uint8 device tensor of at least ``fa_bwd_workspace_size``
-    bytes) may be given preallocated.
+    workspace (a device tensor of at least ``fa_bwd_workspace_size`` bytes)
+    may be given preallocated.
     """
     import torch
 
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("dout", dout)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+    _require("q", q, q.device if isinstance(q, torch.Tensor) else None, dim=4)
+    dev, dt = q.device, q.dtype
     B, H, Nq, D = q.shape
+    _require("k", k, dev, dt, dim=4)
     Nk = k.shape[2]
-    if tuple(k.shape) != (B, H, Nk, D) or tuple(v.shape) != (B, H, Nk, D):
-        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
-    for name, t in (("o", o), ("dout", dout)):
-        if t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError(f"{name} must be like q")
-    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32:
-        raise ValueError("lse must be a float32 (B, H, Nq) tensor")
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share one dtype")
+    _require("k", k, dev, dt, (B, H, Nk, D))
+    _require("v", v, dev, dt, (B, H, Nk, D))
+    _require("o", o, dev, dt, (B, H, Nq, D))
+    _require("lse", lse, dev, torch.float32, (B, H, Nq))
+    _require("dout", dout, dev, dt, (B, H, Nq, D))
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous tensor like {name[1:]}")
+    _require("dq", dq, dev, dt, (B, H, Nq, D))
+    _require("dk", dk, dev, dt, (B, H, Nk, D))
+    _require("dv", dv, dev, dt, (B, H, Nk, D))
     need = fa_bwd_workspace_size(B, H, Nq)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    scale = 1.0 / D**0.5 if softmax_scale is None else float(softmax_scale)
-    if stream is None:
-        with torch.cuda.device(q.device):
-            stream = torch.cuda.current_stream().cuda_stream
-    with torch.cuda.device(q.device):
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _require("workspace", workspace, dev)
+    code = _dtype_code(q)
+    stream = _stream(dev, stream)
+    with torch.cuda.device(dev):
         rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                     dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-                    workspace.numel() * workspace.element_size(), B, H, Nq, Nk, D, scale, bool(causal),
-                    _dtype_code(q), stream)
+                    _nbytes(workspace), B, H, Nq, Nk, D, _scale_arg(softmax_scale), bool(causal), code, stream)
     if rc != FA_OK:
         raise FaError(rc)
     return dq, dk, dv
@@ -248,35 +272,47 @@ def forward_splitkv(q, k, v, causal: bool = False, num_splits: int = 0, softmax_
                     workspace=None, stream=None):
     """``forward`` computed with the keys split into ranges (decoding shape:
     few query rows, many keys).  Dtypes and head dimensions as ``forward``.  ``num_splits`` 0 picks
-    the count automatically; ``workspace`` (uint8 device tensor of at least
+    the count automatically; ``workspace`` (a device tensor of at least
     ``fa_fwd_splitkv_workspace_size`` bytes) may be given preallocated."""
     import torch
 
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
-            raise ValueError(f"{name} must be a contiguous (B, H, N, D) GPU tensor")
+    _require("q", q, q.device if isinstance(q, torch.Tensor) else None, dim=4)
+    dev, dt = q.device, q.dtype
     B, H, Nq, D = q.shape
+    _require("k", k, dev, dt, dim=4)
     Nk = k.shape[2]
-    if tuple(k.shape) != (B, H, Nk, D) or tuple(v.shape) != (B, H, Nk, D):
-        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    _require("k", k, dev, dt, (B, H, Nk, D))
+    _require("v", v, dev, dt, (B, H, Nk, D))
     out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
-    need = fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D, num_splits)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev) if lse is None else lse
+    _require("out", out, dev, dt, (B, H, Nq, D))
+    _require("lse", lse, dev, torch.float32, (B, H, Nq))
+    with torch.cuda.device(dev):
+        need = fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D, num_splits)
     if need < 0:
         raise ValueError("invalid sizes or num_splits")
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    scale = 1.0 / D**0.5 if softmax_scale is None else float(softmax_scale)
-    if stream is None:
-        with torch.cuda.device(q.device):
-            stream = torch.cuda.current_stream().cuda_stream
-    with torch.cuda.device(q.device):
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _require("workspace", workspace, dev)
+    code = _dtype_code(q)
+    stream = _stream(dev, stream)
+    with torch.cuda.device(dev):
         rc = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                            workspace.data_ptr(), workspace.numel() * workspace.element_size(), B, H, Nq, Nk,
-                            D, scale, num_splits, bool(causal), _dtype_code(q), stream)
+                            workspace.data_ptr(), _nbytes(workspace), B, H, Nq, Nk, D, _scale_arg(softmax_scale),
+                            num_splits, bool(causal), code, stream)
     if rc != FA_OK:
         raise FaError(rc)
     return out, lse
+
+
+def _check_offsets(cu_seqlens_q, cu_seqlens_k, dev):
+    import torch
+
+    _require("cu_seqlens_q", cu_seqlens_q, dev, torch.int32, dim=1)
+    _require("cu_seqlens_k", cu_seqlens_k, dev, torch.int32, tuple(cu_seqlens_q.shape))
+    if cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must hold B + 1 offsets each")
+    return cu_seqlens_q.numel() - 1
 
 
 def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool = False,
@@ -291,28 +327,24 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causa
     """
     import torch
 
-    for name, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous GPU tensor")
-    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2]:
-        raise ValueError(f"expected q (H, total_q, D), k and v (H, total_k, D); got {tuple(q.shape)} {tuple(k.shape)}")
-    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
-        raise TypeError("cu_seqlens must be int32")
-    if cu_seqlens_q.shape != cu_seqlens_k.shape or cu_seqlens_q.dim() != 1:
-        raise ValueError("cu_seqlens_q and cu_seqlens_k must be (B + 1,)")
+    _require("q", q, q.device if isinstance(q, torch.Tensor) else None, dim=3)
+    dev, dt = q.device, q.dtype
     H, total_q, D = q.shape
+    _require("k", k, dev, dt, dim=3)
     total_k = k.shape[1]
-    B = cu_seqlens_q.shape[0] - 1
+    _require("k", k, dev, dt, (H, total_k, D))
+    _require("v", v, dev, dt, (H, total_k, D))
+    B = _check_offsets(cu_seqlens_q, cu_seqlens_k, dev)
     out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
-    scale = 1.0 / D**0.5 if softmax_scale is None else float(softmax_scale)
-    if stream is None:
-        with torch.cuda.device(q.device):
-            stream = torch.cuda.current_stream().cuda_stream
-    with torch.cuda.device(q.device):
+    lse = torch.empty((H, total_q), dtype=torch.float32, device=dev) if lse is None else lse
+    _require("out", out, dev, dt, (H, total_q, D))
+    _require("lse", lse, dev, torch.float32, (H, total_q))
+    code = _dtype_code(q)
+    stream = _stream(dev, stream)
+    with torch.cuda.device(dev):
         rc = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                            cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, total_q, total_k,
-                           int(max_seqlen_q), D, scale, bool(causal), _dtype_code(q), stream)
+                           int(max_seqlen_q), D, _scale_arg(softmax_scale), bool(causal), code, stream)
     if rc != FA_OK:
         raise FaError(rc)
     return out, lse
@@ -329,47 +361,35 @@ def backward_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqle
     """
     import torch
 
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("dout", dout),
-                    ("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+    _require("q", q, q.device if isinstance(q, torch.Tensor) else None, dim=3)
+    dev, dt = q.device, q.dtype
     H, total_q, D = q.shape
+    _require("k", k, dev, dt, dim=3)
     total_k = k.shape[1]
-    if tuple(k.shape) != (H, total_k, D) or tuple(v.shape) != (H, total_k, D):
-        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
-    for name, t in (("o", o), ("dout", dout)):
-        if t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError(f"{name} must be like q")
-    if lse.shape != (H, total_q) or lse.dtype != torch.float32:
-        raise ValueError("lse must be a float32 (H, total_q) tensor")
-    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
-        raise TypeError("cu_seqlens must be int32")
-    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
-        raise ValueError("cu_seqlens_q and cu_seqlens_k must hold B + 1 offsets each")
-    B = cu_seqlens_q.numel() - 1
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share one dtype")
+    _require("k", k, dev, dt, (H, total_k, D))
+    _require("v", v, dev, dt, (H, total_k, D))
+    _require("o", o, dev, dt, (H, total_q, D))
+    _require("lse", lse, dev, torch.float32, (H, total_q))
+    _require("dout", dout, dev, dt, (H, total_q, D))
+    B = _check_offsets(cu_seqlens_q, cu_seqlens_k, dev)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous tensor like {name[1:]}")
+    _require("dq", dq, dev, dt, (H, total_q, D))
+    _require("dk", dk, dev, dt, (H, total_k, D))
+    _require("dv", dv, dev, dt, (H, total_k, D))
     need = fa_bwd_workspace_size(1, H, total_q)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    scale = 1.0 / D**0.5 if softmax_scale is None else float(softmax_scale)
-    if stream is None:
-        with torch.cuda.device(q.device):
-            stream = torch.cuda.current_stream().cuda_stream
-    with torch.cuda.device(q.device):
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _require("workspace", workspace, dev)
+    code = _dtype_code(q)
+    stream = _stream(dev, stream)
+    with torch.cuda.device(dev):
         rc = fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens_q.data_ptr(),
-                           cu_seqlens_k.data_ptr(), workspace.data_ptr(),
-                           workspace.numel() * workspace.element_size(), B, H, total_q, total_k,
-                           int(max_seqlen_q), int(max_seqlen_k), D, scale, bool(causal), _dtype_code(q), stream)
+                           cu_seqlens_k.data_ptr(), workspace.data_ptr(), _nbytes(workspace), B, H, total_q,
+                           total_k, int(max_seqlen_q), int(max_seqlen_k), D, _scale_arg(softmax_scale),
+                           bool(causal), code, stream)
     if rc != FA_OK:
         raise FaError(rc)
     return dq, dk, dv

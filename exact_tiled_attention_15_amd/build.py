@@ -20,10 +20,12 @@ ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# The kernels never need NaN-preserving max/min (no input-quieting
-# v_max x, x before each v_max of an MFMA result).
-FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fno-honor-nans",
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
+# Kernel units only: the kernels never need NaN-preserving max/min (no
+# input-quieting v_max x, x before each v_max of an MFMA result).  The C ABI
+# unit keeps IEEE comparisons, which its argument checks (NaN scales) rely on.
+KERNEL = ["-fno-honor-nans"]
 # MFMA destinations and accumulators in VGPRs instead of AGPRs.
 VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
@@ -33,11 +35,11 @@ VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 # forward at D = 256 and the backward at D = 32 and 64; the forward at D = 64
 # and the backward at D = 128 lose with it).
 UNITS = [
-    ("fwd", os.path.join(CSRC, "fa_kernels.hip"), []),
-    ("fwd_d256", os.path.join(CSRC, "fa_kernels.hip"), ["-DFA_FWD_D256", *VGPR_MFMA]),
-    ("bwd", os.path.join(CSRC, "fa_bwd.hip"), []),
-    ("bwd_small_d", os.path.join(CSRC, "fa_bwd.hip"), ["-DFA_BWD_SMALL_D", *VGPR_MFMA]),
-    ("bwd32", os.path.join(CSRC, "fa_bwd32.hip"), []),
+    ("fwd", os.path.join(CSRC, "fa_kernels.hip"), [*KERNEL]),
+    ("fwd_d256", os.path.join(CSRC, "fa_kernels.hip"), [*KERNEL, "-DFA_FWD_D256", *VGPR_MFMA]),
+    ("bwd", os.path.join(CSRC, "fa_bwd.hip"), [*KERNEL]),
+    ("bwd_small_d", os.path.join(CSRC, "fa_bwd.hip"), [*KERNEL, "-DFA_BWD_SMALL_D", *VGPR_MFMA]),
+    ("bwd32", os.path.join(CSRC, "fa_bwd32.hip"), [*KERNEL]),
     ("api", os.path.join(CSRC, "fa_api.cpp"), []),
 ]
 

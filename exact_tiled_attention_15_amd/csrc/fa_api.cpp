@@ -1,5 +1,6 @@
 // C ABI of the exact tiled attention forward pass: argument validation
 // (before any HIP call) and dispatch to the gfx950 kernels.
+#include <hip/hip_runtime_api.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -7,6 +8,16 @@
 #include "fa_internal.h"
 
 namespace {
+
+// Compute units of the current device, read on every call: the workgroup
+// shapes and the automatic key-range count are chosen against it.  0 when
+// the runtime cannot say (no device).
+int64_t device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+  return n;
+}
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   if (a < 0 || b < 0) return false;
@@ -60,12 +71,21 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   return FA_OK;
 }
 
-// The kernels work in the log2 domain with scale * log2(e) as one fp32
-// factor; it must be a normal, finite, positive float.
-bool scale_ok(double scale) {
-  if (!(scale > 0.0) || !isfinite(scale)) return false;
-  const float sl2 = (float)(scale * 1.4426950408889634074);
-  return isnormal(sl2) && isfinite(sl2);
+// The softmax scale a call asked for: FA_DEFAULT_SCALE (0) selects
+// 1/sqrt(D), the scale every page divides the scores by; any other value
+// must be finite and positive, and the kernels work in the log2 domain with
+// scale * log2(e) as one fp32 factor, which must be a normal float.  False
+// for an invalid scale.
+bool resolve_scale(double requested, int64_t D, double* scale) {
+  if (requested == FA_DEFAULT_SCALE) {
+    *scale = 1.0 / sqrt((double)(D > 0 ? D : 1));
+    return true;
+  }
+  if (!(requested > 0.0) || !isfinite(requested)) return false;
+  const float sl2 = (float)(requested * 1.4426950408889634074);
+  if (!isnormal(sl2) || !isfinite(sl2)) return false;
+  *scale = requested;
+  return true;
 }
 
 int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
@@ -73,7 +93,8 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_
   bool empty = false;
   const int st = validate(q, k, v, o, lse, B, H, Nq, Nk, D, dtype, &empty);
   if (st != FA_OK) return st;
-  if (scale && !scale_ok(*scale)) return FA_ERR_SCALE;
+  double sc;
+  if (!resolve_scale(scale ? *scale : FA_DEFAULT_SCALE, D, &sc)) return FA_ERR_SCALE;
   if (empty) return FA_OK;
   FaLaunch a;
   a.q = q;
@@ -87,16 +108,18 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_
   a.D = (int)D;
   a.causal = causal != 0;
   a.dtype = dtype;
-  a.scale = scale ? *scale : 1.0 / sqrt((double)D);
+  a.scale = sc;
   a.stream = stream;
   a.workspace = nullptr;
+  a.cus = device_cus();
+  if (a.cus <= 0) return FA_ERR_HIP;
   return fa_launch_fwd(a) == 0 ? FA_OK : FA_ERR_HIP;
 }
 
 constexpr int64_t kMaxSplits = 1024;
 
 // Key ranges of the split-KV forward.  Automatic count: the one that
-// minimises (waves of workgroups over the 256 CUs) x (keys per workgroup),
+// minimises (waves of workgroups over the device's `cus` CUs) x (keys per workgroup),
 // the fewest ranges among equals (each range adds partials to merge), with
 // at least 256 keys a range.  A workgroup takes a 256-row Q tile and, at
 // D = 128, an LDS ring that leaves room for one workgroup per CU, so a
@@ -104,9 +127,7 @@ constexpr int64_t kMaxSplits = 1024;
 // the decoding shapes: 16 ranges of 32 heads, 512 workgroups, ran 6% slower
 // than 8 ranges, 256 workgroups).  Range length: ceil(Nk / splits) rounded
 // up to whole 64-key tiles; `n` is the number of non-empty ranges it gives.
-constexpr int64_t kCUs = 256;
-
-void split_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t splits, int64_t* len, int64_t* n) {
+void split_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t splits, int64_t cus, int64_t* len, int64_t* n) {
   if (splits <= 0) {
     const int64_t wgs = BH * ((Nq + 255) / 256);
     int64_t most = Nk / 256;
@@ -114,7 +135,7 @@ void split_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t splits, int64_t* len
     splits = 1;
     int64_t best = -1;
     for (int64_t s = 1; s <= most && wgs > 0; ++s) {
-      const int64_t waves = (wgs * s + kCUs - 1) / kCUs;
+      const int64_t waves = (wgs * s + cus - 1) / cus;
       const int64_t cost = waves * ((Nk + s - 1) / s);
       if (best < 0 || cost < best) {
         best = cost;
@@ -131,6 +152,14 @@ void split_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t splits, int64_t* len
   *n = Nk > 0 ? (Nk + l - 1) / l : 1;
 }
 
+// The CU count the automatic key-range count is planned against: the current
+// device's, or the MI355X's 256 when no device answers (so that the
+// workspace size can still be asked for without a GPU).
+int64_t plan_cus() {
+  const int64_t c = device_cus();
+  return c > 0 ? c : 256;
+}
+
 }  // namespace
 
 extern "C" int64_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
@@ -140,7 +169,7 @@ extern "C" int64_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t N
   if (!mul_ok(B, H, &BH) || !mul_ok(BH, Nq, &rows) || !mul_ok(rows, D + 1, &per) || !mul_ok(per, 4, &per))
     return -1;
   int64_t len, n;
-  split_plan(BH, Nq, Nk, num_splits, &len, &n);
+  split_plan(BH, Nq, Nk, num_splits, plan_cus(), &len, &n);
   if (n <= 1) return 0;  // one range: the plain forward, no workspace
   int64_t bytes;
   if (!mul_ok(per, n, &bytes)) return -1;
@@ -154,12 +183,14 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
   bool empty = false;
   const int st = validate(q, k, v, o, lse, B, H, Nq, Nk, D, dtype, &empty);
   if (st != FA_OK) return st;
-  if (!scale_ok(softmax_scale)) return FA_ERR_SCALE;
+  double sc;
+  if (!resolve_scale(softmax_scale, D, &sc)) return FA_ERR_SCALE;
   if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_SHAPE;
   if (empty) return FA_OK;
   const int64_t BH = B * H, rows = BH * Nq;
+  const int64_t cus = device_cus();
   int64_t len, n;
-  split_plan(BH, Nq, Nk, num_splits, &len, &n);
+  split_plan(BH, Nq, Nk, num_splits, cus > 0 ? cus : 256, &len, &n);
   FaLaunch a;
   a.q = q;
   a.k = k;
@@ -172,10 +203,11 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
   a.D = (int)D;
   a.causal = causal != 0;
   a.dtype = dtype;
-  a.scale = softmax_scale;
+  a.scale = sc;
   a.stream = stream;
   a.workspace = nullptr;
-  if (n <= 1) return fa_launch_fwd(a) == 0 ? FA_OK : FA_ERR_HIP;
+  a.cus = cus;
+  if (n <= 1) return cus > 0 && fa_launch_fwd(a) == 0 ? FA_OK : FA_ERR_HIP;
   // fp32 partials of one (range, head) are addressed with 32-bit offsets
   if ((Nq + 256) * (D * 4) > INT32_MAX) return FA_ERR_SHAPE;
   int64_t grid;  // Q tiles of 256 rows (16-bit) or 128 (fp32)
@@ -193,6 +225,7 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
       overlaps(workspace, need, lse, lbytes))
     return FA_ERR_ALIAS;
   a.workspace = workspace;
+  if (cus <= 0) return FA_ERR_HIP;
   return fa_launch_fwd_splitkv(a, (int)n, (int)len) == 0 ? FA_OK : FA_ERR_HIP;
 }
 
@@ -216,7 +249,8 @@ extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* 
   if (B < 0 || H < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || D < 0) return FA_ERR_SHAPE;
   if (D != 32 && D != 64 && D != 128 && D != 256) return FA_ERR_HEAD_DIM;
   if (D == 256 && dtype == FA_DTYPE_FP32) return FA_ERR_HEAD_DIM;
-  if (!scale_ok(softmax_scale)) return FA_ERR_SCALE;
+  double sc;
+  if (!resolve_scale(softmax_scale, D, &sc)) return FA_ERR_SCALE;
   int64_t BH, qel, kel;
   if (!mul_ok(B, H, &BH) || !mul_ok(H, total_q, &qel) || !mul_ok(qel, D, &qel) || !mul_ok(H, total_k, &kel) ||
       !mul_ok(kel, D, &kel))
@@ -251,8 +285,10 @@ extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* 
   a.D = (int)D;
   a.causal = causal != 0;
   a.dtype = dtype;
-  a.scale = softmax_scale;
+  a.scale = sc;
   a.stream = stream;
+  a.cus = device_cus();
+  if (a.cus <= 0) return FA_ERR_HIP;
   a.workspace = nullptr;
   a.cu_q = cu_seqlens_q;
   a.cu_k = cu_seqlens_k;
@@ -276,7 +312,8 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || D < 0) return FA_ERR_SHAPE;
   if (D != 32 && D != 64 && D != 128 && D != 256) return FA_ERR_HEAD_DIM;
   if (D == 256 && dtype == FA_DTYPE_FP32) return FA_ERR_HEAD_DIM;
-  if (!scale_ok(softmax_scale)) return FA_ERR_SCALE;
+  double sc;
+  if (!resolve_scale(softmax_scale, D, &sc)) return FA_ERR_SCALE;
   int64_t BH, qel, kel;
   if (!mul_ok(B, H, &BH) || !mul_ok(BH, Nq, &qel) || !mul_ok(qel, D, &qel) || !mul_ok(BH, Nk, &kel) ||
       !mul_ok(kel, D, &kel))
@@ -331,8 +368,10 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   a.D = (int)D;
   a.causal = causal != 0;
   a.dtype = dtype;
-  a.scale = softmax_scale;
+  a.scale = sc;
   a.stream = stream;
+  a.cus = device_cus();
+  if (a.cus <= 0) return FA_ERR_HIP;
   return fa_launch_bwd(a) == 0 ? FA_OK : FA_ERR_HIP;
 }
 
@@ -347,7 +386,8 @@ extern "C" int fa_bwd_varlen(const void* q, const void* k, const void* v, const 
     return FA_ERR_SHAPE;
   if (D != 32 && D != 64 && D != 128 && D != 256) return FA_ERR_HEAD_DIM;
   if (D == 256 && dtype == FA_DTYPE_FP32) return FA_ERR_HEAD_DIM;
-  if (!scale_ok(softmax_scale)) return FA_ERR_SCALE;
+  double sc;
+  if (!resolve_scale(softmax_scale, D, &sc)) return FA_ERR_SCALE;
   int64_t BH, qel, kel;
   if (!mul_ok(B, H, &BH) || !mul_ok(H, total_q, &qel) || !mul_ok(qel, D, &qel) || !mul_ok(H, total_k, &kel) ||
       !mul_ok(kel, D, &kel))
@@ -402,8 +442,10 @@ extern "C" int fa_bwd_varlen(const void* q, const void* k, const void* v, const 
   a.D = (int)D;
   a.causal = causal != 0;
   a.dtype = dtype;
-  a.scale = softmax_scale;
+  a.scale = sc;
   a.stream = stream;
+  a.cus = device_cus();
+  if (a.cus <= 0) return FA_ERR_HIP;
   a.cu_q = cu_seqlens_q;
   a.cu_k = cu_seqlens_k;
   a.H = H;

@@ -559,32 +559,34 @@ int launch_bwd(const FaBwdLaunch& a, float sl2, float scale) {
   if (rows > 0) {
     const int64_t threads = rows * (D / 8);
     const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
-    hipLaunchKernelGGL((bwd_prep<DT, D>), grid, block, 0, st, (const u16*)a.o, (const u16*)a.dout, a.lse, lse2,
-                       delta, rows);
+    int rc = launch_kernel(bwd_prep<DT, D>, grid, block, st, (const u16*)a.o, (const u16*)a.dout, a.lse, lse2,
+                           delta, rows);
+    if (rc != 0) return rc;
     constexpr int NWQ = dq_waves<D>();
     const int nqt = (int)((a.Nq + 32 * NWQ - 1) / (32 * NWQ));
     if (nqt > 0)
-      hipLaunchKernelGGL((bwd_dq<DT, D, CAUSAL, VARLEN>), dim3((unsigned)(a.BH * nqt)), dim3(64 * NWQ), 0, st,
+      rc = launch_kernel(bwd_dq<DT, D, CAUSAL, VARLEN>, dim3((unsigned)(a.BH * nqt)), dim3(64 * NWQ), st,
                          (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, (const float*)lse2,
                          (const float*)delta, (u16*)a.dq, (int)a.BH, (int)a.Nq, (int)a.Nk, nqt, sl2, scale, a.cu_q,
                          a.cu_k, H, tq, tk);
+    if (rc != 0) return rc;
   }
   const int nkt = (int)((a.Nk + 32 * kWavesKV - 1) / (32 * kWavesKV));
   if (nkt > 0) {
     const dim3 grid((unsigned)(a.BH * nkt)), block(64 * kWavesKV);
     auto run = [&](auto kern) {
-      hipLaunchKernelGGL(kern, grid, block, 0, st, (const u16*)a.q, (const u16*)a.k, (const u16*)a.v,
-                         (const u16*)a.dout, (const float*)lse2, (const float*)delta, (u16*)a.dk, (u16*)a.dv,
-                         (int)a.BH, (int)a.Nq, (int)a.Nk, sl2, scale, a.cu_q, a.cu_k, H, tq, tk);
+      return launch_kernel(kern, grid, block, st, (const u16*)a.q, (const u16*)a.k, (const u16*)a.v,
+                           (const u16*)a.dout, (const float*)lse2, (const float*)delta, (u16*)a.dk, (u16*)a.dv,
+                           (int)a.BH, (int)a.Nq, (int)a.Nk, sl2, scale, a.cu_q, a.cu_k, H, tq, tk);
     };
     if constexpr (D == 256) {  // one kernel per gradient: dV, then dK
-      run(bwd_dkdv<DT, D, CAUSAL, 2, VARLEN>);
-      run(bwd_dkdv<DT, D, CAUSAL, 1, VARLEN>);
+      const int rc = run(bwd_dkdv<DT, D, CAUSAL, 2, VARLEN>);
+      return rc != 0 ? rc : run(bwd_dkdv<DT, D, CAUSAL, 1, VARLEN>);
     } else {
-      run(bwd_dkdv<DT, D, CAUSAL, 3, VARLEN>);
+      return run(bwd_dkdv<DT, D, CAUSAL, 3, VARLEN>);
     }
   }
-  return (int)hipGetLastError();
+  return 0;
 }
 
 template <int DT, int D>
@@ -609,7 +611,6 @@ int fa_launch_bwd_small_d(const FaBwdLaunch& a, float sl2, float scale) {
 int fa_launch_bwd(const FaBwdLaunch& a) {
   const float sl2 = (float)(a.scale * 1.4426950408889634074);
   const float scale = (float)a.scale;
-  (void)hipGetLastError();  // clear a stale error so that the check below is ours
   if (a.dtype != kBF16 && a.dtype != kFP16) return fa_launch_bwd32(a, sl2, scale);
   if (a.D < 128) return fa_launch_bwd_small_d(a, sl2, scale);
   if (a.D == 256)

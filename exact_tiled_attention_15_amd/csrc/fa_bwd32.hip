@@ -33,7 +33,6 @@ namespace {
 
 constexpr float kLog2e32 = 1.4426950408889634074f;
 constexpr int kThreads32 = 256;  // 4 waves
-constexpr int64_t kNumCUs32 = 256;  // compute units of the MI355X
 
 __device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -387,44 +386,47 @@ int launch_bwd32(const FaBwdLaunch& a, float sl2, float scale) {
   const int H = (int)a.H, tq = (int)a.total_q, tk = (int)a.total_k;
   float* lse2 = (float*)a.workspace;
   float* delta = lse2 + rows;
+  int rc = 0;
   if (rows > 0) {
     const int64_t threads = rows * (D / 4);
-    hipLaunchKernelGGL((bwd32_prep<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
-                       (const float*)a.o, (const float*)a.dout, a.lse, lse2, delta, rows);
+    rc = launch_kernel(bwd32_prep<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), st, (const float*)a.o,
+                       (const float*)a.dout, a.lse, lse2, delta, rows);
+    if (rc != 0) return rc;
     // At most one 128-row workgroup per CU: the key-split form (four times
     // the waves), as in the fp32 forward.
     const int nqt = (int)((a.Nq + 127) / 128);
-    const bool ks = !VARLEN && a.BH * nqt <= kNumCUs32;
+    const bool ks = !VARLEN && a.BH * nqt <= a.cus;
     if (nqt > 0 && ks) {
       if constexpr (!VARLEN)
-        hipLaunchKernelGGL((bwd32_dq<D, CAUSAL, false, true>), dim3((unsigned)(a.BH * ((a.Nq + 31) / 32))),
-                           dim3(kThreads32), 0, st, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+        rc = launch_kernel(bwd32_dq<D, CAUSAL, false, true>, dim3((unsigned)(a.BH * ((a.Nq + 31) / 32))),
+                           dim3(kThreads32), st, (const float*)a.q, (const float*)a.k, (const float*)a.v,
                            (const float*)a.dout, (const float*)lse2, (const float*)delta, (float*)a.dq, (int)a.BH,
                            (int)a.Nq, (int)a.Nk, (int)((a.Nq + 31) / 32), sl2, scale, a.cu_q, a.cu_k, H, tq, tk);
     } else if (nqt > 0) {
-      hipLaunchKernelGGL((bwd32_dq<D, CAUSAL, VARLEN>), dim3((unsigned)(a.BH * nqt)), dim3(kThreads32), 0, st,
+      rc = launch_kernel(bwd32_dq<D, CAUSAL, VARLEN>, dim3((unsigned)(a.BH * nqt)), dim3(kThreads32), st,
                          (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout,
                          (const float*)lse2, (const float*)delta, (float*)a.dq, (int)a.BH, (int)a.Nq, (int)a.Nk,
                          nqt, sl2, scale, a.cu_q, a.cu_k, H, tq, tk);
     }
+    if (rc != 0) return rc;
   }
   const int nkt = (int)((a.Nk + 127) / 128);
   // (not at D = 128: staging 128 query rows of Q and dO next to the K, V
   // fragments and both gradients spills registers)
-  const bool ks = !VARLEN && D <= 64 && a.BH * nkt <= kNumCUs32;
+  const bool ks = !VARLEN && D <= 64 && a.BH * nkt <= a.cus;
   if (nkt > 0 && ks) {
     if constexpr (!VARLEN && D <= 64)
-      hipLaunchKernelGGL((bwd32_dkdv<D, CAUSAL, false, true>), dim3((unsigned)(a.BH * ((a.Nk + 31) / 32))),
-                         dim3(kThreads32), 0, st, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+      rc = launch_kernel(bwd32_dkdv<D, CAUSAL, false, true>, dim3((unsigned)(a.BH * ((a.Nk + 31) / 32))),
+                         dim3(kThreads32), st, (const float*)a.q, (const float*)a.k, (const float*)a.v,
                          (const float*)a.dout, (const float*)lse2, (const float*)delta, (float*)a.dk, (float*)a.dv,
                          (int)a.BH, (int)a.Nq, (int)a.Nk, sl2, scale, a.cu_q, a.cu_k, H, tq, tk);
   } else if (nkt > 0) {
-    hipLaunchKernelGGL((bwd32_dkdv<D, CAUSAL, VARLEN>), dim3((unsigned)(a.BH * nkt)), dim3(kThreads32), 0, st,
+    rc = launch_kernel(bwd32_dkdv<D, CAUSAL, VARLEN>, dim3((unsigned)(a.BH * nkt)), dim3(kThreads32), st,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout,
                        (const float*)lse2, (const float*)delta, (float*)a.dk, (float*)a.dv, (int)a.BH, (int)a.Nq,
                        (int)a.Nk, sl2, scale, a.cu_q, a.cu_k, H, tq, tk);
   }
-  return (int)hipGetLastError();
+  return rc;
 }
 
 template <int D>

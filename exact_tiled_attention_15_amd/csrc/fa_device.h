@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+
 namespace {
 
 typedef unsigned short u16;
@@ -274,6 +276,22 @@ __device__ __forceinline__ void init_operand_offsets(Wave16& w) {
       asm volatile("" : "+v"(w.vb_hi[q]));
     }
   }
+}
+
+// Host side: enqueue kernel<<<grid, block, 0, st>>>(args...) through
+// hipLaunchKernel and return that launch's own status.  The runtime's
+// last-error state (which may hold an error of the caller's earlier work) is
+// not read or cleared, so a failure reported here is this launch's.
+template <typename... P, typename... A>
+int launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t st, A... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "one argument per kernel parameter");
+  std::tuple<P...> t{static_cast<P>(args)...};
+  return std::apply(
+      [&](auto&... p) {
+        void* ptrs[] = {(void*)&p...};
+        return (int)hipLaunchKernel((const void*)kernel, grid, block, ptrs, 0, st);
+      },
+      t);
 }
 
 }  // namespace

@@ -18,6 +18,7 @@ struct FaLaunch {
   int dtype;  // fa_dtype
   double scale;  // softmax scale applied to q.k (validated: finite, > 0)
   void* stream;
+  int64_t cus;  // compute units of the current device (sizes the dispatch choices)
   void* workspace;  // split-KV partials (fa_launch_fwd_splitkv only)
   // packed variable-length batches (fa_launch_fwd_varlen only): BH = B*H,
   // Nq = longest sequence's query count, offsets on the device
@@ -29,7 +30,9 @@ struct FaLaunch {
 };
 
 // Enqueues the forward pass.  Arguments are already validated.  Returns 0 on
-// success, otherwise the HIP error code of the launch.
+// success, otherwise the HIP error code of the first launch that failed (the
+// launches' own status: an error the caller's earlier HIP work left pending
+// is neither reported nor cleared).
 int fa_launch_fwd(const FaLaunch& a);
 
 // Split-KV forward (16-bit dtypes): nsplit key ranges of split_len keys
@@ -66,6 +69,7 @@ struct FaBwdLaunch {
   int dtype;  // fa_dtype
   double scale;
   void* stream;
+  int64_t cus;  // compute units of the current device
   // Packed sequences (fa_bwd_varlen), NULL otherwise: q, o, dout, dq are
   // [H, total_q, D], k, v, dk, dv [H, total_k, D], lse and the workspace
   // [H, total_q]; BH = B*H, Nq / Nk the longest sequence's counts.

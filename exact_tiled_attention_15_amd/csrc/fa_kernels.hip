@@ -51,7 +51,6 @@ namespace {
 
 constexpr int kThreads = 256;                     // 4 waves of 64 (fp32 kernel)
 constexpr int kBR = 128;                          // query rows per workgroup (fp32 kernel)
-constexpr int kNumCUs = 256;                      // compute units of the MI355X
 
 // 16-bit kernel shape: a workgroup of waves16<D>() waves owns 32 query rows
 // per wave and streams K/V tiles of bc16<D>() keys through a 4-stage LDS ring
@@ -732,25 +731,25 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_32(const float* __restrict
 }
 
 template <int D, bool CAUSAL, bool SPLIT, bool VARLEN = false, bool KS = false>
-void launch32(const FaLaunch& a, float sl2, int nsplit, int split_len, float* Po, float* Pl) {
+int launch32(const FaLaunch& a, float sl2, int nsplit, int split_len, float* Po, float* Pl) {
   const int nqt = (int)((a.Nq + (KS ? 32 : kBR) - 1) / (KS ? 32 : kBR));
   // VARLEN maps block ids per XCD (8 of them): round B*H up to a multiple of 8
   const int64_t heads = VARLEN ? (a.BH + 7) / 8 * 8 : a.BH;
   const dim3 grid((unsigned)(heads * nqt * nsplit)), block(kThreads);
-  hipLaunchKernelGGL((fa_fwd_32<D, CAUSAL, SPLIT, VARLEN, KS>), grid, block, 0, (hipStream_t)a.stream,
+  return launch_kernel(fa_fwd_32<D, CAUSAL, SPLIT, VARLEN, KS>, grid, block, (hipStream_t)a.stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, (int)a.BH,
                      (int)a.Nq, (int)a.Nk, nqt, sl2, split_len, Po, Pl, a.cu_q, a.cu_k, (int)a.H, (int)a.total_q,
                      (int)a.total_k);
 }
 
 template <int DT, int D, bool CAUSAL, bool SPLIT, bool VARLEN = false, int NW = waves16<D>()>
-void launch16(const FaLaunch& a, float sl2, int nsplit, int split_len, float* Po, float* Pl) {
+int launch16(const FaLaunch& a, float sl2, int nsplit, int split_len, float* Po, float* Pl) {
   constexpr int BR = 32 * NW;
   const int nqt = (int)((a.Nq + BR - 1) / BR);
   // VARLEN maps block ids per XCD (8 of them): round B*H up to a multiple of 8
   const int64_t heads = VARLEN ? (a.BH + 7) / 8 * 8 : a.BH;
   const dim3 grid((unsigned)(heads * nqt * nsplit)), block(64 * NW);
-  hipLaunchKernelGGL((fa_fwd_16<DT, D, CAUSAL, SPLIT, VARLEN, NW>), grid, block, 0, (hipStream_t)a.stream,
+  return launch_kernel(fa_fwd_16<DT, D, CAUSAL, SPLIT, VARLEN, NW>, grid, block, (hipStream_t)a.stream,
                      (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (u16*)a.o, a.lse, (int)a.BH, (int)a.Nq,
                      (int)a.Nk, nqt, sl2, split_len, Po, Pl, a.cu_q, a.cu_k, (int)a.H, (int)a.total_q,
                      (int)a.total_k);
@@ -761,17 +760,12 @@ int dispatch16(const FaLaunch& a, float sl2) {
   // Fewer 8-wave workgroups than CUs: the 4-wave form (128 rows, one wave
   // per SIMD, pipelined steps) doubles the workgroups.
   constexpr int NW8 = waves16<D>();
-  if (NW8 == 8 && a.BH * ((a.Nq + 32 * NW8 - 1) / (32 * NW8)) < kNumCUs) {
-    if (a.causal)
-      launch16<DT, D, true, false, false, 4>(a, sl2, 1, 0, nullptr, nullptr);
-    else
-      launch16<DT, D, false, false, false, 4>(a, sl2, 1, 0, nullptr, nullptr);
-  } else if (a.causal) {
-    launch16<DT, D, true, false>(a, sl2, 1, 0, nullptr, nullptr);
-  } else {
-    launch16<DT, D, false, false>(a, sl2, 1, 0, nullptr, nullptr);
+  if (NW8 == 8 && a.BH * ((a.Nq + 32 * NW8 - 1) / (32 * NW8)) < a.cus) {
+    return a.causal ? launch16<DT, D, true, false, false, 4>(a, sl2, 1, 0, nullptr, nullptr)
+                    : launch16<DT, D, false, false, false, 4>(a, sl2, 1, 0, nullptr, nullptr);
   }
-  return (int)hipGetLastError();
+  return a.causal ? launch16<DT, D, true, false>(a, sl2, 1, 0, nullptr, nullptr)
+                  : launch16<DT, D, false, false>(a, sl2, 1, 0, nullptr, nullptr);
 }
 
 // Merge of the key-range partials: the numerically stable associative
@@ -818,14 +812,12 @@ int dispatch16_split(const FaLaunch& a, float sl2, int nsplit, int split_len) {
   const int64_t rows = a.BH * a.Nq;
   float* Po = (float*)a.workspace;
   float* Pl = Po + (size_t)nsplit * rows * D;
-  if (a.causal)
-    launch16<DT, D, true, true>(a, sl2, nsplit, split_len, Po, Pl);
-  else
-    launch16<DT, D, false, true>(a, sl2, nsplit, split_len, Po, Pl);
+  const int st = a.causal ? launch16<DT, D, true, true>(a, sl2, nsplit, split_len, Po, Pl)
+                          : launch16<DT, D, false, true>(a, sl2, nsplit, split_len, Po, Pl);
+  if (st != 0) return st;
   const int64_t threads = rows * (D / 4);
-  hipLaunchKernelGGL((merge_splits<DT, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                     (hipStream_t)a.stream, (const float*)Po, (const float*)Pl, a.o, a.lse, rows, nsplit);
-  return (int)hipGetLastError();
+  return launch_kernel(merge_splits<DT, D>, dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                       (hipStream_t)a.stream, (const float*)Po, (const float*)Pl, a.o, a.lse, rows, nsplit);
 }
 
 template <int D>
@@ -835,15 +827,12 @@ int dispatch32(const FaLaunch& a, float sl2) {
   // the waves.  Measured: +25-33% at 256 workgroups (causal), 2.6x at 64;
   // at 512 workgroups the 128-row tiles win (the split re-reads each K/V
   // tile for every 32 rows).
-  const bool ks = a.BH * ((a.Nq + kBR - 1) / kBR) <= kNumCUs;
-  if (a.causal) {
-    if (ks) launch32<D, true, false, false, true>(a, sl2, 1, 0, nullptr, nullptr);
-    else launch32<D, true, false>(a, sl2, 1, 0, nullptr, nullptr);
-  } else {
-    if (ks) launch32<D, false, false, false, true>(a, sl2, 1, 0, nullptr, nullptr);
-    else launch32<D, false, false>(a, sl2, 1, 0, nullptr, nullptr);
-  }
-  return (int)hipGetLastError();
+  const bool ks = a.BH * ((a.Nq + kBR - 1) / kBR) <= a.cus;
+  if (a.causal)
+    return ks ? launch32<D, true, false, false, true>(a, sl2, 1, 0, nullptr, nullptr)
+              : launch32<D, true, false>(a, sl2, 1, 0, nullptr, nullptr);
+  return ks ? launch32<D, false, false, false, true>(a, sl2, 1, 0, nullptr, nullptr)
+            : launch32<D, false, false>(a, sl2, 1, 0, nullptr, nullptr);
 }
 
 template <int D>
@@ -851,32 +840,24 @@ int dispatch32_split(const FaLaunch& a, float sl2, int nsplit, int split_len) {
   const int64_t rows = a.BH * a.Nq;
   float* Po = (float*)a.workspace;
   float* Pl = Po + (size_t)nsplit * rows * D;
-  if (a.causal)
-    launch32<D, true, true>(a, sl2, nsplit, split_len, Po, Pl);
-  else
-    launch32<D, false, true>(a, sl2, nsplit, split_len, Po, Pl);
+  const int st = a.causal ? launch32<D, true, true>(a, sl2, nsplit, split_len, Po, Pl)
+                          : launch32<D, false, true>(a, sl2, nsplit, split_len, Po, Pl);
+  if (st != 0) return st;
   const int64_t threads = rows * (D / 4);
-  hipLaunchKernelGGL((merge_splits<0, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                     (hipStream_t)a.stream, (const float*)Po, (const float*)Pl, a.o, a.lse, rows, nsplit);
-  return (int)hipGetLastError();
+  return launch_kernel(merge_splits<0, D>, dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                       (hipStream_t)a.stream, (const float*)Po, (const float*)Pl, a.o, a.lse, rows, nsplit);
 }
 
 template <int D>
 int dispatch32_varlen(const FaLaunch& a, float sl2) {
-  if (a.causal)
-    launch32<D, true, false, true>(a, sl2, 1, 0, nullptr, nullptr);
-  else
-    launch32<D, false, false, true>(a, sl2, 1, 0, nullptr, nullptr);
-  return (int)hipGetLastError();
+  return a.causal ? launch32<D, true, false, true>(a, sl2, 1, 0, nullptr, nullptr)
+                  : launch32<D, false, false, true>(a, sl2, 1, 0, nullptr, nullptr);
 }
 
 template <int DT, int D>
 int dispatch16_varlen(const FaLaunch& a, float sl2) {
-  if (a.causal)
-    launch16<DT, D, true, false, true>(a, sl2, 1, 0, nullptr, nullptr);
-  else
-    launch16<DT, D, false, false, true>(a, sl2, 1, 0, nullptr, nullptr);
-  return (int)hipGetLastError();
+  return a.causal ? launch16<DT, D, true, false, true>(a, sl2, 1, 0, nullptr, nullptr)
+                  : launch16<DT, D, false, false, true>(a, sl2, 1, 0, nullptr, nullptr);
 }
 
 }  // namespace
@@ -900,7 +881,6 @@ int fa_launch_fwd_varlen_d256(const FaLaunch& a, float sl2) {
 
 int fa_launch_fwd_varlen(const FaLaunch& a) {
   const float sl2 = (float)(a.scale * 1.4426950408889634074);
-  (void)hipGetLastError();  // clear a stale error so that the check below is ours
   if (a.D == 256) return fa_launch_fwd_varlen_d256(a, sl2);
   switch (a.dtype) {
     case kBF16:
@@ -917,7 +897,6 @@ int fa_launch_fwd_varlen(const FaLaunch& a) {
 
 int fa_launch_fwd_splitkv(const FaLaunch& a, int nsplit, int split_len) {
   const float sl2 = (float)(a.scale * 1.4426950408889634074);
-  (void)hipGetLastError();  // clear a stale error so that the check below is ours
   if (a.D == 256) return fa_launch_fwd_splitkv_d256(a, sl2, nsplit, split_len);
   switch (a.dtype) {
     case kBF16:
@@ -938,7 +917,6 @@ int fa_launch_fwd_splitkv(const FaLaunch& a, int nsplit, int split_len) {
 int fa_launch_fwd(const FaLaunch& a) {
   // scale * log2(e), computed in double and rounded once.
   const float sl2 = (float)(a.scale * 1.4426950408889634074);
-  (void)hipGetLastError();  // clear a stale error so that the check below is ours
   if (a.D == 256) return fa_launch_fwd_d256(a, sl2);
   switch (a.dtype) {
     case kBF16:

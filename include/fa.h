@@ -25,11 +25,17 @@
  * asynchronously.  Calls are re-entrant and thread-safe (no global mutable
  * state).  Every element of o and lse is written.
  *
- * Errors: arguments are validated before any HIP call; a non-zero status
- * means nothing was enqueued.  FA_ERR_HIP reports a launch error.  Faults
- * during execution surface at the caller's next synchronisation on
+ * Errors: arguments are validated before any work is enqueued; a status
+ * other than FA_OK and FA_ERR_HIP means nothing was enqueued.  FA_ERR_HIP
+ * reports that the runtime refused a launch of this call (or that no device
+ * is current); it comes from the launches' own status, so an error that the
+ * caller's earlier HIP work left pending is neither reported nor cleared.
+ * Faults during execution surface at the caller's next synchronisation on
  * `stream`.  NaN or Inf inputs are not checked and propagate to the rows
  * they touch.
+ *
+ * Workgroup shapes (and fa_fwd_splitkv's automatic range count) are chosen
+ * against the compute-unit count of the current device, read on every call.
  */
 #ifndef FA_H
 #define FA_H
@@ -57,11 +63,20 @@ typedef enum {
   FA_ERR_DTYPE = 4,    /* unknown dtype code */
   FA_ERR_ALIGN = 5,    /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
   FA_ERR_ALIAS = 6,    /* o or lse overlaps an input, or o overlaps lse */
-  FA_ERR_HIP = 7,      /* the HIP runtime reported an error at launch */
-  FA_ERR_SCALE = 8,    /* softmax_scale not a finite number > 0 (or so small that
-                          softmax_scale * log2(e) is not a normal float) */
+  FA_ERR_HIP = 7,      /* the HIP runtime refused a launch of this call, or no
+                          device is current */
+  FA_ERR_SCALE = 8,    /* softmax_scale neither FA_DEFAULT_SCALE nor a finite
+                          number > 0 (or so small or large that softmax_scale
+                          * log2(e) is not a normal float) */
   FA_ERR_WORKSPACE = 9 /* workspace_bytes below the matching *_workspace_size() */
 } fa_status;
+
+/*
+ * The softmax_scale value that selects the default scale 1/sqrt(D) in every
+ * entry point that takes a scale (every page divides the scores by the
+ * square root of the head dimension).
+ */
+#define FA_DEFAULT_SCALE 0.0
 
 /*
  * fa_fwd -- exact attention forward.
@@ -91,11 +106,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * softmax_scale argument ("Flash Attention vs Standard Attention",
  * Implementation), set there to 1/sqrt(D); any finite softmax_scale > 0 is
  * accepted (the kernels take the row max of the raw dot products, which
- * commutes with a positive scale).  Scores whose scaled value overflows
- * fp32 behave like Inf inputs.  Every other argument, the layouts, the
+ * commutes with a positive scale), and FA_DEFAULT_SCALE selects 1/sqrt(D).
+ * Scores whose scaled value overflows fp32 behave like Inf inputs.  Every other argument, the layouts, the
  * ownership and the errors are those of fa_fwd; an invalid softmax_scale
  * returns FA_ERR_SCALE before any HIP call.  fa_fwd(...) is
- * fa_fwd_scaled(..., 1/sqrt(D), ...).
+ * fa_fwd_scaled(..., FA_DEFAULT_SCALE, ...), i.e. with 1/sqrt(D).
  */
 int fa_fwd_scaled(const void* q, const void* k, const void* v, void* o, float* lse,
                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
@@ -106,7 +121,9 @@ int fa_fwd_scaled(const void* q, const void* k, const void* v, void* o, float* l
  * needs for these sizes and num_splits (0 = automatic, as fa_fwd_splitkv
  * chooses): (D + 1) fp32 values per query row and key range, or 0 when the
  * call runs as one range.  -1 for negative or overflowing sizes or
- * num_splits outside [0, 1024].
+ * num_splits outside [0, 1024].  The automatic count depends on the current
+ * device's compute units: ask with the device current that the call will
+ * run on (with no device, the count is planned for 256 compute units).
  */
 int64_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
                                       int64_t num_splits);
@@ -126,9 +143,10 @@ int64_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t 
  *     LSE = ln sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s.
  *
  *   num_splits  number of key ranges, 0 for automatic (enough workgroups to
- *               fill the GPU, at least 256 keys a range); at most 1024.  The
- *               range length is rounded up to whole 64-key tiles, so fewer
- *               ranges may result; with one range this is fa_fwd_scaled.
+ *               fill the current device's compute units, at least 256 keys
+ *               a range); at most 1024.  The range length is rounded up to
+ *               whole 64-key tiles, so fewer ranges may result; with one
+ *               range this is fa_fwd_scaled.
  *   workspace   device memory of fa_fwd_splitkv_workspace_size(...) bytes
  *               (may be NULL when that is 0), 16-byte aligned, owned by the
  *               caller; scratch after the call.
@@ -203,7 +221,8 @@ int64_t fa_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq);
  *   workspace device memory of at least fa_bwd_workspace_size(B, H, Nq)
  *             bytes, 16-byte aligned, owned by the caller; its contents on
  *             entry do not matter and are scratch after the call
- *   softmax_scale  the forward's scale (1/sqrt(D) for fa_fwd); finite, > 0
+ *   softmax_scale  the forward's scale: finite and > 0, or FA_DEFAULT_SCALE
+ *             for 1/sqrt(D) (fa_fwd's)
  *   causal, dtype, stream   as fa_fwd
  *   B, H, Nq, Nk, D   sizes as fa_fwd; D in {32, 64, 128, 256} (256: fp16
  *             and bf16 only)

@@ -86,3 +86,49 @@ def compare_sampled(w, inputs_cpu, o_gpu, lse_gpu, rows, tag=""):
     assert eo <= to, f"{tag}: O error {eo} > {to}"
     assert el <= tl, f"{tag}: LSE error {el} > {tl}"
     return eo, el
+
+
+def _oracle_pool():
+    """Threads for head-by-head oracle calls (numpy releases the GIL in its
+    matrix products and exponentials); BLAS limited to a few threads each so
+    the pool does not oversubscribe the host's cores."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    n = max(1, min(8, (os.cpu_count() or 2) // 2))
+    return ThreadPoolExecutor(n), threadpool_limits(limits=2)
+
+
+def compare_whole(w, inputs_cpu, o_gpu, lse_gpu, tag="", scale=None):
+    """Every element of O and LSE against the oracle, one (b, h) head at a
+    time (the oracle's own row-chunked definition on each head), with the
+    maximum errors over the whole tensors."""
+    import torch
+
+    assert bool(torch.isfinite(o_gpu).all()), f"{tag}: non-finite O"
+    assert bool(torch.isfinite(lse_gpu).all()), f"{tag}: non-finite LSE"
+    q, k, v = inputs_cpu
+    og = o_gpu.float().cpu()
+    lg = lse_gpu.cpu()
+
+    def head(bh):
+        b, h = divmod(bh, w.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        O, L = oracle.attention_forward(q[sl], k[sl], v[sl], w.causal, scale=scale)
+        eo = float(np.max(np.abs(og[sl].double().numpy() - O)))
+        el = float(np.max(np.abs(lg[sl].double().numpy() - L)))
+        return eo, el
+
+    pool, limits = _oracle_pool()
+    with pool, limits:
+        errs = list(pool.map(head, range(w.B * w.H)))
+    eo = max(e[0] for e in errs)
+    el = max(e[1] for e in errs)
+    to, tl = TOL[w.dtype]
+    log(f"  {tag} {w.name} (whole tensors, {w.B * w.H} heads): max|dO|={eo:.3e} (tol {to}) "
+        f"max|dLSE|={el:.3e} (tol {tl})")
+    assert eo <= to, f"{tag}: O error {eo} > {to}"
+    assert el <= tl, f"{tag}: LSE error {el} > {tl}"
+    return eo, el

@@ -74,11 +74,32 @@ def call_scaled(scale, q=Q, k=K, v=V, o=O, lse=L, B=2, H=4, Nq=128, Nk=128, D=64
     return fa.fa_fwd_scaled(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, dtype, None)
 
 
-@pytest.mark.parametrize("scale", [0.0, -0.125, float("nan"), float("inf"), -float("inf"), 1e-300, 1e300])
+@pytest.mark.parametrize("scale", [-1e-9, -0.125, float("nan"), float("inf"), -float("inf"), 1e-300, 1e300])
 def test_scaled_rejects_bad_scale(scale):
     assert call_scaled(scale) == 8
     # an empty call still validates the scale
     assert call_scaled(scale, B=0, q=0, k=0, v=0, o=0, lse=0) == 8
+
+
+def test_default_scale_is_accepted_everywhere():
+    # FA_DEFAULT_SCALE (0) asks the library for 1/sqrt(D): every entry point
+    # that takes a scale accepts it (empty calls: validation only, nothing is
+    # enqueued), where a negative scale is rejected.  That it selects exactly
+    # 1/sqrt(D) is checked bit for bit on the GPU.
+    assert fa.FA_DEFAULT_SCALE == 0.0
+    empty = dict(B=0, q=0, k=0, v=0, o=0, lse=0)
+    assert call_scaled(fa.FA_DEFAULT_SCALE, **empty) == 0
+    assert call_scaled(-1.0, **empty) == 8
+    assert call_split(B=0, q=0, k=0, v=0, o=0, lse=0, ws=0, ws_bytes=0, scale=fa.FA_DEFAULT_SCALE) == 0
+    assert call_split(B=0, q=0, k=0, v=0, o=0, lse=0, ws=0, ws_bytes=0, scale=-1.0) == 8
+    assert call_varlen(B=0, q=0, k=0, v=0, o=0, lse=0, cu_q=0, cu_k=0, scale=fa.FA_DEFAULT_SCALE) == 0
+    assert call_varlen(B=0, q=0, k=0, v=0, o=0, lse=0, cu_q=0, cu_k=0, scale=-1.0) == 8
+    bwd_empty = dict(B=0, q=0, k=0, v=0, o=0, lse=0, dout=0, dq=0, dk=0, dv=0, ws=0, ws_bytes=0)
+    assert call_bwd(scale=fa.FA_DEFAULT_SCALE, **bwd_empty) == 0
+    assert call_bwd(scale=-1.0, **bwd_empty) == 8
+    bv_empty = dict(B=0, q=0, k=0, v=0, o=0, lse=0, dout=0, dq=0, dk=0, dv=0, cu_q=0, cu_k=0, ws=0, ws_bytes=0)
+    assert call_bwd_varlen(scale=fa.FA_DEFAULT_SCALE, **bv_empty) == 0
+    assert call_bwd_varlen(scale=-1.0, **bv_empty) == 8
 
 
 def test_scaled_validates_like_fa_fwd():
@@ -129,7 +150,7 @@ def test_bwd_workspace_size():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=7), 4), (dict(dtype=-1), 4), (dict(D=16), 3), (dict(D=512), 3), (dict(D=256, dtype=0), 3),
-    (dict(scale=0.0), 8), (dict(scale=float("nan")), 8), (dict(scale=-1.0), 8),
+    (dict(scale=-0.5), 8), (dict(scale=float("nan")), 8), (dict(scale=-1.0), 8),
     (dict(Nk=0), 2), (dict(B=-1), 2), (dict(Nq=1 << 40), 2),
     (dict(q=0), 1), (dict(o=0), 1), (dict(lse=0), 1), (dict(dout=0), 1), (dict(dq=0), 1), (dict(dk=0), 1),
     (dict(dv=0), 1), (dict(ws=0), 1),
@@ -174,7 +195,7 @@ def test_splitkv_workspace_size():
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=7), 4), (dict(D=256, dtype=0), 3), (dict(D=16), 3), (dict(scale=0.0), 8), (dict(splits=-1), 2),
+    (dict(dtype=7), 4), (dict(D=256, dtype=0), 3), (dict(D=16), 3), (dict(scale=-2.0), 8), (dict(splits=-1), 2),
     (dict(splits=5000), 2),
     (dict(q=0), 1), (dict(ws=0), 1), (dict(ws_bytes=32 * 4 * 4 * 129 * 4 - 1), 9), (dict(ws=WS + 8), 5),
     (dict(ws=K + 4096), 6), (dict(ws=L - 64), 6), (dict(o=Q), 6), (dict(Nk=0), 2),
@@ -220,8 +241,8 @@ def call_bwd_varlen(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, cu_
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=7), 4), (dict(D=256, dtype=0), 3), (dict(D=512), 3), (dict(scale=0.0), 8), (dict(B=-1), 2),
-    (dict(max_q=501), 2), (dict(max_k=701), 2), (dict(total_k=1 << 40), 2),
+    (dict(dtype=7), 4), (dict(D=256, dtype=0), 3), (dict(D=512), 3), (dict(scale=float("inf")), 8),
+    (dict(B=-1), 2), (dict(max_q=501), 2), (dict(max_k=701), 2), (dict(total_k=1 << 40), 2),
     (dict(cu_q=0), 1), (dict(cu_k=0), 1), (dict(dq=0), 1), (dict(dk=0), 1), (dict(ws=0), 1),
     (dict(ws_bytes=8 * 4 * 500 - 1), 9),
     (dict(cu_k=CK + 2), 5), (dict(dv=DV + 8), 5), (dict(lse=L + 2), 5),

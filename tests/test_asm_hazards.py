@@ -36,7 +36,7 @@ def _asm(unit, out):
     import exact_tiled_attention_15_amd.build as b
 
     _, src, extra = unit
-    cmd = [_hipcc(), "-O3", "-std=c++17", f"--offload-arch={b.ARCH}", "-fno-honor-nans", "--cuda-device-only",
+    cmd = [_hipcc(), "-O3", "-std=c++17", f"--offload-arch={b.ARCH}", "--cuda-device-only",
            "-S", *b.DEVICE_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), src, "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]

@@ -88,6 +88,22 @@ def test_parity_16bit_grid_sizes(dt, D, causal, B, H, Nq, Nk):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "fp16"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_parity_8wave_several_q_tiles(dt, D, causal):
+    # The 8-wave form (256-row workgroups) at a grid of more workgroups than
+    # CUs (128 heads x 3 Q tiles = 384), with several Q tiles per head (causal
+    # diagonals at q0 > 0, running maxima rescaled mid-stream), a ragged Q
+    # tile (520 = 2 x 256 + 8 rows) and a ragged key tail (700 = 10 x 64 +
+    # 60), every element compared.
+    w = workloads.Workload(f"w8_{dt}_d{D}_{'c' if causal else 'n'}_h128_520x700", 1, 128, 520, 700, D, dt,
+                           causal, 8800 + D)
+    cpu, gpu = _case(w)
+    o, l = run_gpu(*gpu, w.causal)
+    compare_full(w, cpu, o, l, "8wave")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("Nq,Nk", [(300, 300), (257, 517), (130, 70), (1, 200)])
 def test_parity_d256(dt, causal, Nq, Nk):
@@ -106,17 +122,21 @@ def test_parity_d256_scaled_and_moves():
     compare_full(w, cpu, o, l, "d256-scaled", scale=0.04)
 
 
+@pytest.mark.parametrize("H", [2, 128])
 @pytest.mark.parametrize("dt,D,causal", [("bf16", 128, True), ("bf16", 128, False), ("fp16", 64, True),
                                          ("fp16", 128, False), ("fp32", 64, True), ("bf16", 256, True)])
-def test_parity_reference_moves(dt, D, causal):
+def test_parity_reference_moves(dt, D, causal, H):
     # Keys whose norm grows along the sequence (K row j scaled by
     # 1 + a j/Nk, Q by a): each row's running max climbs tile after tile, so
     # the softmax reference moves mid-stream (about one move per row for
     # a = 3) and every rescale path of the kernel (l and O, with PV work in
     # flight) is exercised.  fp32 takes a = 2 (|LSE| up to ~22 rather than
     # ~44): its absolute LSE tolerance of 1e-5 is a few fp32 ulps of such
-    # values, below what the rounding of larger scores allows.
-    w = workloads.Workload(f"moves_{dt}_d{D}_{'c' if causal else 'n'}", 1, 2, 700, 700, D, dt, causal, 4242 + D)
+    # values, below what the rounding of larger scores allows.  H = 2 runs
+    # the small-grid workgroup forms (4-wave 16-bit, key-split fp32), H = 128
+    # the large-grid ones (8-wave 16-bit at D <= 128, 128-row fp32).
+    w = workloads.Workload(f"moves_{dt}_d{D}_{'c' if causal else 'n'}_h{H}", 1, H, 700, 700, D, dt, causal,
+                           4242 + D)
     q64, k64, v64 = workloads.draw_float64(w)
     a = 2.0 if dt == "fp32" else 3.0
     ramp = 1.0 + a * np.arange(w.Nk, dtype=np.float64) / w.Nk

@@ -76,16 +76,21 @@ def test_varlen_explicit_scale_and_large_max():
     _compare("bf16", inputs, o, lse, True, "varlen-scaled", scale=0.2)
 
 
-@pytest.mark.parametrize("dt", ["bf16", "fp32"])
-def test_varlen_equals_dense_for_equal_lengths(dt):
-    # equal lengths: the same tiles as the dense kernel, bit for bit.  fp32
-    # takes enough heads (3*32*ceil(300/128) = 288 workgroups of 128 rows)
-    # that the dense forward keeps its 128-row tiles: on grids of at most one
+@pytest.mark.parametrize("dt,H", [("bf16", 4), ("bf16", 96), ("fp32", 32)])
+def test_varlen_equals_dense_for_equal_lengths(dt, H):
+    # Equal lengths: bit for bit the dense forward's result.  The varlen
+    # 16-bit kernel always runs 8-wave workgroups of 256 rows; the dense one
+    # runs them too with H = 96 (3*96*ceil(300/256) = 576 workgroups, the
+    # same tiles), and its 4-wave, 128-row form with pipelined steps on the
+    # small grid of H = 4 (24 workgroups of 256 rows, fewer than the CUs):
+    # the same arithmetic in the same order, so the same bits.  fp32 takes
+    # enough heads (3*32*ceil(300/128) = 288 workgroups of 128 rows) that the
+    # dense forward keeps its 128-row tiles: on grids of at most one
     # workgroup per CU it splits keys over the waves instead (another
     # addition order, equal only within the tolerance).
     import exact_tiled_attention_15_amd as fa
 
-    B, H, N, D = 3, 4 if dt != "fp32" else 32, 300, 128
+    B, N, D = 3, 300, 128
     inputs = _inputs(dt, H, D, [N] * B, [N] * B, 11)
     q, k, v = inputs[:3]
     o, lse = _run(*inputs, True)
