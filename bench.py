@@ -19,10 +19,13 @@ O and LSE written once) per second in GB/s against 8 TB/s.
 sequences of mixed lengths; FLOPs = the forward convention summed over the
 sequences.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--op fwd|bwd|decode|varlen] [--no-cpu-baseline] [--all]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-seconds S]
+                    [--workload NAME] [--op fwd|bwd|decode|varlen] [--no-cpu-baseline] [--all]
 
-Prints one JSON line per workload.
+Warm-up: W launches, then more until S seconds have passed and the launch
+time has settled (the shader clock ramps up over the first few hundred
+milliseconds of load); the extra launches are reported in ``warmup_settle``,
+``warmup`` stays W.  Prints one JSON line per workload.
 """
 from __future__ import annotations
 
@@ -53,6 +56,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--settle-seconds", type=float, default=1.0,
+                   help="after the --warmup launches, keep launching until at least this long has passed "
+                        "since the first one and two successive batches agree within 2%% (the GPU's clock "
+                        "and caches reach steady state); reported in the line's warmup_settle field")
     p.add_argument("--workload", default=workloads.HEADLINE)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -120,22 +127,40 @@ def kernel_code_sha256(paths=KERNEL_SOURCES) -> str:
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
-def measured_traffic(w: workloads.Workload, op: str = "fwd"):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary of this kernel and workload, or None when there is none or the
-    kernel code has changed since the counters were taken."""
+COUNTER_KEYS = ("kernel_code_sha256", "traffic_bytes_per_launch", "mfma_busy_pct", "valu_trans_f32_per_launch")
+
+
+def committed_counters(w, op: str = "fwd"):
+    """The machine-readable fields of the committed rocprofv3 counter summary
+    of this op's kernels on this workload (HBM bytes per launch from the
+    FETCH_SIZE / WRITE_SIZE passes; MFMA-busy percent and transcendental VALU
+    instructions per launch from the SQ pass), or {} when there is none or
+    the kernel code has changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"{kernel_tag(w, op)}__{w.name}__hbm_traffic_and_counters.md")
     if not os.path.exists(path):
-        return None
+        return {}
     fields = {}
     for line in open(path):
-        if ":" in line and line.split(":")[0] in ("kernel_code_sha256", "traffic_bytes_per_launch"):
+        if ":" in line and line.split(":")[0] in COUNTER_KEYS:
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    code = kernel_code_sha256(kernel_sources(w, op))
-    if fields.get("kernel_code_sha256") != code or "traffic_bytes_per_launch" not in fields:
-        return None
-    return int(fields["traffic_bytes_per_launch"])
+    if fields.get("kernel_code_sha256") != kernel_code_sha256(kernel_sources(w, op)):
+        return {}
+    return fields
+
+
+def counter_fields(w, op: str, ms_per_step: float):
+    """Roofline extras from the committed counters: the HBM rate those bytes
+    make at this run's step time (GB/s, against the 8 TB/s datasheet peak),
+    the MFMA-busy fraction and the transcendental (exp) instruction count of
+    the SQ pass; None where the summary lacks them or is stale."""
+    c = committed_counters(w, op)
+    traffic = int(c["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in c else None
+    busy = float(c["mfma_busy_pct"]) / 100.0 if "mfma_busy_pct" in c else None
+    trans = int(c["valu_trans_f32_per_launch"]) if "valu_trans_f32_per_launch" in c else None
+    gbs = round(traffic / (ms_per_step * 1e-3) / 1e9, 1) if traffic is not None and ms_per_step > 0 else None
+    return {"traffic": traffic, "hbm_gbs": gbs, "hbm_frac": round(gbs / HBM_PEAK_GBS, 4) if gbs else None,
+            "mfma_busy": busy, "valu_trans_f32": trans}
 
 
 def blas_threads() -> int:
@@ -191,7 +216,37 @@ def cpu_baseline(w: workloads.Workload, target_s: float, op: str = "fwd"):
     }
 
 
-def bench_one(w: workloads.Workload, steps: int, warmup: int, op: str = "fwd"):
+def settle(step, warmup: int, seconds: float, batch: int = 20, cap_s: float = 10.0):
+    """Warm-up: ``warmup`` launches, then batches of ``batch`` launches until
+    at least ``seconds`` have passed since the first launch and two
+    successive batches take the same time within 2% (the clock and caches at
+    steady state), or ``cap_s`` has passed.  Returns the extra launches and
+    the seconds spent, reported beside the requested warm-up count."""
+    import torch
+
+    t0 = time.perf_counter()
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    extra, prev = 0, None
+    while True:
+        elapsed = time.perf_counter() - t0
+        if elapsed >= cap_s:
+            break
+        tb = time.perf_counter()
+        for _ in range(batch):
+            step()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - tb
+        extra += batch
+        settled = prev is not None and abs(dt - prev) <= 0.02 * prev
+        prev = dt
+        if time.perf_counter() - t0 >= seconds and settled:
+            break
+    return {"extra_launches": extra, "seconds": round(time.perf_counter() - t0, 3)}
+
+
+def bench_one(w: workloads.Workload, steps: int, warmup: int, op: str = "fwd", settle_s: float = 1.0):
     import torch
 
     import exact_tiled_attention_15_amd as fa
@@ -242,9 +297,7 @@ def bench_one(w: workloads.Workload, steps: int, warmup: int, op: str = "fwd"):
 
         step = decode_step
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm = settle(step, warmup, settle_s)
     # Whole timed region: K back-to-back launches between two events on the
     # launch stream.
     e0 = torch.cuda.Event(enable_timing=True)
@@ -282,6 +335,7 @@ def bench_one(w: workloads.Workload, steps: int, warmup: int, op: str = "fwd"):
             "bytes": nbytes,
             "flops": flops,
             "splits_workspace_bytes": ws_bytes,
+            "warmup_settle": warm,
         }
     return {
         "ms_per_step": ms_region,
@@ -291,10 +345,11 @@ def bench_one(w: workloads.Workload, steps: int, warmup: int, op: str = "fwd"):
         "tflops": tflops,
         "peak": peak,
         "flops": flops,
+        "warmup_settle": warm,
     }
 
 
-def bench_varlen(w: workloads.VarlenWorkload, steps: int, warmup: int):
+def bench_varlen(w: workloads.VarlenWorkload, steps: int, warmup: int, settle_s: float = 1.0):
     import torch
 
     import exact_tiled_attention_15_amd as fa
@@ -319,9 +374,7 @@ def bench_varlen(w: workloads.VarlenWorkload, steps: int, warmup: int):
         if rc != 0:
             raise fa.FaError(rc)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm = settle(step, warmup, settle_s)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -331,7 +384,8 @@ def bench_varlen(w: workloads.VarlenWorkload, steps: int, warmup: int):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     flops = workloads.varlen_flops(w)
-    return {"ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12, "flops": flops, "peak": PEAK_TFLOPS[w.dtype]}
+    return {"ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12, "flops": flops, "peak": PEAK_TFLOPS[w.dtype],
+            "warmup_settle": warm}
 
 
 def cpu_baseline_varlen(w: workloads.VarlenWorkload, target_s: float):
@@ -370,8 +424,9 @@ def line_varlen(w, r, steps, warmup, cpu):
         "config": {"workload": w.name, "B": w.B, "H": w.H, "D": w.D, "causal": w.causal, "seed": w.seed,
                    "total_q": int(sum(w.lens_q)), "total_k": int(sum(w.lens_k)), "lens_q": list(w.lens_q),
                    "flops_per_step": r["flops"], "parallelism": "single GPU", "op": "varlen"},
+        "warmup_settle": r.get("warmup_settle"),
         "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 3), "peak": r["peak"], "unit": "TFLOP/s",
-                     "frac": round(r["tflops"] / r["peak"], 4), "traffic": measured_traffic(w, "varlen")},
+                     "frac": round(r["tflops"] / r["peak"], 4), **counter_fields(w, "varlen", r["ms_per_step"])},
         "cpu_baseline": cpu,
     }
 
@@ -405,8 +460,9 @@ def line_for(w, r, steps, warmup, cpu, op="fwd"):
                        "splits_workspace_bytes": r["splits_workspace_bytes"], "parallelism": "single GPU",
                        "median_launch_ms": round(r["median_launch_ms"], 5),
                        "min_launch_ms": round(r["min_launch_ms"], 5), "op": op, **props},
+            "warmup_settle": r.get("warmup_settle"),
             "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(r["gbs"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w, op)},
+                         "frac": round(r["gbs"] / HBM_PEAK_GBS, 4), **counter_fields(w, op, r["ms_per_step"])},
             "cpu_baseline": cpu,
         }
     return {
@@ -427,9 +483,10 @@ def line_for(w, r, steps, warmup, cpu, op="fwd"):
                    "flops_per_step": r["flops"], "parallelism": "single GPU",
                    "median_launch_ms": round(r["median_launch_ms"], 5),
                    "min_launch_ms": round(r["min_launch_ms"], 5), "op": op, **props},
+        "warmup_settle": r.get("warmup_settle"),
         "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 3), "peak": r["peak"],
                      "unit": "TFLOP/s", "frac": round(r["tflops"] / r["peak"], 4),
-                     "traffic": measured_traffic(w, op)},
+                     **counter_fields(w, op, r["ms_per_step"])},
         "cpu_baseline": cpu,
     }
 
@@ -445,7 +502,7 @@ def main():
         names = (list(workloads.VARLEN_WORKLOADS) if a.all or a.workload == workloads.HEADLINE else [a.workload])
         for i, n in enumerate(names):
             w = workloads.VARLEN_WORKLOADS[n]
-            r = bench_varlen(w, a.steps, a.warmup)
+            r = bench_varlen(w, a.steps, a.warmup, a.settle_seconds)
             cpu = None if a.no_cpu_baseline or i else cpu_baseline_varlen(w, a.cpu_seconds)
             print(json.dumps(line_varlen(w, r, a.steps, a.warmup, cpu)), flush=True)
         copy_calibration(a.copy_calib_mib)
@@ -457,7 +514,7 @@ def main():
                  else [a.workload])
     for n in names:
         w = workloads.WORKLOADS[n]
-        r = bench_one(w, a.steps, a.warmup, a.op)
+        r = bench_one(w, a.steps, a.warmup, a.op, a.settle_seconds)
         cpu = None
         if not a.no_cpu_baseline and n == names[0]:
             cpu = cpu_baseline(w, a.cpu_seconds, a.op)

@@ -48,6 +48,20 @@ __device__ __forceinline__ unsigned pack2(float lo, float hi) {
   }
 }
 
+// Add both 16-bit values of a packed pair (as packed by pack2) to `acc`:
+// one v_dot2c_f32_{bf16,f16} against (1, 1).  The products are exact; the
+// sum is an fp32 sum.
+template <int DT>
+__device__ __forceinline__ float add_pair16(unsigned pair, float acc) {
+  if constexpr (DT == kBF16) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+  } else {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
+  }
+}
+
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
 // Lanes l and l^32 hold the two halves of one query row; these combine a

@@ -92,7 +92,7 @@ template <int DT, int D, bool CAUSAL, int NW = waves16<D>()>
 __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes, int j, int nt,
                                        const unsigned char* src, unsigned char* dst,
                                        const Wave16& w, const u32x4 (&qf)[D / 16],
-                                       f32x16 (&oacc)[D / 32], float& mref, float& l, float sl2) {
+                                       f32x16 (&oacc)[D / 32], float& mref, float& l, float& lr, float sl2) {
   constexpr int BC = bc16<D>();
   constexpr int TILEB = BC * D * 2;
   constexpr int NKK = D / 16, NDT = D / 32;
@@ -160,14 +160,21 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
       const float mnew = fmaxf(mref, pair_max(mx));
       const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
       l *= alpha;
+      lr *= alpha;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
       mref = mnew;
     }
     const float nm = -mref;
     u32x4 pf[NB][2];
-    // l sums the fp32 P (its rounding to 16 bits would leave a relative
-    // error of up to 2^-9 in the LSE of rows that see few keys).
+    // l sums the fp32 P, for the LSE (its rounding to 16 bits would leave a
+    // relative error of up to 2^-8 in the LSE of rows that see few keys).
+    // bf16: lr sums the P as rounded for the PV product, and O is divided by
+    // it, so that the weights applied to the V rows sum to one (a key that
+    // dominates its row then passes its V row through exactly, where the
+    // fp32 sum would leave P's rounding error, up to 2^-8 relative, on it:
+    // with the output's own rounding that exceeded 2e-2 on peaky rows with
+    // |O| >= 4).  fp16 rounds P 8 times more finely, and O is divided by l.
     float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
     for (int n = 0; n < NB; ++n)
@@ -180,6 +187,7 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
           pf[n][hh][i] = pack2<DT>(p0, p1);
           ls0 += p0;
           ls1 += p1;
+          if constexpr (DT == kBF16) lr = add_pair16<DT>(pf[n][hh][i], lr);
         }
     l += ls0 + ls1;
     // O^T += V^T P^T, V^T operands read vPre MFMAs ahead.
@@ -207,7 +215,8 @@ template <int DT, int D, bool CAUSAL, int NW = waves16<D>()>
 __device__ __forceinline__ void step16p(const u16* Kh, const u16* Vh, int kbytes, int j, int nt,
                                         const unsigned char* cur, const unsigned char* nxt, unsigned char* dst,
                                         const Wave16& w, const u32x4 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
-                                        f32x16 (&s)[bc16<D>() / 32], float& mref, float& l, float sl2) {
+                                        f32x16 (&s)[bc16<D>() / 32], float& mref, float& l, float& lr,
+                                        float sl2) {
   constexpr int BC = bc16<D>();
   constexpr int TILEB = BC * D * 2;
   constexpr int NKK = D / 16, NDT = D / 32, NB = BC / 32, KS = BC / 16;
@@ -251,6 +260,7 @@ __device__ __forceinline__ void step16p(const u16* Kh, const u16* Vh, int kbytes
       const float mnew = fmaxf(mref, pair_max(mx));
       const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
       l *= alpha;
+      lr *= alpha;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
       mref = mnew;
@@ -279,6 +289,7 @@ __device__ __forceinline__ void step16p(const u16* Kh, const u16* Vh, int kbytes
         pf[n][hh][q] = pack2<DT>(p0, p1);
         ls0 += p0;
         ls1 += p1;
+        if constexpr (DT == kBF16) lr = add_pair16<DT>(pf[n][hh][q], lr);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -411,7 +422,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fa_fwd_16(const u16* __restrict__ 
   if (nt > 1) issue_tile16<D, NW, BC>(Kh, Vh, kbytes, 1, stage1, w);
   if (nt > 2) issue_tile16<D, NW, BC>(Kh, Vh, kbytes, 2, stage2, w);
 
-  float mref = kMinit, l = 0.f;
+  float mref = kMinit, l = 0.f, lr = 0.f;
   f32x16 oacc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
@@ -429,21 +440,22 @@ __global__ __launch_bounds__(64 * NW, 1) void fa_fwd_16(const u16* __restrict__ 
         s[i / NKK] = mfma_32x32x16<DT>(ks_operand<D>(stage0, w, i), qf[i % NKK], s[i / NKK]);
     }
     for (int j = 0; j < nt; j += 4) {
-      step16p<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j, nt, stage0, stage1, stage3, w, qf, oacc, s, mref, l, sl2);
-      if (j + 1 < nt) step16p<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j + 1, nt, stage1, stage2, stage0, w, qf, oacc, s, mref, l, sl2);
-      if (j + 2 < nt) step16p<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j + 2, nt, stage2, stage3, stage1, w, qf, oacc, s, mref, l, sl2);
-      if (j + 3 < nt) step16p<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j + 3, nt, stage3, stage0, stage2, w, qf, oacc, s, mref, l, sl2);
+      step16p<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j, nt, stage0, stage1, stage3, w, qf, oacc, s, mref, l, lr, sl2);
+      if (j + 1 < nt) step16p<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j + 1, nt, stage1, stage2, stage0, w, qf, oacc, s, mref, l, lr, sl2);
+      if (j + 2 < nt) step16p<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j + 2, nt, stage2, stage3, stage1, w, qf, oacc, s, mref, l, lr, sl2);
+      if (j + 3 < nt) step16p<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j + 3, nt, stage3, stage0, stage2, w, qf, oacc, s, mref, l, lr, sl2);
     }
   } else {
     for (int j = 0; j < nt; j += 4) {
-      tile16<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j, nt, stage0, stage3, w, qf, oacc, mref, l, sl2);
-      if (j + 1 < nt) tile16<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j + 1, nt, stage1, stage0, w, qf, oacc, mref, l, sl2);
-      if (j + 2 < nt) tile16<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j + 2, nt, stage2, stage1, w, qf, oacc, mref, l, sl2);
-      if (j + 3 < nt) tile16<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j + 3, nt, stage3, stage2, w, qf, oacc, mref, l, sl2);
+      tile16<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j, nt, stage0, stage3, w, qf, oacc, mref, l, lr, sl2);
+      if (j + 1 < nt) tile16<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j + 1, nt, stage1, stage0, w, qf, oacc, mref, l, lr, sl2);
+      if (j + 2 < nt) tile16<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j + 2, nt, stage2, stage1, w, qf, oacc, mref, l, lr, sl2);
+      if (j + 3 < nt) tile16<DT, D, CAUSAL, NW>(Kh, Vh, kbytes, j + 3, nt, stage3, stage2, w, qf, oacc, mref, l, lr, sl2);
     }
   }
 
   const float lt = pair_sum(l);
+  const float ltr = DT == kBF16 ? pair_sum(lr) : lt;
   if constexpr (SPLIT) {
     // fp32 partial of this key range (rows past Nq dropped by the range check).
     // Stores of 8 bytes, from two address registers so that they are not
@@ -452,7 +464,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fa_fwd_16(const u16* __restrict__ 
     // and on gfx950 the store then wrote corrupted data (seen on the first
     // dword, in the last four lanes of each 16).
     const bool none = !(lt > 0.f);
-    const float inv = none ? 0.f : 1.0f / lt;
+    const float inv = none ? 0.f : 1.0f / ltr;
     const size_t slot = (size_t)split * BH + bh;
     const auto rP = make_rsrc(Po + slot * Nq * D, nq * D * 4);
     const int off0 = (32 * w.wave + w.l32) * D * 4 + 4 * w.hf * 4;
@@ -479,7 +491,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fa_fwd_16(const u16* __restrict__ 
   // Epilogue: normalise by the combined half-row sums, round to 16 bits,
   // store (rows past Nq are dropped by the buffer range check).
   const bool none = VARLEN && !(lt > 0.f);  // a sequence without keys
-  const float inv = none ? 0.f : 1.0f / lt;
+  const float inv = none ? 0.f : 1.0f / ltr;
   const auto rO = make_rsrc(Oh, nq * ROWB);
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)

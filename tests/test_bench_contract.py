@@ -17,15 +17,16 @@ import workloads
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KEYS = {"metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
         "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"}
-ROOF = {"bound", "achieved", "peak", "unit", "frac", "traffic"}
+ROOF = {"bound", "achieved", "peak", "unit", "frac", "traffic", "hbm_gbs", "hbm_frac", "mfma_busy", "valu_trans_f32"}
 
 
 def _timing(op, peak=2500.0):
+    settle = {"extra_launches": 100, "seconds": 1.0}
     if op == "decode":
         return {"gbs": 5000.0, "ms_per_step": 1.0, "bytes": 5 << 30, "splits_workspace_bytes": 0,
-                "median_launch_ms": 1.0, "min_launch_ms": 0.9}
+                "median_launch_ms": 1.0, "min_launch_ms": 0.9, "warmup_settle": settle}
     return {"tflops": 1000.0, "ms_per_step": 0.3, "flops": 2.7e11, "peak": peak, "median_launch_ms": 0.3,
-            "min_launch_ms": 0.29}
+            "min_launch_ms": 0.29, "warmup_settle": settle}
 
 
 def _check(line, name, bound, unit):
@@ -38,6 +39,15 @@ def _check(line, name, bound, unit):
     assert r["bound"] == bound and r["unit"] == unit and line["unit"] == unit
     assert r["frac"] == round(r["achieved"] / r["peak"], 4)
     assert r["traffic"] is None or isinstance(r["traffic"], int)
+    # counter-derived fields come together from one hash-checked summary
+    if r["traffic"] is None:
+        assert r["hbm_gbs"] is None and r["hbm_frac"] is None
+    else:
+        assert r["hbm_gbs"] == round(r["traffic"] / (line["ms_per_step"] * 1e-3) / 1e9, 1)
+        assert r["hbm_frac"] == round(r["hbm_gbs"] / bench.HBM_PEAK_GBS, 4)
+    assert r["mfma_busy"] is None or 0.0 < r["mfma_busy"] <= 1.0
+    assert r["valu_trans_f32"] is None or isinstance(r["valu_trans_f32"], int)
+    assert "warmup_settle" in line
 
 
 @pytest.mark.parametrize("op,name", [("fwd", workloads.HEADLINE), ("bwd", workloads.HEADLINE),
@@ -79,6 +89,8 @@ def test_committed_counter_summaries_are_well_formed():
         text = open(os.path.join(ROOT, "profiles", p)).read()
         assert re.search(r"^kernel_code_sha256: [0-9a-f]{64}$", text, re.M), p
         assert re.search(r"^traffic_bytes_per_launch: \d+$", text, re.M), p
+        assert re.search(r"^mfma_busy_pct: [0-9.]+$", text, re.M), p
+        assert re.search(r"^valu_trans_f32_per_launch: \d+$", text, re.M), p
         assert "rocprofv3 --pmc FETCH_SIZE" in text and "rocprofv3 --pmc WRITE_SIZE" in text, p
         trace = os.path.join(ROOT, "profiles", f"{tag}__{wl}__kernel_trace.md")
         assert os.path.exists(trace), f"{p}: no kernel trace summary beside it"
