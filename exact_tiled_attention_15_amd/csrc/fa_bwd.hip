@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void bwd_prep(const u16* __restrict__ O, const
 // multiplied by `mul`; rows past the buffer range are dropped.
 template <int DT, int D>
 __device__ __forceinline__ void store_rows16(const f32x16 (&acc)[D / 32], float mul, __amdgpu_buffer_rsrc_t r,
-                                             int row_byte, int base_byte, int hf) {
+                                             int row_byte, int hf) {
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -115,7 +115,7 @@ __device__ __forceinline__ void store_rows16(const f32x16 (&acc)[D / 32], float 
       u32x2 v;
       v[0] = pack2<DT>(acc[dt][4 * g + 0] * mul, acc[dt][4 * g + 1] * mul);
       v[1] = pack2<DT>(acc[dt][4 * g + 2] * mul, acc[dt][4 * g + 3] * mul);
-      __builtin_amdgcn_raw_buffer_store_b64(v, r, row_byte + (32 * dt + 8 * g + 4 * hf) * 2, base_byte, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(v, r, row_byte + (32 * dt + 8 * g + 4 * hf) * 2, 0, 0);
     }
 }
 
@@ -125,10 +125,10 @@ __device__ __forceinline__ void store_rows16(const f32x16 (&acc)[D / 32], float 
 template <int D>
 __device__ __forceinline__ void load_frag(u32x4 (&f)[D / 16], const u16* base, int rows, int row0,
                                           const Wave16& w) {
-  const auto r = make_rsrc(base, rows * D * 2);
+  const auto r = make_rsrc_at(base, row0 * D * 2, rows * D * 2);
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
-    f[kk] = __builtin_amdgcn_raw_buffer_load_b128(r, w.l32 * D * 2 + (16 * kk + 8 * w.hf) * 2, row0 * D * 2, 0);
+    f[kk] = __builtin_amdgcn_raw_buffer_load_b128(r, w.l32 * D * 2 + (16 * kk + 8 * w.hf) * 2, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -253,8 +253,8 @@ __global__ __launch_bounds__(64 * dq_waves<D>(), 1) void bwd_dq(const u16* __res
         dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 1, nt, stage1, stage0, w, qf, dof, acc, lse2, delta, sl2);
     }
   }
-  const auto rq = make_rsrc(dQg + hr.qo, nq * ROWB);
-  store_rows16<DT, D>(acc, scale, rq, (32 * w.wave + w.l32) * ROWB, q0 * ROWB, w.hf);
+  const auto rq = make_rsrc_at(dQg + hr.qo, q0 * ROWB, nq * ROWB);
+  store_rows16<DT, D>(acc, scale, rq, (32 * w.wave + w.l32) * ROWB, w.hf);
 }
 
 // ---------------------------------------------------------------------------
@@ -281,10 +281,10 @@ __device__ __forceinline__ void issue_kv_tile(const u16* Qh, const u16* dOh, int
   constexpr int TILEB = 64 * D * 2;
   issue_tile16<D, kWavesKV>(Qh, dOh, qbytes, t, dst, w);
   if (w.wave == 0) {
-    const auto rl = make_rsrc(l2h, Nq * 4);
-    const auto rd = make_rsrc(dlh, Nq * 4);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)(dst + 2 * TILEB), 4, w.lane * 4, t * 256, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)(dst + 2 * TILEB + 256), 4, w.lane * 4, t * 256, 0, 0);
+    const auto rl = make_rsrc_at(l2h, t * 256, Nq * 4);
+    const auto rd = make_rsrc_at(dlh, t * 256, Nq * 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)(dst + 2 * TILEB), 4, w.lane * 4, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)(dst + 2 * TILEB + 256), 4, w.lane * 4, 0, 0, 0);
   }
 }
 
@@ -540,10 +540,10 @@ __global__ __launch_bounds__(64 * kWavesKV, 1) void bwd_dkdv(const u16* __restri
       }
     }
   }
-  const auto rk = make_rsrc(dKg + hr.ko, nk * ROWB);
-  const auto rv = make_rsrc(dVg + hr.ko, nk * ROWB);
-  if constexpr (GRADS & 1) store_rows16<DT, D>(dk, scale, rk, (32 * w.wave + w.l32) * ROWB, kb0 * ROWB, w.hf);
-  if constexpr (GRADS & 2) store_rows16<DT, D>(dv, 1.0f, rv, (32 * w.wave + w.l32) * ROWB, kb0 * ROWB, w.hf);
+  const auto rk = make_rsrc_at(dKg + hr.ko, kb0 * ROWB, nk * ROWB);
+  const auto rv = make_rsrc_at(dVg + hr.ko, kb0 * ROWB, nk * ROWB);
+  if constexpr (GRADS & 1) store_rows16<DT, D>(dk, scale, rk, (32 * w.wave + w.l32) * ROWB, w.hf);
+  if constexpr (GRADS & 2) store_rows16<DT, D>(dv, 1.0f, rv, (32 * w.wave + w.l32) * ROWB, w.hf);
 }
 
 // VARLEN: q, o, dout, dq [H, total_q, D]; k, v, dk, dv [H, total_k, D]; lse

@@ -119,12 +119,20 @@ __device__ __forceinline__ HeadRows head_rows(int bh, int Nq, int Nk, int D, con
 // ---------------------------------------------------------------------------
 // 16-bit kernel (bf16 / fp16), D in {32, 64, 128}, 64-key tiles.
 // ---------------------------------------------------------------------------
-// Buffer resources: 32-bit byte offsets from a per-head base, with the
-// hardware range check (loads past num_records return 0, stores past it are
-// dropped), which handles the ragged Nq / Nk tails.
+// Buffer resources for the ragged Nq / Nk tails.  Every buffer access here
+// is a raw (stride 0) access whose scalar offset is 0: the resource's base
+// is the start of the tile or row block being accessed, num_records the
+// bytes of the tensor from there on, and the per-lane VGPR offset plus the
+// instruction's immediate offset is range-checked against num_records:
+// loads past it return 0 (into LDS too, for the direct-to-LDS form) and
+// stores past it are dropped.
 constexpr int kBufFlags = 0x00020000;  // gfx9 buffer descriptor word 3 (32-bit data format)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufFlags);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes > 0 ? bytes : 0, kBufFlags);
+}
+// The resource of the bytes [off, total) of a tensor at `base`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_at(const void* base, int off, int total) {
+  return make_rsrc((const unsigned char*)base + off, total - off);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -210,15 +218,15 @@ __device__ __forceinline__ void issue_tile16(const u16* Kh, const u16* Vh, int k
   static_assert(BC % 16 == 0 && BC * D * 2 % 1024 == 0, "whole 16-row groups and 1 KB pieces");
   constexpr int TILEB = BC * D * 2;
   constexpr int NG = TILEB / 1024;
-  const auto rk = make_rsrc(Kh, kbytes);
-  const auto rv = make_rsrc(Vh, kbytes);
+  const auto rk = make_rsrc_at(Kh, t * TILEB, kbytes);
+  const auto rv = make_rsrc_at(Vh, t * TILEB, kbytes);
 #pragma unroll
   for (int I = 0; I < (NG + NW - 1) / NW; ++I) {
     const int G = w.wave + NW * I;
     if (G < NG) {
       const int go = dma_src_off<D>(G, w.lane);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst + G * 1024), 16, go, t * TILEB, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst + TILEB + G * 1024), 16, go, t * TILEB, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst + G * 1024), 16, go, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst + TILEB + G * 1024), 16, go, 0, 0, 0);
     }
   }
 }

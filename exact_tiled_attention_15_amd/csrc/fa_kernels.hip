@@ -411,11 +411,11 @@ __global__ __launch_bounds__(64 * NW, 1) void fa_fwd_16(const u16* __restrict__ 
   // in order, so waiting for a K/V tile also covers Q.
   u32x4 qf[NKK];
   {
-    const auto rQ = make_rsrc(Qh, nq * ROWB);
+    const auto rQ = make_rsrc_at(Qh, q0 * ROWB, nq * ROWB);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
       qf[kk] = __builtin_amdgcn_raw_buffer_load_b128(rQ, (32 * w.wave + w.l32) * ROWB + (16 * kk + 8 * w.hf) * 2,
-                                                     q0 * ROWB, 0);
+                                                     0, 0);
   }
   // Tiles 0..2 into stages 0..2.
   if ((!SPLIT && !VARLEN) || nt > 0) issue_tile16<D, NW, BC>(Kh, Vh, kbytes, 0, stage0, w);
@@ -466,7 +466,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fa_fwd_16(const u16* __restrict__ 
     const bool none = !(lt > 0.f);
     const float inv = none ? 0.f : 1.0f / ltr;
     const size_t slot = (size_t)split * BH + bh;
-    const auto rP = make_rsrc(Po + slot * Nq * D, nq * D * 4);
+    const auto rP = make_rsrc_at(Po + slot * Nq * D, q0 * D * 4, nq * D * 4);
     const int off0 = (32 * w.wave + w.l32) * D * 4 + 4 * w.hf * 4;
     int off1 = off0 + 8;
     asm volatile("" : "+v"(off1));
@@ -477,14 +477,14 @@ __global__ __launch_bounds__(64 * NW, 1) void fa_fwd_16(const u16* __restrict__ 
         const f32x2 v0 = {oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv};
         const f32x2 v1 = {oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv};
         const int col = (32 * dt + 8 * g) * 4;
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v0), rP, off0 + col, q0 * D * 4, 0);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v1), rP, off1 + col, q0 * D * 4, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v0), rP, off0 + col, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v1), rP, off1 + col, 0, 0);
       }
     if (w.hf == 0) {
-      const auto rL = make_rsrc(Pl + slot * Nq, nq * 4);
+      const auto rL = make_rsrc_at(Pl + slot * Nq, q0 * 4, nq * 4);
       const float lse = none ? -INFINITY : (mref + __log2f(lt)) * kLn2;
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse), rL, (32 * w.wave + w.l32) * 4,
-                                            q0 * 4, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse), rL, (32 * w.wave + w.l32) * 4, 0,
+                                            0);
     }
     return;
   }
@@ -492,7 +492,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fa_fwd_16(const u16* __restrict__ 
   // store (rows past Nq are dropped by the buffer range check).
   const bool none = VARLEN && !(lt > 0.f);  // a sequence without keys
   const float inv = none ? 0.f : 1.0f / ltr;
-  const auto rO = make_rsrc(Oh, nq * ROWB);
+  const auto rO = make_rsrc_at(Oh, q0 * ROWB, nq * ROWB);
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -501,13 +501,13 @@ __global__ __launch_bounds__(64 * NW, 1) void fa_fwd_16(const u16* __restrict__ 
       v[0] = pack2<DT>(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv);
       v[1] = pack2<DT>(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
       __builtin_amdgcn_raw_buffer_store_b64(v, rO, (32 * w.wave + w.l32) * ROWB + (32 * dt + 8 * g + 4 * w.hf) * 2,
-                                            q0 * ROWB, 0);
+                                            0, 0);
     }
   if (w.hf == 0) {
-    const auto rL = make_rsrc(Lh, nq * 4);
+    const auto rL = make_rsrc_at(Lh, q0 * 4, nq * 4);
     const float lse = none ? -INFINITY : (mref + __log2f(lt)) * kLn2;
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse), rL, (32 * w.wave + w.l32) * 4,
-                                          q0 * 4, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse), rL, (32 * w.wave + w.l32) * 4, 0,
+                                          0);
   }
 }
 
