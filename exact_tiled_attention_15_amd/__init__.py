@@ -13,6 +13,7 @@ import ctypes
 import os
 
 __all__ = ["fa_fwd", "fa_fwd_scaled", "fa_fwd_varlen", "forward_varlen", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "forward_splitkv",
+           "fa_fwd_splitkv_static", "FA_STATIC_SCRATCH_BYTES",
            "fa_bwd", "fa_bwd_workspace_size", "backward", "fa_bwd_varlen", "backward_varlen", "fa_status_str", "forward", "load_library", "LIB_PATH",
            "FA_DTYPE_FP32", "FA_DTYPE_FP16", "FA_DTYPE_BF16", "FA_OK", "FA_DEFAULT_SCALE", "FaError",
            "EXPORTED_SYMBOLS"]
@@ -23,8 +24,10 @@ FA_DTYPE_FP32, FA_DTYPE_FP16, FA_DTYPE_BF16 = 0, 1, 2
 FA_OK = 0
 # softmax_scale value that makes the C entry points use 1/sqrt(D)
 FA_DEFAULT_SCALE = 0.0
-EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_scaled", "fa_fwd_varlen", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_bwd",
-                    "fa_bwd_workspace_size", "fa_bwd_varlen", "fa_status_str")
+# device scratch of fa_fwd_splitkv_static (bytes, per device)
+FA_STATIC_SCRATCH_BYTES = 32 * 1024 * 1024
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_scaled", "fa_fwd_varlen", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
+                    "fa_fwd_splitkv_static", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_varlen", "fa_status_str")
 
 _lib = None
 
@@ -59,6 +62,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fa_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int64] * 6
     lib.fa_fwd_splitkv.restype = ctypes.c_int
     lib.fa_fwd_splitkv.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 6 + \
+        [ctypes.c_double, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_fwd_splitkv_static.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_static.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + \
         [ctypes.c_double, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.fa_bwd_workspace_size.restype = ctypes.c_int64
     lib.fa_bwd_workspace_size.argtypes = [ctypes.c_int64] * 3
@@ -110,6 +116,16 @@ def fa_fwd_splitkv(q: int, k: int, v: int, o: int, lse: int, workspace: int, wor
     """Call the C ``fa_fwd_splitkv`` with raw device addresses; returns the status code."""
     return load_library().fa_fwd_splitkv(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, D,
                                          float(softmax_scale), int(num_splits), int(causal), int(dtype), stream)
+
+
+def fa_fwd_splitkv_static(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int, Nk: int, D: int,
+                          softmax_scale: float, num_splits: int, causal: int, dtype: int,
+                          stream: int | None) -> int:
+    """Call the C ``fa_fwd_splitkv_static`` (split-KV with the library's static
+    device scratch, no allocation) with raw device addresses; returns the
+    status code."""
+    return load_library().fa_fwd_splitkv_static(q, k, v, o, lse, B, H, Nq, Nk, D, float(softmax_scale),
+                                                int(num_splits), int(causal), int(dtype), stream)
 
 
 def fa_bwd_workspace_size(B: int, H: int, Nq: int) -> int:

@@ -176,10 +176,13 @@ extern "C" int64_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t N
   return bytes;
 }
 
-extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
-                              void* workspace, int64_t workspace_bytes, int64_t B, int64_t H, int64_t Nq,
-                              int64_t Nk, int64_t D, double softmax_scale, int64_t num_splits, int causal,
-                              int dtype, void* stream) {
+namespace {
+
+// fa_fwd_splitkv and fa_fwd_splitkv_static: the partials go to the caller's
+// workspace, or (use_static) to the library's static scratch.
+int splitkv(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+            int64_t workspace_bytes, bool use_static, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+            double softmax_scale, int64_t num_splits, int causal, int dtype, void* stream) {
   bool empty = false;
   const int st = validate(q, k, v, o, lse, B, H, Nq, Nk, D, dtype, &empty);
   if (st != FA_OK) return st;
@@ -215,6 +218,12 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
     return FA_ERR_SHAPE;
   const int64_t need = fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D, num_splits);
   if (need < 0) return FA_ERR_SHAPE;
+  if (use_static) {
+    if (need > FA_STATIC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+    if (cus <= 0 || fa_static_scratch(&workspace) != 0) return FA_ERR_HIP;
+    a.workspace = workspace;
+    return fa_launch_fwd_splitkv(a, (int)n, (int)len) == 0 ? FA_OK : FA_ERR_HIP;
+  }
   if (!workspace) return FA_ERR_NULL;
   if (workspace_bytes < need) return FA_ERR_WORKSPACE;
   if ((uintptr_t)workspace & 15u) return FA_ERR_ALIGN;
@@ -227,6 +236,24 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
   a.workspace = workspace;
   if (cus <= 0) return FA_ERR_HIP;
   return fa_launch_fwd_splitkv(a, (int)n, (int)len) == 0 ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                              void* workspace, int64_t workspace_bytes, int64_t B, int64_t H, int64_t Nq,
+                              int64_t Nk, int64_t D, double softmax_scale, int64_t num_splits, int causal,
+                              int dtype, void* stream) {
+  return splitkv(q, k, v, o, lse, workspace, workspace_bytes, false, B, H, Nq, Nk, D, softmax_scale, num_splits,
+                 causal, dtype, stream);
+}
+
+extern "C" int fa_fwd_splitkv_static(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                                     double softmax_scale, int64_t num_splits, int causal, int dtype,
+                                     void* stream) {
+  return splitkv(q, k, v, o, lse, nullptr, 0, true, B, H, Nq, Nk, D, softmax_scale, num_splits, causal, dtype,
+                 stream);
 }
 
 extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
@@ -466,6 +493,9 @@ extern "C" const char* fa_status_str(int status) {
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch error";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: softmax_scale must be a finite number > 0";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace smaller than the *_workspace_size() call returns";
+    case FA_ERR_SCRATCH:
+      return "FA_ERR_SCRATCH: the split-KV partials of this call exceed the library's static scratch "
+             "(FA_STATIC_SCRATCH_BYTES = 32 MiB); use fa_fwd_splitkv with a workspace or fewer ranges";
     default: return "unknown fa_status code";
   }
 }

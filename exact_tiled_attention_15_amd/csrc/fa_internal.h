@@ -40,6 +40,11 @@ int fa_launch_fwd(const FaLaunch& a);
 // (nsplit * BH * Nq * (D + 1) floats), then a merge kernel writes o and lse.
 int fa_launch_fwd_splitkv(const FaLaunch& a, int nsplit, int split_len);
 
+// Device address of the library's static split-KV scratch
+// (FA_STATIC_SCRATCH_BYTES) on the current device, looked up once per device.
+// Returns 0, or the HIP error of the lookup.
+int fa_static_scratch(void** addr);
+
 // Packed variable-length forward (16-bit dtypes): q, o [H, total_q, D];
 // k, v [H, total_k, D]; lse [H, total_q]; per-sequence offsets cu_q, cu_k.
 int fa_launch_fwd_varlen(const FaLaunch& a);

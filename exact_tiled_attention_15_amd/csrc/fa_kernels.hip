@@ -44,6 +44,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
+#include "../../include/fa.h"
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -940,6 +943,37 @@ int fa_launch_fwd(const FaLaunch& a) {
     default:
       return a.D == 32 ? dispatch32<32>(a, sl2) : a.D == 64 ? dispatch32<64>(a, sl2) : dispatch32<128>(a, sl2);
   }
+}
+
+// Scratch of fa_fwd_splitkv_static, for callers that cannot allocate: the
+// key-range partials go to this file-scope device array instead of a caller
+// workspace.  Every device the library runs on holds its own copy, at its
+// own address, until the process ends; all calls on one device share it.
+// In host code `scratch` is only a stand-in for the device symbol: its
+// device address is looked up once per device (fa_static_scratch) and only
+// that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[FA_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kMaxDevices];  // device address of `scratch`, per device
+}  // namespace
+
+int fa_static_scratch(void** addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    scratch_addr[dev] = p;
+  }
+  *addr = scratch_addr[dev];
+  return 0;
 }
 
 #endif  // FA_FWD_D256

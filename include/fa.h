@@ -68,7 +68,9 @@ typedef enum {
   FA_ERR_SCALE = 8,    /* softmax_scale neither FA_DEFAULT_SCALE nor a finite
                           number > 0 (or so small or large that softmax_scale
                           * log2(e) is not a normal float) */
-  FA_ERR_WORKSPACE = 9 /* workspace_bytes below the matching *_workspace_size() */
+  FA_ERR_WORKSPACE = 9, /* workspace_bytes below the matching *_workspace_size() */
+  FA_ERR_SCRATCH = 10    /* fa_fwd_splitkv_static: the call's partials need more
+                            than FA_STATIC_SCRATCH_BYTES */
 } fa_status;
 
 /*
@@ -159,6 +161,36 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    void* workspace, int64_t workspace_bytes, int64_t B, int64_t H, int64_t Nq,
                    int64_t Nk, int64_t D, double softmax_scale, int64_t num_splits, int causal,
                    int dtype, void* stream);
+
+/* Size of the device scratch that fa_fwd_splitkv_static uses: 32 MiB. */
+#define FA_STATIC_SCRATCH_BYTES (32 * 1024 * 1024)
+
+/*
+ * fa_fwd_splitkv_static -- fa_fwd_splitkv for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same key ranges, kernels and result,
+ * but the fp32 partials go to a scratch array that the library holds in
+ * device memory (FA_STATIC_SCRATCH_BYTES on every device it runs on, kept
+ * until the process ends) instead of a caller workspace.  The call allocates
+ * nothing; the caller still passes every input and output.
+ *
+ * Every argument, layout and error is that of fa_fwd_splitkv without its
+ * workspace arguments, plus FA_ERR_SCRATCH (before anything is enqueued)
+ * when the call's partials, fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, D,
+ * num_splits) bytes, exceed FA_STATIC_SCRATCH_BYTES: at D = 128 the scratch
+ * holds 65027 (query row, key range) partials, e.g. 32 heads x 16 rows x 64
+ * ranges.  A call that runs as one range uses no scratch.
+ *
+ * All calls on one device share its scratch array: calls that overlap in
+ * time on one device (on different streams, or from different host threads
+ * without ordering) race and may return wrong results; calls on one stream
+ * run in order.  Each call writes every partial it reads, so nothing has to
+ * be cleared between calls.
+ */
+int fa_fwd_splitkv_static(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                          double softmax_scale, int64_t num_splits, int causal, int dtype,
+                          void* stream);
 
 /*
  * fa_fwd_varlen -- fa_fwd_scaled over a batch of B packed sequences of

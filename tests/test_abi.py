@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings():
     for code, tag in [(0, "FA_OK"), (1, "FA_ERR_NULL"), (2, "FA_ERR_SHAPE"), (3, "FA_ERR_HEAD_DIM"),
                       (4, "FA_ERR_DTYPE"), (5, "FA_ERR_ALIGN"), (6, "FA_ERR_ALIAS"), (7, "FA_ERR_HIP"),
-                      (8, "FA_ERR_SCALE"), (9, "FA_ERR_WORKSPACE")]:
+                      (8, "FA_ERR_SCALE"), (9, "FA_ERR_WORKSPACE"), (10, "FA_ERR_SCRATCH")]:
         assert fa.fa_status_str(code).startswith(tag)
     assert "unknown" in fa.fa_status_str(99)
 
@@ -206,6 +206,30 @@ def test_splitkv_validation_codes(kw, code):
 
 def test_splitkv_noop():
     assert call_split(B=0, q=0, k=0, v=0, o=0, lse=0, ws=0, ws_bytes=0) == 0
+
+
+def call_static(q=Q, k=K, v=V, o=O, lse=L, B=1, H=4, Nq=4, Nk=8192, D=128, scale=0.1, splits=0, causal=0, dtype=2):
+    return fa.fa_fwd_splitkv_static(q, k, v, o, lse, B, H, Nq, Nk, D, scale, splits, causal, dtype, None)
+
+
+def test_splitkv_static_checks():
+    # partials beyond the static scratch: FA_ERR_SCRATCH before anything is
+    # enqueued (1024 ranges x 64 heads x 256 rows x 129 floats > 32 MiB);
+    # one range more than fits is rejected, one that fits would run
+    assert fa.FA_STATIC_SCRATCH_BYTES == 32 << 20
+    assert fa.fa_fwd_splitkv_workspace_size(1, 64, 256, 1 << 20, 128, 1024) > fa.FA_STATIC_SCRATCH_BYTES
+    assert call_static(H=64, Nq=256, Nk=1 << 20, splits=1024) == 10
+    per_range = 64 * 256 * 129 * 4
+    fits = fa.FA_STATIC_SCRATCH_BYTES // per_range
+    assert fa.fa_fwd_splitkv_workspace_size(1, 64, 256, 1 << 20, 128, fits + 1) > fa.FA_STATIC_SCRATCH_BYTES
+    assert call_static(H=64, Nq=256, Nk=1 << 20, splits=fits + 1) == 10
+    # the other checks are fa_fwd_splitkv's
+    assert call_static(q=0) == 1
+    assert call_static(scale=-1.0) == 8
+    assert call_static(D=96) == 3
+    assert call_static(splits=5000) == 2
+    assert call_static(o=Q) == 6
+    assert call_static(B=0, q=0, k=0, v=0, o=0, lse=0) == 0
 
 
 CQ, CK = (11 << 40), (12 << 40)
