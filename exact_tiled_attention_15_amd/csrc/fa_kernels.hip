@@ -81,6 +81,43 @@ constexpr int bc16() {
   return D == 256 ? 32 : 64;
 }
 
+// P = exp2(s sl2 + nm) of a lane's scores (16 per 32-key block), packed to
+// 16 bits for the PV product; tl sums the fp32 P (bf16 only, for the LSE),
+// tr the P as rounded (the normaliser; for fp16 also the LSE's sum, whose
+// rounding error, at most 2^-11 relative, stays below the LSE tolerance).
+template <int DT, int NB>
+__device__ __forceinline__ void exp_tile(const f32x16 (&s)[NB], float sl2, float nm, u32x4 (&pf)[NB][2],
+                                         float& tl, float& tr) {
+  float ls0 = 0.f, ls1 = 0.f, lr0 = 0.f;
+#pragma unroll
+  for (int n = 0; n < NB; ++n)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[n][8 * hh + 2 * i], sl2, nm));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[n][8 * hh + 2 * i + 1], sl2, nm));
+        pf[n][hh][i] = pack2<DT>(p0, p1);
+        if constexpr (DT == kBF16) {
+          ls0 += p0;
+          ls1 += p1;
+        }
+        lr0 = add_pair16<DT>(pf[n][hh][i], lr0);
+      }
+  tl = ls0 + ls1;
+  tr = lr0;
+}
+
+// Which rule moves the reference max of the 8-wave tile (see tile16):
+// the tile's P sums (no per-score max) where that pays: D = 128, and fp16 at
+// D = 64, whose kernel still fits the 128 registers that let two workgroups
+// share a CU (bf16 at D = 64, with its second sum, does not; and there the
+// per-score max is kept).
+template <int DT, int D>
+constexpr bool sum_checked() {
+  return D == 128 || (D == 64 && DT == kFP16);
+}
+
 // One K/V tile of the 16-bit kernel (stage `src`).  Tile j is complete in
 // LDS since the previous tile's barrier (each barrier waits for the tile
 // after its own), so the wave first reads the first K operands of its score
@@ -100,9 +137,11 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
   constexpr int TILEB = BC * D * 2;
   constexpr int NKK = D / 16, NDT = D / 32;
   constexpr int NB = BC / 32;  // 32-key score blocks per tile
-  // mref is raised only when a tile's row max exceeds it by more than kTau
-  // (log2 units), so P = exp2(t - mref) stays below 2^kTau; O and l always
-  // share mref, so O / l and mref + log2(l) are exact whatever mref is.
+  // The reference mref moves lazily: under the max rule only when a tile's
+  // row max exceeds it by more than kTau (log2 units), so P = exp2(t - mref)
+  // stays below 2^kTau; under the sum rule (sum_checked) only when a lane's
+  // P sum exceeds 2^15.  O and l always share mref, so O / l and
+  // mref + log2(l) are exact whatever mref is.
   constexpr float kTau = 8.0f;
   // S^T = K Q^T.  The K operands are read kPre MFMAs ahead of their use
   // (LDS latency, not bandwidth, bounds these reads); kPre also bounds the
@@ -149,50 +188,81 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
         for (int r = 0; r < 16; ++r)
           s[n][r] = (32 * n + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[n][r];
     }
-    // Row max of the raw scores (scale > 0 commutes with max).
-    float mx = s[0][0];
-#pragma unroll
-    for (int n = 0; n < NB; ++n)
-#pragma unroll
-      for (int r = (n == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[n][r]);
-    // Half-row max in the scaled log2 domain: a row's max exceeds mref + kTau
-    // exactly when one of its halves does, so the lane-pair exchange is only
-    // needed on the (rare) path that moves the reference.
-    mx *= sl2;
-    if (__builtin_amdgcn_ballot_w64(mx > mref + kTau)) {
-      const float mnew = fmaxf(mref, pair_max(mx));
-      const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
-      l *= alpha;
-      lr *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
-      mref = mnew;
-    }
-    const float nm = -mref;
     u32x4 pf[NB][2];
-    // l sums the fp32 P, for the LSE (its rounding to 16 bits would leave a
-    // relative error of up to 2^-8 in the LSE of rows that see few keys).
-    // bf16: lr sums the P as rounded for the PV product, and O is divided by
-    // it, so that the weights applied to the V rows sum to one (a key that
-    // dominates its row then passes its V row through exactly, where the
-    // fp32 sum would leave P's rounding error, up to 2^-8 relative, on it:
-    // with the output's own rounding that exceeded 2e-2 on peaky rows with
-    // |O| >= 4).  fp16 rounds P 8 times more finely, and O is divided by l.
-    float ls0 = 0.f, ls1 = 0.f;
+    if constexpr (sum_checked<DT, D>()) {
+      // P = exp2(t - mref) with the current reference first: each P is at
+      // most its lane's sum of 32 P, so the reference is moved (and the P
+      // recomputed) only when such a sum exceeds kBound = 2^15 (P then fits
+      // fp16 and nothing overflows), and on the wave's first tile.
+      constexpr float kBound = 32768.0f;
+      float tl = 0.f, tr = 0.f;
+      bool redo = j == 0;
+      if (!redo) {
+        exp_tile<DT, NB>(s, sl2, -mref, pf, tl, tr);
+        redo = __builtin_amdgcn_ballot_w64(!((DT == kBF16 ? tl : tr) <= kBound)) != 0;
+      }
+      if (redo) {
+        float mx = s[0][0];
 #pragma unroll
-    for (int n = 0; n < NB; ++n)
+        for (int n = 0; n < NB; ++n)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+          for (int r = (n == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[n][r]);
+        const float mnew = fmaxf(mref, pair_max(mx * sl2));
+        const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+        l *= alpha;
+        lr *= alpha;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[n][8 * hh + 2 * i], sl2, nm));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[n][8 * hh + 2 * i + 1], sl2, nm));
-          pf[n][hh][i] = pack2<DT>(p0, p1);
-          ls0 += p0;
-          ls1 += p1;
-          if constexpr (DT == kBF16) lr = add_pair16<DT>(pf[n][hh][i], lr);
-        }
-    l += ls0 + ls1;
+        for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+        mref = mnew;
+        exp_tile<DT, NB>(s, sl2, -mref, pf, tl, tr);
+      }
+      l += DT == kBF16 ? tl : tr;
+      lr += tr;
+    } else {
+      // Row max of the raw scores (scale > 0 commutes with max).
+      float mx = s[0][0];
+#pragma unroll
+      for (int n = 0; n < NB; ++n)
+#pragma unroll
+        for (int r = (n == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[n][r]);
+      // Half-row max in the scaled log2 domain: a row's max exceeds mref + kTau
+      // exactly when one of its halves does, so the lane-pair exchange is only
+      // needed on the (rare) path that moves the reference.
+      mx *= sl2;
+      if (__builtin_amdgcn_ballot_w64(mx > mref + kTau)) {
+        const float mnew = fmaxf(mref, pair_max(mx));
+        const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+        l *= alpha;
+        lr *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+        mref = mnew;
+      }
+      const float nm = -mref;
+      // l sums the fp32 P, for the LSE (its rounding to 16 bits would leave a
+      // relative error of up to 2^-8 in the LSE of rows that see few keys).
+      // bf16: lr sums the P as rounded for the PV product, and O is divided by
+      // it, so that the weights applied to the V rows sum to one (a key that
+      // dominates its row then passes its V row through exactly, where the
+      // fp32 sum would leave P's rounding error, up to 2^-8 relative, on it:
+      // with the output's own rounding that exceeded 2e-2 on peaky rows with
+      // |O| >= 4).  fp16 rounds P 8 times more finely, and O is divided by l.
+      float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+      for (int n = 0; n < NB; ++n)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[n][8 * hh + 2 * i], sl2, nm));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[n][8 * hh + 2 * i + 1], sl2, nm));
+            pf[n][hh][i] = pack2<DT>(p0, p1);
+            ls0 += p0;
+            ls1 += p1;
+            if constexpr (DT == kBF16) lr = add_pair16<DT>(pf[n][hh][i], lr);
+          }
+      l += ls0 + ls1;
+    }
     // O^T += V^T P^T, V^T operands read vPre MFMAs ahead.
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
@@ -351,7 +421,7 @@ __device__ __forceinline__ bool fwd_block(int nqt, int BH, int& bh, int& qt, int
 // BH = B*H, Nq = the longest sequence's query count (sets nqt).  Rows of a
 // sequence without keys get O = 0 and LSE = -inf.
 template <int DT, int D, bool CAUSAL, bool SPLIT = false, bool VARLEN = false, int NW = waves16<D>()>
-__global__ __launch_bounds__(64 * NW, 1) void fa_fwd_16(const u16* __restrict__ Qg,
+__global__ __launch_bounds__(64 * NW, (D == 64 && NW == 8) ? 4 : 1) void fa_fwd_16(const u16* __restrict__ Qg,
                                                            const u16* __restrict__ Kg,
                                                            const u16* __restrict__ Vg,
                                                            u16* __restrict__ Og,
