@@ -23,7 +23,8 @@
  * no pointer after a call returns, allocates nothing, copies nothing and
  * does not synchronise; work is enqueued on `stream` and completes
  * asynchronously.  Calls are re-entrant and thread-safe (no global mutable
- * state).  Every element of o and lse is written.
+ * state), except that fa_fwd_splitkv_static calls share one device array per
+ * device (see there).  Every element of o and lse is written.
  *
  * Errors: arguments are validated before any work is enqueued; a status
  * other than FA_OK and FA_ERR_HIP means nothing was enqueued.  FA_ERR_HIP
