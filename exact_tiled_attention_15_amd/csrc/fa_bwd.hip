@@ -24,7 +24,11 @@
 //    rows plus their LSE and delta stream through a 4-stage ring; per tile
 //    S = Q K^T, dP = dO V^T (the wave's keys along the MFMA N dimension, so
 //    P and dS come out in the B-operand layout of the next products), then
-//    dV^T += dO^T P and dK^T += Q^T dS (dO and Q read transposed).
+//    dV^T += dO^T P and dK^T += Q^T dS (dO and Q read transposed);
+//  * bwd_dkdv2 (D = 128): the same products with 8 waves, two per key group
+//    on one SIMD: one computes S, P and dV, the other dP, dS and dK with the
+//    P its sibling passes through LDS, so that each holds one fragment and
+//    one gradient and two waves fit each SIMD.
 // S and dP are recomputed in both kernels: seven tile products instead of
 // the five a single kernel with atomic dQ updates would need.
 // At D = 256 bwd_dq has 4 waves (one per SIMD), bwd_dkdv runs as two kernels
@@ -307,161 +311,52 @@ __device__ __forceinline__ void kv_tile(const u16* Qh, const u16* dOh, int qbyte
   wait_tile_and_barrier(ST == 4 && j + 2 < nt ? kv_loads_per_tile<D>(w.wave) : 0);
   if (j + ST - 1 < nt) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t + ST - 1, dst, w);
   if (CAUSAL && q0 + 63 < wk0) return;  // every query of the tile precedes the wave's keys
+  static_assert(D != 128, "D = 128 runs bwd_dkdv2");
   static_assert(GRADS == 3 || D == 256, "one gradient per kernel only at D = 256");
-  if constexpr (D == 128) {
-    // Queries of the tile below `qlim` (relative to q0) precede this lane's key
-    // and are masked (causal diagonal tiles only; elsewhere no query is).
-    const int qlim = (CAUSAL && q0 < wk0 + 31) ? wk0 + w.l32 - q0 : 0;
-    // One wave per SIMD, so the wave overlaps its own work, in an order fixed
-    // by scheduling fences: block 1's S and dP MFMAs each carry one score of
-    // block 0's softmax arithmetic, block 0's dV and dK MFMAs each carry one of
-    // block 1's, and every LDS operand is read a few MFMAs ahead.
-    constexpr int NS = 2 * NKK;  // S and dP MFMAs of a 32-query block (interleaved)
-    constexpr int NG = 4 * NDT;  // dV and dK MFMAs of a block (interleaved)
-    // Lane l holds key wk0 + l % 32 and queries q0 + 32n + 8g + 4hf + e (r = 4g + e).
-    f32x16 s[2], dp[2];
-    u32x4 pf[2][2], dsf[2][2];
-    float pv[2][16], dsv[2][16];
-    // operand i of the score MFMAs of block n: even i -> Q row operand for S,
-    // odd i -> dO row operand for dP, both at head-dimension step i / 2
-    auto score_operand = [&](int n, int i) -> u32x4 {
-      return (i & 1) ? ks_operand<D>(dos, w, n * NKK + (i >> 1)) : ks_operand<D>(qs, w, n * NKK + (i >> 1));
-    };
-    auto score_mfma = [&](int n, int i, u32x4 a) {
-      if (i & 1)
-        dp[n] = mfma_32x32x16<DT>(a, vf[i >> 1], dp[n]);
-      else
-        s[n] = mfma_32x32x16<DT>(a, kf[i >> 1], s[n]);
-    };
-    // operand i of the gradient MFMAs of block n: even i -> dO^T for dV,
-    // odd i -> Q^T for dK, at (dt, hh) = ((i / 2) / 2, (i / 2) % 2)
-    auto grad_operand = [&](int n, int i) -> u32x4 {
-      const int u = i >> 1, idx = 4 * (u >> 1) + 2 * n + (u & 1);
-      return (i & 1) ? vt_operand<D>(qs, w, idx) : vt_operand<D>(dos, w, idx);
-    };
-    auto grad_mfma = [&](int n, int i, u32x4 a) {
-      const int u = i >> 1;
-      if (i & 1)
-        dk[u >> 1] = mfma_32x32x16<DT>(a, dsf[n][u & 1], dk[u >> 1]);
-      else
-        dv[u >> 1] = mfma_32x32x16<DT>(a, pf[n][u & 1], dv[u >> 1]);
-    };
-    // softmax-gradient arithmetic of score r of block n (and the packing of a
-    // finished pair)
-    f32x4 l4[2][4], d4[2][4];
-    auto score_math = [&](int n, int r) {
-      const int g = r >> 2, e = r & 3, qo = 32 * n + 8 * g + 4 * w.hf;
-      float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[n][r], sl2, -l4[n][g][e]));
-      pr = qo + e < qlim ? 0.f : pr;
-      pv[n][r] = pr;
-      dsv[n][r] = pr * (dp[n][r] - d4[n][g][e]);
-      if (r & 1) {
-        const int hh = r >> 3, i = (r & 7) >> 1;
-        pf[n][hh][i] = pack2<DT>(pv[n][r - 1], pv[n][r]);
-        dsf[n][hh][i] = pack2<DT>(dsv[n][r - 1], dsv[n][r]);
+  constexpr bool kDK = GRADS & 1, kDV = GRADS & 2;
+  const bool need_mask = CAUSAL && q0 < wk0 + 31;
+  const int mykey = wk0 + w.l32;
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) s = mfma_32x32x16<DT>(ks_operand<D>(qs, w, n * NKK + kk), kf[kk], s);
+    if constexpr (kDK) {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) dp = mfma_32x32x16<DT>(ks_operand<D>(dos, w, n * NKK + kk), vf[kk], dp);
+    }
+    // Lane l holds key mykey and queries q0 + 32n + 8g + 4hf + e (r = 4g + e).
+    float p[16], ds[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int qo = 32 * n + 8 * g + 4 * w.hf;
+      const f32x4 l4 = *(const f32x4*)(st + qo * 4);
+      const f32x4 d4 = *(const f32x4*)(st + 256 + qo * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l4[e]));
+        if (need_mask && q0 + qo + e < mykey) pr = 0.f;
+        p[r] = pr;
+        ds[r] = kDK ? pr * (dp[r] - d4[e]) : 0.f;
       }
-    };
-    auto load_stats = [&](int n) {
-  #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qo = 32 * n + 8 * g + 4 * w.hf;
-        l4[n][g] = *(const f32x4*)(st + qo * 4);
-        d4[n][g] = *(const f32x4*)(st + 256 + qo * 4);
+    }
+    u32x4 pf[2], dsf[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pf[hh][i] = pack2<DT>(p[8 * hh + 2 * i], p[8 * hh + 2 * i + 1]);
+        dsf[hh][i] = pack2<DT>(ds[8 * hh + 2 * i], ds[8 * hh + 2 * i + 1]);
       }
-    };
-    constexpr int PRE = 8;  // operand read-ahead, in MFMAs
-    u32x4 op[NS > NG ? NS : NG];
-    s[0] = dp[0] = s[1] = dp[1] = f32x16{};
-    // block 0: score MFMAs
-  #pragma unroll
-    for (int i = 0; i < PRE; ++i) op[i] = score_operand(0, i);
-    load_stats(0);
-  #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      if (i + PRE < NS) op[i + PRE] = score_operand(0, i + PRE);
-      score_mfma(0, i, op[i]);
-    }
-    // block 1: score MFMAs, each with one score of block 0's arithmetic
-  #pragma unroll
-    for (int i = 0; i < PRE; ++i) op[i] = score_operand(1, i);
-    load_stats(1);
-    __builtin_amdgcn_sched_barrier(0);
-  #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      if (i + PRE < NS) op[i + PRE] = score_operand(1, i + PRE);
-      score_mfma(1, i, op[i]);
-  #pragma unroll
-      for (int r = i * 16 / NS; r < (i + 1) * 16 / NS; ++r) score_math(0, r);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // block 0: gradient MFMAs, each with one score of block 1's arithmetic
-  #pragma unroll
-    for (int i = 0; i < PRE; ++i) op[i] = grad_operand(0, i);
-    __builtin_amdgcn_sched_barrier(0);
-  #pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      if (i + PRE < NG) op[i + PRE] = grad_operand(0, i + PRE);
-      grad_mfma(0, i, op[i]);
-  #pragma unroll
-      for (int r = i * 16 / NG; r < (i + 1) * 16 / NG; ++r) score_math(1, r);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // block 1: gradient MFMAs
-  #pragma unroll
-    for (int i = 0; i < PRE; ++i) op[i] = grad_operand(1, i);
-  #pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      if (i + PRE < NG) op[i + PRE] = grad_operand(1, i + PRE);
-      grad_mfma(1, i, op[i]);
-    }
-  } else {
-    // D <= 64 and D = 256: the compiler's own schedule (below D = 128 it
-    // measured faster than the fenced one).
-    constexpr bool kDK = GRADS & 1, kDV = GRADS & 2;
-    const bool need_mask = CAUSAL && q0 < wk0 + 31;
-    const int mykey = wk0 + w.l32;
-  #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      f32x16 s = {}, dp = {};
-  #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) s = mfma_32x32x16<DT>(ks_operand<D>(qs, w, n * NKK + kk), kf[kk], s);
-      if constexpr (kDK) {
-  #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) dp = mfma_32x32x16<DT>(ks_operand<D>(dos, w, n * NKK + kk), vf[kk], dp);
+    // dV^T += dO^T P and dK^T += Q^T dS over this block's 32 queries.
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        if constexpr (kDV) dv[dt] = mfma_32x32x16<DT>(vt_operand<D>(dos, w, 4 * dt + 2 * n + hh), pf[hh], dv[dt]);
+        if constexpr (kDK) dk[dt] = mfma_32x32x16<DT>(vt_operand<D>(qs, w, 4 * dt + 2 * n + hh), dsf[hh], dk[dt]);
       }
-      // Lane l holds key mykey and queries q0 + 32n + 8g + 4hf + e (r = 4g + e).
-      float p[16], ds[16];
-  #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qo = 32 * n + 8 * g + 4 * w.hf;
-        const f32x4 l4 = *(const f32x4*)(st + qo * 4);
-        const f32x4 d4 = *(const f32x4*)(st + 256 + qo * 4);
-  #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l4[e]));
-          if (need_mask && q0 + qo + e < mykey) pr = 0.f;
-          p[r] = pr;
-          ds[r] = kDK ? pr * (dp[r] - d4[e]) : 0.f;
-        }
-      }
-      u32x4 pf[2], dsf[2];
-  #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-  #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pf[hh][i] = pack2<DT>(p[8 * hh + 2 * i], p[8 * hh + 2 * i + 1]);
-          dsf[hh][i] = pack2<DT>(ds[8 * hh + 2 * i], ds[8 * hh + 2 * i + 1]);
-        }
-      // dV^T += dO^T P and dK^T += Q^T dS over this block's 32 queries.
-  #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-  #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          if constexpr (kDV) dv[dt] = mfma_32x32x16<DT>(vt_operand<D>(dos, w, 4 * dt + 2 * n + hh), pf[hh], dv[dt]);
-          if constexpr (kDK) dk[dt] = mfma_32x32x16<DT>(vt_operand<D>(qs, w, 4 * dt + 2 * n + hh), dsf[hh], dk[dt]);
-        }
-    }
   }
 }
 
@@ -546,6 +441,260 @@ __global__ __launch_bounds__(64 * kWavesKV, 1) void bwd_dkdv(const u16* __restri
   if constexpr (GRADS & 2) store_rows16<DT, D>(dv, 1.0f, rv, (32 * w.wave + w.l32) * ROWB, w.hf);
 }
 
+// ---------------------------------------------------------------------------
+// dK / dV kernel at D = 128 with two waves per SIMD.
+// ---------------------------------------------------------------------------
+// One workgroup per (batch*head, 128 keys), 8 waves.  Waves g and g + 4 share
+// a SIMD and key group g (32 keys) and split the work of each 64-row Q/dO
+// tile between them: wave g (the P wave) computes S = Q K^T, P and
+// dV^T += dO^T P; wave g + 4 (the dS wave) computes dP = dO V^T and, with
+// the P its sibling leaves in LDS, dS = P (dP - delta) and dK^T += Q^T dS.
+// Each wave then holds one fragment (K or V) and one fp32 gradient, which
+// fits two waves per SIMD, and one wave's exponentials and softmax-gradient
+// arithmetic run while its sibling's MFMAs do.  A tile takes two barriers:
+// the first (tile complete) opens the score phase, the second (P written)
+// the gradient phase.  Q/dO tiles stream through a 3-stage ring; each key
+// group's P travels in fp32, so dS is computed exactly as with one wave.
+constexpr int kWavesKV2 = 8;
+constexpr int kStagesKV2 = 3;
+
+// Every wave loads the tile's lse2 and delta rows (the same 512 bytes; the
+// copies write identical values), so that all waves issue the same number of
+// loads per tile and every wait count is a compile-time constant.
+template <int D>
+constexpr int kv2_loads_per_tile() {
+  static_assert(64 * D * 2 / 1024 % kWavesKV2 == 0, "whole 1 KB pieces per wave");
+  return 2 * (64 * D * 2 / 1024 / kWavesKV2) + 2;
+}
+
+template <int D>
+__device__ __forceinline__ void issue_kv2_tile(const u16* Qh, const u16* dOh, int qbytes, const float* l2h,
+                                               const float* dlh, int Nq, int t, unsigned char* dst, const Wave16& w) {
+  constexpr int TILEB = 64 * D * 2;
+  issue_tile16<D, kWavesKV2>(Qh, dOh, qbytes, t, dst, w);
+  const auto rl = make_rsrc_at(l2h, t * 256, Nq * 4);
+  const auto rd = make_rsrc_at(dlh, t * 256, Nq * 4);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)(dst + 2 * TILEB), 4, w.lane * 4, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)(dst + 2 * TILEB + 256), 4, w.lane * 4, 0, 0, 0);
+}
+
+// Meet the other waves once this wave's LDS writes have completed, leaving
+// its direct-to-LDS loads in flight (s_waitcnt: vmcnt 63 and expcnt 7, i.e.
+// no wait; lgkmcnt 0).
+__device__ __forceinline__ void lds_write_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Score MFMAs of the two-role kernel: x[n] = A(block n) frag^T over the tile
+// `as` (Q or dO rows), operands read PRE MFMAs ahead.
+template <int DT, int D>
+__device__ __forceinline__ void kv2_scores(const unsigned char* as, const Wave16& w, const u32x4 (&frag)[D / 16],
+                                           f32x16 (&x)[2]) {
+  constexpr int NKK = D / 16, NS = 2 * NKK, PRE = 8;
+  u32x4 op[NS];
+#pragma unroll
+  for (int i = 0; i < PRE; ++i) op[i] = ks_operand<D>(as, w, i);
+  x[0] = x[1] = f32x16{};
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    if (i + PRE < NS) op[i + PRE] = ks_operand<D>(as, w, i + PRE);
+    x[i / NKK] = mfma_32x32x16<DT>(op[i], frag[i % NKK], x[i / NKK]);
+  }
+}
+
+// Gradient MFMAs of the two-role kernel: acc[dt] += A^T pk over the tile `gs`
+// (dO rows for dV, Q rows for dK) read transposed; operand i is
+// dt = i / 4, block n = (i / 2) % 2, 16-row half hh = i % 2.
+template <int DT, int D>
+__device__ __forceinline__ void kv2_grads(const unsigned char* gs, const Wave16& w, const u32x4 (&pk)[2][2],
+                                          f32x16 (&acc)[D / 32]) {
+  constexpr int NG = 4 * (D / 32), PRE = 8;
+  u32x4 op[NG];
+#pragma unroll
+  for (int i = 0; i < PRE; ++i) op[i] = vt_operand<D>(gs, w, i);
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    if (i + PRE < NG) op[i + PRE] = vt_operand<D>(gs, w, i + PRE);
+    acc[i >> 2] = mfma_32x32x16<DT>(op[i], pk[(i >> 1) & 1][i & 1], acc[i >> 2]);
+  }
+}
+
+// Tile j of the two-role kernel.  `frag` is the wave's K (P wave) or V (dS
+// wave) fragment, `acc` its dV^T or dK^T accumulator, `xp` the key group's
+// P exchange area (2048 floats: chunk c = 4n + g of lane l at
+// xp[4 (64 c + l)], the values of rows 32n + 8g + 4hf + 0..3).
+template <int DT, int D, bool CAUSAL, bool PW>
+__device__ __forceinline__ void kv2_tile(const u16* Qh, const u16* dOh, int qbytes, const float* l2h,
+                                         const float* dlh, int Nq, int t0, int j, int nt, const unsigned char* src,
+                                         unsigned char* dst, float* xp, const Wave16& w, int wk0,
+                                         const u32x4 (&frag)[D / 16], f32x16 (&acc)[D / 32], float sl2) {
+  constexpr int TILEB = 64 * D * 2;
+  const int t = t0 + j;
+  const int q0 = 64 * t;
+  const unsigned char* qs = src;
+  const unsigned char* dos = src + TILEB;
+  const unsigned char* st = src + 2 * TILEB;
+  // Tile j+1 is always in flight: the loads run two tiles past the last one
+  // (rows past Nq, read as zeros and never used), so that every tile waits
+  // for the same count and the compiler's own waits can count exactly.
+  wait_tile_and_barrier(kv2_loads_per_tile<D>());
+  issue_kv2_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t + kStagesKV2 - 1, dst, w);
+  // No query of the tile sees the group's keys (causal): nothing to do, but
+  // both barriers are still met.
+  const bool live = !(CAUSAL && q0 + 63 < wk0);
+  // Queries of the tile below `qlim` (relative to q0) precede this lane's key.
+  const int qlim = (CAUSAL && q0 < wk0 + 31) ? wk0 + w.l32 - q0 : 0;
+  // Lane l holds key wk0 + l % 32 and queries q0 + 32n + 8g + 4hf + e (r = 4g + e).
+  f32x16 x[2];
+  u32x4 pk[2][2];  // P wave: P packed for dV; dS wave: dS packed for dK
+  if (live) {
+    // Score phase: S = Q K^T (P wave) or dP = dO V^T (dS wave), both blocks.
+    kv2_scores<DT, D>(PW ? qs : dos, w, frag, x);
+    if constexpr (PW) {
+      // P = exp2(s scale log2 e - LSE log2 e), 0 where masked; fp32 to the
+      // sibling, rounded to 16 bits for dV.
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int qo = 32 * n + 8 * g + 4 * w.hf;
+          const f32x4 l4 = *(const f32x4*)(st + qo * 4);
+          f32x4 p4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x[n][4 * g + e], sl2, -l4[e]));
+            p4[e] = qo + e < qlim ? 0.f : pr;
+            x[n][4 * g + e] = p4[e];
+          }
+          *(f32x4*)(xp + 4 * (64 * (4 * n + g) + w.lane)) = p4;
+        }
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pk[n][hh][i] = pack2<DT>(x[n][8 * hh + 2 * i], x[n][8 * hh + 2 * i + 1]);
+    }
+  }
+  lds_write_barrier();
+  if (live) {
+    if constexpr (!PW) {
+      // dS = P (dP - delta), rounded to 16 bits.
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        float ds[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int qo = 32 * n + 8 * g + 4 * w.hf;
+          const f32x4 d4 = *(const f32x4*)(st + 256 + qo * 4);
+          const f32x4 p4 = *(const f32x4*)(xp + 4 * (64 * (4 * n + g) + w.lane));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ds[4 * g + e] = p4[e] * (x[n][4 * g + e] - d4[e]);
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pk[n][hh][i] = pack2<DT>(ds[8 * hh + 2 * i], ds[8 * hh + 2 * i + 1]);
+      }
+    }
+    // Gradient phase: dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave).
+    kv2_grads<DT, D>(PW ? dos : qs, w, pk, acc);
+  }
+}
+
+// The tile loop of one role over the 3-stage ring (stages passed as the
+// distinct __shared__ arrays they are).
+template <int DT, int D, bool CAUSAL, bool PW>
+__device__ __forceinline__ void kv2_loop(const u16* Qh, const u16* dOh, int qbytes, const float* l2h,
+                                         const float* dlh, int nq, int t0, int nt, unsigned char* s0,
+                                         unsigned char* s1, unsigned char* s2, float* xp, const Wave16& w, int wk0,
+                                         const u32x4 (&frag)[D / 16], f32x16 (&acc)[D / 32], float sl2) {
+  issue_kv2_tile<D>(Qh, dOh, qbytes, l2h, dlh, nq, t0, s0, w);
+  issue_kv2_tile<D>(Qh, dOh, qbytes, l2h, dlh, nq, t0 + 1, s1, w);
+  for (int j = 0; j < nt; j += 3) {
+    kv2_tile<DT, D, CAUSAL, PW>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j, nt, s0, s2, xp, w, wk0, frag, acc, sl2);
+    if (j + 1 < nt)
+      kv2_tile<DT, D, CAUSAL, PW>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 1, nt, s1, s0, xp, w, wk0, frag, acc, sl2);
+    if (j + 2 < nt)
+      kv2_tile<DT, D, CAUSAL, PW>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 2, nt, s2, s1, xp, w, wk0, frag, acc, sl2);
+  }
+  // The loads past the last tile complete before the workgroup's LDS is
+  // released.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); lgkmcnt, expcnt: no wait
+}
+
+template <int DT, int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(64 * kWavesKV2, 1) void bwd_dkdv2(const u16* __restrict__ Qg, const u16* __restrict__ Kg,
+                                                               const u16* __restrict__ Vg, const u16* __restrict__ dOg,
+                                                               const float* __restrict__ lse2g,
+                                                               const float* __restrict__ deltag, u16* __restrict__ dKg,
+                                                               u16* __restrict__ dVg, int BH, int Nq, int Nk,
+                                                               float sl2, float scale, const int* __restrict__ cuq,
+                                                               const int* __restrict__ cuk, int H, int tq, int tk) {
+  constexpr int ROWB = D * 2, SB = kv_stage_bytes<D>(), BK = 128;
+  static_assert(kStagesKV2 == 3, "the loop below is unrolled for three stages");
+  __shared__ __attribute__((aligned(1024))) unsigned char stage0[SB];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage1[SB];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage2[SB];
+  __shared__ __attribute__((aligned(1024))) float xbuf[4 * 2048];
+
+  Wave16 w;
+  const int tid = threadIdx.x;
+  w.lane = tid & 63;
+  w.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  w.hf = w.lane >> 5;
+  w.l32 = w.lane & 31;
+  const int grp = w.wave & 3;
+  const bool pwave = w.wave < 4;
+  // Key blocks in ascending order: under the causal mask the first keys are
+  // seen by the most queries, so the heaviest workgroups start first.
+  const int bid = blockIdx.x;
+  const int bh = bid % BH, kt = bid / BH;
+  const int kb0 = kt * BK;
+  const int wk0 = kb0 + 32 * grp;
+  const HeadRows hr = head_rows<VARLEN>(bh, Nq, Nk, D, cuq, cuk, H, tq, tk);
+  const int nq = hr.nq, nk = hr.nk;
+  if (kb0 >= nk) return;  // past this sequence's keys: the whole workgroup
+  const u16* Qh = Qg + hr.qo;
+  const u16* dOh = dOg + hr.qo;
+  const float* l2h = lse2g + hr.so;
+  const float* dlh = deltag + hr.so;
+  const int qbytes = nq * ROWB;
+  const int t0 = CAUSAL ? kb0 / 64 : 0;  // first query tile that sees a key of the block
+  const int nt = max((nq + 63) / 64 - t0, 0);
+  w.wq0 = w.wkend = w.wklim = w.klim = 0;  // forward-only fields
+  init_operand_offsets<D>(w);
+  float* xp = xbuf + 2048 * grp;
+
+  u32x4 frag[D / 16];
+  load_frag<D>(frag, (pwave ? Kg : Vg) + hr.ko, nk, wk0, w);
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+
+  // Each role runs its own copy of the loop (the same barriers in the same
+  // order), so that its LDS reads name their arrays directly.
+  if (nt > 0) {
+    if (pwave)
+      kv2_loop<DT, D, CAUSAL, true>(Qh, dOh, qbytes, l2h, dlh, nq, t0, nt, stage0, stage1, stage2, xp, w, wk0, frag,
+                                    acc, sl2);
+    else
+      kv2_loop<DT, D, CAUSAL, false>(Qh, dOh, qbytes, l2h, dlh, nq, t0, nt, stage0, stage1, stage2, xp, w, wk0, frag,
+                                     acc, sl2);
+  }
+  const int row = (32 * grp + w.l32) * ROWB;
+  if (pwave) {
+    const auto rv = make_rsrc_at(dVg + hr.ko, kb0 * ROWB, nk * ROWB);
+    store_rows16<DT, D>(acc, 1.0f, rv, row, w.hf);
+  } else {
+    const auto rk = make_rsrc_at(dKg + hr.ko, kb0 * ROWB, nk * ROWB);
+    store_rows16<DT, D>(acc, scale, rk, row, w.hf);
+  }
+}
+
 // VARLEN: q, o, dout, dq [H, total_q, D]; k, v, dk, dv [H, total_k, D]; lse
 // and the workspace [H, total_q]; a.Nq / a.Nk are the longest sequence's
 // query / key counts and size the grids.
@@ -582,6 +731,11 @@ int launch_bwd(const FaBwdLaunch& a, float sl2, float scale) {
     if constexpr (D == 256) {  // one kernel per gradient: dV, then dK
       const int rc = run(bwd_dkdv<DT, D, CAUSAL, 2, VARLEN>);
       return rc != 0 ? rc : run(bwd_dkdv<DT, D, CAUSAL, 1, VARLEN>);
+    } else if constexpr (D == 128) {
+      return launch_kernel(bwd_dkdv2<DT, D, CAUSAL, VARLEN>, grid, dim3(64 * kWavesKV2), st, (const u16*)a.q,
+                           (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, (const float*)lse2,
+                           (const float*)delta, (u16*)a.dk, (u16*)a.dv, (int)a.BH, (int)a.Nq, (int)a.Nk, sl2, scale,
+                           a.cu_q, a.cu_k, H, tq, tk);
     } else {
       return run(bwd_dkdv<DT, D, CAUSAL, 3, VARLEN>);
     }
