@@ -127,7 +127,8 @@ def kernel_code_sha256(paths=KERNEL_SOURCES) -> str:
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
-COUNTER_KEYS = ("kernel_code_sha256", "traffic_bytes_per_launch", "mfma_busy_pct", "valu_trans_f32_per_launch")
+COUNTER_KEYS = ("kernel_code_sha256", "traffic_bytes_per_launch", "mfma_busy_pct", "valu_trans_f32_per_launch",
+                "mfma_flop_executed_over_convention", "valu_active_pct")
 
 
 def committed_counters(w, op: str = "fwd"):
@@ -153,14 +154,18 @@ def counter_fields(w, op: str, ms_per_step: float):
     """Roofline extras from the committed counters: the HBM rate those bytes
     make at this run's step time (GB/s, against the 8 TB/s datasheet peak),
     the MFMA-busy fraction and the transcendental (exp) instruction count of
-    the SQ pass; None where the summary lacks them or is stale."""
+    the SQ pass, and from the wave-cycle pass the executed MFMA FLOPs over the
+    convention's and the share of wave-cycles issuing VALU/MFMA instructions;
+    None where the summary lacks them or is stale."""
     c = committed_counters(w, op)
     traffic = int(c["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in c else None
     busy = float(c["mfma_busy_pct"]) / 100.0 if "mfma_busy_pct" in c else None
     trans = int(c["valu_trans_f32_per_launch"]) if "valu_trans_f32_per_launch" in c else None
+    ratio = float(c["mfma_flop_executed_over_convention"]) if "mfma_flop_executed_over_convention" in c else None
+    valu = float(c["valu_active_pct"]) / 100.0 if "valu_active_pct" in c else None
     gbs = round(traffic / (ms_per_step * 1e-3) / 1e9, 1) if traffic is not None and ms_per_step > 0 else None
     return {"traffic": traffic, "hbm_gbs": gbs, "hbm_frac": round(gbs / HBM_PEAK_GBS, 4) if gbs else None,
-            "mfma_busy": busy, "valu_trans_f32": trans}
+            "mfma_busy": busy, "valu_trans_f32": trans, "mfma_exec_over_conv": ratio, "valu_active": valu}
 
 
 def blas_threads() -> int:
@@ -246,6 +251,36 @@ def settle(step, warmup: int, seconds: float, batch: int = 20, cap_s: float = 10
     return {"extra_launches": extra, "seconds": round(time.perf_counter() - t0, 3)}
 
 
+COLD_FLUSH_MIB = 512  # bytes written between cold calls: more than the L2s and the MALL hold
+
+
+def cold_timing(step, stream, calls: int):
+    """Per-call durations (ms) with the caches cold: before each call a
+    COLD_FLUSH_MIB MiB device buffer is overwritten on the same stream, which
+    evicts the inputs from every L2 and from the MALL (inputs stay in HBM),
+    and the device is synchronized before and after that write, so that the
+    call does not overlap its tail; HIP events bracket the call alone.
+    (Launched back to back behind the write, the calls measured 10-25%
+    slower still, and varied more.)"""
+    import torch
+
+    flush = torch.empty(COLD_FLUSH_MIB << 20, dtype=torch.uint8, device=torch.device("cuda:0"))
+    out = []
+    for _ in range(calls):
+        torch.cuda.synchronize()
+        flush.zero_()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b))
+    del flush
+    return out
+
+
 def bench_one(w: workloads.Workload, steps: int, warmup: int, op: str = "fwd", settle_s: float = 1.0):
     import torch
 
@@ -320,6 +355,7 @@ def bench_one(w: workloads.Workload, steps: int, warmup: int, op: str = "fwd", s
         b.record(stream)
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in evs]
+    cold = statistics.median(cold_timing(step, stream, min(steps, 20)))
     conv = workloads.conv_flops_bwd if op == "bwd" else workloads.conv_flops
     flops = conv(w.B, w.H, w.Nq, w.Nk, w.D, w.causal)
     tflops = flops / (ms_region * 1e-3) / 1e12
@@ -327,6 +363,7 @@ def bench_one(w: workloads.Workload, steps: int, warmup: int, op: str = "fwd", s
     if op == "decode":
         nbytes = workloads.algorithmic_bytes(w)
         return {
+            "cold_median_launch_ms": cold,
             "ms_per_step": ms_region,
             "wall_s": wall,
             "median_launch_ms": statistics.median(per),
@@ -338,6 +375,7 @@ def bench_one(w: workloads.Workload, steps: int, warmup: int, op: str = "fwd", s
             "warmup_settle": warm,
         }
     return {
+        "cold_median_launch_ms": cold,
         "ms_per_step": ms_region,
         "wall_s": wall,
         "median_launch_ms": statistics.median(per),
@@ -383,9 +421,10 @@ def bench_varlen(w: workloads.VarlenWorkload, steps: int, warmup: int, settle_s:
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    cold = statistics.median(cold_timing(step, stream, min(steps, 20)))
     flops = workloads.varlen_flops(w)
     return {"ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12, "flops": flops, "peak": PEAK_TFLOPS[w.dtype],
-            "warmup_settle": warm}
+            "warmup_settle": warm, "cold_median_launch_ms": cold}
 
 
 def cpu_baseline_varlen(w: workloads.VarlenWorkload, target_s: float):
@@ -407,6 +446,18 @@ def cpu_baseline_varlen(w: workloads.VarlenWorkload, target_s: float):
             "sample": f"{n} of {w.B} sequences of {w.name}, all heads, float64, {t_total:.1f} s"}
 
 
+def cold_cache(r, unit: str):
+    """Secondary figure: the median per-call time with the caches flushed
+    before each call (cold_timing) and the rate it gives, or None when it was
+    not measured."""
+    ms = r.get("cold_median_launch_ms")
+    if ms is None:
+        return None
+    work = r["bytes"] / 1e9 if unit == "GB/s" else r["flops"] / 1e12
+    return {"median_launch_ms": round(ms, 5), "value": round(work / (ms * 1e-3), 3), "unit": unit,
+            "flush_mib": COLD_FLUSH_MIB}
+
+
 def line_varlen(w, r, steps, warmup, cpu):
     return {
         "metric": METRIC_VARLEN,
@@ -425,6 +476,7 @@ def line_varlen(w, r, steps, warmup, cpu):
                    "total_q": int(sum(w.lens_q)), "total_k": int(sum(w.lens_k)), "lens_q": list(w.lens_q),
                    "flops_per_step": r["flops"], "parallelism": "single GPU", "op": "varlen"},
         "warmup_settle": r.get("warmup_settle"),
+        "cold_cache": cold_cache(r, "TFLOP/s"),
         "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 3), "peak": r["peak"], "unit": "TFLOP/s",
                      "frac": round(r["tflops"] / r["peak"], 4), **counter_fields(w, "varlen", r["ms_per_step"])},
         "cpu_baseline": cpu,
@@ -461,6 +513,7 @@ def line_for(w, r, steps, warmup, cpu, op="fwd"):
                        "median_launch_ms": round(r["median_launch_ms"], 5),
                        "min_launch_ms": round(r["min_launch_ms"], 5), "op": op, **props},
             "warmup_settle": r.get("warmup_settle"),
+            "cold_cache": cold_cache(r, "GB/s"),
             "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(r["gbs"] / HBM_PEAK_GBS, 4), **counter_fields(w, op, r["ms_per_step"])},
             "cpu_baseline": cpu,
@@ -484,6 +537,7 @@ def line_for(w, r, steps, warmup, cpu, op="fwd"):
                    "median_launch_ms": round(r["median_launch_ms"], 5),
                    "min_launch_ms": round(r["min_launch_ms"], 5), "op": op, **props},
         "warmup_settle": r.get("warmup_settle"),
+        "cold_cache": cold_cache(r, "TFLOP/s"),
         "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 3), "peak": r["peak"],
                      "unit": "TFLOP/s", "frac": round(r["tflops"] / r["peak"], 4),
                      **counter_fields(w, op, r["ms_per_step"])},

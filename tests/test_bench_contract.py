@@ -24,9 +24,10 @@ def _timing(op, peak=2500.0):
     settle = {"extra_launches": 100, "seconds": 1.0}
     if op == "decode":
         return {"gbs": 5000.0, "ms_per_step": 1.0, "bytes": 5 << 30, "splits_workspace_bytes": 0,
-                "median_launch_ms": 1.0, "min_launch_ms": 0.9, "warmup_settle": settle}
+                "median_launch_ms": 1.0, "min_launch_ms": 0.9, "warmup_settle": settle,
+                "cold_median_launch_ms": 1.2}
     return {"tflops": 1000.0, "ms_per_step": 0.3, "flops": 2.7e11, "peak": peak, "median_launch_ms": 0.3,
-            "min_launch_ms": 0.29, "warmup_settle": settle}
+            "min_launch_ms": 0.29, "warmup_settle": settle, "cold_median_launch_ms": 0.32}
 
 
 def _check(line, name, bound, unit):
@@ -48,6 +49,8 @@ def _check(line, name, bound, unit):
     assert r["mfma_busy"] is None or 0.0 < r["mfma_busy"] <= 1.0
     assert r["valu_trans_f32"] is None or isinstance(r["valu_trans_f32"], int)
     assert "warmup_settle" in line
+    c = line["cold_cache"]
+    assert c is None or (c["unit"] == unit and c["value"] > 0 and c["median_launch_ms"] > 0)
 
 
 @pytest.mark.parametrize("op,name", [("fwd", workloads.HEADLINE), ("bwd", workloads.HEADLINE),
