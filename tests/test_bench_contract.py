@@ -17,7 +17,8 @@ import workloads
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KEYS = {"metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
         "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"}
-ROOF = {"bound", "achieved", "peak", "unit", "frac", "traffic", "hbm_gbs", "hbm_frac", "mfma_busy", "valu_trans_f32"}
+ROOF = {"bound", "achieved", "peak", "unit", "frac", "traffic", "hbm_gbs", "hbm_frac", "mfma_busy", "valu_trans_f32",
+        "mfma_exec_over_conv", "valu_active"}
 
 
 def _timing(op, peak=2500.0):
@@ -48,6 +49,8 @@ def _check(line, name, bound, unit):
         assert r["hbm_frac"] == round(r["hbm_gbs"] / bench.HBM_PEAK_GBS, 4)
     assert r["mfma_busy"] is None or 0.0 < r["mfma_busy"] <= 1.0
     assert r["valu_trans_f32"] is None or isinstance(r["valu_trans_f32"], int)
+    assert r["mfma_exec_over_conv"] is None or r["mfma_exec_over_conv"] >= 0.99
+    assert r["valu_active"] is None or 0.0 < r["valu_active"] < 1.0
     assert "warmup_settle" in line
     c = line["cold_cache"]
     assert c is None or (c["unit"] == unit and c["value"] > 0 and c["median_launch_ms"] > 0)
@@ -94,6 +97,8 @@ def test_committed_counter_summaries_are_well_formed():
         assert re.search(r"^traffic_bytes_per_launch: \d+$", text, re.M), p
         assert re.search(r"^mfma_busy_pct: [0-9.]+$", text, re.M), p
         assert re.search(r"^valu_trans_f32_per_launch: \d+$", text, re.M), p
+        assert re.search(r"^mfma_flop_executed_over_convention: [0-9.]+$", text, re.M), p
+        assert re.search(r"^valu_active_pct: [0-9.]+$", text, re.M), p
         assert "rocprofv3 --pmc FETCH_SIZE" in text and "rocprofv3 --pmc WRITE_SIZE" in text, p
         trace = os.path.join(ROOT, "profiles", f"{tag}__{wl}__kernel_trace.md")
         assert os.path.exists(trace), f"{p}: no kernel trace summary beside it"
