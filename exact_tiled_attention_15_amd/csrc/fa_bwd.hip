@@ -539,7 +539,7 @@ __device__ __forceinline__ void kv2_tile(const u16* Qh, const u16* dOh, int qbyt
   const unsigned char* st = src + 2 * TILEB;
   // Tile j+1 is always in flight: the loads run two tiles past the last one
   // (rows past Nq, read as zeros and never used), so that every tile waits
-  // for the same count and the compiler's own waits can count exactly.
+  // for the same fixed count.
   wait_tile_and_barrier(kv2_loads_per_tile<D>());
   issue_kv2_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t + kStagesKV2 - 1, dst, w);
   // No query of the tile sees the group's keys (causal): nothing to do, but
