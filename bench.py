@@ -257,21 +257,19 @@ COLD_FLUSH_MIB = 512  # bytes written between cold calls: more than the L2s and 
 def cold_timing(step, stream, calls: int):
     """Per-call durations (ms) with the caches cold: before each call a
     COLD_FLUSH_MIB MiB device buffer is overwritten on the same stream, which
-    evicts the inputs from every L2 and from the MALL (inputs stay in HBM),
-    and the device is synchronized before and after that write, so that the
-    call does not overlap its tail; HIP events bracket the call alone.
-    (Launched back to back behind the write, the calls measured 10-25%
-    slower still, and varied more.)"""
+    evicts the inputs from every L2 and from the MALL (inputs stay in HBM).
+    The call is queued right behind that write, so the device never idles
+    between the two (an idle gap lets the shader clock drop, and the call
+    then measured 15% slower for that reason alone); HIP events bracket the
+    call, and the device is synchronized after each call."""
     import torch
 
     flush = torch.empty(COLD_FLUSH_MIB << 20, dtype=torch.uint8, device=torch.device("cuda:0"))
     out = []
     for _ in range(calls):
-        torch.cuda.synchronize()
-        flush.zero_()
-        torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
+        flush.zero_()
         a.record(stream)
         step()
         b.record(stream)
