@@ -157,10 +157,37 @@ __device__ __forceinline__ void dq_tile(const u16* Kh, const u16* Vh, int kbytes
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     f32x16 s = {}, dp = {};
+    if constexpr (D == 128) {
+      // S and dP MFMAs interleaved, operands read PRE MFMAs ahead; then the
+      // K^T operands of this block's dQ MFMAs, read now so that the softmax
+      // hides their latency (6 ahead leaves exactly 256 VGPRs; 8 spills).
+      constexpr int NS = 2 * NKK, PRE = 6;
+      u32x4 op[NS];
+#pragma unroll
+      for (int i = 0; i < PRE; ++i)
+        op[i] = (i & 1) ? ks_operand<D>(vs, w, n * NKK + (i >> 1)) : ks_operand<D>(ks, w, n * NKK + (i >> 1));
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        if (i + PRE < NS) {
+          const int ip = i + PRE;
+          op[ip] = (ip & 1) ? ks_operand<D>(vs, w, n * NKK + (ip >> 1)) : ks_operand<D>(ks, w, n * NKK + (ip >> 1));
+        }
+        if (i & 1)
+          dp = mfma_32x32x16<DT>(op[i], dof[i >> 1], dp);
+        else
+          s = mfma_32x32x16<DT>(op[i], qf[i >> 1], s);
+      }
+    } else {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) s = mfma_32x32x16<DT>(ks_operand<D>(ks, w, n * NKK + kk), qf[kk], s);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) dp = mfma_32x32x16<DT>(ks_operand<D>(vs, w, n * NKK + kk), dof[kk], dp);
+    }
+    u32x4 kt[2 * NDT];
+    if constexpr (D == 128) {
+#pragma unroll
+      for (int i = 0; i < 2 * NDT; ++i) kt[i] = vt_operand<D>(ks, w, 4 * (i >> 1) + 2 * n + (i & 1));
+    }
     // P = exp2(s sl2 - lse2) (masked keys: 0), dS = P (dP - delta).
     float ds[16];
 #pragma unroll
@@ -179,7 +206,8 @@ __device__ __forceinline__ void dq_tile(const u16* Kh, const u16* Vh, int kbytes
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
-        acc[dt] = mfma_32x32x16<DT>(vt_operand<D>(ks, w, 4 * dt + 2 * n + hh), dsf[hh], acc[dt]);
+        acc[dt] = mfma_32x32x16<DT>(D == 128 ? kt[2 * dt + hh] : vt_operand<D>(ks, w, 4 * dt + 2 * n + hh), dsf[hh],
+                                    acc[dt]);
   }
 }
 
