@@ -11,8 +11,9 @@
 //
 // Work decomposition: one workgroup per (batch*head, Q tile); each wave owns
 // 32 query rows.  16-bit kernel: 8 waves (256 rows), K/V tiles of 64 keys
-// loaded straight from HBM into a 4-stage LDS ring (one barrier per tile);
-// at D = 256, 4 waves (128 rows), 32-key tiles and software-pipelined steps.
+// loaded straight from HBM into a 4-stage LDS ring (one barrier per tile).
+// At D = 256 (fa_fwd_rs): 8 waves over 128 rows, two per 32-row group, one
+// running the scores and softmax, the other O += P V; 32-key tiles.
 // fp32 kernel: 4 waves (128 rows), K/V staged through registers into a
 // double-buffered LDS stage; on grids with at most one such workgroup per CU,
 // 32-row workgroups whose waves split each 128-key tile and merge at the end.
@@ -37,10 +38,10 @@
 //
 // The library compiles this file twice.  Without FA_FWD_D256 it defines the
 // fa_launch_fwd* entry points and every kernel up to D = 128; with
-// FA_FWD_D256 it defines only the D = 256 launchers (fa_launch_fwd*_d256),
-// compiled with the MFMA accumulators in VGPRs (in the AGPR form the loop
-// carried O of 32 rows x 256 columns was copied between the two register
-// files on every tile), which the D <= 128 kernels do not want.
+// FA_FWD_D256 it defines only the D = 256 launchers (fa_launch_fwd*_d256)
+// and fa_fwd_rs, compiled with the MFMA accumulators in VGPRs, which the
+// D <= 128 kernels do not want (fa_fwd_rs takes 191 VGPRs and no AGPRs in
+// either form).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -55,30 +56,29 @@ namespace {
 constexpr int kThreads = 256;                     // 4 waves of 64 (fp32 kernel)
 constexpr int kBR = 128;                          // query rows per workgroup (fp32 kernel)
 
-// 16-bit kernel shape: a workgroup of waves16<D>() waves owns 32 query rows
-// per wave and streams K/V tiles of bc16<D>() keys through a 4-stage LDS ring
-// (three tiles in flight while one is consumed; each stage holds a K tile and
-// a V tile, 32 KB).  D <= 128: 8 waves (256 rows, two waves per SIMD) and
-// 64-key tiles.  D = 256: the Q fragment and fp32 O of 32 rows take more than
-// half of a SIMD's registers, so 4 waves (128 rows, one wave per SIMD), and
-// 32-key tiles, so that the ring still holds four stages in 128 KB (with two
-// 64-key stages, one tile in flight left the loads' latency exposed).  Either
-// way a tile is 32 MFMAs per wave.
+// 16-bit kernel shape (fa_fwd_16, D <= 128): a workgroup of waves16<D>()
+// waves owns 32 query rows per wave and streams K/V tiles of bc16<D>() keys
+// through a 4-stage LDS ring (three tiles in flight while one is consumed;
+// each stage holds a K tile and a V tile, 32 KB): 8 waves (256 rows, two
+// waves per SIMD) and 64-key tiles, a tile being 32 MFMAs per wave at
+// D = 128.  (D = 256 runs fa_fwd_rs below: there the Q fragment and fp32 O of
+// 32 rows take more than half of a SIMD's registers.)
 #ifndef FA_WAVES16
 #define FA_WAVES16 8
 #endif
 template <int D>
 constexpr int waves16() {
-  return D == 256 ? 4 : FA_WAVES16;
+  static_assert(D <= 128, "D = 256 runs fa_fwd_rs");
+  return FA_WAVES16;
 }
 // Software pipelining (step16p) pays only where a SIMD runs one wave, i.e.
-// in the 4-wave form (D = 256, and small grids at D <= 128, see dispatch16):
-// with 8 waves the two waves of a SIMD already overlap one's softmax with the
-// other's MFMAs, and the fixed interleave of step16p measured slower there
-// (6% at D = 128, 22% at D = 64), while at D = 256 it gains 9%.
+// in the 4-wave form (small grids, see dispatch16): with 8 waves the two
+// waves of a SIMD already overlap one's softmax with the other's MFMAs, and
+// the fixed interleave of step16p measured slower there (6% at D = 128, 22%
+// at D = 64).
 template <int D>
 constexpr int bc16() {
-  return D == 256 ? 32 : 64;
+  return 64;
 }
 
 // P = exp2(s sl2 + nm) of a lane's scores (16 per 32-key block), packed to
@@ -273,9 +273,9 @@ __device__ __forceinline__ void tile16(const u16* Kh, const u16* Vh, int kbytes,
   }
 }
 
-// Software-pipelined step j of the 16-bit kernel (used at D = 256, where one
-// wave per SIMD leaves no other wave to fill the matrix core while a wave
-// runs its softmax; see the note above waves16/bc16).  On entry `s` holds the raw scores S(j) of
+// Software-pipelined step j of the 16-bit kernel (used by the 4-wave form,
+// where one wave per SIMD leaves no other wave to fill the matrix core while
+// a wave runs its softmax; see the note above waves16/bc16).  On entry `s` holds the raw scores S(j) of
 // tile j, computed by the previous step; the step meets the other waves
 // (tile j+1 is then complete, and every wave is done with stage `dst`, tile
 // j-1's), starts the loads of tile j+3 into `dst`, and then runs the softmax
@@ -582,6 +582,302 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && NW == 8) ? 4 : 1) void fa_fwd_
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse), rL, (32 * w.wave + w.l32) * 4, 0,
                                           0);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Role-split 16-bit kernel at D = 256.
+// ---------------------------------------------------------------------------
+// One workgroup of 8 waves per (batch*head, 128 query rows, key range).
+// Waves g and g + 4 share a SIMD and the 32 rows of group g.  Wave g, the
+// score wave, holds the rows' Q fragment and runs S^T = K Q^T, the mask and
+// the online-softmax update of each 32-key tile, and leaves P (rounded to
+// 16 bits) in LDS; wave g + 4, the PV wave, holds the rows' fp32 O and one
+// tile later rescales it (when the score wave moved the reference) and adds
+// V^T P^T.  A wave holding both the Q fragment and O of 32 rows at D = 256
+// needs more than half of a SIMD's registers (one wave per SIMD, nothing to
+// run while a wave computes its exponentials); split, each role fits two
+// waves per SIMD, and one wave's softmax runs beside its sibling's MFMAs.
+// K and V tiles stream through two 3-stage rings; in period p every wave
+// meets the others once (K tile p and V tile p-1 are then complete), starts
+// the loads of V tile p+1 and K tile p+2, and the score waves handle tile p
+// while the PV waves handle tile p-1.  P, a flag for a moved reference and
+// the rescale factors travel through double-buffered LDS areas.
+namespace rs {
+constexpr int D = 256, BC = 32, ROWB = D * 2, TILEB = BC * ROWB, NKK = D / 16, NDT = D / 32;
+constexpr int kLoads = 2 * (TILEB / 1024 / 8);  // direct-to-LDS loads per wave per period
+constexpr int XG = 2 * 64;                      // u32x4 of P per group and buffer
+}  // namespace rs
+
+// This wave's two 1 KB pieces of tile t of one [N, D] tensor (16 KB).
+__device__ __forceinline__ void rs_issue(const u16* Xh, int kbytes, int t, unsigned char* dst, const Wave16& w) {
+  const auto r = make_rsrc_at(Xh, t * rs::TILEB, kbytes);
+#pragma unroll
+  for (int I = 0; I < rs::TILEB / 1024 / 8; ++I) {
+    const int G = w.wave + 8 * I;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + G * 1024), 16, dma_src_off<rs::D>(G, w.lane), 0,
+                                             0, 0);
+  }
+}
+
+// Score wave, tile j (K stage ks): S^T, mask, online softmax with the sum
+// rule (the reference moves only when a lane's sum of its 16 P exceeds
+// 2^15, and on the first tile), then P to xo, the move flag to *fl and,
+// when it moved, the factor to fo.
+template <int DT>
+__device__ __forceinline__ void rs_score(int j, const unsigned char* ks, u32x4* xo, float* fo, int* fl,
+                                         const Wave16& w, const u32x4 (&qf)[rs::NKK], float& mref, float& l,
+                                         float& lr, float sl2) {
+  using namespace rs;
+  const int k0 = j * BC;
+  if (k0 >= w.wkend) return;
+  constexpr int PRE = 8;
+  f32x16 s[1];
+  s[0] = f32x16{};
+  u32x4 ka[NKK];
+#pragma unroll
+  for (int i = 0; i < PRE; ++i) ka[i] = ks_operand<D>(ks, w, i);
+#pragma unroll
+  for (int i = 0; i < NKK; ++i) {
+    if (i + PRE < NKK) ka[i + PRE] = ks_operand<D>(ks, w, i + PRE);
+    s[0] = mfma_32x32x16<DT>(ka[i], qf[i], s[0]);
+  }
+  // Mask (diagonal and tail tiles only): key = k0 + 4*hf + 8*(r/4) + r%4.
+  if (k0 + BC - 1 > w.wklim) {
+    const int lim = w.klim - (k0 + 4 * w.hf);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[0][r] = (8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[0][r];
+  }
+  constexpr float kBound = 32768.0f;
+  u32x4 pf[1][2];
+  float tl = 0.f, tr = 0.f;
+  bool redo = j == 0;
+  if (!redo) {
+    exp_tile<DT, 1>(s, sl2, -mref, pf, tl, tr);
+    redo = __builtin_amdgcn_ballot_w64(!((DT == kBF16 ? tl : tr) <= kBound)) != 0;
+  }
+  if (redo) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+    const float mnew = fmaxf(mref, pair_max(mx * sl2));
+    const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+    l *= alpha;
+    lr *= alpha;
+    mref = mnew;
+    exp_tile<DT, 1>(s, sl2, -mref, pf, tl, tr);
+    fo[w.lane] = alpha;
+  }
+  l += DT == kBF16 ? tl : tr;
+  lr += tr;
+  xo[w.lane] = pf[0][0];
+  xo[64 + w.lane] = pf[0][1];
+  *fl = redo ? 1 : 0;
+}
+
+// PV wave, tile jj (V stage vs): rescale O if the score wave moved the
+// reference, then O^T += V^T P^T with the P from xi (16-key step major, so
+// consecutive MFMAs use different accumulators).
+template <int DT>
+__device__ __forceinline__ void rs_pv(int jj, const unsigned char* vs, const u32x4* xi, const float* fi,
+                                      const int* fl, const Wave16& w, f32x16 (&oacc)[rs::NDT]) {
+  using namespace rs;
+  if (jj * BC >= w.wkend) return;
+  constexpr int NPV = 2 * NDT, PRE = 8;
+  u32x4 va[NPV];
+#pragma unroll
+  for (int i = 0; i < PRE; ++i) va[i] = vt_operand<D, BC>(vs, w, (i % NDT) * 2 + i / NDT);
+  const u32x4 p0 = xi[w.lane], p1 = xi[64 + w.lane];
+  if (__builtin_amdgcn_readfirstlane(*fl)) {
+    const float a = fi[w.lane];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= a;
+  }
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) {
+    const int ip = i + PRE;
+    if (ip < NPV) va[ip] = vt_operand<D, BC>(vs, w, (ip % NDT) * 2 + ip / NDT);
+    oacc[i % NDT] = mfma_32x32x16<DT>(va[i], i < NDT ? p0 : p1, oacc[i % NDT]);
+  }
+}
+
+// Period p of one role (P6 = p mod 6: stages p mod 3, buffers p mod 2).
+template <int DT, bool SCORE, int P6>
+__device__ __forceinline__ void rs_period(int p, int nt, const u16* Kh, const u16* Vh, int kbytes,
+                                          unsigned char* const (&kr)[3], unsigned char* const (&vr)[3],
+                                          u32x4* const (&xb)[2], float* const (&fb)[2], int* const (&flb)[2],
+                                          const Wave16& w, const u32x4 (&qf)[rs::NKK], f32x16 (&oacc)[rs::NDT],
+                                          float& mref, float& l, float& lr, float sl2) {
+  wait_tile_and_barrier(rs::kLoads);
+  rs_issue(Vh, kbytes, p + 1, vr[(P6 + 1) % 3], w);
+  rs_issue(Kh, kbytes, p + 2, kr[(P6 + 2) % 3], w);
+  if constexpr (SCORE) {
+    if (p < nt) rs_score<DT>(p, kr[P6 % 3], xb[P6 % 2], fb[P6 % 2], flb[P6 % 2], w, qf, mref, l, lr, sl2);
+  } else {
+    if (p >= 1) rs_pv<DT>(p - 1, vr[(P6 + 2) % 3], xb[(P6 + 1) % 2], fb[(P6 + 1) % 2], flb[(P6 + 1) % 2], w, oacc);
+  }
+}
+
+template <int DT, bool SCORE>
+__device__ __forceinline__ void rs_loop(int nt, const u16* Kh, const u16* Vh, int kbytes,
+                                        unsigned char* const (&kr)[3], unsigned char* const (&vr)[3],
+                                        u32x4* const (&xb)[2], float* const (&fb)[2], int* const (&flb)[2],
+                                        const Wave16& w, const u32x4 (&qf)[rs::NKK], f32x16 (&oacc)[rs::NDT],
+                                        float& mref, float& l, float& lr, float sl2) {
+  // K tiles 0 and 1 and V tile 0; each period then starts two more tiles.
+  // Loads run past the last tile (reading zeros into stages nobody reads),
+  // so that every period waits for the same count.
+  rs_issue(Kh, kbytes, 0, kr[0], w);
+  rs_issue(Kh, kbytes, 1, kr[1], w);
+  rs_issue(Vh, kbytes, 0, vr[0], w);
+#define RS_PERIOD(P6) \
+  rs_period<DT, SCORE, P6>(p + P6, nt, Kh, Vh, kbytes, kr, vr, xb, fb, flb, w, qf, oacc, mref, l, lr, sl2)
+  for (int p = 0; p <= nt; p += 6) {
+    RS_PERIOD(0);
+    if (p + 1 <= nt) RS_PERIOD(1);
+    if (p + 2 <= nt) RS_PERIOD(2);
+    if (p + 3 <= nt) RS_PERIOD(3);
+    if (p + 4 <= nt) RS_PERIOD(4);
+    if (p + 5 <= nt) RS_PERIOD(5);
+  }
+#undef RS_PERIOD
+  // The loads past the last tile complete before the workgroup's LDS is
+  // released.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); lgkmcnt, expcnt: no wait
+}
+
+// SPLIT and VARLEN as in fa_fwd_16.
+template <int DT, bool CAUSAL, bool SPLIT = false, bool VARLEN = false>
+__global__ __launch_bounds__(512, 1) void fa_fwd_rs(const u16* __restrict__ Qg, const u16* __restrict__ Kg,
+                                                    const u16* __restrict__ Vg, u16* __restrict__ Og,
+                                                    float* __restrict__ Lg, int BH, int Nq, int Nk, int nqt,
+                                                    float sl2, int split_len, float* __restrict__ Po,
+                                                    float* __restrict__ Pl, const int* __restrict__ cuq,
+                                                    const int* __restrict__ cuk, int H, int tq, int tk) {
+  using namespace rs;
+  constexpr int BR = 128;
+  // Ring stages of 16 KB, aligned to their size so that none straddles a
+  // 64 KB boundary (the operand reads address one 64 KB window each).
+  __shared__ __attribute__((aligned(16384))) unsigned char k0s[TILEB];
+  __shared__ __attribute__((aligned(16384))) unsigned char k1s[TILEB];
+  __shared__ __attribute__((aligned(16384))) unsigned char k2s[TILEB];
+  __shared__ __attribute__((aligned(16384))) unsigned char v0s[TILEB];
+  __shared__ __attribute__((aligned(16384))) unsigned char v1s[TILEB];
+  __shared__ __attribute__((aligned(16384))) unsigned char v2s[TILEB];
+  __shared__ u32x4 x0[4 * XG];
+  __shared__ u32x4 x1[4 * XG];
+  __shared__ float f0[4 * 64];
+  __shared__ float f1[4 * 64];
+  __shared__ float finv[4 * 64];
+  __shared__ int fl0[4];
+  __shared__ int fl1[4];
+
+  Wave16 w;
+  const int tid = threadIdx.x;
+  w.lane = tid & 63;
+  w.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  w.hf = w.lane >> 5;
+  w.l32 = w.lane & 31;
+  int bh, qt, split;
+  if (!fwd_block<SPLIT, VARLEN>(nqt, BH, bh, qt, split)) return;
+  const int q0 = qt * BR;
+  const HeadRows hr = head_rows<VARLEN>(bh, Nq, Nk, D, cuq, cuk, H, tq, tk);
+  const int nq = hr.nq, NK = hr.nk;
+  if (q0 >= nq) return;  // past this sequence's rows: the whole workgroup
+  const u16* Qh = Qg + hr.qo;
+  u16* Oh = Og + hr.qo;
+  float* Lh = Lg + hr.so;
+  const int kb = SPLIT ? split * split_len : 0;
+  const int nk = SPLIT ? min(split_len, NK - kb) : NK;
+  const u16* Kh = Kg + hr.ko + (size_t)kb * D;
+  const u16* Vh = Vg + hr.ko + (size_t)kb * D;
+  const int kbytes = nk * ROWB;
+  const int kend = CAUSAL ? min(nk, min(q0 + BR, nq) - kb) : nk;
+  const int nt = kend > 0 ? (kend + BC - 1) / BC : 0;
+  const int grp = w.wave & 3;
+  const bool score = w.wave < 4;
+  w.wq0 = q0 + 32 * grp;
+  const int myq = w.wq0 + w.l32;
+  w.wkend = w.wq0 >= nq ? 0 : CAUSAL ? min(kend, w.wq0 + 32 - kb) : kend;
+  w.klim = CAUSAL ? min(myq - kb, nk - 1) : nk - 1;
+  w.wklim = CAUSAL ? min(w.wq0 - kb, nk - 1) : nk - 1;
+  init_operand_offsets<D>(w);
+
+  unsigned char* const kr[3] = {k0s, k1s, k2s};
+  unsigned char* const vr[3] = {v0s, v1s, v2s};
+  u32x4* const xb[2] = {x0 + XG * grp, x1 + XG * grp};
+  float* const fb[2] = {f0 + 64 * grp, f1 + 64 * grp};
+  int* const flb[2] = {fl0 + grp, fl1 + grp};
+  float* const fi = finv + 64 * grp;
+
+  u32x4 qf[NKK];
+  f32x16 oacc[NDT];
+  float mref = kMinit, l = 0.f, lr = 0.f;
+  if (score) {
+    // Q fragment (B operand of S^T): lane holds Q[myq][16 kk + 8 hf .. +7];
+    // rows past Nq read as zero.
+    const auto rQ = make_rsrc_at(Qh, w.wq0 * ROWB, nq * ROWB);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      qf[kk] = __builtin_amdgcn_raw_buffer_load_b128(rQ, w.l32 * ROWB + (16 * kk + 8 * w.hf) * 2, 0, 0);
+    rs_loop<DT, true>(nt, Kh, Vh, kbytes, kr, vr, xb, fb, flb, w, qf, oacc, mref, l, lr, sl2);
+    const float lt = pair_sum(l);
+    const float ltr = DT == kBF16 ? pair_sum(lr) : lt;
+    const bool none = (SPLIT || VARLEN) && !(lt > 0.f);
+    fi[w.lane] = none ? 0.f : 1.0f / ltr;
+    if (w.hf == 0) {
+      const float lse = none ? -INFINITY : (mref + __log2f(lt)) * kLn2;
+      const auto rL = SPLIT ? make_rsrc_at(Pl + ((size_t)split * BH + bh) * Nq, w.wq0 * 4, nq * 4)
+                            : make_rsrc_at(Lh, w.wq0 * 4, nq * 4);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse), rL, w.l32 * 4, 0, 0);
+    }
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
+    rs_loop<DT, false>(nt, Kh, Vh, kbytes, kr, vr, xb, fb, flb, w, qf, oacc, mref, l, lr, sl2);
+    __syncthreads();
+    const float inv = fi[w.lane];
+    if constexpr (SPLIT) {
+      // fp32 partial of this key range, stored 8 bytes at a time from two
+      // address registers (see fa_fwd_16).
+      const size_t slot = (size_t)split * BH + bh;
+      const auto rP = make_rsrc_at(Po + slot * Nq * D, w.wq0 * D * 4, nq * D * 4);
+      const int off0 = w.l32 * D * 4 + 4 * w.hf * 4;
+      int off1 = off0 + 8;
+      asm volatile("" : "+v"(off1));
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x2 v0 = {oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv};
+          const f32x2 v1 = {oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv};
+          const int col = (32 * dt + 8 * g) * 4;
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v0), rP, off0 + col, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v1), rP, off1 + col, 0, 0);
+        }
+    } else {
+      const auto rO = make_rsrc_at(Oh, w.wq0 * ROWB, nq * ROWB);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2 v;
+          v[0] = pack2<DT>(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv);
+          v[1] = pack2<DT>(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
+          __builtin_amdgcn_raw_buffer_store_b64(v, rO, w.l32 * ROWB + (32 * dt + 8 * g + 4 * w.hf) * 2, 0, 0);
+        }
+    }
+  }
+}
+
+template <int DT, bool CAUSAL, bool SPLIT, bool VARLEN = false>
+int launch_rs(const FaLaunch& a, float sl2, int nsplit, int split_len, float* Po, float* Pl) {
+  const int nqt = (int)((a.Nq + 127) / 128);
+  const int64_t heads = VARLEN ? (a.BH + 7) / 8 * 8 : a.BH;
+  const dim3 grid((unsigned)(heads * nqt * nsplit)), block(512);
+  return launch_kernel(fa_fwd_rs<DT, CAUSAL, SPLIT, VARLEN>, grid, block, (hipStream_t)a.stream, (const u16*)a.q,
+                       (const u16*)a.k, (const u16*)a.v, (u16*)a.o, a.lse, (int)a.BH, (int)a.Nq, (int)a.Nk, nqt,
+                       sl2, split_len, Po, Pl, a.cu_q, a.cu_k, (int)a.H, (int)a.total_q, (int)a.total_k);
 }
 
 // ---------------------------------------------------------------------------
@@ -949,17 +1245,46 @@ int dispatch16_varlen(const FaLaunch& a, float sl2) {
 
 #ifdef FA_FWD_D256
 
+namespace {
+
+template <int DT>
+int dispatch_rs(const FaLaunch& a, float sl2) {
+  return a.causal ? launch_rs<DT, true, false>(a, sl2, 1, 0, nullptr, nullptr)
+                  : launch_rs<DT, false, false>(a, sl2, 1, 0, nullptr, nullptr);
+}
+
+template <int DT>
+int dispatch_rs_split(const FaLaunch& a, float sl2, int nsplit, int split_len) {
+  const int64_t rows = a.BH * a.Nq;
+  float* Po = (float*)a.workspace;
+  float* Pl = Po + (size_t)nsplit * rows * rs::D;
+  const int st = a.causal ? launch_rs<DT, true, true>(a, sl2, nsplit, split_len, Po, Pl)
+                          : launch_rs<DT, false, true>(a, sl2, nsplit, split_len, Po, Pl);
+  if (st != 0) return st;
+  const int64_t threads = rows * (rs::D / 4);
+  return launch_kernel(merge_splits<DT, rs::D>, dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                       (hipStream_t)a.stream, (const float*)Po, (const float*)Pl, a.o, a.lse, rows, nsplit);
+}
+
+template <int DT>
+int dispatch_rs_varlen(const FaLaunch& a, float sl2) {
+  return a.causal ? launch_rs<DT, true, false, true>(a, sl2, 1, 0, nullptr, nullptr)
+                  : launch_rs<DT, false, false, true>(a, sl2, 1, 0, nullptr, nullptr);
+}
+
+}  // namespace
+
 int fa_launch_fwd_d256(const FaLaunch& a, float sl2) {
-  return a.dtype == kBF16 ? dispatch16<kBF16, 256>(a, sl2) : dispatch16<kFP16, 256>(a, sl2);
+  return a.dtype == kBF16 ? dispatch_rs<kBF16>(a, sl2) : dispatch_rs<kFP16>(a, sl2);
 }
 
 int fa_launch_fwd_splitkv_d256(const FaLaunch& a, float sl2, int nsplit, int split_len) {
-  return a.dtype == kBF16 ? dispatch16_split<kBF16, 256>(a, sl2, nsplit, split_len)
-                          : dispatch16_split<kFP16, 256>(a, sl2, nsplit, split_len);
+  return a.dtype == kBF16 ? dispatch_rs_split<kBF16>(a, sl2, nsplit, split_len)
+                          : dispatch_rs_split<kFP16>(a, sl2, nsplit, split_len);
 }
 
 int fa_launch_fwd_varlen_d256(const FaLaunch& a, float sl2) {
-  return a.dtype == kBF16 ? dispatch16_varlen<kBF16, 256>(a, sl2) : dispatch16_varlen<kFP16, 256>(a, sl2);
+  return a.dtype == kBF16 ? dispatch_rs_varlen<kBF16>(a, sl2) : dispatch_rs_varlen<kFP16>(a, sl2);
 }
 
 #else

@@ -105,14 +105,29 @@ def test_parity_8wave_several_q_tiles(dt, D, causal):
 
 @pytest.mark.parametrize("dt", ["bf16", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("Nq,Nk", [(300, 300), (257, 517), (130, 70), (1, 200)])
+@pytest.mark.parametrize("Nq,Nk", [(300, 300), (257, 517), (130, 70), (1, 200), (40, 300), (129, 33),
+                                   (300, 100), (64, 17)])
 def test_parity_d256(dt, causal, Nq, Nk):
-    # head dimension 256: 4 waves per workgroup, 32-key tiles, pipelined steps
+    # head dimension 256: 128-row workgroups of score and PV waves (one pair
+    # per 32 rows), 32-key tiles.  Nq = 40 leaves two row groups with no row
+    # at all, 129 a workgroup with one row; Nk = 33 and 17 give a ragged or
+    # lone partial key tile; 300 x 100 under the causal mask has rows that see
+    # every key.
     w = workloads.Workload(f"d256_{dt}_{'c' if causal else 'n'}_{Nq}x{Nk}", 2, 2, Nq, Nk, 256, dt, causal,
                            2560 + Nq + Nk)
     cpu, gpu = _case(w)
     o, l = run_gpu(*gpu, w.causal)
     compare_full(w, cpu, o, l, "d256")
+
+
+@pytest.mark.parametrize("dt,causal", [("bf16", True), ("fp16", False)])
+def test_parity_d256_many_workgroups(dt, causal):
+    # More 128-row workgroups than CUs (96 heads x 3 = 288): CUs run
+    # workgroups back to back, every element compared.
+    w = workloads.Workload(f"d256_many_{dt}", 1, 96, 300, 333, 256, dt, causal, 2600)
+    cpu, gpu = _case(w)
+    o, l = run_gpu(*gpu, w.causal)
+    compare_full(w, cpu, o, l, "d256-many")
 
 
 def test_parity_d256_scaled_and_moves():
