@@ -12,8 +12,9 @@
 // Work decomposition: one workgroup per (batch*head, Q tile); each wave owns
 // 32 query rows.  16-bit kernel: 8 waves (256 rows), K/V tiles of 64 keys
 // loaded straight from HBM into a 4-stage LDS ring (one barrier per tile).
-// At D = 256 (fa_fwd_rs): 8 waves over 128 rows, two per 32-row group, one
-// running the scores and softmax, the other O += P V; 32-key tiles.
+// At D = 256, and on grids with fewer 256-row workgroups than CUs
+// (fa_fwd_rs): 8 waves over 128 rows, two per 32-row group, one running the
+// scores and softmax, the other O += P V.
 // fp32 kernel: 4 waves (128 rows), K/V staged through registers into a
 // double-buffered LDS stage; on grids with at most one such workgroup per CU,
 // 32-row workgroups whose waves split each 128-key tile and merge at the end.
@@ -72,10 +73,10 @@ constexpr int waves16() {
   return FA_WAVES16;
 }
 // Software pipelining (step16p) pays only where a SIMD runs one wave, i.e.
-// in the 4-wave form (small grids, see dispatch16): with 8 waves the two
-// waves of a SIMD already overlap one's softmax with the other's MFMAs, and
-// the fixed interleave of step16p measured slower there (6% at D = 128, 22%
-// at D = 64).
+// in the 4-wave form (small grids at D = 32, see dispatch16): with 8 waves
+// the two waves of a SIMD already overlap one's softmax with the other's
+// MFMAs, and the fixed interleave of step16p measured slower there (6% at
+// D = 128, 22% at D = 64).
 template <int D>
 constexpr int bc16() {
   return 64;
@@ -585,108 +586,128 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && NW == 8) ? 4 : 1) void fa_fwd_
 }
 
 // ---------------------------------------------------------------------------
-// Role-split 16-bit kernel at D = 256.
+// Role-split 16-bit kernel (D = 256; small grids at D = 64 and 128).
 // ---------------------------------------------------------------------------
 // One workgroup of 8 waves per (batch*head, 128 query rows, key range).
 // Waves g and g + 4 share a SIMD and the 32 rows of group g.  Wave g, the
 // score wave, holds the rows' Q fragment and runs S^T = K Q^T, the mask and
-// the online-softmax update of each 32-key tile, and leaves P (rounded to
-// 16 bits) in LDS; wave g + 4, the PV wave, holds the rows' fp32 O and one
-// tile later rescales it (when the score wave moved the reference) and adds
+// the online-softmax update of each key tile, and leaves P (rounded to 16
+// bits) in LDS; wave g + 4, the PV wave, holds the rows' fp32 O and one tile
+// later rescales it (when the score wave moved the reference) and adds
 // V^T P^T.  A wave holding both the Q fragment and O of 32 rows at D = 256
 // needs more than half of a SIMD's registers (one wave per SIMD, nothing to
 // run while a wave computes its exponentials); split, each role fits two
 // waves per SIMD, and one wave's softmax runs beside its sibling's MFMAs.
-// K and V tiles stream through two 3-stage rings; in period p every wave
-// meets the others once (K tile p and V tile p-1 are then complete), starts
-// the loads of V tile p+1 and K tile p+2, and the score waves handle tile p
-// while the PV waves handle tile p-1.  P, a flag for a moved reference and
-// the rescale factors travel through double-buffered LDS areas.
-namespace rs {
-constexpr int D = 256, BC = 32, ROWB = D * 2, TILEB = BC * ROWB, NKK = D / 16, NDT = D / 32;
-constexpr int kLoads = 2 * (TILEB / 1024 / 8);  // direct-to-LDS loads per wave per period
-constexpr int XG = 2 * 64;                      // u32x4 of P per group and buffer
-}  // namespace rs
+// The same holds for the grids too small to give the 256-row kernel a
+// workgroup per CU.  K and V tiles stream through two 3-stage rings; in
+// period p every wave meets the others once (K tile p and V tile p-1 are
+// then complete), starts the loads of V tile p+1 and K tile p+2, and the
+// score waves handle tile p while the PV waves handle tile p-1.  P, a flag
+// for a moved reference and the rescale factors travel through
+// double-buffered LDS areas.
+template <int D>
+struct RsShape {
+  static constexpr int BC = D == 256 ? 32 : 64;  // keys per tile
+  static constexpr int ROWB = D * 2, TILEB = BC * ROWB, NKK = D / 16, NDT = D / 32;
+  static constexpr int NB = BC / 32, KS = BC / 16;       // 32-key blocks, 16-key PV steps
+  static constexpr int NPIECE = TILEB / 1024 / 8;        // 1 KB loads per wave and tile
+  static constexpr int kLoads = 2 * NPIECE;              // loads per wave and period
+  static constexpr int XG = KS * 64;                     // u32x4 of P per group and buffer
+  static_assert(TILEB % 8192 == 0, "whole 1 KB pieces for each of the 8 waves");
+};
 
-// This wave's two 1 KB pieces of tile t of one [N, D] tensor (16 KB).
+// One 1 KB direct-to-LDS load: 16 bytes a lane from byte `go` of `r`.
+__device__ __forceinline__ void rs_piece(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int go) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, go, 0, 0, 0);
+}
+
+// This wave's 1 KB pieces of tile t of one [N, D] tensor.
+template <int D>
 __device__ __forceinline__ void rs_issue(const u16* Xh, int kbytes, int t, unsigned char* dst, const Wave16& w) {
-  const auto r = make_rsrc_at(Xh, t * rs::TILEB, kbytes);
+  using S = RsShape<D>;
+  const auto r = make_rsrc_at(Xh, t * S::TILEB, kbytes);
 #pragma unroll
-  for (int I = 0; I < rs::TILEB / 1024 / 8; ++I) {
+  for (int I = 0; I < S::NPIECE; ++I) {
     const int G = w.wave + 8 * I;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + G * 1024), 16, dma_src_off<rs::D>(G, w.lane), 0,
-                                             0, 0);
+    rs_piece(r, dst + G * 1024, dma_src_off<D>(G, w.lane));
   }
 }
 
 // Score wave, tile j (K stage ks): S^T, mask, online softmax with the sum
-// rule (the reference moves only when a lane's sum of its 16 P exceeds
-// 2^15, and on the first tile), then P to xo, the move flag to *fl and,
-// when it moved, the factor to fo.
-template <int DT>
+// rule (the reference moves only when a lane's sum of its P exceeds 2^15,
+// and on the first tile), then P to xo, the move flag to *fl and, when it
+// moved, the factor to fo.
+template <int DT, int D>
 __device__ __forceinline__ void rs_score(int j, const unsigned char* ks, u32x4* xo, float* fo, int* fl,
-                                         const Wave16& w, const u32x4 (&qf)[rs::NKK], float& mref, float& l,
+                                         const Wave16& w, const u32x4 (&qf)[D / 16], float& mref, float& l,
                                          float& lr, float sl2) {
-  using namespace rs;
+  using S = RsShape<D>;
+  constexpr int NB = S::NB, NKK = S::NKK, BC = S::BC, NQK = NB * NKK, PRE = NQK < 8 ? NQK : 8;
   const int k0 = j * BC;
   if (k0 >= w.wkend) return;
-  constexpr int PRE = 8;
-  f32x16 s[1];
-  s[0] = f32x16{};
-  u32x4 ka[NKK];
+  f32x16 s[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) s[n] = f32x16{};
+  u32x4 ka[NQK];
 #pragma unroll
   for (int i = 0; i < PRE; ++i) ka[i] = ks_operand<D>(ks, w, i);
 #pragma unroll
-  for (int i = 0; i < NKK; ++i) {
-    if (i + PRE < NKK) ka[i + PRE] = ks_operand<D>(ks, w, i + PRE);
-    s[0] = mfma_32x32x16<DT>(ka[i], qf[i], s[0]);
+  for (int i = 0; i < NQK; ++i) {
+    if (i + PRE < NQK) ka[i + PRE] = ks_operand<D>(ks, w, i + PRE);
+    s[i / NKK] = mfma_32x32x16<DT>(ka[i], qf[i % NKK], s[i / NKK]);
   }
-  // Mask (diagonal and tail tiles only): key = k0 + 4*hf + 8*(r/4) + r%4.
+  // Mask (diagonal and tail tiles only): key = k0 + 4*hf + 32*n + 8*(r/4) + r%4.
   if (k0 + BC - 1 > w.wklim) {
     const int lim = w.klim - (k0 + 4 * w.hf);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[0][r] = (8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[0][r];
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[n][r] = (32 * n + 8 * (r >> 2) + (r & 3) > lim) ? -INFINITY : s[n][r];
   }
   constexpr float kBound = 32768.0f;
-  u32x4 pf[1][2];
+  u32x4 pf[NB][2];
   float tl = 0.f, tr = 0.f;
   bool redo = j == 0;
   if (!redo) {
-    exp_tile<DT, 1>(s, sl2, -mref, pf, tl, tr);
+    exp_tile<DT, NB>(s, sl2, -mref, pf, tl, tr);
     redo = __builtin_amdgcn_ballot_w64(!((DT == kBF16 ? tl : tr) <= kBound)) != 0;
   }
   if (redo) {
     float mx = s[0][0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int r = (n == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[n][r]);
     const float mnew = fmaxf(mref, pair_max(mx * sl2));
     const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
     l *= alpha;
     lr *= alpha;
     mref = mnew;
-    exp_tile<DT, 1>(s, sl2, -mref, pf, tl, tr);
+    exp_tile<DT, NB>(s, sl2, -mref, pf, tl, tr);
     fo[w.lane] = alpha;
   }
   l += DT == kBF16 ? tl : tr;
   lr += tr;
-  xo[w.lane] = pf[0][0];
-  xo[64 + w.lane] = pf[0][1];
+#pragma unroll
+  for (int g = 0; g < 2 * NB; ++g) xo[64 * g + w.lane] = pf[g >> 1][g & 1];
   *fl = redo ? 1 : 0;
 }
 
 // PV wave, tile jj (V stage vs): rescale O if the score wave moved the
-// reference, then O^T += V^T P^T with the P from xi (16-key step major, so
-// consecutive MFMAs use different accumulators).
-template <int DT>
+// reference, then O^T += V^T P^T with the P from xi (16-key step g major,
+// so consecutive MFMAs use different accumulators).
+template <int DT, int D>
 __device__ __forceinline__ void rs_pv(int jj, const unsigned char* vs, const u32x4* xi, const float* fi,
-                                      const int* fl, const Wave16& w, f32x16 (&oacc)[rs::NDT]) {
-  using namespace rs;
+                                      const int* fl, const Wave16& w, f32x16 (&oacc)[D / 32]) {
+  using S = RsShape<D>;
+  constexpr int NDT = S::NDT, KS = S::KS, BC = S::BC, NPV = KS * NDT, PRE = 8;
   if (jj * BC >= w.wkend) return;
-  constexpr int NPV = 2 * NDT, PRE = 8;
   u32x4 va[NPV];
 #pragma unroll
-  for (int i = 0; i < PRE; ++i) va[i] = vt_operand<D, BC>(vs, w, (i % NDT) * 2 + i / NDT);
-  const u32x4 p0 = xi[w.lane], p1 = xi[64 + w.lane];
+  for (int i = 0; i < PRE; ++i) va[i] = vt_operand<D, BC>(vs, w, (i % NDT) * KS + i / NDT);
+  u32x4 pk[KS];
+#pragma unroll
+  for (int g = 0; g < KS; ++g) pk[g] = xi[64 * g + w.lane];
   if (__builtin_amdgcn_readfirstlane(*fl)) {
     const float a = fi[w.lane];
 #pragma unroll
@@ -695,42 +716,43 @@ __device__ __forceinline__ void rs_pv(int jj, const unsigned char* vs, const u32
 #pragma unroll
   for (int i = 0; i < NPV; ++i) {
     const int ip = i + PRE;
-    if (ip < NPV) va[ip] = vt_operand<D, BC>(vs, w, (ip % NDT) * 2 + ip / NDT);
-    oacc[i % NDT] = mfma_32x32x16<DT>(va[i], i < NDT ? p0 : p1, oacc[i % NDT]);
+    if (ip < NPV) va[ip] = vt_operand<D, BC>(vs, w, (ip % NDT) * KS + ip / NDT);
+    oacc[i % NDT] = mfma_32x32x16<DT>(va[i], pk[i / NDT], oacc[i % NDT]);
   }
 }
 
 // Period p of one role (P6 = p mod 6: stages p mod 3, buffers p mod 2).
-template <int DT, bool SCORE, int P6>
+template <int DT, int D, bool SCORE, int P6>
 __device__ __forceinline__ void rs_period(int p, int nt, const u16* Kh, const u16* Vh, int kbytes,
                                           unsigned char* const (&kr)[3], unsigned char* const (&vr)[3],
                                           u32x4* const (&xb)[2], float* const (&fb)[2], int* const (&flb)[2],
-                                          const Wave16& w, const u32x4 (&qf)[rs::NKK], f32x16 (&oacc)[rs::NDT],
+                                          const Wave16& w, const u32x4 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
                                           float& mref, float& l, float& lr, float sl2) {
-  wait_tile_and_barrier(rs::kLoads);
-  rs_issue(Vh, kbytes, p + 1, vr[(P6 + 1) % 3], w);
-  rs_issue(Kh, kbytes, p + 2, kr[(P6 + 2) % 3], w);
+  wait_tile_and_barrier(RsShape<D>::kLoads);
+  rs_issue<D>(Vh, kbytes, p + 1, vr[(P6 + 1) % 3], w);
+  rs_issue<D>(Kh, kbytes, p + 2, kr[(P6 + 2) % 3], w);
   if constexpr (SCORE) {
-    if (p < nt) rs_score<DT>(p, kr[P6 % 3], xb[P6 % 2], fb[P6 % 2], flb[P6 % 2], w, qf, mref, l, lr, sl2);
+    if (p < nt) rs_score<DT, D>(p, kr[P6 % 3], xb[P6 % 2], fb[P6 % 2], flb[P6 % 2], w, qf, mref, l, lr, sl2);
   } else {
-    if (p >= 1) rs_pv<DT>(p - 1, vr[(P6 + 2) % 3], xb[(P6 + 1) % 2], fb[(P6 + 1) % 2], flb[(P6 + 1) % 2], w, oacc);
+    if (p >= 1)
+      rs_pv<DT, D>(p - 1, vr[(P6 + 2) % 3], xb[(P6 + 1) % 2], fb[(P6 + 1) % 2], flb[(P6 + 1) % 2], w, oacc);
   }
 }
 
-template <int DT, bool SCORE>
+template <int DT, int D, bool SCORE>
 __device__ __forceinline__ void rs_loop(int nt, const u16* Kh, const u16* Vh, int kbytes,
                                         unsigned char* const (&kr)[3], unsigned char* const (&vr)[3],
                                         u32x4* const (&xb)[2], float* const (&fb)[2], int* const (&flb)[2],
-                                        const Wave16& w, const u32x4 (&qf)[rs::NKK], f32x16 (&oacc)[rs::NDT],
+                                        const Wave16& w, const u32x4 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
                                         float& mref, float& l, float& lr, float sl2) {
   // K tiles 0 and 1 and V tile 0; each period then starts two more tiles.
   // Loads run past the last tile (reading zeros into stages nobody reads),
   // so that every period waits for the same count.
-  rs_issue(Kh, kbytes, 0, kr[0], w);
-  rs_issue(Kh, kbytes, 1, kr[1], w);
-  rs_issue(Vh, kbytes, 0, vr[0], w);
+  rs_issue<D>(Kh, kbytes, 0, kr[0], w);
+  rs_issue<D>(Kh, kbytes, 1, kr[1], w);
+  rs_issue<D>(Vh, kbytes, 0, vr[0], w);
 #define RS_PERIOD(P6) \
-  rs_period<DT, SCORE, P6>(p + P6, nt, Kh, Vh, kbytes, kr, vr, xb, fb, flb, w, qf, oacc, mref, l, lr, sl2)
+  rs_period<DT, D, SCORE, P6>(p + P6, nt, Kh, Vh, kbytes, kr, vr, xb, fb, flb, w, qf, oacc, mref, l, lr, sl2)
   for (int p = 0; p <= nt; p += 6) {
     RS_PERIOD(0);
     if (p + 1 <= nt) RS_PERIOD(1);
@@ -746,23 +768,24 @@ __device__ __forceinline__ void rs_loop(int nt, const u16* Kh, const u16* Vh, in
 }
 
 // SPLIT and VARLEN as in fa_fwd_16.
-template <int DT, bool CAUSAL, bool SPLIT = false, bool VARLEN = false>
+template <int DT, int D, bool CAUSAL, bool SPLIT = false, bool VARLEN = false>
 __global__ __launch_bounds__(512, 1) void fa_fwd_rs(const u16* __restrict__ Qg, const u16* __restrict__ Kg,
                                                     const u16* __restrict__ Vg, u16* __restrict__ Og,
                                                     float* __restrict__ Lg, int BH, int Nq, int Nk, int nqt,
                                                     float sl2, int split_len, float* __restrict__ Po,
                                                     float* __restrict__ Pl, const int* __restrict__ cuq,
                                                     const int* __restrict__ cuk, int H, int tq, int tk) {
-  using namespace rs;
-  constexpr int BR = 128;
-  // Ring stages of 16 KB, aligned to their size so that none straddles a
-  // 64 KB boundary (the operand reads address one 64 KB window each).
-  __shared__ __attribute__((aligned(16384))) unsigned char k0s[TILEB];
-  __shared__ __attribute__((aligned(16384))) unsigned char k1s[TILEB];
-  __shared__ __attribute__((aligned(16384))) unsigned char k2s[TILEB];
-  __shared__ __attribute__((aligned(16384))) unsigned char v0s[TILEB];
-  __shared__ __attribute__((aligned(16384))) unsigned char v1s[TILEB];
-  __shared__ __attribute__((aligned(16384))) unsigned char v2s[TILEB];
+  using S = RsShape<D>;
+  constexpr int BR = 128, BC = S::BC, ROWB = S::ROWB, TILEB = S::TILEB, NKK = S::NKK, NDT = S::NDT, XG = S::XG;
+  // Ring stages aligned to their size so that none straddles a 64 KB
+  // boundary (the operand reads address one 64 KB window each); as the most
+  // aligned arrays they are also laid out first, within the first 96 KB.
+  __shared__ __attribute__((aligned(TILEB))) unsigned char k0s[TILEB];
+  __shared__ __attribute__((aligned(TILEB))) unsigned char k1s[TILEB];
+  __shared__ __attribute__((aligned(TILEB))) unsigned char k2s[TILEB];
+  __shared__ __attribute__((aligned(TILEB))) unsigned char v0s[TILEB];
+  __shared__ __attribute__((aligned(TILEB))) unsigned char v1s[TILEB];
+  __shared__ __attribute__((aligned(TILEB))) unsigned char v2s[TILEB];
   __shared__ u32x4 x0[4 * XG];
   __shared__ u32x4 x1[4 * XG];
   __shared__ float f0[4 * 64];
@@ -819,7 +842,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_rs(const u16* __restrict__ Qg, 
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
       qf[kk] = __builtin_amdgcn_raw_buffer_load_b128(rQ, w.l32 * ROWB + (16 * kk + 8 * w.hf) * 2, 0, 0);
-    rs_loop<DT, true>(nt, Kh, Vh, kbytes, kr, vr, xb, fb, flb, w, qf, oacc, mref, l, lr, sl2);
+    rs_loop<DT, D, true>(nt, Kh, Vh, kbytes, kr, vr, xb, fb, flb, w, qf, oacc, mref, l, lr, sl2);
     const float lt = pair_sum(l);
     const float ltr = DT == kBF16 ? pair_sum(lr) : lt;
     const bool none = (SPLIT || VARLEN) && !(lt > 0.f);
@@ -834,7 +857,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_rs(const u16* __restrict__ Qg, 
   } else {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
-    rs_loop<DT, false>(nt, Kh, Vh, kbytes, kr, vr, xb, fb, flb, w, qf, oacc, mref, l, lr, sl2);
+    rs_loop<DT, D, false>(nt, Kh, Vh, kbytes, kr, vr, xb, fb, flb, w, qf, oacc, mref, l, lr, sl2);
     __syncthreads();
     const float inv = fi[w.lane];
     if constexpr (SPLIT) {
@@ -870,12 +893,12 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_rs(const u16* __restrict__ Qg, 
   }
 }
 
-template <int DT, bool CAUSAL, bool SPLIT, bool VARLEN = false>
+template <int DT, int D, bool CAUSAL, bool SPLIT, bool VARLEN = false>
 int launch_rs(const FaLaunch& a, float sl2, int nsplit, int split_len, float* Po, float* Pl) {
   const int nqt = (int)((a.Nq + 127) / 128);
   const int64_t heads = VARLEN ? (a.BH + 7) / 8 * 8 : a.BH;
   const dim3 grid((unsigned)(heads * nqt * nsplit)), block(512);
-  return launch_kernel(fa_fwd_rs<DT, CAUSAL, SPLIT, VARLEN>, grid, block, (hipStream_t)a.stream, (const u16*)a.q,
+  return launch_kernel(fa_fwd_rs<DT, D, CAUSAL, SPLIT, VARLEN>, grid, block, (hipStream_t)a.stream, (const u16*)a.q,
                        (const u16*)a.k, (const u16*)a.v, (u16*)a.o, a.lse, (int)a.BH, (int)a.Nq, (int)a.Nk, nqt,
                        sl2, split_len, Po, Pl, a.cu_q, a.cu_k, (int)a.H, (int)a.total_q, (int)a.total_k);
 }
@@ -1138,10 +1161,17 @@ int launch16(const FaLaunch& a, float sl2, int nsplit, int split_len, float* Po,
 
 template <int DT, int D>
 int dispatch16(const FaLaunch& a, float sl2) {
-  // Fewer 8-wave workgroups than CUs: the 4-wave form (128 rows, one wave
-  // per SIMD, pipelined steps) doubles the workgroups.
+  // Fewer 8-wave workgroups than CUs: 128-row workgroups, which double them.
+  // D >= 64: the role-split kernel (two waves per SIMD; 35-55% faster than
+  // the 4-wave form on such grids, 15-34% slower than the 256-row kernel on
+  // grids that fill the CUs).  D = 32 (a 64-key tile is 4 KB, too little
+  // for eight waves' 1 KB loads): the 4-wave form (one wave per SIMD,
+  // pipelined steps).
   constexpr int NW8 = waves16<D>();
   if (NW8 == 8 && a.BH * ((a.Nq + 32 * NW8 - 1) / (32 * NW8)) < a.cus) {
+    if constexpr (D >= 64)
+      return a.causal ? launch_rs<DT, D, true, false>(a, sl2, 1, 0, nullptr, nullptr)
+                      : launch_rs<DT, D, false, false>(a, sl2, 1, 0, nullptr, nullptr);
     return a.causal ? launch16<DT, D, true, false, false, 4>(a, sl2, 1, 0, nullptr, nullptr)
                     : launch16<DT, D, false, false, false, 4>(a, sl2, 1, 0, nullptr, nullptr);
   }
@@ -1249,27 +1279,27 @@ namespace {
 
 template <int DT>
 int dispatch_rs(const FaLaunch& a, float sl2) {
-  return a.causal ? launch_rs<DT, true, false>(a, sl2, 1, 0, nullptr, nullptr)
-                  : launch_rs<DT, false, false>(a, sl2, 1, 0, nullptr, nullptr);
+  return a.causal ? launch_rs<DT, 256, true, false>(a, sl2, 1, 0, nullptr, nullptr)
+                  : launch_rs<DT, 256, false, false>(a, sl2, 1, 0, nullptr, nullptr);
 }
 
 template <int DT>
 int dispatch_rs_split(const FaLaunch& a, float sl2, int nsplit, int split_len) {
   const int64_t rows = a.BH * a.Nq;
   float* Po = (float*)a.workspace;
-  float* Pl = Po + (size_t)nsplit * rows * rs::D;
-  const int st = a.causal ? launch_rs<DT, true, true>(a, sl2, nsplit, split_len, Po, Pl)
-                          : launch_rs<DT, false, true>(a, sl2, nsplit, split_len, Po, Pl);
+  float* Pl = Po + (size_t)nsplit * rows * 256;
+  const int st = a.causal ? launch_rs<DT, 256, true, true>(a, sl2, nsplit, split_len, Po, Pl)
+                          : launch_rs<DT, 256, false, true>(a, sl2, nsplit, split_len, Po, Pl);
   if (st != 0) return st;
-  const int64_t threads = rows * (rs::D / 4);
-  return launch_kernel(merge_splits<DT, rs::D>, dim3((unsigned)((threads + 255) / 256)), dim3(256),
+  const int64_t threads = rows * (256 / 4);
+  return launch_kernel(merge_splits<DT, 256>, dim3((unsigned)((threads + 255) / 256)), dim3(256),
                        (hipStream_t)a.stream, (const float*)Po, (const float*)Pl, a.o, a.lse, rows, nsplit);
 }
 
 template <int DT>
 int dispatch_rs_varlen(const FaLaunch& a, float sl2) {
-  return a.causal ? launch_rs<DT, true, false, true>(a, sl2, 1, 0, nullptr, nullptr)
-                  : launch_rs<DT, false, false, true>(a, sl2, 1, 0, nullptr, nullptr);
+  return a.causal ? launch_rs<DT, 256, true, false, true>(a, sl2, 1, 0, nullptr, nullptr)
+                  : launch_rs<DT, 256, false, false, true>(a, sl2, 1, 0, nullptr, nullptr);
 }
 
 }  // namespace

@@ -73,13 +73,17 @@ def test_parity_fp32_grid_sizes(D, causal, B, H, Nq, Nk):
 @pytest.mark.parametrize("dt", ["bf16", "fp16"])
 @pytest.mark.parametrize("D", [32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("B,H,Nq,Nk", [(1, 3, 300, 700), (1, 256, 130, 300)])
+@pytest.mark.parametrize("B,H,Nq,Nk", [(1, 3, 300, 700), (1, 256, 130, 300), (1, 2, 40, 300), (1, 4, 129, 33),
+                                       (1, 2, 300, 100), (1, 3, 1, 17)])
 def test_parity_16bit_grid_sizes(dt, D, causal, B, H, Nq, Nk):
     # The 16-bit forward picks its workgroup from the grid: with fewer
     # 256-row (8-wave) workgroups than the 256 CUs (B*H*ceil(Nq/256) < 256,
-    # the first shape) it runs 128-row 4-wave workgroups with pipelined
-    # steps; the second shape (256 workgroups) keeps the 8-wave form.  Both
-    # compared element by element, with ragged Q and K tails.
+    # every shape but the second) it runs 128-row workgroups, of score and
+    # PV waves at D >= 64 and of 4 waves with pipelined steps at D = 32; the
+    # second shape (256 workgroups) keeps the 8-wave form.  All compared
+    # element by element, with ragged Q and K tails; Nq = 40 leaves row
+    # groups without rows, Nk = 33 and 17 a ragged or lone partial key tile,
+    # 300 x 100 (causal) rows that see every key.
     w = workloads.Workload(f"g16_{dt}_d{D}_{'c' if causal else 'n'}_h{H}_{Nq}x{Nk}", B, H, Nq, Nk, D, dt, causal,
                            1600 + D + Nq)
     cpu, gpu = _case(w)
@@ -148,8 +152,8 @@ def test_parity_reference_moves(dt, D, causal, H):
     # flight) is exercised.  fp32 takes a = 2 (|LSE| up to ~22 rather than
     # ~44): its absolute LSE tolerance of 1e-5 is a few fp32 ulps of such
     # values, below what the rounding of larger scores allows.  H = 2 runs
-    # the small-grid workgroup forms (4-wave 16-bit, key-split fp32), H = 128
-    # the large-grid ones (8-wave 16-bit at D <= 128, 128-row fp32).
+    # the small-grid workgroup forms (role-split 16-bit, key-split fp32),
+    # H = 128 the large-grid ones (8-wave 16-bit at D <= 128, 128-row fp32).
     w = workloads.Workload(f"moves_{dt}_d{D}_{'c' if causal else 'n'}_h{H}", 1, H, 700, 700, D, dt, causal,
                            4242 + D)
     q64, k64, v64 = workloads.draw_float64(w)

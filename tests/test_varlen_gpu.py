@@ -81,7 +81,7 @@ def test_varlen_equals_dense_for_equal_lengths(dt, H):
     # Equal lengths: bit for bit the dense forward's result.  The varlen
     # 16-bit kernel always runs 8-wave workgroups of 256 rows; the dense one
     # runs them too with H = 96 (3*96*ceil(300/256) = 576 workgroups, the
-    # same tiles), and its 4-wave, 128-row form with pipelined steps on the
+    # same tiles), and its role-split 128-row form (score and PV waves) on the
     # small grid of H = 4 (24 workgroups of 256 rows, fewer than the CUs):
     # the same arithmetic in the same order, so the same bits.  fp32 takes
     # enough heads (3*32*ceil(300/128) = 288 workgroups of 128 rows) that the
