@@ -18,22 +18,21 @@
 //    rows (the forward's shape): K/V tiles stream through the same 4-stage
 //    direct-to-LDS ring; per tile S^T = K Q^T, dP^T = V dO^T, then
 //    dQ^T += K^T dS^T (K read transposed);
-//  * bwd_dkdv: one workgroup per (batch*head, 128 keys), 4 waves of 32 keys
-//    (one wave per SIMD: 32 keys of K and V fragments plus fp32 dK and dV
-//    accumulators need more than 256 registers); Q/dO tiles of 64 query
+//  * bwd_dkdv (D = 32, 64): one workgroup per (batch*head, 128 keys), 4
+//    waves of 32 keys (one wave per SIMD); Q/dO tiles of 64 query
 //    rows plus their LSE and delta stream through a 4-stage ring; per tile
 //    S = Q K^T, dP = dO V^T (the wave's keys along the MFMA N dimension, so
 //    P and dS come out in the B-operand layout of the next products), then
 //    dV^T += dO^T P and dK^T += Q^T dS (dO and Q read transposed);
-//  * bwd_dkdv2 (D = 128): the same products with 8 waves, two per key group
-//    on one SIMD: one computes S, P and dV, the other dP, dS and dK with the
-//    P its sibling passes through LDS, so that each holds one fragment and
-//    one gradient and two waves fit each SIMD.
+//  * bwd_dkdv2 (D = 128 and 256): the same products with 8 waves, two per
+//    key group on one SIMD: one computes S, P and dV, the other dP, dS and
+//    dK with the P its sibling passes through LDS, so that each holds one
+//    fragment and one gradient and two waves fit each SIMD (bwd_dkdv, one
+//    wave per key group, serves D = 32 and 64).
 // S and dP are recomputed in both kernels: seven tile products instead of
 // the five a single kernel with atomic dQ updates would need.
-// At D = 256 bwd_dq has 4 waves (one per SIMD), bwd_dkdv runs as two kernels
-// (dV, then dK: one gradient's accumulators per wave), and both rings have 2
-// stages (a stage of two 64-row tiles takes 64 KB).
+// At D = 256 bwd_dq has 4 waves (one per SIMD) and a 2-stage ring (a stage
+// of two 64-row tiles takes 64 KB), and bwd_dkdv2 streams 32-row Q/dO tiles.
 //
 // The library compiles this file twice.  Without FA_BWD_SMALL_D it defines
 // fa_launch_bwd and the D = 128 kernels; with FA_BWD_SMALL_D only the D = 32
@@ -60,9 +59,10 @@ template <int D>
 constexpr int dq_waves() {
   return D == 256 ? 4 : 8;
 }
-// Stages of both kernels' LDS rings: 4 up to D = 128 (three tiles in flight);
-// at D = 256 a stage (64 rows of two tensors) takes 64 KB, so 2 (one tile in
-// flight: each tile waits for itself, then the next one starts).
+// Stages of the LDS rings of bwd_dq and bwd_dkdv: 4 up to D = 128 (three
+// tiles in flight); at D = 256 (bwd_dq) a stage (64 rows of two tensors)
+// takes 64 KB, so 2 (one tile in flight: each tile waits for itself, then
+// the next one starts).
 template <int D>
 constexpr int bwd_stages() {
   return D == 256 ? 2 : 4;
@@ -320,10 +320,7 @@ __device__ __forceinline__ void issue_kv_tile(const u16* Qh, const u16* dOh, int
   }
 }
 
-// GRADS: 3 = dK and dV, 1 = dK only, 2 = dV only (D = 256, where the fp32 dK
-// and dV of 32 keys plus the K and V fragments do not fit one wave's
-// registers, so one kernel runs per gradient).
-template <int DT, int D, bool CAUSAL, int GRADS>
+template <int DT, int D, bool CAUSAL>
 __device__ __forceinline__ void kv_tile(const u16* Qh, const u16* dOh, int qbytes, const float* l2h,
                                         const float* dlh, int Nq, int t0, int j, int nt, const unsigned char* src,
                                         unsigned char* dst, const Wave16& w, int wk0, const u32x4 (&kf)[D / 16],
@@ -339,9 +336,7 @@ __device__ __forceinline__ void kv_tile(const u16* Qh, const u16* dOh, int qbyte
   wait_tile_and_barrier(ST == 4 && j + 2 < nt ? kv_loads_per_tile<D>(w.wave) : 0);
   if (j + ST - 1 < nt) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t + ST - 1, dst, w);
   if (CAUSAL && q0 + 63 < wk0) return;  // every query of the tile precedes the wave's keys
-  static_assert(D != 128, "D = 128 runs bwd_dkdv2");
-  static_assert(GRADS == 3 || D == 256, "one gradient per kernel only at D = 256");
-  constexpr bool kDK = GRADS & 1, kDV = GRADS & 2;
+  static_assert(D <= 64, "D = 128 and 256 run bwd_dkdv2");
   const bool need_mask = CAUSAL && q0 < wk0 + 31;
   const int mykey = wk0 + w.l32;
 #pragma unroll
@@ -349,10 +344,8 @@ __device__ __forceinline__ void kv_tile(const u16* Qh, const u16* dOh, int qbyte
     f32x16 s = {}, dp = {};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) s = mfma_32x32x16<DT>(ks_operand<D>(qs, w, n * NKK + kk), kf[kk], s);
-    if constexpr (kDK) {
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) dp = mfma_32x32x16<DT>(ks_operand<D>(dos, w, n * NKK + kk), vf[kk], dp);
-    }
+    for (int kk = 0; kk < NKK; ++kk) dp = mfma_32x32x16<DT>(ks_operand<D>(dos, w, n * NKK + kk), vf[kk], dp);
     // Lane l holds key mykey and queries q0 + 32n + 8g + 4hf + e (r = 4g + e).
     float p[16], ds[16];
 #pragma unroll
@@ -366,7 +359,7 @@ __device__ __forceinline__ void kv_tile(const u16* Qh, const u16* dOh, int qbyte
         float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l4[e]));
         if (need_mask && q0 + qo + e < mykey) pr = 0.f;
         p[r] = pr;
-        ds[r] = kDK ? pr * (dp[r] - d4[e]) : 0.f;
+        ds[r] = pr * (dp[r] - d4[e]);
       }
     }
     u32x4 pf[2], dsf[2];
@@ -382,15 +375,15 @@ __device__ __forceinline__ void kv_tile(const u16* Qh, const u16* dOh, int qbyte
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        if constexpr (kDV) dv[dt] = mfma_32x32x16<DT>(vt_operand<D>(dos, w, 4 * dt + 2 * n + hh), pf[hh], dv[dt]);
-        if constexpr (kDK) dk[dt] = mfma_32x32x16<DT>(vt_operand<D>(qs, w, 4 * dt + 2 * n + hh), dsf[hh], dk[dt]);
+        dv[dt] = mfma_32x32x16<DT>(vt_operand<D>(dos, w, 4 * dt + 2 * n + hh), pf[hh], dv[dt]);
+        dk[dt] = mfma_32x32x16<DT>(vt_operand<D>(qs, w, 4 * dt + 2 * n + hh), dsf[hh], dk[dt]);
       }
   }
 }
 
 // VARLEN: packed sequences (the rows of head_rows); a workgroup past its
 // sequence's keys exits, keys of a sequence without queries get zeros.
-template <int DT, int D, bool CAUSAL, int GRADS, bool VARLEN>
+template <int DT, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(64 * kWavesKV, 1) void bwd_dkdv(const u16* __restrict__ Qg, const u16* __restrict__ Kg,
                                                              const u16* __restrict__ Vg, const u16* __restrict__ dOg,
                                                              const float* __restrict__ lse2g,
@@ -431,7 +424,7 @@ __global__ __launch_bounds__(64 * kWavesKV, 1) void bwd_dkdv(const u16* __restri
 
   u32x4 kf[D / 16], vf[D / 16];
   load_frag<D>(kf, Kg + hr.ko, nk, wk0, w);
-  if constexpr (GRADS & 1) load_frag<D>(vf, Vg + hr.ko, nk, wk0, w);
+  load_frag<D>(vf, Vg + hr.ko, nk, wk0, w);
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) dk[dt] = dv[dt] = f32x16{};
@@ -440,9 +433,9 @@ __global__ __launch_bounds__(64 * kWavesKV, 1) void bwd_dkdv(const u16* __restri
     issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, nq, t0, stage0, w);
     if constexpr (ST == 2) {
       for (int j = 0; j < nt; j += 2) {
-        kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j, nt, stage0, stage1, w, wk0, kf, vf, dk, dv, sl2);
+        kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j, nt, stage0, stage1, w, wk0, kf, vf, dk, dv, sl2);
         if (j + 1 < nt)
-          kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 1, nt, stage1, stage0, w, wk0, kf, vf, dk, dv,
+          kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 1, nt, stage1, stage0, w, wk0, kf, vf, dk, dv,
                                  sl2);
       }
     } else {
@@ -450,31 +443,31 @@ __global__ __launch_bounds__(64 * kWavesKV, 1) void bwd_dkdv(const u16* __restri
       if (nt > 2) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, nq, t0 + 2, stage2, w);
       wait_tile_and_barrier(nt > 2 ? kv_loads_per_tile<D>(w.wave) : 0);
       for (int j = 0; j < nt; j += 4) {
-        kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j, nt, stage0, stage3, w, wk0, kf, vf, dk, dv, sl2);
+        kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j, nt, stage0, stage3, w, wk0, kf, vf, dk, dv, sl2);
         if (j + 1 < nt)
-          kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 1, nt, stage1, stage0, w, wk0, kf, vf, dk, dv,
+          kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 1, nt, stage1, stage0, w, wk0, kf, vf, dk, dv,
                                  sl2);
         if (j + 2 < nt)
-          kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 2, nt, stage2, stage1, w, wk0, kf, vf, dk, dv,
+          kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 2, nt, stage2, stage1, w, wk0, kf, vf, dk, dv,
                                  sl2);
         if (j + 3 < nt)
-          kv_tile<DT, D, CAUSAL, GRADS>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 3, nt, stage3, stage2, w, wk0, kf, vf, dk, dv,
+          kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 3, nt, stage3, stage2, w, wk0, kf, vf, dk, dv,
                                  sl2);
       }
     }
   }
   const auto rk = make_rsrc_at(dKg + hr.ko, kb0 * ROWB, nk * ROWB);
   const auto rv = make_rsrc_at(dVg + hr.ko, kb0 * ROWB, nk * ROWB);
-  if constexpr (GRADS & 1) store_rows16<DT, D>(dk, scale, rk, (32 * w.wave + w.l32) * ROWB, w.hf);
-  if constexpr (GRADS & 2) store_rows16<DT, D>(dv, 1.0f, rv, (32 * w.wave + w.l32) * ROWB, w.hf);
+  store_rows16<DT, D>(dk, scale, rk, (32 * w.wave + w.l32) * ROWB, w.hf);
+  store_rows16<DT, D>(dv, 1.0f, rv, (32 * w.wave + w.l32) * ROWB, w.hf);
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV kernel at D = 128 with two waves per SIMD.
+// dK / dV kernel at D = 128 and 256 with two waves per SIMD.
 // ---------------------------------------------------------------------------
 // One workgroup per (batch*head, 128 keys), 8 waves.  Waves g and g + 4 share
-// a SIMD and key group g (32 keys) and split the work of each 64-row Q/dO
-// tile between them: wave g (the P wave) computes S = Q K^T, P and
+// a SIMD and key group g (32 keys) and split the work of each Q/dO tile
+// between them: wave g (the P wave) computes S = Q K^T, P and
 // dV^T += dO^T P; wave g + 4 (the dS wave) computes dP = dO V^T and, with
 // the P its sibling leaves in LDS, dS = P (dP - delta) and dK^T += Q^T dS.
 // Each wave then holds one fragment (K or V) and one fp32 gradient, which
@@ -483,25 +476,41 @@ __global__ __launch_bounds__(64 * kWavesKV, 1) void bwd_dkdv(const u16* __restri
 // the first (tile complete) opens the score phase, the second (P written)
 // the gradient phase.  Q/dO tiles stream through a 3-stage ring; each key
 // group's P travels in fp32, so dS is computed exactly as with one wave.
+// At D = 256 the K or V fragment (64 registers) and the fp32 gradient (128)
+// of 32 keys leave a wave few registers, so the tiles have 32 rows and the
+// operands are read only 2 MFMAs ahead (with 4 ahead the causal kernel
+// spilled inside its loop and ran 15% slower).
 constexpr int kWavesKV2 = 8;
 constexpr int kStagesKV2 = 3;
+// Query rows per Q/dO tile: 64 at D = 128; 32 at D = 256, where a stage of
+// 64 rows of two tensors (64 KB) leaves no room for three stages.
+template <int D>
+constexpr int kv2_rows() {
+  return D == 256 ? 32 : 64;
+}
+// Bytes of one stage: the Q tile, the dO tile, then lse2 and delta (256
+// bytes each, of which the tile's rows use the first 4 * rows).
+template <int D>
+constexpr int kv2_stage_bytes() {
+  return 2 * kv2_rows<D>() * D * 2 + 1024;
+}
 
 // Every wave loads the tile's lse2 and delta rows (the same 512 bytes; the
 // copies write identical values), so that all waves issue the same number of
 // loads per tile and every wait count is a compile-time constant.
 template <int D>
 constexpr int kv2_loads_per_tile() {
-  static_assert(64 * D * 2 / 1024 % kWavesKV2 == 0, "whole 1 KB pieces per wave");
-  return 2 * (64 * D * 2 / 1024 / kWavesKV2) + 2;
+  static_assert(kv2_rows<D>() * D * 2 / 1024 % kWavesKV2 == 0, "whole 1 KB pieces per wave");
+  return 2 * (kv2_rows<D>() * D * 2 / 1024 / kWavesKV2) + 2;
 }
 
 template <int D>
 __device__ __forceinline__ void issue_kv2_tile(const u16* Qh, const u16* dOh, int qbytes, const float* l2h,
                                                const float* dlh, int Nq, int t, unsigned char* dst, const Wave16& w) {
-  constexpr int TILEB = 64 * D * 2;
-  issue_tile16<D, kWavesKV2>(Qh, dOh, qbytes, t, dst, w);
-  const auto rl = make_rsrc_at(l2h, t * 256, Nq * 4);
-  const auto rd = make_rsrc_at(dlh, t * 256, Nq * 4);
+  constexpr int QR = kv2_rows<D>(), TILEB = QR * D * 2;
+  issue_tile16<D, kWavesKV2, QR>(Qh, dOh, qbytes, t, dst, w);
+  const auto rl = make_rsrc_at(l2h, t * QR * 4, Nq * 4);
+  const auto rd = make_rsrc_at(dlh, t * QR * 4, Nq * 4);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)(dst + 2 * TILEB), 4, w.lane * 4, 0, 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)(dst + 2 * TILEB + 256), 4, w.lane * 4, 0, 0, 0);
 }
@@ -517,15 +526,17 @@ __device__ __forceinline__ void lds_write_barrier() {
 }
 
 // Score MFMAs of the two-role kernel: x[n] = A(block n) frag^T over the tile
-// `as` (Q or dO rows), operands read PRE MFMAs ahead.
+// `as` (Q or dO rows; one 32-row block n per 32 rows), operands read PRE
+// MFMAs ahead.
 template <int DT, int D>
 __device__ __forceinline__ void kv2_scores(const unsigned char* as, const Wave16& w, const u32x4 (&frag)[D / 16],
-                                           f32x16 (&x)[2]) {
-  constexpr int NKK = D / 16, NS = 2 * NKK, PRE = 8;
+                                           f32x16 (&x)[kv2_rows<D>() / 32]) {
+  constexpr int NB = kv2_rows<D>() / 32, NKK = D / 16, NS = NB * NKK, PRE = D == 256 ? 2 : 8;
   u32x4 op[NS];
 #pragma unroll
   for (int i = 0; i < PRE; ++i) op[i] = ks_operand<D>(as, w, i);
-  x[0] = x[1] = f32x16{};
+#pragma unroll
+  for (int n = 0; n < NB; ++n) x[n] = f32x16{};
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
     if (i + PRE < NS) op[i + PRE] = ks_operand<D>(as, w, i + PRE);
@@ -535,33 +546,35 @@ __device__ __forceinline__ void kv2_scores(const unsigned char* as, const Wave16
 
 // Gradient MFMAs of the two-role kernel: acc[dt] += A^T pk over the tile `gs`
 // (dO rows for dV, Q rows for dK) read transposed; operand i is
-// dt = i / 4, block n = (i / 2) % 2, 16-row half hh = i % 2.
+// dt = i / KS and 16-row step g = i % KS (block g / 2, half g % 2), with KS
+// the tile's 16-row steps.
 template <int DT, int D>
-__device__ __forceinline__ void kv2_grads(const unsigned char* gs, const Wave16& w, const u32x4 (&pk)[2][2],
-                                          f32x16 (&acc)[D / 32]) {
-  constexpr int NG = 4 * (D / 32), PRE = 8;
+__device__ __forceinline__ void kv2_grads(const unsigned char* gs, const Wave16& w,
+                                          const u32x4 (&pk)[kv2_rows<D>() / 32][2], f32x16 (&acc)[D / 32]) {
+  constexpr int QR = kv2_rows<D>(), KS = QR / 16, NG = KS * (D / 32), PRE = D == 256 ? 2 : 8;
   u32x4 op[NG];
 #pragma unroll
-  for (int i = 0; i < PRE; ++i) op[i] = vt_operand<D>(gs, w, i);
+  for (int i = 0; i < PRE; ++i) op[i] = vt_operand<D, QR>(gs, w, i);
 #pragma unroll
   for (int i = 0; i < NG; ++i) {
-    if (i + PRE < NG) op[i + PRE] = vt_operand<D>(gs, w, i + PRE);
-    acc[i >> 2] = mfma_32x32x16<DT>(op[i], pk[(i >> 1) & 1][i & 1], acc[i >> 2]);
+    if (i + PRE < NG) op[i + PRE] = vt_operand<D, QR>(gs, w, i + PRE);
+    const int g = i % KS;  // 16-row step: block g / 2, half g % 2
+    acc[i / KS] = mfma_32x32x16<DT>(op[i], pk[g >> 1][g & 1], acc[i / KS]);
   }
 }
 
 // Tile j of the two-role kernel.  `frag` is the wave's K (P wave) or V (dS
 // wave) fragment, `acc` its dV^T or dK^T accumulator, `xp` the key group's
-// P exchange area (2048 floats: chunk c = 4n + g of lane l at
+// P exchange area (32 floats per tile row: chunk c = 4n + g of lane l at
 // xp[4 (64 c + l)], the values of rows 32n + 8g + 4hf + 0..3).
 template <int DT, int D, bool CAUSAL, bool PW>
 __device__ __forceinline__ void kv2_tile(const u16* Qh, const u16* dOh, int qbytes, const float* l2h,
                                          const float* dlh, int Nq, int t0, int j, int nt, const unsigned char* src,
                                          unsigned char* dst, float* xp, const Wave16& w, int wk0,
                                          const u32x4 (&frag)[D / 16], f32x16 (&acc)[D / 32], float sl2) {
-  constexpr int TILEB = 64 * D * 2;
+  constexpr int QR = kv2_rows<D>(), NB = QR / 32, TILEB = QR * D * 2;
   const int t = t0 + j;
-  const int q0 = 64 * t;
+  const int q0 = QR * t;
   const unsigned char* qs = src;
   const unsigned char* dos = src + TILEB;
   const unsigned char* st = src + 2 * TILEB;
@@ -572,20 +585,20 @@ __device__ __forceinline__ void kv2_tile(const u16* Qh, const u16* dOh, int qbyt
   issue_kv2_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t + kStagesKV2 - 1, dst, w);
   // No query of the tile sees the group's keys (causal): nothing to do, but
   // both barriers are still met.
-  const bool live = !(CAUSAL && q0 + 63 < wk0);
+  const bool live = !(CAUSAL && q0 + QR - 1 < wk0);
   // Queries of the tile below `qlim` (relative to q0) precede this lane's key.
   const int qlim = (CAUSAL && q0 < wk0 + 31) ? wk0 + w.l32 - q0 : 0;
   // Lane l holds key wk0 + l % 32 and queries q0 + 32n + 8g + 4hf + e (r = 4g + e).
-  f32x16 x[2];
-  u32x4 pk[2][2];  // P wave: P packed for dV; dS wave: dS packed for dK
+  f32x16 x[NB];
+  u32x4 pk[NB][2];  // P wave: P packed for dV; dS wave: dS packed for dK
   if (live) {
-    // Score phase: S = Q K^T (P wave) or dP = dO V^T (dS wave), both blocks.
+    // Score phase: S = Q K^T (P wave) or dP = dO V^T (dS wave), every block.
     kv2_scores<DT, D>(PW ? qs : dos, w, frag, x);
     if constexpr (PW) {
       // P = exp2(s scale log2 e - LSE log2 e), 0 where masked; fp32 to the
       // sibling, rounded to 16 bits for dV.
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
+      for (int n = 0; n < NB; ++n)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int qo = 32 * n + 8 * g + 4 * w.hf;
@@ -600,7 +613,7 @@ __device__ __forceinline__ void kv2_tile(const u16* Qh, const u16* dOh, int qbyt
           *(f32x4*)(xp + 4 * (64 * (4 * n + g) + w.lane)) = p4;
         }
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
+      for (int n = 0; n < NB; ++n)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -612,7 +625,7 @@ __device__ __forceinline__ void kv2_tile(const u16* Qh, const u16* dOh, int qbyt
     if constexpr (!PW) {
       // dS = P (dP - delta), rounded to 16 bits.
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
+      for (int n = 0; n < NB; ++n) {
         float ds[16];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -662,12 +675,12 @@ __global__ __launch_bounds__(64 * kWavesKV2, 1) void bwd_dkdv2(const u16* __rest
                                                                u16* __restrict__ dVg, int BH, int Nq, int Nk,
                                                                float sl2, float scale, const int* __restrict__ cuq,
                                                                const int* __restrict__ cuk, int H, int tq, int tk) {
-  constexpr int ROWB = D * 2, SB = kv_stage_bytes<D>(), BK = 128;
+  constexpr int ROWB = D * 2, SB = kv2_stage_bytes<D>(), BK = 128, QR = kv2_rows<D>();
   static_assert(kStagesKV2 == 3, "the loop below is unrolled for three stages");
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[SB];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[SB];
   __shared__ __attribute__((aligned(1024))) unsigned char stage2[SB];
-  __shared__ __attribute__((aligned(1024))) float xbuf[4 * 2048];
+  __shared__ __attribute__((aligned(1024))) float xbuf[4 * 32 * QR];
 
   Wave16 w;
   const int tid = threadIdx.x;
@@ -691,11 +704,11 @@ __global__ __launch_bounds__(64 * kWavesKV2, 1) void bwd_dkdv2(const u16* __rest
   const float* l2h = lse2g + hr.so;
   const float* dlh = deltag + hr.so;
   const int qbytes = nq * ROWB;
-  const int t0 = CAUSAL ? kb0 / 64 : 0;  // first query tile that sees a key of the block
-  const int nt = max((nq + 63) / 64 - t0, 0);
+  const int t0 = CAUSAL ? kb0 / QR : 0;  // first query tile that sees a key of the block
+  const int nt = max((nq + QR - 1) / QR - t0, 0);
   w.wq0 = w.wkend = w.wklim = w.klim = 0;  // forward-only fields
   init_operand_offsets<D>(w);
-  float* xp = xbuf + 2048 * grp;
+  float* xp = xbuf + 32 * QR * grp;
 
   u32x4 frag[D / 16];
   load_frag<D>(frag, (pwave ? Kg : Vg) + hr.ko, nk, wk0, w);
@@ -756,16 +769,13 @@ int launch_bwd(const FaBwdLaunch& a, float sl2, float scale) {
                            (const u16*)a.dout, (const float*)lse2, (const float*)delta, (u16*)a.dk, (u16*)a.dv,
                            (int)a.BH, (int)a.Nq, (int)a.Nk, sl2, scale, a.cu_q, a.cu_k, H, tq, tk);
     };
-    if constexpr (D == 256) {  // one kernel per gradient: dV, then dK
-      const int rc = run(bwd_dkdv<DT, D, CAUSAL, 2, VARLEN>);
-      return rc != 0 ? rc : run(bwd_dkdv<DT, D, CAUSAL, 1, VARLEN>);
-    } else if constexpr (D == 128) {
+    if constexpr (D >= 128) {
       return launch_kernel(bwd_dkdv2<DT, D, CAUSAL, VARLEN>, grid, dim3(64 * kWavesKV2), st, (const u16*)a.q,
                            (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, (const float*)lse2,
                            (const float*)delta, (u16*)a.dk, (u16*)a.dv, (int)a.BH, (int)a.Nq, (int)a.Nk, sl2, scale,
                            a.cu_q, a.cu_k, H, tq, tk);
     } else {
-      return run(bwd_dkdv<DT, D, CAUSAL, 3, VARLEN>);
+      return run(bwd_dkdv<DT, D, CAUSAL, VARLEN>);
     }
   }
   return 0;

@@ -134,20 +134,23 @@ def test_backward_edge_shapes(dt, Nq, Nk, causal):
     _compare(w, cpu, dout, grads, tag="edge")
 
 
-# D = 128 runs the two-wave-per-SIMD dK/dV kernel (a P wave and a dS wave per
-# 32-key group): shapes with fewer keys than one 128-key block, a partial
-# last key group, tiny and ragged query tails, both mask modes.
-EDGE128 = [(dt, Nq, Nk, c) for dt in ("bf16", "fp16")
-           for (Nq, Nk, c) in ((1, 1, True), (1, 33, False), (5, 200, True), (200, 5, True), (64, 64, False),
-                               (65, 129, True), (300, 161, False), (130, 97, True))]
+# D = 128 and 256 run the two-wave-per-SIMD dK/dV kernel (a P wave and a dS
+# wave per 32-key group): shapes with fewer keys than one 128-key block, a
+# partial last key group, tiny and ragged query tails, both mask modes.
+EDGE2 = [(dt, D, Nq, Nk, c) for dt in ("bf16", "fp16") for D in (128, 256)
+         for (Nq, Nk, c) in ((1, 1, True), (1, 33, False), (5, 200, True), (200, 5, True), (64, 64, False),
+                             (65, 129, True), (300, 161, False), (130, 97, True), (33, 300, True))]
 
 
-@pytest.mark.parametrize("dt,Nq,Nk,causal", EDGE128)
-def test_backward_edge_shapes_d128(dt, Nq, Nk, causal):
-    w = workloads.Workload(f"bwd_edge128_{dt}_{Nq}x{Nk}", 1, 3, Nq, Nk, 128, dt, causal, Nq * 5 + Nk)
+@pytest.mark.parametrize("dt,D,Nq,Nk,causal", EDGE2)
+def test_backward_edge_shapes_two_role(dt, D, Nq, Nk, causal):
+    # the two-role dK/dV kernel (D = 128: 64-row Q/dO tiles; D = 256: 32-row
+    # tiles): fewer keys than one 128-key block, a partial last key group,
+    # tiny and ragged query tails (33 rows: one row past a 32-row tile)
+    w = workloads.Workload(f"bwd_edge{D}_{dt}_{Nq}x{Nk}", 1, 3, Nq, Nk, D, dt, causal, Nq * 5 + Nk + D)
     log(f"case {w.name} causal={causal}")
     cpu, dout, grads = _run(w)
-    _compare(w, cpu, dout, grads, tag="edge128")
+    _compare(w, cpu, dout, grads, tag=f"edge{D}")
 
 
 @pytest.mark.parametrize("name", ["c1_fp32_causal_b2h4n128d64", "c2_fp32_b1h8n1024d64"])
