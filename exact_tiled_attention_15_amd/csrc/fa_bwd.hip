@@ -31,8 +31,8 @@
 //    wave per key group, serves D = 32 and 64).
 // S and dP are recomputed in both kernels: seven tile products instead of
 // the five a single kernel with atomic dQ updates would need.
-// At D = 256 bwd_dq has 4 waves (one per SIMD) and a 2-stage ring (a stage
-// of two 64-row tiles takes 64 KB), and bwd_dkdv2 streams 32-row Q/dO tiles.
+// At D = 256 the dQ kernel is bwd_dq_rs (score and dQ waves sharing each
+// SIMD, 32-key tiles) and bwd_dkdv2 streams 32-row Q/dO tiles.
 //
 // The library compiles this file twice.  Without FA_BWD_SMALL_D it defines
 // fa_launch_bwd and the D = 128 kernels; with FA_BWD_SMALL_D only the D = 32
@@ -52,21 +52,11 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634074f;
 constexpr int kWavesKV = 4;  // bwd_dkdv: waves per workgroup (32 keys each)
 
-// bwd_dq: waves per workgroup (32 query rows each).  Up to D = 128, 8 (two
-// per SIMD); at D = 256 the Q and dO fragments and the fp32 dQ of 32 rows take
-// more than half of a SIMD's registers, so 4 (one per SIMD).
-template <int D>
-constexpr int dq_waves() {
-  return D == 256 ? 4 : 8;
-}
-// Stages of the LDS rings of bwd_dq and bwd_dkdv: 4 up to D = 128 (three
-// tiles in flight); at D = 256 (bwd_dq) a stage (64 rows of two tensors)
-// takes 64 KB, so 2 (one tile in flight: each tile waits for itself, then
-// the next one starts).
-template <int D>
-constexpr int bwd_stages() {
-  return D == 256 ? 2 : 4;
-}
+// Waves per workgroup of bwd_dq (32 query rows each, two waves per SIMD) and
+// stages of the LDS rings of bwd_dq and bwd_dkdv (three tiles in flight).
+// D = 256 runs bwd_dq_rs and bwd_dkdv2 instead.
+constexpr int kWavesDQ = 8;
+constexpr int kStagesBwd = 4;
 
 template <int DT>
 __device__ __forceinline__ float lo16(unsigned x) {
@@ -143,13 +133,14 @@ __device__ __forceinline__ void dq_tile(const u16* Kh, const u16* Vh, int kbytes
                                         const unsigned char* src, unsigned char* dst, const Wave16& w,
                                         const u32x4 (&qf)[D / 16], const u32x4 (&dof)[D / 16],
                                         f32x16 (&acc)[D / 32], float lse2, float delta, float sl2) {
-  constexpr int BC = 64, TILEB = BC * D * 2, NKK = D / 16, NDT = D / 32, NW = dq_waves<D>(), ST = bwd_stages<D>();
+  constexpr int BC = 64, TILEB = BC * D * 2, NKK = D / 16, NDT = D / 32, NW = kWavesDQ, ST = kStagesBwd;
   const int k0 = j * BC;
   const unsigned char* ks = src;
   const unsigned char* vs = src + TILEB;
-  // 4 stages: tile j is complete since the previous barrier; wait for tile
-  // j+1.  2 stages: wait for tile j itself.  Then refill the stage of tile j-1.
-  wait_tile_and_barrier(ST == 4 && j + 2 < nt ? loads_per_tile<D, NW>(w.wave) : 0);
+  // Tile j is complete since the previous barrier; wait for tile j+1, then
+  // refill the stage of tile j-1.
+  static_assert(D <= 128 && ST == 4, "D = 256 runs bwd_dq_rs");
+  wait_tile_and_barrier(j + 2 < nt ? loads_per_tile<D, NW>(w.wave) : 0);
   if (j + ST - 1 < nt) issue_tile16<D, NW>(Kh, Vh, kbytes, j + ST - 1, dst, w);
   if (k0 >= w.wkend) return;
   const bool need_mask = k0 + BC - 1 > w.wklim;  // causal diagonal or past Nk
@@ -214,18 +205,18 @@ __device__ __forceinline__ void dq_tile(const u16* Kh, const u16* Vh, int kbytes
 // VARLEN: packed sequences (the rows of head_rows); a workgroup past its
 // sequence's queries exits, a sequence without keys gets dQ = 0.
 template <int DT, int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(64 * dq_waves<D>(), 1) void bwd_dq(const u16* __restrict__ Qg, const u16* __restrict__ Kg,
+__global__ __launch_bounds__(64 * kWavesDQ, 1) void bwd_dq(const u16* __restrict__ Qg, const u16* __restrict__ Kg,
                                                           const u16* __restrict__ Vg, const u16* __restrict__ dOg,
                                                           const float* __restrict__ lse2g,
                                                           const float* __restrict__ deltag, u16* __restrict__ dQg,
                                                           int BH, int Nq, int Nk, int nqt, float sl2, float scale,
                                                           const int* __restrict__ cuq, const int* __restrict__ cuk,
                                                           int H, int tq, int tk) {
-  constexpr int BC = 64, ROWB = D * 2, TILEB = BC * ROWB, NW = dq_waves<D>(), BR = 32 * NW, ST = bwd_stages<D>();
+  constexpr int BC = 64, ROWB = D * 2, TILEB = BC * ROWB, NW = kWavesDQ, BR = 32 * NW;
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * TILEB];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage2[ST == 4 ? 2 * TILEB : 1024];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage3[ST == 4 ? 2 * TILEB : 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage2[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage3[2 * TILEB];
 
   Wave16 w;
   const int tid = threadIdx.x;
@@ -264,29 +255,234 @@ __global__ __launch_bounds__(64 * dq_waves<D>(), 1) void bwd_dq(const u16* __res
   f32x16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
-  if constexpr (ST == 4) {
-    if (nt > 1) issue_tile16<D, NW>(Kh, Vh, kbytes, 1, stage1, w);
-    if (nt > 2) issue_tile16<D, NW>(Kh, Vh, kbytes, 2, stage2, w);
-    // Tile 0 complete before the first tile's reads.
-    wait_tile_and_barrier(nt > 2 ? loads_per_tile<D, NW>(w.wave) : 0);
-    for (int j = 0; j < nt; j += 4) {
-      dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j, nt, stage0, stage3, w, qf, dof, acc, lse2, delta, sl2);
-      if (j + 1 < nt)
-        dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 1, nt, stage1, stage0, w, qf, dof, acc, lse2, delta, sl2);
-      if (j + 2 < nt)
-        dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 2, nt, stage2, stage1, w, qf, dof, acc, lse2, delta, sl2);
-      if (j + 3 < nt)
-        dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 3, nt, stage3, stage2, w, qf, dof, acc, lse2, delta, sl2);
-    }
-  } else {
-    for (int j = 0; j < nt; j += 2) {
-      dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j, nt, stage0, stage1, w, qf, dof, acc, lse2, delta, sl2);
-      if (j + 1 < nt)
-        dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 1, nt, stage1, stage0, w, qf, dof, acc, lse2, delta, sl2);
-    }
+  if (nt > 1) issue_tile16<D, NW>(Kh, Vh, kbytes, 1, stage1, w);
+  if (nt > 2) issue_tile16<D, NW>(Kh, Vh, kbytes, 2, stage2, w);
+  // Tile 0 complete before the first tile's reads.
+  wait_tile_and_barrier(nt > 2 ? loads_per_tile<D, NW>(w.wave) : 0);
+  for (int j = 0; j < nt; j += 4) {
+    dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j, nt, stage0, stage3, w, qf, dof, acc, lse2, delta, sl2);
+    if (j + 1 < nt)
+      dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 1, nt, stage1, stage0, w, qf, dof, acc, lse2, delta, sl2);
+    if (j + 2 < nt)
+      dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 2, nt, stage2, stage1, w, qf, dof, acc, lse2, delta, sl2);
+    if (j + 3 < nt)
+      dq_tile<DT, D, CAUSAL>(Kh, Vh, kbytes, j + 3, nt, stage3, stage2, w, qf, dof, acc, lse2, delta, sl2);
   }
   const auto rq = make_rsrc_at(dQg + hr.qo, q0 * ROWB, nq * ROWB);
   store_rows16<DT, D>(acc, scale, rq, (32 * w.wave + w.l32) * ROWB, w.hf);
+}
+
+// ---------------------------------------------------------------------------
+// dQ kernel at D = 256 with two waves per SIMD.
+// ---------------------------------------------------------------------------
+// One workgroup per (batch*head, 128 query rows), 8 waves.  Waves g and g + 4
+// share a SIMD and the 32 rows of group g: wave g (the score wave) holds the
+// rows' Q and dO fragments and, per 32-key tile, computes S^T = K Q^T,
+// dP^T = V dO^T, P and dS = P (dP - delta), and leaves dS (rounded to 16
+// bits) in LDS; wave g + 4 (the dQ wave) holds the rows' fp32 dQ and one
+// tile later adds K^T dS^T, its K^T operands read from the same K tile.  One
+// wave holding both fragments and dQ (64 + 64 + 128 registers) would fill a
+// SIMD alone; split, two waves share each SIMD.  K and V
+// tiles stream through two 4-stage rings (a K tile is read in its own
+// period and in the next); in period p every wave meets the others once (K
+// and V tile p are then complete), starts the loads of K and V tile p+2, and
+// the score waves handle tile p while the dQ waves handle tile p-1.
+namespace dqrs {
+constexpr int D = 256, BC = 32, ROWB = D * 2, TILEB = BC * ROWB, NKK = D / 16, NDT = D / 32;
+constexpr int kLoads = 2 * (TILEB / 1024 / 8);  // direct-to-LDS loads per wave and period
+constexpr int XG = 2 * 64;                      // u32x4 of dS per group and buffer
+}  // namespace dqrs
+
+// One 1 KB direct-to-LDS load: 16 bytes a lane from byte `go` of `r`.
+__device__ __forceinline__ void dqrs_piece(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int go) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, go, 0, 0, 0);
+}
+
+// This wave's two 1 KB pieces of 32-row tile t of one [N, 256] tensor.
+__device__ __forceinline__ void dqrs_issue(const u16* Xh, int kbytes, int t, unsigned char* dst, const Wave16& w) {
+  const auto r = make_rsrc_at(Xh, t * dqrs::TILEB, kbytes);
+#pragma unroll
+  for (int I = 0; I < dqrs::TILEB / 1024 / 8; ++I) {
+    const int G = w.wave + 8 * I;
+    dqrs_piece(r, dst + G * 1024, dma_src_off<dqrs::D>(G, w.lane));
+  }
+}
+
+// Score wave, tile j (K stage ks, V stage vs): S and dP (MFMAs interleaved,
+// operands read 4 ahead), P = exp2(s scale log2 e - LSE log2 e) (masked keys
+// 0), dS = P (dP - delta), packed to 16 bits into xo.
+template <int DT>
+__device__ __forceinline__ void dqrs_score(int j, const unsigned char* ks, const unsigned char* vs, u32x4* xo,
+                                           const Wave16& w, const u32x4 (&qf)[dqrs::NKK],
+                                           const u32x4 (&dof)[dqrs::NKK], float lse2, float delta, float sl2) {
+  using namespace dqrs;
+  const int k0 = j * BC;
+  if (k0 >= w.wkend) return;
+  constexpr int NS = 2 * NKK, PRE = 4;
+  f32x16 s = {}, dp = {};
+  u32x4 op[NS];
+#pragma unroll
+  for (int i = 0; i < PRE; ++i) op[i] = (i & 1) ? ks_operand<D>(vs, w, i >> 1) : ks_operand<D>(ks, w, i >> 1);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int ip = i + PRE;
+    if (ip < NS) op[ip] = (ip & 1) ? ks_operand<D>(vs, w, ip >> 1) : ks_operand<D>(ks, w, ip >> 1);
+    if (i & 1)
+      dp = mfma_32x32x16<DT>(op[i], dof[i >> 1], dp);
+    else
+      s = mfma_32x32x16<DT>(op[i], qf[i >> 1], s);
+  }
+  const bool need_mask = k0 + BC - 1 > w.wklim;  // causal diagonal or past Nk
+  const int lim = w.klim - (k0 + 4 * w.hf);
+  float ds[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -lse2));
+    if (need_mask && 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
+    ds[r] = p * (dp[r] - delta);
+  }
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    u32x4 d;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = pack2<DT>(ds[8 * hh + 2 * i], ds[8 * hh + 2 * i + 1]);
+    xo[64 * hh + w.lane] = d;
+  }
+}
+
+// dQ wave, tile jj (K stage ks): dQ^T += K^T dS^T with the dS from xi
+// (16-key step major, so consecutive MFMAs use different accumulators).
+template <int DT>
+__device__ __forceinline__ void dqrs_acc(int jj, const unsigned char* ks, const u32x4* xi, const Wave16& w,
+                                         f32x16 (&acc)[dqrs::NDT]) {
+  using namespace dqrs;
+  if (jj * BC >= w.wkend) return;
+  constexpr int NG = 2 * NDT, PRE = 4;
+  u32x4 op[NG];
+#pragma unroll
+  for (int i = 0; i < PRE; ++i) op[i] = vt_operand<D, BC>(ks, w, (i % NDT) * 2 + i / NDT);
+  const u32x4 d0 = xi[w.lane], d1 = xi[64 + w.lane];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const int ip = i + PRE;
+    if (ip < NG) op[ip] = vt_operand<D, BC>(ks, w, (ip % NDT) * 2 + ip / NDT);
+    acc[i % NDT] = mfma_32x32x16<DT>(op[i], i < NDT ? d0 : d1, acc[i % NDT]);
+  }
+}
+
+// Period p of one role (P4 = p mod 4: stages p mod 4, buffers p mod 2).
+template <int DT, bool SCORE, int P4>
+__device__ __forceinline__ void dqrs_period(int p, int nt, const u16* Kh, const u16* Vh, int kbytes,
+                                            unsigned char* const (&kr)[4], unsigned char* const (&vr)[4],
+                                            u32x4* const (&xb)[2], const Wave16& w, const u32x4 (&qf)[dqrs::NKK],
+                                            const u32x4 (&dof)[dqrs::NKK], f32x16 (&acc)[dqrs::NDT], float lse2,
+                                            float delta, float sl2) {
+  wait_tile_and_barrier(dqrs::kLoads);
+  dqrs_issue(Kh, kbytes, p + 2, kr[(P4 + 2) % 4], w);
+  dqrs_issue(Vh, kbytes, p + 2, vr[(P4 + 2) % 4], w);
+  if constexpr (SCORE) {
+    if (p < nt) dqrs_score<DT>(p, kr[P4], vr[P4], xb[P4 % 2], w, qf, dof, lse2, delta, sl2);
+  } else {
+    if (p >= 1) dqrs_acc<DT>(p - 1, kr[(P4 + 3) % 4], xb[(P4 + 1) % 2], w, acc);
+  }
+}
+
+template <int DT, bool SCORE>
+__device__ __forceinline__ void dqrs_loop(int nt, const u16* Kh, const u16* Vh, int kbytes,
+                                          unsigned char* const (&kr)[4], unsigned char* const (&vr)[4],
+                                          u32x4* const (&xb)[2], const Wave16& w, const u32x4 (&qf)[dqrs::NKK],
+                                          const u32x4 (&dof)[dqrs::NKK], f32x16 (&acc)[dqrs::NDT], float lse2,
+                                          float delta, float sl2) {
+  // K and V tiles 0 and 1; each period then starts both tensors' tile p+2.
+  // Loads run past the last tile (reading zeros into stages nobody reads),
+  // so that every period waits for the same count.
+  dqrs_issue(Kh, kbytes, 0, kr[0], w);
+  dqrs_issue(Vh, kbytes, 0, vr[0], w);
+  dqrs_issue(Kh, kbytes, 1, kr[1], w);
+  dqrs_issue(Vh, kbytes, 1, vr[1], w);
+#define DQRS_PERIOD(P4) \
+  dqrs_period<DT, SCORE, P4>(p + P4, nt, Kh, Vh, kbytes, kr, vr, xb, w, qf, dof, acc, lse2, delta, sl2)
+  for (int p = 0; p <= nt; p += 4) {
+    DQRS_PERIOD(0);
+    if (p + 1 <= nt) DQRS_PERIOD(1);
+    if (p + 2 <= nt) DQRS_PERIOD(2);
+    if (p + 3 <= nt) DQRS_PERIOD(3);
+  }
+#undef DQRS_PERIOD
+  // The loads past the last tile complete before the workgroup's LDS is
+  // released.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); lgkmcnt, expcnt: no wait
+}
+
+template <int DT, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(512, 1) void bwd_dq_rs(const u16* __restrict__ Qg, const u16* __restrict__ Kg,
+                                                    const u16* __restrict__ Vg, const u16* __restrict__ dOg,
+                                                    const float* __restrict__ lse2g,
+                                                    const float* __restrict__ deltag, u16* __restrict__ dQg,
+                                                    int BH, int Nq, int Nk, int nqt, float sl2, float scale,
+                                                    const int* __restrict__ cuq, const int* __restrict__ cuk,
+                                                    int H, int tq, int tk) {
+  using namespace dqrs;
+  constexpr int BR = 128;
+  // Ring stages of 16 KB aligned to their size: none straddles a 64 KB
+  // boundary, and as the most aligned arrays they come first (0-128 KB).
+  __shared__ __attribute__((aligned(16384))) unsigned char k0s[TILEB];
+  __shared__ __attribute__((aligned(16384))) unsigned char k1s[TILEB];
+  __shared__ __attribute__((aligned(16384))) unsigned char k2s[TILEB];
+  __shared__ __attribute__((aligned(16384))) unsigned char k3s[TILEB];
+  __shared__ __attribute__((aligned(16384))) unsigned char v0s[TILEB];
+  __shared__ __attribute__((aligned(16384))) unsigned char v1s[TILEB];
+  __shared__ __attribute__((aligned(16384))) unsigned char v2s[TILEB];
+  __shared__ __attribute__((aligned(16384))) unsigned char v3s[TILEB];
+  __shared__ u32x4 x0[4 * XG];
+  __shared__ u32x4 x1[4 * XG];
+
+  Wave16 w;
+  const int tid = threadIdx.x;
+  w.lane = tid & 63;
+  w.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  w.hf = w.lane >> 5;
+  w.l32 = w.lane & 31;
+  int bh, qt;
+  tile_of_block(nqt, BH, bh, qt);
+  const int q0 = qt * BR;
+  const HeadRows hr = head_rows<VARLEN>(bh, Nq, Nk, D, cuq, cuk, H, tq, tk);
+  const int nq = hr.nq, nk = hr.nk;
+  if (q0 >= nq) return;  // past this sequence's queries: the whole workgroup
+  const u16* Kh = Kg + hr.ko;
+  const u16* Vh = Vg + hr.ko;
+  const int kbytes = nk * ROWB;
+  const int kend = CAUSAL ? min(nk, min(q0 + BR, nq)) : nk;
+  const int nt = (kend + BC - 1) / BC;
+  const int grp = w.wave & 3;
+  const bool score = w.wave < 4;
+  w.wq0 = q0 + 32 * grp;
+  const int myq = w.wq0 + w.l32;
+  w.wkend = CAUSAL ? min(kend, w.wq0 + 32) : kend;
+  w.klim = CAUSAL ? min(myq, nk - 1) : nk - 1;
+  w.wklim = CAUSAL ? min(w.wq0, nk - 1) : nk - 1;
+  init_operand_offsets<D>(w);
+
+  unsigned char* const kr[4] = {k0s, k1s, k2s, k3s};
+  unsigned char* const vr[4] = {v0s, v1s, v2s, v3s};
+  u32x4* const xb[2] = {x0 + XG * grp, x1 + XG * grp};
+  u32x4 qf[NKK], dof[NKK];
+  f32x16 acc[NDT];
+  if (score) {
+    load_frag<D>(qf, Qg + hr.qo, nq, w.wq0, w);
+    load_frag<D>(dof, dOg + hr.qo, nq, w.wq0, w);
+    const auto rs = make_rsrc(lse2g + hr.so, nq * 4);
+    const auto rd = make_rsrc(deltag + hr.so, nq * 4);
+    const float lse2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, myq * 4, 0, 0));
+    const float delta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, myq * 4, 0, 0));
+    dqrs_loop<DT, true>(nt, Kh, Vh, kbytes, kr, vr, xb, w, qf, dof, acc, lse2, delta, sl2);
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
+    dqrs_loop<DT, false>(nt, Kh, Vh, kbytes, kr, vr, xb, w, qf, dof, acc, 0.f, 0.f, sl2);
+    const auto rq = make_rsrc_at(dQg + hr.qo, q0 * ROWB, nq * ROWB);
+    store_rows16<DT, D>(acc, scale, rq, (32 * grp + w.l32) * ROWB, w.hf);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -326,17 +522,17 @@ __device__ __forceinline__ void kv_tile(const u16* Qh, const u16* dOh, int qbyte
                                         unsigned char* dst, const Wave16& w, int wk0, const u32x4 (&kf)[D / 16],
                                         const u32x4 (&vf)[D / 16], f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32],
                                         float sl2) {
-  constexpr int TILEB = 64 * D * 2, NKK = D / 16, NDT = D / 32, ST = bwd_stages<D>();
+  constexpr int TILEB = 64 * D * 2, NKK = D / 16, NDT = D / 32, ST = kStagesBwd;
+  static_assert(D <= 64 && ST == 4, "D = 128 and 256 run bwd_dkdv2");
   const int t = t0 + j;
   const int q0 = 64 * t;
   const unsigned char* qs = src;
   const unsigned char* dos = src + TILEB;
   const unsigned char* st = src + 2 * TILEB;
-  // As in dq_tile: 4 stages wait for tile j+1, 2 stages for tile j.
-  wait_tile_and_barrier(ST == 4 && j + 2 < nt ? kv_loads_per_tile<D>(w.wave) : 0);
+  // As in dq_tile: wait for tile j+1.
+  wait_tile_and_barrier(j + 2 < nt ? kv_loads_per_tile<D>(w.wave) : 0);
   if (j + ST - 1 < nt) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t + ST - 1, dst, w);
   if (CAUSAL && q0 + 63 < wk0) return;  // every query of the tile precedes the wave's keys
-  static_assert(D <= 64, "D = 128 and 256 run bwd_dkdv2");
   const bool need_mask = CAUSAL && q0 < wk0 + 31;
   const int mykey = wk0 + w.l32;
 #pragma unroll
@@ -391,11 +587,11 @@ __global__ __launch_bounds__(64 * kWavesKV, 1) void bwd_dkdv(const u16* __restri
                                                              u16* __restrict__ dVg, int BH, int Nq, int Nk,
                                                              float sl2, float scale, const int* __restrict__ cuq,
                                                              const int* __restrict__ cuk, int H, int tq, int tk) {
-  constexpr int ROWB = D * 2, SB = kv_stage_bytes<D>(), BK = 32 * kWavesKV, ST = bwd_stages<D>();
+  constexpr int ROWB = D * 2, SB = kv_stage_bytes<D>(), BK = 32 * kWavesKV;
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[SB];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[SB];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage2[ST == 4 ? SB : 1024];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage3[ST == 4 ? SB : 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage2[SB];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage3[SB];
 
   Wave16 w;
   const int tid = threadIdx.x;
@@ -431,29 +627,20 @@ __global__ __launch_bounds__(64 * kWavesKV, 1) void bwd_dkdv(const u16* __restri
 
   if (nt > 0) {
     issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, nq, t0, stage0, w);
-    if constexpr (ST == 2) {
-      for (int j = 0; j < nt; j += 2) {
-        kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j, nt, stage0, stage1, w, wk0, kf, vf, dk, dv, sl2);
-        if (j + 1 < nt)
-          kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 1, nt, stage1, stage0, w, wk0, kf, vf, dk, dv,
-                                 sl2);
-      }
-    } else {
-      if (nt > 1) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, nq, t0 + 1, stage1, w);
-      if (nt > 2) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, nq, t0 + 2, stage2, w);
-      wait_tile_and_barrier(nt > 2 ? kv_loads_per_tile<D>(w.wave) : 0);
-      for (int j = 0; j < nt; j += 4) {
-        kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j, nt, stage0, stage3, w, wk0, kf, vf, dk, dv, sl2);
-        if (j + 1 < nt)
-          kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 1, nt, stage1, stage0, w, wk0, kf, vf, dk, dv,
-                                 sl2);
-        if (j + 2 < nt)
-          kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 2, nt, stage2, stage1, w, wk0, kf, vf, dk, dv,
-                                 sl2);
-        if (j + 3 < nt)
-          kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 3, nt, stage3, stage2, w, wk0, kf, vf, dk, dv,
-                                 sl2);
-      }
+    if (nt > 1) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, nq, t0 + 1, stage1, w);
+    if (nt > 2) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, nq, t0 + 2, stage2, w);
+    wait_tile_and_barrier(nt > 2 ? kv_loads_per_tile<D>(w.wave) : 0);
+    for (int j = 0; j < nt; j += 4) {
+      kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j, nt, stage0, stage3, w, wk0, kf, vf, dk, dv, sl2);
+      if (j + 1 < nt)
+        kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 1, nt, stage1, stage0, w, wk0, kf, vf, dk, dv,
+                               sl2);
+      if (j + 2 < nt)
+        kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 2, nt, stage2, stage1, w, wk0, kf, vf, dk, dv,
+                               sl2);
+      if (j + 3 < nt)
+        kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 3, nt, stage3, stage2, w, wk0, kf, vf, dk, dv,
+                               sl2);
     }
   }
   const auto rk = make_rsrc_at(dKg + hr.ko, kb0 * ROWB, nk * ROWB);
@@ -752,13 +939,22 @@ int launch_bwd(const FaBwdLaunch& a, float sl2, float scale) {
     int rc = launch_kernel(bwd_prep<DT, D>, grid, block, st, (const u16*)a.o, (const u16*)a.dout, a.lse, lse2,
                            delta, rows);
     if (rc != 0) return rc;
-    constexpr int NWQ = dq_waves<D>();
-    const int nqt = (int)((a.Nq + 32 * NWQ - 1) / (32 * NWQ));
-    if (nqt > 0)
-      rc = launch_kernel(bwd_dq<DT, D, CAUSAL, VARLEN>, dim3((unsigned)(a.BH * nqt)), dim3(64 * NWQ), st,
-                         (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, (const float*)lse2,
-                         (const float*)delta, (u16*)a.dq, (int)a.BH, (int)a.Nq, (int)a.Nk, nqt, sl2, scale, a.cu_q,
-                         a.cu_k, H, tq, tk);
+    if constexpr (D == 256) {
+      const int nqt = (int)((a.Nq + 127) / 128);
+      if (nqt > 0)
+        rc = launch_kernel(bwd_dq_rs<DT, CAUSAL, VARLEN>, dim3((unsigned)(a.BH * nqt)), dim3(512), st,
+                           (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, (const float*)lse2,
+                           (const float*)delta, (u16*)a.dq, (int)a.BH, (int)a.Nq, (int)a.Nk, nqt, sl2, scale,
+                           a.cu_q, a.cu_k, H, tq, tk);
+    } else {
+      constexpr int NWQ = kWavesDQ;
+      const int nqt = (int)((a.Nq + 32 * NWQ - 1) / (32 * NWQ));
+      if (nqt > 0)
+        rc = launch_kernel(bwd_dq<DT, D, CAUSAL, VARLEN>, dim3((unsigned)(a.BH * nqt)), dim3(64 * NWQ), st,
+                           (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, (const float*)lse2,
+                           (const float*)delta, (u16*)a.dq, (int)a.BH, (int)a.Nq, (int)a.Nk, nqt, sl2, scale,
+                           a.cu_q, a.cu_k, H, tq, tk);
+    }
     if (rc != 0) return rc;
   }
   const int nkt = (int)((a.Nk + 32 * kWavesKV - 1) / (32 * kWavesKV));
