@@ -12,9 +12,9 @@
 // Work decomposition: one workgroup per (batch*head, Q tile); each wave owns
 // 32 query rows.  16-bit kernel: 8 waves (256 rows), K/V tiles of 64 keys
 // loaded straight from HBM into a 4-stage LDS ring (one barrier per tile).
-// At D = 256, and on grids with fewer 256-row workgroups than CUs
-// (fa_fwd_rs): 8 waves over 128 rows, two per 32-row group, one running the
-// scores and softmax, the other O += P V.
+// Role-split kernel (fa_fwd_rs: D = 256, D = 128, and small grids at D = 64):
+// two waves per 32-row group, one running the scores and softmax, the other
+// O += P V; 16 waves over 256 rows at D = 128, 8 over 128 rows otherwise.
 // fp32 kernel: 4 waves (128 rows), K/V staged through registers into a
 // double-buffered LDS stage; on grids with at most one such workgroup per CU,
 // 32-row workgroups whose waves split each 128-key tile and merge at the end.
@@ -586,35 +586,55 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && NW == 8) ? 4 : 1) void fa_fwd_
 }
 
 // ---------------------------------------------------------------------------
-// Role-split 16-bit kernel (D = 256; small grids at D = 64 and 128).
+// Role-split 16-bit kernel: D = 256, full grids at D = 128, small grids at
+// D = 64 and 128.
 // ---------------------------------------------------------------------------
-// One workgroup of 8 waves per (batch*head, 128 query rows, key range).
-// Waves g and g + 4 share a SIMD and the 32 rows of group g.  Wave g, the
+// One workgroup of 2 NG waves per (batch*head, 32 NG query rows, key range).
+// Waves g and g + NG share a SIMD and the 32 rows of group g.  Wave g, the
 // score wave, holds the rows' Q fragment and runs S^T = K Q^T, the mask and
 // the online-softmax update of each key tile, and leaves P (rounded to 16
-// bits) in LDS; wave g + 4, the PV wave, holds the rows' fp32 O and one tile
-// later rescales it (when the score wave moved the reference) and adds
-// V^T P^T.  A wave holding both the Q fragment and O of 32 rows at D = 256
-// needs more than half of a SIMD's registers (one wave per SIMD, nothing to
-// run while a wave computes its exponentials); split, each role fits two
-// waves per SIMD, and one wave's softmax runs beside its sibling's MFMAs.
-// The same holds for the grids too small to give the 256-row kernel a
-// workgroup per CU.  K and V tiles stream through two 3-stage rings; in
-// period p every wave meets the others once (K tile p and V tile p-1 are
-// then complete), starts the loads of V tile p+1 and K tile p+2, and the
-// score waves handle tile p while the PV waves handle tile p-1.  P, a flag
-// for a moved reference and the rescale factors travel through
-// double-buffered LDS areas.
-template <int D>
+// bits) in LDS; wave g + NG, the PV wave, holds the rows' fp32 O and one tile
+// later rescales it (by the factor the score wave leaves, 1 when the
+// reference did not move) and adds V^T P^T.  No wave holds both a Q fragment
+// and an O accumulator, and one wave's softmax runs beside another's MFMAs.
+//  * NG = 4 (8 waves, 128 rows): D = 256, where a wave holding both would
+//    need more than half of a SIMD's registers, and grids too small to give
+//    the 256-row kernel a workgroup per CU.  K and V tiles stream through
+//    two 3-stage rings; in period p every wave meets the others once (K tile
+//    p and V tile p-1 are then complete), starts the loads of V tile p+1 and
+//    K tile p+2, and the score waves handle tile p while the PV waves handle
+//    tile p-1.
+//  * NG = 8 (16 waves, 256 rows, four waves per SIMD in 128 registers each):
+//    D = 128 on full grids.  The LDS then holds a 3-stage K ring and a
+//    2-stage V ring: V tile p is loaded in period p and read in period p+1.
+// P and the rescale factors travel through double-buffered LDS areas.
+template <int D, int NG>
 struct RsShape {
   static constexpr int BC = D == 256 ? 32 : 64;  // keys per tile
   static constexpr int ROWB = D * 2, TILEB = BC * ROWB, NKK = D / 16, NDT = D / 32;
-  static constexpr int NB = BC / 32, KS = BC / 16;       // 32-key blocks, 16-key PV steps
-  static constexpr int NPIECE = TILEB / 1024 / 8;        // 1 KB loads per wave and tile
-  static constexpr int kLoads = 2 * NPIECE;              // loads per wave and period
-  static constexpr int XG = KS * 64;                     // u32x4 of P per group and buffer
-  static_assert(TILEB % 8192 == 0, "whole 1 KB pieces for each of the 8 waves");
+  static constexpr int NB = BC / 32, KS = BC / 16;  // 32-key blocks, 16-key PV steps
+  static constexpr int NW = 2 * NG;                 // waves
+  static constexpr int NPIECE = TILEB / 1024 / NW;  // 1 KB loads per wave and tile
+  static constexpr int VST = NG == 8 ? 2 : 3;       // V ring stages
+  // Loads a wave may leave in flight at a period's barrier: the previous
+  // period's V and K tiles (VST = 3) or its K tile (VST = 2, whose V tile is
+  // read in the period that follows).
+  static constexpr int kWait = VST == 3 ? 2 * NPIECE : NPIECE;
+  static constexpr int XG = KS * 64;         // u32x4 of P per group and buffer
+  static constexpr int PRE = NG == 8 ? 2 : 8;  // operand read-ahead (MFMAs)
+  static_assert(NPIECE >= 1 && TILEB % (1024 * NW) == 0, "whole 1 KB pieces for every wave");
+  static_assert(kWait < 16, "vmcnt field");
 };
+
+// Meet the other waves once at most N of this wave's direct-to-LDS loads
+// remain in flight (loads complete in order) and its LDS operations are done.
+template <int N>
+__device__ __forceinline__ void rs_wait_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0070 | N);  // vmcnt(N), expcnt: no wait, lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // One 1 KB direct-to-LDS load: 16 bytes a lane from byte `go` of `r`.
 __device__ __forceinline__ void rs_piece(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int go) {
@@ -622,27 +642,25 @@ __device__ __forceinline__ void rs_piece(__amdgpu_buffer_rsrc_t r, unsigned char
 }
 
 // This wave's 1 KB pieces of tile t of one [N, D] tensor.
-template <int D>
+template <int D, int NG>
 __device__ __forceinline__ void rs_issue(const u16* Xh, int kbytes, int t, unsigned char* dst, const Wave16& w) {
-  using S = RsShape<D>;
+  using S = RsShape<D, NG>;
   const auto r = make_rsrc_at(Xh, t * S::TILEB, kbytes);
 #pragma unroll
   for (int I = 0; I < S::NPIECE; ++I) {
-    const int G = w.wave + 8 * I;
+    const int G = w.wave + S::NW * I;
     rs_piece(r, dst + G * 1024, dma_src_off<D>(G, w.lane));
   }
 }
 
 // Score wave, tile j (K stage ks): S^T, mask, online softmax with the sum
 // rule (the reference moves only when a lane's sum of its P exceeds 2^15,
-// and on the first tile), then P to xo, the move flag to *fl and, when it
-// moved, the factor to fo.
-template <int DT, int D>
-__device__ __forceinline__ void rs_score(int j, const unsigned char* ks, u32x4* xo, float* fo, int* fl,
-                                         const Wave16& w, const u32x4 (&qf)[D / 16], float& mref, float& l,
-                                         float& lr, float sl2) {
-  using S = RsShape<D>;
-  constexpr int NB = S::NB, NKK = S::NKK, BC = S::BC, NQK = NB * NKK, PRE = NQK < 8 ? NQK : 8;
+// and on the first tile), then P to xo and O's rescale factor to fo.
+template <int DT, int D, int NG>
+__device__ __forceinline__ void rs_score(int j, const unsigned char* ks, u32x4* xo, float* fo, const Wave16& w,
+                                         const u32x4 (&qf)[D / 16], float& mref, float& l, float& lr, float sl2) {
+  using S = RsShape<D, NG>;
+  constexpr int NB = S::NB, NKK = S::NKK, BC = S::BC, NQK = NB * NKK, PRE = NQK < S::PRE ? NQK : S::PRE;
   const int k0 = j * BC;
   if (k0 >= w.wkend) return;
   f32x16 s[NB];
@@ -667,6 +685,7 @@ __device__ __forceinline__ void rs_score(int j, const unsigned char* ks, u32x4* 
   constexpr float kBound = 32768.0f;
   u32x4 pf[NB][2];
   float tl = 0.f, tr = 0.f;
+  float fac = 1.0f;
   bool redo = j == 0;
   if (!redo) {
     exp_tile<DT, NB>(s, sl2, -mref, pf, tl, tr);
@@ -679,28 +698,27 @@ __device__ __forceinline__ void rs_score(int j, const unsigned char* ks, u32x4* 
 #pragma unroll
       for (int r = (n == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[n][r]);
     const float mnew = fmaxf(mref, pair_max(mx * sl2));
-    const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
-    l *= alpha;
-    lr *= alpha;
+    fac = __builtin_amdgcn_exp2f(mref - mnew);
+    l *= fac;
+    lr *= fac;
     mref = mnew;
     exp_tile<DT, NB>(s, sl2, -mref, pf, tl, tr);
-    fo[w.lane] = alpha;
   }
   l += DT == kBF16 ? tl : tr;
   lr += tr;
 #pragma unroll
   for (int g = 0; g < 2 * NB; ++g) xo[64 * g + w.lane] = pf[g >> 1][g & 1];
-  *fl = redo ? 1 : 0;
+  fo[w.lane] = fac;
 }
 
-// PV wave, tile jj (V stage vs): rescale O if the score wave moved the
-// reference, then O^T += V^T P^T with the P from xi (16-key step g major,
-// so consecutive MFMAs use different accumulators).
-template <int DT, int D>
+// PV wave, tile jj (V stage vs): rescale O where the factor differs from 1,
+// then O^T += V^T P^T with the P from xi (16-key step g major, so
+// consecutive MFMAs use different accumulators).
+template <int DT, int D, int NG>
 __device__ __forceinline__ void rs_pv(int jj, const unsigned char* vs, const u32x4* xi, const float* fi,
-                                      const int* fl, const Wave16& w, f32x16 (&oacc)[D / 32]) {
-  using S = RsShape<D>;
-  constexpr int NDT = S::NDT, KS = S::KS, BC = S::BC, NPV = KS * NDT, PRE = 8;
+                                      const Wave16& w, f32x16 (&oacc)[D / 32]) {
+  using S = RsShape<D, NG>;
+  constexpr int NDT = S::NDT, KS = S::KS, BC = S::BC, NPV = KS * NDT, PRE = S::PRE;
   if (jj * BC >= w.wkend) return;
   u32x4 va[NPV];
 #pragma unroll
@@ -708,8 +726,8 @@ __device__ __forceinline__ void rs_pv(int jj, const unsigned char* vs, const u32
   u32x4 pk[KS];
 #pragma unroll
   for (int g = 0; g < KS; ++g) pk[g] = xi[64 * g + w.lane];
-  if (__builtin_amdgcn_readfirstlane(*fl)) {
-    const float a = fi[w.lane];
+  const float a = fi[w.lane];
+  if (__builtin_amdgcn_ballot_w64(a != 1.0f)) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= a;
   }
@@ -721,38 +739,40 @@ __device__ __forceinline__ void rs_pv(int jj, const unsigned char* vs, const u32
   }
 }
 
-// Period p of one role (P6 = p mod 6: stages p mod 3, buffers p mod 2).
-template <int DT, int D, bool SCORE, int P6>
+// Period p of one role (P6 = p mod 6: K stages p mod 3, V stages p mod VST,
+// buffers p mod 2).  V tile p+VST-2 is loaded in period p.
+template <int DT, int D, int NG, bool SCORE, int P6>
 __device__ __forceinline__ void rs_period(int p, int nt, const u16* Kh, const u16* Vh, int kbytes,
                                           unsigned char* const (&kr)[3], unsigned char* const (&vr)[3],
-                                          u32x4* const (&xb)[2], float* const (&fb)[2], int* const (&flb)[2],
-                                          const Wave16& w, const u32x4 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
-                                          float& mref, float& l, float& lr, float sl2) {
-  wait_tile_and_barrier(RsShape<D>::kLoads);
-  rs_issue<D>(Vh, kbytes, p + 1, vr[(P6 + 1) % 3], w);
-  rs_issue<D>(Kh, kbytes, p + 2, kr[(P6 + 2) % 3], w);
+                                          u32x4* const (&xb)[2],
+                                          float* const (&fb)[2], const Wave16& w, const u32x4 (&qf)[D / 16],
+                                          f32x16 (&oacc)[D / 32], float& mref, float& l, float& lr, float sl2) {
+  using S = RsShape<D, NG>;
+  constexpr int VST = S::VST;
+  rs_wait_barrier<S::kWait>();
+  rs_issue<D, NG>(Vh, kbytes, p + VST - 2, vr[(P6 + VST - 2) % VST], w);
+  rs_issue<D, NG>(Kh, kbytes, p + 2, kr[(P6 + 2) % 3], w);
   if constexpr (SCORE) {
-    if (p < nt) rs_score<DT, D>(p, kr[P6 % 3], xb[P6 % 2], fb[P6 % 2], flb[P6 % 2], w, qf, mref, l, lr, sl2);
+    if (p < nt) rs_score<DT, D, NG>(p, kr[P6 % 3], xb[P6 % 2], fb[P6 % 2], w, qf, mref, l, lr, sl2);
   } else {
-    if (p >= 1)
-      rs_pv<DT, D>(p - 1, vr[(P6 + 2) % 3], xb[(P6 + 1) % 2], fb[(P6 + 1) % 2], flb[(P6 + 1) % 2], w, oacc);
+    if (p >= 1) rs_pv<DT, D, NG>(p - 1, vr[(P6 + VST - 1) % VST], xb[(P6 + 1) % 2], fb[(P6 + 1) % 2], w, oacc);
   }
 }
 
-template <int DT, int D, bool SCORE>
+template <int DT, int D, int NG, bool SCORE>
 __device__ __forceinline__ void rs_loop(int nt, const u16* Kh, const u16* Vh, int kbytes,
                                         unsigned char* const (&kr)[3], unsigned char* const (&vr)[3],
-                                        u32x4* const (&xb)[2], float* const (&fb)[2], int* const (&flb)[2],
-                                        const Wave16& w, const u32x4 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
-                                        float& mref, float& l, float& lr, float sl2) {
-  // K tiles 0 and 1 and V tile 0; each period then starts two more tiles.
-  // Loads run past the last tile (reading zeros into stages nobody reads),
-  // so that every period waits for the same count.
-  rs_issue<D>(Kh, kbytes, 0, kr[0], w);
-  rs_issue<D>(Kh, kbytes, 1, kr[1], w);
-  rs_issue<D>(Vh, kbytes, 0, vr[0], w);
+                                        u32x4* const (&xb)[2], float* const (&fb)[2], const Wave16& w,
+                                        const u32x4 (&qf)[D / 16], f32x16 (&oacc)[D / 32], float& mref, float& l,
+                                        float& lr, float sl2) {
+  // K tiles 0 and 1 (and V tile 0 with three V stages); each period then
+  // starts two more tiles.  Loads run past the last tile (reading zeros into
+  // stages nobody reads), so that every period waits for the same count.
+  rs_issue<D, NG>(Kh, kbytes, 0, kr[0], w);
+  rs_issue<D, NG>(Kh, kbytes, 1, kr[1], w);
+  if constexpr (RsShape<D, NG>::VST == 3) rs_issue<D, NG>(Vh, kbytes, 0, vr[0], w);
 #define RS_PERIOD(P6) \
-  rs_period<DT, D, SCORE, P6>(p + P6, nt, Kh, Vh, kbytes, kr, vr, xb, fb, flb, w, qf, oacc, mref, l, lr, sl2)
+  rs_period<DT, D, NG, SCORE, P6>(p + P6, nt, Kh, Vh, kbytes, kr, vr, xb, fb, w, qf, oacc, mref, l, lr, sl2)
   for (int p = 0; p <= nt; p += 6) {
     RS_PERIOD(0);
     if (p + 1 <= nt) RS_PERIOD(1);
@@ -768,15 +788,16 @@ __device__ __forceinline__ void rs_loop(int nt, const u16* Kh, const u16* Vh, in
 }
 
 // SPLIT and VARLEN as in fa_fwd_16.
-template <int DT, int D, bool CAUSAL, bool SPLIT = false, bool VARLEN = false>
-__global__ __launch_bounds__(512, 1) void fa_fwd_rs(const u16* __restrict__ Qg, const u16* __restrict__ Kg,
-                                                    const u16* __restrict__ Vg, u16* __restrict__ Og,
-                                                    float* __restrict__ Lg, int BH, int Nq, int Nk, int nqt,
-                                                    float sl2, int split_len, float* __restrict__ Po,
-                                                    float* __restrict__ Pl, const int* __restrict__ cuq,
-                                                    const int* __restrict__ cuk, int H, int tq, int tk) {
-  using S = RsShape<D>;
-  constexpr int BR = 128, BC = S::BC, ROWB = S::ROWB, TILEB = S::TILEB, NKK = S::NKK, NDT = S::NDT, XG = S::XG;
+template <int DT, int D, int NG, bool CAUSAL, bool SPLIT = false, bool VARLEN = false>
+__global__ __launch_bounds__(128 * NG, 1) void fa_fwd_rs(const u16* __restrict__ Qg, const u16* __restrict__ Kg,
+                                                         const u16* __restrict__ Vg, u16* __restrict__ Og,
+                                                         float* __restrict__ Lg, int BH, int Nq, int Nk, int nqt,
+                                                         float sl2, int split_len, float* __restrict__ Po,
+                                                         float* __restrict__ Pl, const int* __restrict__ cuq,
+                                                         const int* __restrict__ cuk, int H, int tq, int tk) {
+  using S = RsShape<D, NG>;
+  constexpr int BR = 32 * NG, BC = S::BC, ROWB = S::ROWB, TILEB = S::TILEB, NKK = S::NKK, NDT = S::NDT, XG = S::XG;
+  constexpr int VST = S::VST;
   // Ring stages aligned to their size so that none straddles a 64 KB
   // boundary (the operand reads address one 64 KB window each); as the most
   // aligned arrays they are also laid out first, within the first 96 KB.
@@ -785,14 +806,12 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_rs(const u16* __restrict__ Qg, 
   __shared__ __attribute__((aligned(TILEB))) unsigned char k2s[TILEB];
   __shared__ __attribute__((aligned(TILEB))) unsigned char v0s[TILEB];
   __shared__ __attribute__((aligned(TILEB))) unsigned char v1s[TILEB];
-  __shared__ __attribute__((aligned(TILEB))) unsigned char v2s[TILEB];
-  __shared__ u32x4 x0[4 * XG];
-  __shared__ u32x4 x1[4 * XG];
-  __shared__ float f0[4 * 64];
-  __shared__ float f1[4 * 64];
-  __shared__ float finv[4 * 64];
-  __shared__ int fl0[4];
-  __shared__ int fl1[4];
+  __shared__ __attribute__((aligned(VST == 3 ? TILEB : 16))) unsigned char v2s[VST == 3 ? TILEB : 16];
+  __shared__ u32x4 x0[NG * XG];
+  __shared__ u32x4 x1[NG * XG];
+  __shared__ float f0[NG * 64];
+  __shared__ float f1[NG * 64];
+  __shared__ float finv[NG * 64];
 
   Wave16 w;
   const int tid = threadIdx.x;
@@ -816,8 +835,8 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_rs(const u16* __restrict__ Qg, 
   const int kbytes = nk * ROWB;
   const int kend = CAUSAL ? min(nk, min(q0 + BR, nq) - kb) : nk;
   const int nt = kend > 0 ? (kend + BC - 1) / BC : 0;
-  const int grp = w.wave & 3;
-  const bool score = w.wave < 4;
+  const int grp = w.wave & (NG - 1);
+  const bool score = w.wave < NG;
   w.wq0 = q0 + 32 * grp;
   const int myq = w.wq0 + w.l32;
   w.wkend = w.wq0 >= nq ? 0 : CAUSAL ? min(kend, w.wq0 + 32 - kb) : kend;
@@ -826,10 +845,9 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_rs(const u16* __restrict__ Qg, 
   init_operand_offsets<D>(w);
 
   unsigned char* const kr[3] = {k0s, k1s, k2s};
-  unsigned char* const vr[3] = {v0s, v1s, v2s};
+  unsigned char* const vr[3] = {v0s, v1s, v2s};  // v2s: 3 V stages only
   u32x4* const xb[2] = {x0 + XG * grp, x1 + XG * grp};
   float* const fb[2] = {f0 + 64 * grp, f1 + 64 * grp};
-  int* const flb[2] = {fl0 + grp, fl1 + grp};
   float* const fi = finv + 64 * grp;
 
   u32x4 qf[NKK];
@@ -842,7 +860,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_rs(const u16* __restrict__ Qg, 
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
       qf[kk] = __builtin_amdgcn_raw_buffer_load_b128(rQ, w.l32 * ROWB + (16 * kk + 8 * w.hf) * 2, 0, 0);
-    rs_loop<DT, D, true>(nt, Kh, Vh, kbytes, kr, vr, xb, fb, flb, w, qf, oacc, mref, l, lr, sl2);
+    rs_loop<DT, D, NG, true>(nt, Kh, Vh, kbytes, kr, vr, xb, fb, w, qf, oacc, mref, l, lr, sl2);
     const float lt = pair_sum(l);
     const float ltr = DT == kBF16 ? pair_sum(lr) : lt;
     const bool none = (SPLIT || VARLEN) && !(lt > 0.f);
@@ -857,7 +875,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_rs(const u16* __restrict__ Qg, 
   } else {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
-    rs_loop<DT, D, false>(nt, Kh, Vh, kbytes, kr, vr, xb, fb, flb, w, qf, oacc, mref, l, lr, sl2);
+    rs_loop<DT, D, NG, false>(nt, Kh, Vh, kbytes, kr, vr, xb, fb, w, qf, oacc, mref, l, lr, sl2);
     __syncthreads();
     const float inv = fi[w.lane];
     if constexpr (SPLIT) {
@@ -893,12 +911,12 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_rs(const u16* __restrict__ Qg, 
   }
 }
 
-template <int DT, int D, bool CAUSAL, bool SPLIT, bool VARLEN = false>
+template <int DT, int D, int NG, bool CAUSAL, bool SPLIT, bool VARLEN = false>
 int launch_rs(const FaLaunch& a, float sl2, int nsplit, int split_len, float* Po, float* Pl) {
-  const int nqt = (int)((a.Nq + 127) / 128);
+  const int nqt = (int)((a.Nq + 32 * NG - 1) / (32 * NG));
   const int64_t heads = VARLEN ? (a.BH + 7) / 8 * 8 : a.BH;
-  const dim3 grid((unsigned)(heads * nqt * nsplit)), block(512);
-  return launch_kernel(fa_fwd_rs<DT, D, CAUSAL, SPLIT, VARLEN>, grid, block, (hipStream_t)a.stream, (const u16*)a.q,
+  const dim3 grid((unsigned)(heads * nqt * nsplit)), block(128 * NG);
+  return launch_kernel(fa_fwd_rs<DT, D, NG, CAUSAL, SPLIT, VARLEN>, grid, block, (hipStream_t)a.stream, (const u16*)a.q,
                        (const u16*)a.k, (const u16*)a.v, (u16*)a.o, a.lse, (int)a.BH, (int)a.Nq, (int)a.Nk, nqt,
                        sl2, split_len, Po, Pl, a.cu_q, a.cu_k, (int)a.H, (int)a.total_q, (int)a.total_k);
 }
@@ -1161,20 +1179,25 @@ int launch16(const FaLaunch& a, float sl2, int nsplit, int split_len, float* Po,
 
 template <int DT, int D>
 int dispatch16(const FaLaunch& a, float sl2) {
-  // Fewer 8-wave workgroups than CUs: 128-row workgroups, which double them.
-  // D >= 64: the role-split kernel (two waves per SIMD; 35-55% faster than
-  // the 4-wave form on such grids, 15-34% slower than the 256-row kernel on
-  // grids that fill the CUs).  D = 32 (a 64-key tile is 4 KB, too little
-  // for eight waves' 1 KB loads): the 4-wave form (one wave per SIMD,
-  // pipelined steps).
+  // Fewer 256-row workgroups than CUs: 128-row workgroups, which double them.
+  // D >= 64: the 8-wave role-split kernel (two waves per SIMD; 35-55% faster
+  // than the 4-wave form on such grids, while on grids that fill the CUs it
+  // lost 15-34% to the 256-row kernels).  D = 32 (a 64-key tile is 4 KB, too
+  // little for eight waves' 1 KB loads): the 4-wave form (one wave per SIMD,
+  // pipelined steps).  Otherwise 256-row workgroups: at D = 128 the 16-wave
+  // role-split kernel (four waves per SIMD; 1-3% faster than fa_fwd_16, the
+  // same results), at D <= 64 fa_fwd_16 (two workgroups per CU).
   constexpr int NW8 = waves16<D>();
   if (NW8 == 8 && a.BH * ((a.Nq + 32 * NW8 - 1) / (32 * NW8)) < a.cus) {
     if constexpr (D >= 64)
-      return a.causal ? launch_rs<DT, D, true, false>(a, sl2, 1, 0, nullptr, nullptr)
-                      : launch_rs<DT, D, false, false>(a, sl2, 1, 0, nullptr, nullptr);
+      return a.causal ? launch_rs<DT, D, 4, true, false>(a, sl2, 1, 0, nullptr, nullptr)
+                      : launch_rs<DT, D, 4, false, false>(a, sl2, 1, 0, nullptr, nullptr);
     return a.causal ? launch16<DT, D, true, false, false, 4>(a, sl2, 1, 0, nullptr, nullptr)
                     : launch16<DT, D, false, false, false, 4>(a, sl2, 1, 0, nullptr, nullptr);
   }
+  if constexpr (D == 128)
+    return a.causal ? launch_rs<DT, D, 8, true, false>(a, sl2, 1, 0, nullptr, nullptr)
+                    : launch_rs<DT, D, 8, false, false>(a, sl2, 1, 0, nullptr, nullptr);
   return a.causal ? launch16<DT, D, true, false>(a, sl2, 1, 0, nullptr, nullptr)
                   : launch16<DT, D, false, false>(a, sl2, 1, 0, nullptr, nullptr);
 }
@@ -1279,8 +1302,8 @@ namespace {
 
 template <int DT>
 int dispatch_rs(const FaLaunch& a, float sl2) {
-  return a.causal ? launch_rs<DT, 256, true, false>(a, sl2, 1, 0, nullptr, nullptr)
-                  : launch_rs<DT, 256, false, false>(a, sl2, 1, 0, nullptr, nullptr);
+  return a.causal ? launch_rs<DT, 256, 4, true, false>(a, sl2, 1, 0, nullptr, nullptr)
+                  : launch_rs<DT, 256, 4, false, false>(a, sl2, 1, 0, nullptr, nullptr);
 }
 
 template <int DT>
@@ -1288,8 +1311,8 @@ int dispatch_rs_split(const FaLaunch& a, float sl2, int nsplit, int split_len) {
   const int64_t rows = a.BH * a.Nq;
   float* Po = (float*)a.workspace;
   float* Pl = Po + (size_t)nsplit * rows * 256;
-  const int st = a.causal ? launch_rs<DT, 256, true, true>(a, sl2, nsplit, split_len, Po, Pl)
-                          : launch_rs<DT, 256, false, true>(a, sl2, nsplit, split_len, Po, Pl);
+  const int st = a.causal ? launch_rs<DT, 256, 4, true, true>(a, sl2, nsplit, split_len, Po, Pl)
+                          : launch_rs<DT, 256, 4, false, true>(a, sl2, nsplit, split_len, Po, Pl);
   if (st != 0) return st;
   const int64_t threads = rows * (256 / 4);
   return launch_kernel(merge_splits<DT, 256>, dim3((unsigned)((threads + 255) / 256)), dim3(256),
@@ -1298,8 +1321,8 @@ int dispatch_rs_split(const FaLaunch& a, float sl2, int nsplit, int split_len) {
 
 template <int DT>
 int dispatch_rs_varlen(const FaLaunch& a, float sl2) {
-  return a.causal ? launch_rs<DT, 256, true, false, true>(a, sl2, 1, 0, nullptr, nullptr)
-                  : launch_rs<DT, 256, false, false, true>(a, sl2, 1, 0, nullptr, nullptr);
+  return a.causal ? launch_rs<DT, 256, 4, true, false, true>(a, sl2, 1, 0, nullptr, nullptr)
+                  : launch_rs<DT, 256, 4, false, false, true>(a, sl2, 1, 0, nullptr, nullptr);
 }
 
 }  // namespace

@@ -80,7 +80,8 @@ def test_parity_16bit_grid_sizes(dt, D, causal, B, H, Nq, Nk):
     # 256-row (8-wave) workgroups than the 256 CUs (B*H*ceil(Nq/256) < 256,
     # every shape but the second) it runs 128-row workgroups, of score and
     # PV waves at D >= 64 and of 4 waves with pipelined steps at D = 32; the
-    # second shape (256 workgroups) keeps the 8-wave form.  All compared
+    # second shape (256 workgroups) runs 256-row ones (16 score and PV waves
+    # at D = 128, 8 waves below).  All compared
     # element by element, with ragged Q and K tails; Nq = 40 leaves row
     # groups without rows, Nk = 33 and 17 a ragged or lone partial key tile,
     # 300 x 100 (causal) rows that see every key.
@@ -92,11 +93,27 @@ def test_parity_16bit_grid_sizes(dt, D, causal, B, H, Nq, Nk):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq,Nk", [(40, 17), (257, 33), (300, 100)])
+def test_parity_d128_full_grid_edges(dt, causal, Nq, Nk):
+    # D = 128 on a grid that fills the CUs (300 heads): the 16-wave role
+    # split with row groups that hold no row (Nq = 40: six of eight), a lone
+    # or ragged partial key tile, a one-row second Q tile (257), and causal
+    # rows that see every key (300 x 100).
+    w = workloads.Workload(f"rs16_{dt}_{'c' if causal else 'n'}_{Nq}x{Nk}", 1, 300, Nq, Nk, 128, dt, causal,
+                           9100 + Nq + Nk)
+    cpu, gpu = _case(w)
+    o, l = run_gpu(*gpu, w.causal)
+    compare_full(w, cpu, o, l, "rs16")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
 @pytest.mark.parametrize("D", [32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_parity_8wave_several_q_tiles(dt, D, causal):
-    # The 8-wave form (256-row workgroups) at a grid of more workgroups than
-    # CUs (128 heads x 3 Q tiles = 384), with several Q tiles per head (causal
+    # The 256-row workgroups (16-wave role split at D = 128, 8-wave fa_fwd_16
+    # below) at a grid of more workgroups than CUs (128 heads x 3 Q tiles =
+    # 384), with several Q tiles per head (causal
     # diagonals at q0 > 0, running maxima rescaled mid-stream), a ragged Q
     # tile (520 = 2 x 256 + 8 rows) and a ragged key tail (700 = 10 x 64 +
     # 60), every element compared.
