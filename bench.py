@@ -83,7 +83,8 @@ def kernel_tag(w, op: str = "fwd") -> str:
         return f"fa_bwd_16_{w.dtype}_d{w.D}_{'causal' if w.causal else 'noncausal'}"
     if w.dtype == "fp32":
         return f"fa_fwd_32_d{w.D}_{'causal' if w.causal else 'noncausal'}"
-    kern = "fa_fwd_rs" if w.D == 256 else "fa_fwd_16"  # the forward kernel this workload's grid runs
+    # the forward kernel these workloads' grids run (all fill the CUs)
+    kern = "fa_fwd_rs" if w.D in (128, 256) else "fa_fwd_16"
     return f"{kern}_{w.dtype}_d{w.D}_{'causal' if w.causal else 'noncausal'}"
 
 
