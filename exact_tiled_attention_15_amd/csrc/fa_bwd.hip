@@ -141,7 +141,7 @@ __device__ __forceinline__ void dq_tile(const u16* Kh, const u16* Vh, int kbytes
   // refill the stage of tile j-1.
   static_assert(D <= 128 && ST == 4, "D = 256 runs bwd_dq_rs");
   wait_tile_and_barrier(j + 2 < nt ? loads_per_tile<D, NW>(w.wave) : 0);
-  if (j + ST - 1 < nt) issue_tile16<D, NW>(Kh, Vh, kbytes, j + ST - 1, dst, w);
+  if (j + ST - 1 < nt) issue_tile16<D, NW, 64, true>(Kh, Vh, kbytes, j + ST - 1, dst, w);
   if (k0 >= w.wkend) return;
   const bool need_mask = k0 + BC - 1 > w.wklim;  // causal diagonal or past Nk
   const int lim = w.klim - (k0 + 4 * w.hf);
@@ -251,12 +251,17 @@ __global__ __launch_bounds__(64 * kWavesDQ, 1) void bwd_dq(const u16* __restrict
   const float delta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, myq * 4, 0, 0));
 
   // (a sequence without keys has no tile: nothing may be left in flight)
-  if (!VARLEN || nt > 0) issue_tile16<D, NW>(Kh, Vh, kbytes, 0, stage0, w);
+  if (!VARLEN || nt > 0) issue_tile16<D, NW, 64, true>(Kh, Vh, kbytes, 0, stage0, w);
   f32x16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
-  if (nt > 1) issue_tile16<D, NW>(Kh, Vh, kbytes, 1, stage1, w);
-  if (nt > 2) issue_tile16<D, NW>(Kh, Vh, kbytes, 2, stage2, w);
+  if (nt > 1) issue_tile16<D, NW, 64, true>(Kh, Vh, kbytes, 1, stage1, w);
+  // Waits for the fragments, the row statistics and tiles 0 and 1.
+  settle_loads(qf);
+  settle_loads(dof);
+  settle_loads(lse2);
+  settle_loads(delta);
+  if (nt > 2) issue_tile16<D, NW, 64, true>(Kh, Vh, kbytes, 2, stage2, w);
   // Tile 0 complete before the first tile's reads.
   wait_tile_and_barrier(nt > 2 ? loads_per_tile<D, NW>(w.wave) : 0);
   for (int j = 0; j < nt; j += 4) {
@@ -295,7 +300,7 @@ constexpr int XG = 2 * 64;                      // u32x4 of dS per group and buf
 
 // One 1 KB direct-to-LDS load: 16 bytes a lane from byte `go` of `r`.
 __device__ __forceinline__ void dqrs_piece(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int go) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, go, 0, 0, 0);
+  dma_to_lds<16>(r, dst, go);
 }
 
 // This wave's two 1 KB pieces of 32-row tile t of one [N, 256] tensor.
@@ -507,12 +512,12 @@ __device__ __forceinline__ void issue_kv_tile(const u16* Qh, const u16* dOh, int
                                               const float* dlh, int Nq, int t, unsigned char* dst,
                                               const Wave16& w) {
   constexpr int TILEB = 64 * D * 2;
-  issue_tile16<D, kWavesKV>(Qh, dOh, qbytes, t, dst, w);
+  issue_tile16<D, kWavesKV, 64, true>(Qh, dOh, qbytes, t, dst, w);
   if (w.wave == 0) {
-    const auto rl = make_rsrc_at(l2h, t * 256, Nq * 4);
-    const auto rd = make_rsrc_at(dlh, t * 256, Nq * 4);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)(dst + 2 * TILEB), 4, w.lane * 4, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)(dst + 2 * TILEB + 256), 4, w.lane * 4, 0, 0, 0);
+    const auto rl = make_rsrc_uniform(l2h, t * 256, Nq * 4);
+    const auto rd = make_rsrc_uniform(dlh, t * 256, Nq * 4);
+    dma_to_lds<4, true>(rl, dst + 2 * TILEB, w.lane * 4);
+    dma_to_lds<4, true>(rd, dst + 2 * TILEB + 256, w.lane * 4);
   }
 }
 
@@ -628,6 +633,8 @@ __global__ __launch_bounds__(64 * kWavesKV, 1) void bwd_dkdv(const u16* __restri
   if (nt > 0) {
     issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, nq, t0, stage0, w);
     if (nt > 1) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, nq, t0 + 1, stage1, w);
+    settle_loads(kf);  // waits for the fragments and tiles t0 and t0 + 1
+    settle_loads(vf);
     if (nt > 2) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, nq, t0 + 2, stage2, w);
     wait_tile_and_barrier(nt > 2 ? kv_loads_per_tile<D>(w.wave) : 0);
     for (int j = 0; j < nt; j += 4) {
@@ -695,11 +702,14 @@ template <int D>
 __device__ __forceinline__ void issue_kv2_tile(const u16* Qh, const u16* dOh, int qbytes, const float* l2h,
                                                const float* dlh, int Nq, int t, unsigned char* dst, const Wave16& w) {
   constexpr int QR = kv2_rows<D>(), TILEB = QR * D * 2;
-  issue_tile16<D, kWavesKV2, QR>(Qh, dOh, qbytes, t, dst, w);
-  const auto rl = make_rsrc_at(l2h, t * QR * 4, Nq * 4);
-  const auto rd = make_rsrc_at(dlh, t * QR * 4, Nq * 4);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)(dst + 2 * TILEB), 4, w.lane * 4, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)(dst + 2 * TILEB + 256), 4, w.lane * 4, 0, 0, 0);
+  // D = 256 keeps the compiler-tracked loads: with the untracked ones its
+  // schedule of this 256-register kernel spilled.
+  constexpr bool UT = D != 256;
+  issue_tile16<D, kWavesKV2, QR, UT>(Qh, dOh, qbytes, t, dst, w);
+  const auto rl = UT ? make_rsrc_uniform(l2h, t * QR * 4, Nq * 4) : make_rsrc_at(l2h, t * QR * 4, Nq * 4);
+  const auto rd = UT ? make_rsrc_uniform(dlh, t * QR * 4, Nq * 4) : make_rsrc_at(dlh, t * QR * 4, Nq * 4);
+  dma_to_lds<4, UT>(rl, dst + 2 * TILEB, w.lane * 4);
+  dma_to_lds<4, UT>(rd, dst + 2 * TILEB + 256, w.lane * 4);
 }
 
 // Meet the other waves once this wave's LDS writes have completed, leaving
@@ -842,6 +852,9 @@ __device__ __forceinline__ void kv2_loop(const u16* Qh, const u16* dOh, int qbyt
                                          const u32x4 (&frag)[D / 16], f32x16 (&acc)[D / 32], float sl2) {
   issue_kv2_tile<D>(Qh, dOh, qbytes, l2h, dlh, nq, t0, s0, w);
   issue_kv2_tile<D>(Qh, dOh, qbytes, l2h, dlh, nq, t0 + 1, s1, w);
+  // Waits for the fragment and tiles t0 and t0 + 1 (the compiler-tracked
+  // loads at D = 256 need no such wait).
+  if constexpr (D != 256) settle_loads(frag);
   for (int j = 0; j < nt; j += 3) {
     kv2_tile<DT, D, CAUSAL, PW>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j, nt, s0, s2, xp, w, wk0, frag, acc, sl2);
     if (j + 1 < nt)
