@@ -58,6 +58,82 @@ constexpr int kWavesKV = 4;  // bwd_dkdv: waves per workgroup (32 keys each)
 constexpr int kWavesDQ = 8;
 constexpr int kStagesBwd = 4;
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS loads the compiler does not track (the kernels at D <= 128).
+// ---------------------------------------------------------------------------
+// The compiler's tracking of direct-to-LDS writes took some reads of one
+// ring stage for reads of the stage being loaded and waited for loads still
+// in flight (a vmcnt wait in one tile of three, in several of these
+// kernels).  dma_to_lds_u writes the same instruction as assembly, which its
+// wait-count insertion does not see.  A kernel using it waits for its own
+// loads explicitly (a vmcnt count and a barrier before a stage is read,
+// which is what orders the reads after these writes; loads complete in
+// order) and calls settle_loads on the registers of its other global loads.
+
+// A resource with base and size moved to scalar registers, as the resource
+// operand of the assembly load must be (both are wave-uniform, but the
+// compiler cannot always prove it, e.g. for offsets read from the
+// packed-sequence tables).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_uniform(const void* base, int off, int total) {
+  const unsigned long long b = (unsigned long long)((const unsigned char*)base + off);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)b);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
+  const int n = __builtin_amdgcn_readfirstlane(total - off > 0 ? total - off : 0);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((unsigned long long)hi << 32) | lo), 0, n, kBufFlags);
+}
+
+// One direct-to-LDS buffer load: BYTES (16 or 4) per lane from byte `voff`
+// of `r` into LDS from `dst` on (lane i's bytes at dst + BYTES i; the LDS
+// address goes through M0).  The leading s_nop covers the wait states a
+// VALU write of an SGPR (the resource or the M0 value) needs before a
+// vector memory instruction reads it; the one after the M0 write, those of
+// the M0 write.
+template <int BYTES>
+__device__ __forceinline__ void dma_to_lds_u(__amdgpu_buffer_rsrc_t r, const unsigned char* dst, int voff) {
+  static_assert(BYTES == 16 || BYTES == 4, "dwordx4 or dword");
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(__SIZE_TYPE__)(lds_void*)dst);
+  if constexpr (BYTES == 16)
+    asm volatile("s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                 :: "v"(voff), "s"(m0), "s"(r));
+  else
+    asm volatile("s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %0, %2, 0 offen lds"
+                 :: "v"(voff), "s"(m0), "s"(r));
+}
+
+// issue_tile16 (the same pieces into the same layout) with these loads.
+template <int D, int NW, int BC = 64>
+__device__ __forceinline__ void issue_tile16_u(const u16* Kh, const u16* Vh, int kbytes, int t,
+                                               unsigned char* dst, const Wave16& w) {
+  static_assert(BC % 16 == 0 && BC * D * 2 % 1024 == 0, "whole 16-row groups and 1 KB pieces");
+  constexpr int TILEB = BC * D * 2;
+  constexpr int NG = TILEB / 1024;
+  const auto rk = make_rsrc_uniform(Kh, t * TILEB, kbytes);
+  const auto rv = make_rsrc_uniform(Vh, t * TILEB, kbytes);
+#pragma unroll
+  for (int I = 0; I < (NG + NW - 1) / NW; ++I) {
+    const int G = w.wave + NW * I;
+    if (G < NG) {
+      const int go = dma_src_off<D>(G, w.lane);
+      dma_to_lds_u<16>(rk, dst + G * 1024, go);
+      dma_to_lds_u<16>(rv, dst + TILEB + G * 1024, go);
+    }
+  }
+}
+
+// Make the compiler wait here for the global loads that produced these
+// registers (it waits for a load before the first instruction that reads
+// its result; this empty assembly reads them all).  Called once, after the
+// first tiles' loads: the compiler does not count those, so it would
+// otherwise keep treating the fragment loads as possibly in flight and wait
+// for them again inside the tile loop, where its count would also wait for
+// the tile loads.
+template <int N>
+__device__ __forceinline__ void settle_loads(const u32x4 (&f)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(f[i]));
+}
+__device__ __forceinline__ void settle_loads(float a) { asm volatile("" ::"v"(a)); }
+
 template <int DT>
 __device__ __forceinline__ float lo16(unsigned x) {
   if constexpr (DT == kBF16) return __builtin_bit_cast(float, x << 16);
@@ -141,7 +217,7 @@ __device__ __forceinline__ void dq_tile(const u16* Kh, const u16* Vh, int kbytes
   // refill the stage of tile j-1.
   static_assert(D <= 128 && ST == 4, "D = 256 runs bwd_dq_rs");
   wait_tile_and_barrier(j + 2 < nt ? loads_per_tile<D, NW>(w.wave) : 0);
-  if (j + ST - 1 < nt) issue_tile16<D, NW, 64, true>(Kh, Vh, kbytes, j + ST - 1, dst, w);
+  if (j + ST - 1 < nt) issue_tile16_u<D, NW>(Kh, Vh, kbytes, j + ST - 1, dst, w);
   if (k0 >= w.wkend) return;
   const bool need_mask = k0 + BC - 1 > w.wklim;  // causal diagonal or past Nk
   const int lim = w.klim - (k0 + 4 * w.hf);
@@ -251,17 +327,17 @@ __global__ __launch_bounds__(64 * kWavesDQ, 1) void bwd_dq(const u16* __restrict
   const float delta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, myq * 4, 0, 0));
 
   // (a sequence without keys has no tile: nothing may be left in flight)
-  if (!VARLEN || nt > 0) issue_tile16<D, NW, 64, true>(Kh, Vh, kbytes, 0, stage0, w);
+  if (!VARLEN || nt > 0) issue_tile16_u<D, NW>(Kh, Vh, kbytes, 0, stage0, w);
   f32x16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
-  if (nt > 1) issue_tile16<D, NW, 64, true>(Kh, Vh, kbytes, 1, stage1, w);
+  if (nt > 1) issue_tile16_u<D, NW>(Kh, Vh, kbytes, 1, stage1, w);
   // Waits for the fragments, the row statistics and tiles 0 and 1.
   settle_loads(qf);
   settle_loads(dof);
   settle_loads(lse2);
   settle_loads(delta);
-  if (nt > 2) issue_tile16<D, NW, 64, true>(Kh, Vh, kbytes, 2, stage2, w);
+  if (nt > 2) issue_tile16_u<D, NW>(Kh, Vh, kbytes, 2, stage2, w);
   // Tile 0 complete before the first tile's reads.
   wait_tile_and_barrier(nt > 2 ? loads_per_tile<D, NW>(w.wave) : 0);
   for (int j = 0; j < nt; j += 4) {
@@ -300,7 +376,7 @@ constexpr int XG = 2 * 64;                      // u32x4 of dS per group and buf
 
 // One 1 KB direct-to-LDS load: 16 bytes a lane from byte `go` of `r`.
 __device__ __forceinline__ void dqrs_piece(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int go) {
-  dma_to_lds<16>(r, dst, go);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, go, 0, 0, 0);
 }
 
 // This wave's two 1 KB pieces of 32-row tile t of one [N, 256] tensor.
@@ -512,12 +588,12 @@ __device__ __forceinline__ void issue_kv_tile(const u16* Qh, const u16* dOh, int
                                               const float* dlh, int Nq, int t, unsigned char* dst,
                                               const Wave16& w) {
   constexpr int TILEB = 64 * D * 2;
-  issue_tile16<D, kWavesKV, 64, true>(Qh, dOh, qbytes, t, dst, w);
+  issue_tile16_u<D, kWavesKV>(Qh, dOh, qbytes, t, dst, w);
   if (w.wave == 0) {
     const auto rl = make_rsrc_uniform(l2h, t * 256, Nq * 4);
     const auto rd = make_rsrc_uniform(dlh, t * 256, Nq * 4);
-    dma_to_lds<4, true>(rl, dst + 2 * TILEB, w.lane * 4);
-    dma_to_lds<4, true>(rd, dst + 2 * TILEB + 256, w.lane * 4);
+    dma_to_lds_u<4>(rl, dst + 2 * TILEB, w.lane * 4);
+    dma_to_lds_u<4>(rd, dst + 2 * TILEB + 256, w.lane * 4);
   }
 }
 
@@ -704,12 +780,17 @@ __device__ __forceinline__ void issue_kv2_tile(const u16* Qh, const u16* dOh, in
   constexpr int QR = kv2_rows<D>(), TILEB = QR * D * 2;
   // D = 256 keeps the compiler-tracked loads: with the untracked ones its
   // schedule of this 256-register kernel spilled.
-  constexpr bool UT = D != 256;
-  issue_tile16<D, kWavesKV2, QR, UT>(Qh, dOh, qbytes, t, dst, w);
-  const auto rl = UT ? make_rsrc_uniform(l2h, t * QR * 4, Nq * 4) : make_rsrc_at(l2h, t * QR * 4, Nq * 4);
-  const auto rd = UT ? make_rsrc_uniform(dlh, t * QR * 4, Nq * 4) : make_rsrc_at(dlh, t * QR * 4, Nq * 4);
-  dma_to_lds<4, UT>(rl, dst + 2 * TILEB, w.lane * 4);
-  dma_to_lds<4, UT>(rd, dst + 2 * TILEB + 256, w.lane * 4);
+  if constexpr (D != 256) {
+    issue_tile16_u<D, kWavesKV2, QR>(Qh, dOh, qbytes, t, dst, w);
+    dma_to_lds_u<4>(make_rsrc_uniform(l2h, t * QR * 4, Nq * 4), dst + 2 * TILEB, w.lane * 4);
+    dma_to_lds_u<4>(make_rsrc_uniform(dlh, t * QR * 4, Nq * 4), dst + 2 * TILEB + 256, w.lane * 4);
+  } else {
+    issue_tile16<D, kWavesKV2, QR>(Qh, dOh, qbytes, t, dst, w);
+    const auto rl = make_rsrc_at(l2h, t * QR * 4, Nq * 4);
+    const auto rd = make_rsrc_at(dlh, t * QR * 4, Nq * 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)(dst + 2 * TILEB), 4, w.lane * 4, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)(dst + 2 * TILEB + 256), 4, w.lane * 4, 0, 0, 0);
+  }
 }
 
 // Meet the other waves once this wave's LDS writes have completed, leaving

@@ -134,67 +134,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_at(const void* base, int off, int total) {
   return make_rsrc((const unsigned char*)base + off, total - off);
 }
-// The same with base and size moved to scalar registers explicitly, as the
-// resource operand of an assembly load must be.  Every resource here
-// describes a tile or row block of one workgroup or wave, so both are
-// wave-uniform, but the compiler cannot always prove it (offsets read from
-// the packed-sequence tables).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_uniform(const void* base, int off, int total) {
-  const unsigned long long b = (unsigned long long)((const unsigned char*)base + off);
-  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)b);
-  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
-  const int n = __builtin_amdgcn_readfirstlane(total - off > 0 ? total - off : 0);
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(((unsigned long long)hi << 32) | lo), 0, n, kBufFlags);
-}
 
 typedef __attribute__((address_space(3))) void lds_void;
-
-// One direct-to-LDS buffer load: BYTES (16 or 4) per lane from byte `voff`
-// of `r` into LDS from `dst` on (lane i's bytes at dst + BYTES i; the LDS
-// address goes through M0).  By default the compiler's builtin.  UNTRACKED
-// writes the same instruction as assembly, which the compiler's wait-count
-// insertion does not see: its tracking of these LDS writes took some reads
-// of one ring stage for reads of the stage being loaded and waited for loads
-// still in flight (a vmcnt wait in one period of three).  A kernel using it
-// waits for its own loads explicitly (a vmcnt count and a barrier before a
-// stage is read, which is what orders the reads after these writes) and
-// calls settle_loads on the registers of its other global loads.  The
-// leading s_nop covers the wait states a VALU write of an SGPR (the resource
-// or the M0 value) needs before a vector memory instruction reads it; the
-// one after the M0 write, those of the M0 write.
-template <int BYTES, bool UNTRACKED = false>
-__device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t r, const unsigned char* dst, int voff) {
-  static_assert(BYTES == 16 || BYTES == 4, "dwordx4 or dword");
-  if constexpr (!UNTRACKED) {
-    if constexpr (BYTES == 16)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, 0, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, voff, 0, 0, 0);
-    return;
-  }
-  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(__SIZE_TYPE__)(lds_void*)dst);
-  if constexpr (BYTES == 16)
-    asm volatile("s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-                 :: "v"(voff), "s"(m0), "s"(r));
-  else
-    asm volatile("s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %0, %2, 0 offen lds"
-                 :: "v"(voff), "s"(m0), "s"(r));
-}
-
-// Make the compiler wait here for the global loads that produced these
-// registers (it waits for a load before the first instruction that reads
-// its result; this empty assembly reads them all).  A kernel with untracked
-// direct-to-LDS loads calls it once, after its first tiles' loads: the
-// compiler does not count those, so it would otherwise keep treating the
-// fragment loads as possibly in flight and wait for them again inside the
-// tile loop, where its count would also wait for the tile loads.
-template <int N>
-__device__ __forceinline__ void settle_loads(const u32x4 (&f)[N]) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(f[i]));
-}
-__device__ __forceinline__ void settle_loads(float a) { asm volatile("" ::"v"(a)); }
-
 typedef short s16x4 __attribute__((vector_size(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -271,21 +212,21 @@ __device__ __forceinline__ int loads_per_tile(int wave) {
 // Direct-to-LDS loads of BC-row tile t of two [N, D] tensors (K and V in
 // the forward pass) into `dst` (first tensor) and `dst + BC D 2` (second):
 // this wave's 1 KB pieces G = wave, wave + NW, ... of each.
-template <int D, int NW, int BC = 64, bool UNTRACKED = false>
+template <int D, int NW, int BC = 64>
 __device__ __forceinline__ void issue_tile16(const u16* Kh, const u16* Vh, int kbytes, int t,
                                              unsigned char* dst, const Wave16& w) {
   static_assert(BC % 16 == 0 && BC * D * 2 % 1024 == 0, "whole 16-row groups and 1 KB pieces");
   constexpr int TILEB = BC * D * 2;
   constexpr int NG = TILEB / 1024;
-  const auto rk = UNTRACKED ? make_rsrc_uniform(Kh, t * TILEB, kbytes) : make_rsrc_at(Kh, t * TILEB, kbytes);
-  const auto rv = UNTRACKED ? make_rsrc_uniform(Vh, t * TILEB, kbytes) : make_rsrc_at(Vh, t * TILEB, kbytes);
+  const auto rk = make_rsrc_at(Kh, t * TILEB, kbytes);
+  const auto rv = make_rsrc_at(Vh, t * TILEB, kbytes);
 #pragma unroll
   for (int I = 0; I < (NG + NW - 1) / NW; ++I) {
     const int G = w.wave + NW * I;
     if (G < NG) {
       const int go = dma_src_off<D>(G, w.lane);
-      dma_to_lds<16, UNTRACKED>(rk, dst + G * 1024, go);
-      dma_to_lds<16, UNTRACKED>(rv, dst + TILEB + G * 1024, go);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst + G * 1024), 16, go, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst + TILEB + G * 1024), 16, go, 0, 0, 0);
     }
   }
 }
