@@ -280,11 +280,17 @@ __device__ __forceinline__ void dq_tile(const u16* Kh, const u16* Vh, int kbytes
 
 // VARLEN: packed sequences (the rows of head_rows); a workgroup past its
 // sequence's queries exits, a sequence without keys gets dQ = 0.
+// The kernel also computes its rows' statistics (what bwd_prep computes for
+// the D = 256 and fp32 paths): delta = sum_d dO[d] O[d] in fp32 from the
+// stored 16-bit values, from the dO fragment it holds and the same fragment
+// of O, and lse2 = LSE log2(e); it uses them and stores them for the dK/dV
+// kernel that follows on the stream.
 template <int DT, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(64 * kWavesDQ, 1) void bwd_dq(const u16* __restrict__ Qg, const u16* __restrict__ Kg,
                                                           const u16* __restrict__ Vg, const u16* __restrict__ dOg,
-                                                          const float* __restrict__ lse2g,
-                                                          const float* __restrict__ deltag, u16* __restrict__ dQg,
+                                                          const u16* __restrict__ Og, const float* __restrict__ lseg,
+                                                          float* __restrict__ lse2g,
+                                                          float* __restrict__ deltag, u16* __restrict__ dQg,
                                                           int BH, int Nq, int Nk, int nqt, float sl2, float scale,
                                                           const int* __restrict__ cuq, const int* __restrict__ cuk,
                                                           int H, int tq, int tk) {
@@ -318,13 +324,12 @@ __global__ __launch_bounds__(64 * kWavesDQ, 1) void bwd_dq(const u16* __restrict
   w.wklim = CAUSAL ? min(w.wq0, nk - 1) : nk - 1;
   init_operand_offsets<D>(w);
 
-  u32x4 qf[D / 16], dof[D / 16];
+  u32x4 qf[D / 16], dof[D / 16], of[D / 16];
   load_frag<D>(qf, Qg + hr.qo, nq, w.wq0, w);
   load_frag<D>(dof, dOg + hr.qo, nq, w.wq0, w);
-  const auto rs = make_rsrc(lse2g + hr.so, nq * 4);
-  const auto rd = make_rsrc(deltag + hr.so, nq * 4);
-  const float lse2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, myq * 4, 0, 0));
-  const float delta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, myq * 4, 0, 0));
+  load_frag<D>(of, Og + hr.qo, nq, w.wq0, w);
+  const float lse =
+      __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(lseg + hr.so, nq * 4), myq * 4, 0, 0));
 
   // (a sequence without keys has no tile: nothing may be left in flight)
   if (!VARLEN || nt > 0) issue_tile16_u<D, NW>(Kh, Vh, kbytes, 0, stage0, w);
@@ -332,11 +337,31 @@ __global__ __launch_bounds__(64 * kWavesDQ, 1) void bwd_dq(const u16* __restrict
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
   if (nt > 1) issue_tile16_u<D, NW>(Kh, Vh, kbytes, 1, stage1, w);
-  // Waits for the fragments, the row statistics and tiles 0 and 1.
+  // Waits for the fragments and LSE (and with them tiles 0 and 1).
   settle_loads(qf);
   settle_loads(dof);
-  settle_loads(lse2);
-  settle_loads(delta);
+  settle_loads(of);
+  settle_loads(lse);
+  // The rows' statistics.  Lane l holds columns 16 kk + 8 (l / 32) .. +7 of
+  // row l % 32 (rows past Nq read as zero): a half-row sum, then the lane
+  // pair's.  The stores may still be in flight at the barriers below: they
+  // only lengthen the count-based waits, which stay exact for the tile loads
+  // (loads complete in order, so an outstanding needed load would leave all
+  // later loads outstanding too).
+  float dsum = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      dsum += lo16<DT>(of[kk][e]) * lo16<DT>(dof[kk][e]) + hi16<DT>(of[kk][e]) * hi16<DT>(dof[kk][e]);
+  const float delta = pair_sum(dsum);
+  const float lse2 = lse * kLog2e;
+  if (w.hf == 0) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse2), make_rsrc(lse2g + hr.so, nq * 4),
+                                          myq * 4, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, delta), make_rsrc(deltag + hr.so, nq * 4),
+                                          myq * 4, 0, 0);
+  }
   if (nt > 2) issue_tile16_u<D, NW>(Kh, Vh, kbytes, 2, stage2, w);
   // Tile 0 complete before the first tile's reads.
   wait_tile_and_barrier(nt > 2 ? loads_per_tile<D, NW>(w.wave) : 0);
@@ -1028,12 +1053,13 @@ int launch_bwd(const FaBwdLaunch& a, float sl2, float scale) {
   float* lse2 = (float*)a.workspace;
   float* delta = lse2 + rows;
   if (rows > 0) {
-    const int64_t threads = rows * (D / 8);
-    const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
-    int rc = launch_kernel(bwd_prep<DT, D>, grid, block, st, (const u16*)a.o, (const u16*)a.dout, a.lse, lse2,
-                           delta, rows);
-    if (rc != 0) return rc;
+    int rc = 0;
     if constexpr (D == 256) {
+      const int64_t threads = rows * (D / 8);
+      const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+      rc = launch_kernel(bwd_prep<DT, D>, grid, block, st, (const u16*)a.o, (const u16*)a.dout, a.lse, lse2, delta,
+                         rows);
+      if (rc != 0) return rc;
       const int nqt = (int)((a.Nq + 127) / 128);
       if (nqt > 0)
         rc = launch_kernel(bwd_dq_rs<DT, CAUSAL, VARLEN>, dim3((unsigned)(a.BH * nqt)), dim3(512), st,
@@ -1045,9 +1071,9 @@ int launch_bwd(const FaBwdLaunch& a, float sl2, float scale) {
       const int nqt = (int)((a.Nq + 32 * NWQ - 1) / (32 * NWQ));
       if (nqt > 0)
         rc = launch_kernel(bwd_dq<DT, D, CAUSAL, VARLEN>, dim3((unsigned)(a.BH * nqt)), dim3(64 * NWQ), st,
-                           (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, (const float*)lse2,
-                           (const float*)delta, (u16*)a.dq, (int)a.BH, (int)a.Nq, (int)a.Nk, nqt, sl2, scale,
-                           a.cu_q, a.cu_k, H, tq, tk);
+                           (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, (const u16*)a.o,
+                           (const float*)a.lse, lse2, delta, (u16*)a.dq, (int)a.BH, (int)a.Nq, (int)a.Nk, nqt, sl2,
+                           scale, a.cu_q, a.cu_k, H, tq, tk);
     }
     if (rc != 0) return rc;
   }
