@@ -230,7 +230,11 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
 /*
  * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs: two fp32
  * values per query row (8 * B * H * Nq); -1 if that overflows or a size is
- * negative.
+ * negative.  After a call the workspace holds, per query row r (rows in the
+ * order of lse), LSE_r log2(e) at float index r and delta_r = sum_d dO_rd O_rd
+ * (from the stored values, in fp32) at index rows + r: the statistics of the
+ * softmax gradient ("Building a FlashAttention-2 Forward Kernel in Pure
+ * NumPy", Extending It), which the gradient kernels read.
  */
 int64_t fa_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq);
 
