@@ -628,21 +628,25 @@ __device__ __forceinline__ void kv_tile(const u16* Qh, const u16* dOh, int qbyte
                                         unsigned char* dst, const Wave16& w, int wk0, const u32x4 (&kf)[D / 16],
                                         const u32x4 (&vf)[D / 16], f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32],
                                         float sl2) {
-  constexpr int TILEB = 64 * D * 2, NKK = D / 16, NDT = D / 32, ST = kStagesBwd;
-  static_assert(D <= 64 && ST == 4, "D = 128 and 256 run bwd_dkdv2");
+  constexpr int TILEB = 64 * D * 2, NKK = D / 16, NDT = D / 32;
+  static_assert(D <= 64, "D = 128 and 256 run bwd_dkdv2");
   const int t = t0 + j;
   const int q0 = 64 * t;
   const unsigned char* qs = src;
   const unsigned char* dos = src + TILEB;
   const unsigned char* st = src + 2 * TILEB;
-  // As in dq_tile: wait for tile j+1.
-  wait_tile_and_barrier(j + 2 < nt ? kv_loads_per_tile<D>(w.wave) : 0);
-  if (j + ST - 1 < nt) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t + ST - 1, dst, w);
+  // Tile j complete (tile j+1 may still be loading); then tile j+2 into
+  // the stage of tile j-1, which every wave is done with.
+  wait_tile_and_barrier(j + 1 < nt ? kv_loads_per_tile<D>(w.wave) : 0);
+  if (j + 2 < nt) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t + 2, dst, w);
   if (CAUSAL && q0 + 63 < wk0) return;  // every query of the tile precedes the wave's keys
   const bool need_mask = CAUSAL && q0 < wk0 + 31;
   const int mykey = wk0 + w.l32;
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
+    // (fences: one 32-row block at a time, which keeps the kernel within the
+    // 168 registers of three waves per SIMD)
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 s = {}, dp = {};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) s = mfma_32x32x16<DT>(ks_operand<D>(qs, w, n * NKK + kk), kf[kk], s);
@@ -673,6 +677,7 @@ __device__ __forceinline__ void kv_tile(const u16* Qh, const u16* dOh, int qbyte
         dsf[hh][i] = pack2<DT>(ds[8 * hh + 2 * i], ds[8 * hh + 2 * i + 1]);
       }
     // dV^T += dO^T P and dK^T += Q^T dS over this block's 32 queries.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -686,7 +691,7 @@ __device__ __forceinline__ void kv_tile(const u16* Qh, const u16* dOh, int qbyte
 // VARLEN: packed sequences (the rows of head_rows); a workgroup past its
 // sequence's keys exits, keys of a sequence without queries get zeros.
 template <int DT, int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(64 * kWavesKV, 1) void bwd_dkdv(const u16* __restrict__ Qg, const u16* __restrict__ Kg,
+__global__ __launch_bounds__(64 * kWavesKV, 3) void bwd_dkdv(const u16* __restrict__ Qg, const u16* __restrict__ Kg,
                                                              const u16* __restrict__ Vg, const u16* __restrict__ dOg,
                                                              const float* __restrict__ lse2g,
                                                              const float* __restrict__ deltag, u16* __restrict__ dKg,
@@ -697,7 +702,6 @@ __global__ __launch_bounds__(64 * kWavesKV, 1) void bwd_dkdv(const u16* __restri
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[SB];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[SB];
   __shared__ __attribute__((aligned(1024))) unsigned char stage2[SB];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage3[SB];
 
   Wave16 w;
   const int tid = threadIdx.x;
@@ -736,18 +740,13 @@ __global__ __launch_bounds__(64 * kWavesKV, 1) void bwd_dkdv(const u16* __restri
     if (nt > 1) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, nq, t0 + 1, stage1, w);
     settle_loads(kf);  // waits for the fragments and tiles t0 and t0 + 1
     settle_loads(vf);
-    if (nt > 2) issue_kv_tile<D>(Qh, dOh, qbytes, l2h, dlh, nq, t0 + 2, stage2, w);
-    wait_tile_and_barrier(nt > 2 ? kv_loads_per_tile<D>(w.wave) : 0);
-    for (int j = 0; j < nt; j += 4) {
-      kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j, nt, stage0, stage3, w, wk0, kf, vf, dk, dv, sl2);
+    for (int j = 0; j < nt; j += 3) {
+      kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j, nt, stage0, stage2, w, wk0, kf, vf, dk, dv, sl2);
       if (j + 1 < nt)
         kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 1, nt, stage1, stage0, w, wk0, kf, vf, dk, dv,
                                sl2);
       if (j + 2 < nt)
         kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 2, nt, stage2, stage1, w, wk0, kf, vf, dk, dv,
-                               sl2);
-      if (j + 3 < nt)
-        kv_tile<DT, D, CAUSAL>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 3, nt, stage3, stage2, w, wk0, kf, vf, dk, dv,
                                sl2);
     }
   }
