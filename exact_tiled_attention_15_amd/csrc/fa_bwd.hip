@@ -13,7 +13,8 @@
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Three kernels, no atomics, deterministic:
-//  * bwd_prep: delta and LSE * log2(e) per query row, into the workspace;
+//  * bwd_prep: delta and LSE * log2(e) per query row, into the workspace
+//    (before bwd_dq_rs; bwd_dq computes its rows' values itself);
 //  * bwd_dq: one workgroup per (batch*head, 256 query rows), 8 waves of 32
 //    rows (the forward's shape): K/V tiles stream through the same 4-stage
 //    direct-to-LDS ring; per tile S^T = K Q^T, dP^T = V dO^T, then
@@ -31,8 +32,10 @@
 //    wave per key group, serves D = 32 and 64).
 // S and dP are recomputed in both kernels: seven tile products instead of
 // the five a single kernel with atomic dQ updates would need.
-// At D = 256 the dQ kernel is bwd_dq_rs (score and dQ waves sharing each
-// SIMD, 32-key tiles) and bwd_dkdv2 streams 32-row Q/dO tiles.
+// At D = 256, and at D = 128 on grids of fewer 256-row workgroups than CUs,
+// the dQ kernel is bwd_dq_rs (score and dQ waves sharing each SIMD, 32-key
+// tiles, 128 rows a workgroup); at D = 256 bwd_dkdv2 streams 32-row Q/dO
+// tiles.
 //
 // The library compiles this file twice.  Without FA_BWD_SMALL_D it defines
 // fa_launch_bwd and the D = 128 kernels; with FA_BWD_SMALL_D only the D = 32
@@ -54,7 +57,7 @@ constexpr int kWavesKV = 4;  // bwd_dkdv: waves per workgroup (32 keys each)
 
 // Waves per workgroup of bwd_dq (32 query rows each, two waves per SIMD) and
 // stages of the LDS rings of bwd_dq and bwd_dkdv (three tiles in flight).
-// D = 256 runs bwd_dq_rs and bwd_dkdv2 instead.
+// D = 256 (and small grids at D = 128) run bwd_dq_rs instead.
 constexpr int kWavesDQ = 8;
 constexpr int kStagesBwd = 4;
 
@@ -379,7 +382,7 @@ __global__ __launch_bounds__(64 * kWavesDQ, 1) void bwd_dq(const u16* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// dQ kernel at D = 256 with two waves per SIMD.
+// Role-split dQ kernel: D = 256, and small grids at D = 128.
 // ---------------------------------------------------------------------------
 // One workgroup per (batch*head, 128 query rows), 8 waves.  Waves g and g + 4
 // share a SIMD and the 32 rows of group g: wave g (the score wave) holds the
@@ -387,17 +390,23 @@ __global__ __launch_bounds__(64 * kWavesDQ, 1) void bwd_dq(const u16* __restrict
 // dP^T = V dO^T, P and dS = P (dP - delta), and leaves dS (rounded to 16
 // bits) in LDS; wave g + 4 (the dQ wave) holds the rows' fp32 dQ and one
 // tile later adds K^T dS^T, its K^T operands read from the same K tile.  One
-// wave holding both fragments and dQ (64 + 64 + 128 registers) would fill a
-// SIMD alone; split, two waves share each SIMD.  K and V
+// wave holding both fragments and dQ (64 + 64 + 128 registers at D = 256)
+// would fill a SIMD alone; split, two waves share each SIMD.  At D = 128
+// (124 registers, 80 KB of LDS) two workgroups share a CU, and the 128-row
+// workgroups double the grid of bwd_dq's 256-row ones, which is what pays
+// where that grid leaves CUs idle.  K and V
 // tiles stream through two 4-stage rings (a K tile is read in its own
 // period and in the next); in period p every wave meets the others once (K
 // and V tile p are then complete), starts the loads of K and V tile p+2, and
 // the score waves handle tile p while the dQ waves handle tile p-1.
-namespace dqrs {
-constexpr int D = 256, BC = 32, ROWB = D * 2, TILEB = BC * ROWB, NKK = D / 16, NDT = D / 32;
-constexpr int kLoads = 2 * (TILEB / 1024 / 8);  // direct-to-LDS loads per wave and period
-constexpr int XG = 2 * 64;                      // u32x4 of dS per group and buffer
-}  // namespace dqrs
+template <int D_>
+struct Dqrs {
+  static constexpr int D = D_, BC = 32, ROWB = D * 2, TILEB = BC * ROWB, NKK = D / 16, NDT = D / 32;
+  static constexpr int kPieces = TILEB / 1024 / 8;  // 1 KB pieces per wave, tensor and tile
+  static constexpr int kLoads = 2 * kPieces;        // direct-to-LDS loads per wave and period
+  static constexpr int XG = 2 * 64;                 // u32x4 of dS per group and buffer
+  static_assert(kPieces >= 1 && TILEB % 8192 == 0, "whole 1 KB pieces for each of 8 waves");
+};
 
 // One 1 KB direct-to-LDS load: 16 bytes a lane from byte `go` of `r`.
 __device__ __forceinline__ void dqrs_piece(__amdgpu_buffer_rsrc_t r, unsigned char* dst, int go) {
@@ -405,23 +414,25 @@ __device__ __forceinline__ void dqrs_piece(__amdgpu_buffer_rsrc_t r, unsigned ch
 }
 
 // This wave's two 1 KB pieces of 32-row tile t of one [N, 256] tensor.
+template <int D>
 __device__ __forceinline__ void dqrs_issue(const u16* Xh, int kbytes, int t, unsigned char* dst, const Wave16& w) {
-  const auto r = make_rsrc_at(Xh, t * dqrs::TILEB, kbytes);
+  const auto r = make_rsrc_at(Xh, t * Dqrs<D>::TILEB, kbytes);
 #pragma unroll
-  for (int I = 0; I < dqrs::TILEB / 1024 / 8; ++I) {
+  for (int I = 0; I < Dqrs<D>::kPieces; ++I) {
     const int G = w.wave + 8 * I;
-    dqrs_piece(r, dst + G * 1024, dma_src_off<dqrs::D>(G, w.lane));
+    dqrs_piece(r, dst + G * 1024, dma_src_off<D>(G, w.lane));
   }
 }
 
 // Score wave, tile j (K stage ks, V stage vs): S and dP (MFMAs interleaved,
 // operands read 4 ahead), P = exp2(s scale log2 e - LSE log2 e) (masked keys
 // 0), dS = P (dP - delta), packed to 16 bits into xo.
-template <int DT>
+template <int DT, int D>
 __device__ __forceinline__ void dqrs_score(int j, const unsigned char* ks, const unsigned char* vs, u32x4* xo,
-                                           const Wave16& w, const u32x4 (&qf)[dqrs::NKK],
-                                           const u32x4 (&dof)[dqrs::NKK], float lse2, float delta, float sl2) {
-  using namespace dqrs;
+                                           const Wave16& w, const u32x4 (&qf)[Dqrs<D>::NKK],
+                                           const u32x4 (&dof)[Dqrs<D>::NKK], float lse2, float delta, float sl2) {
+  using S = Dqrs<D>;
+  constexpr int BC = S::BC, NKK = S::NKK;
   const int k0 = j * BC;
   if (k0 >= w.wkend) return;
   constexpr int NS = 2 * NKK, PRE = 4;
@@ -458,10 +469,11 @@ __device__ __forceinline__ void dqrs_score(int j, const unsigned char* ks, const
 
 // dQ wave, tile jj (K stage ks): dQ^T += K^T dS^T with the dS from xi
 // (16-key step major, so consecutive MFMAs use different accumulators).
-template <int DT>
+template <int DT, int D>
 __device__ __forceinline__ void dqrs_acc(int jj, const unsigned char* ks, const u32x4* xi, const Wave16& w,
-                                         f32x16 (&acc)[dqrs::NDT]) {
-  using namespace dqrs;
+                                         f32x16 (&acc)[Dqrs<D>::NDT]) {
+  using S = Dqrs<D>;
+  constexpr int BC = S::BC, NDT = S::NDT;
   if (jj * BC >= w.wkend) return;
   constexpr int NG = 2 * NDT, PRE = 4;
   u32x4 op[NG];
@@ -477,37 +489,37 @@ __device__ __forceinline__ void dqrs_acc(int jj, const unsigned char* ks, const 
 }
 
 // Period p of one role (P4 = p mod 4: stages p mod 4, buffers p mod 2).
-template <int DT, bool SCORE, int P4>
+template <int DT, int D, bool SCORE, int P4>
 __device__ __forceinline__ void dqrs_period(int p, int nt, const u16* Kh, const u16* Vh, int kbytes,
                                             unsigned char* const (&kr)[4], unsigned char* const (&vr)[4],
-                                            u32x4* const (&xb)[2], const Wave16& w, const u32x4 (&qf)[dqrs::NKK],
-                                            const u32x4 (&dof)[dqrs::NKK], f32x16 (&acc)[dqrs::NDT], float lse2,
+                                            u32x4* const (&xb)[2], const Wave16& w, const u32x4 (&qf)[Dqrs<D>::NKK],
+                                            const u32x4 (&dof)[Dqrs<D>::NKK], f32x16 (&acc)[Dqrs<D>::NDT], float lse2,
                                             float delta, float sl2) {
-  wait_tile_and_barrier(dqrs::kLoads);
-  dqrs_issue(Kh, kbytes, p + 2, kr[(P4 + 2) % 4], w);
-  dqrs_issue(Vh, kbytes, p + 2, vr[(P4 + 2) % 4], w);
+  wait_tile_and_barrier(Dqrs<D>::kLoads);
+  dqrs_issue<D>(Kh, kbytes, p + 2, kr[(P4 + 2) % 4], w);
+  dqrs_issue<D>(Vh, kbytes, p + 2, vr[(P4 + 2) % 4], w);
   if constexpr (SCORE) {
-    if (p < nt) dqrs_score<DT>(p, kr[P4], vr[P4], xb[P4 % 2], w, qf, dof, lse2, delta, sl2);
+    if (p < nt) dqrs_score<DT, D>(p, kr[P4], vr[P4], xb[P4 % 2], w, qf, dof, lse2, delta, sl2);
   } else {
-    if (p >= 1) dqrs_acc<DT>(p - 1, kr[(P4 + 3) % 4], xb[(P4 + 1) % 2], w, acc);
+    if (p >= 1) dqrs_acc<DT, D>(p - 1, kr[(P4 + 3) % 4], xb[(P4 + 1) % 2], w, acc);
   }
 }
 
-template <int DT, bool SCORE>
+template <int DT, int D, bool SCORE>
 __device__ __forceinline__ void dqrs_loop(int nt, const u16* Kh, const u16* Vh, int kbytes,
                                           unsigned char* const (&kr)[4], unsigned char* const (&vr)[4],
-                                          u32x4* const (&xb)[2], const Wave16& w, const u32x4 (&qf)[dqrs::NKK],
-                                          const u32x4 (&dof)[dqrs::NKK], f32x16 (&acc)[dqrs::NDT], float lse2,
+                                          u32x4* const (&xb)[2], const Wave16& w, const u32x4 (&qf)[Dqrs<D>::NKK],
+                                          const u32x4 (&dof)[Dqrs<D>::NKK], f32x16 (&acc)[Dqrs<D>::NDT], float lse2,
                                           float delta, float sl2) {
   // K and V tiles 0 and 1; each period then starts both tensors' tile p+2.
   // Loads run past the last tile (reading zeros into stages nobody reads),
   // so that every period waits for the same count.
-  dqrs_issue(Kh, kbytes, 0, kr[0], w);
-  dqrs_issue(Vh, kbytes, 0, vr[0], w);
-  dqrs_issue(Kh, kbytes, 1, kr[1], w);
-  dqrs_issue(Vh, kbytes, 1, vr[1], w);
+  dqrs_issue<D>(Kh, kbytes, 0, kr[0], w);
+  dqrs_issue<D>(Vh, kbytes, 0, vr[0], w);
+  dqrs_issue<D>(Kh, kbytes, 1, kr[1], w);
+  dqrs_issue<D>(Vh, kbytes, 1, vr[1], w);
 #define DQRS_PERIOD(P4) \
-  dqrs_period<DT, SCORE, P4>(p + P4, nt, Kh, Vh, kbytes, kr, vr, xb, w, qf, dof, acc, lse2, delta, sl2)
+  dqrs_period<DT, D, SCORE, P4>(p + P4, nt, Kh, Vh, kbytes, kr, vr, xb, w, qf, dof, acc, lse2, delta, sl2)
   for (int p = 0; p <= nt; p += 4) {
     DQRS_PERIOD(0);
     if (p + 1 <= nt) DQRS_PERIOD(1);
@@ -520,7 +532,7 @@ __device__ __forceinline__ void dqrs_loop(int nt, const u16* Kh, const u16* Vh, 
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); lgkmcnt, expcnt: no wait
 }
 
-template <int DT, bool CAUSAL, bool VARLEN>
+template <int DT, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(512, 1) void bwd_dq_rs(const u16* __restrict__ Qg, const u16* __restrict__ Kg,
                                                     const u16* __restrict__ Vg, const u16* __restrict__ dOg,
                                                     const float* __restrict__ lse2g,
@@ -528,18 +540,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_rs(const u16* __restrict__ Qg, 
                                                     int BH, int Nq, int Nk, int nqt, float sl2, float scale,
                                                     const int* __restrict__ cuq, const int* __restrict__ cuk,
                                                     int H, int tq, int tk) {
-  using namespace dqrs;
+  using S = Dqrs<D>;
+  constexpr int BC = S::BC, ROWB = S::ROWB, TILEB = S::TILEB, NKK = S::NKK, NDT = S::NDT, XG = S::XG;
   constexpr int BR = 128;
   // Ring stages of 16 KB aligned to their size: none straddles a 64 KB
   // boundary, and as the most aligned arrays they come first (0-128 KB).
-  __shared__ __attribute__((aligned(16384))) unsigned char k0s[TILEB];
-  __shared__ __attribute__((aligned(16384))) unsigned char k1s[TILEB];
-  __shared__ __attribute__((aligned(16384))) unsigned char k2s[TILEB];
-  __shared__ __attribute__((aligned(16384))) unsigned char k3s[TILEB];
-  __shared__ __attribute__((aligned(16384))) unsigned char v0s[TILEB];
-  __shared__ __attribute__((aligned(16384))) unsigned char v1s[TILEB];
-  __shared__ __attribute__((aligned(16384))) unsigned char v2s[TILEB];
-  __shared__ __attribute__((aligned(16384))) unsigned char v3s[TILEB];
+  __shared__ __attribute__((aligned(S::TILEB))) unsigned char k0s[TILEB];
+  __shared__ __attribute__((aligned(S::TILEB))) unsigned char k1s[TILEB];
+  __shared__ __attribute__((aligned(S::TILEB))) unsigned char k2s[TILEB];
+  __shared__ __attribute__((aligned(S::TILEB))) unsigned char k3s[TILEB];
+  __shared__ __attribute__((aligned(S::TILEB))) unsigned char v0s[TILEB];
+  __shared__ __attribute__((aligned(S::TILEB))) unsigned char v1s[TILEB];
+  __shared__ __attribute__((aligned(S::TILEB))) unsigned char v2s[TILEB];
+  __shared__ __attribute__((aligned(S::TILEB))) unsigned char v3s[TILEB];
   __shared__ u32x4 x0[4 * XG];
   __shared__ u32x4 x1[4 * XG];
 
@@ -581,11 +594,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_rs(const u16* __restrict__ Qg, 
     const auto rd = make_rsrc(deltag + hr.so, nq * 4);
     const float lse2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, myq * 4, 0, 0));
     const float delta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, myq * 4, 0, 0));
-    dqrs_loop<DT, true>(nt, Kh, Vh, kbytes, kr, vr, xb, w, qf, dof, acc, lse2, delta, sl2);
+    dqrs_loop<DT, D, true>(nt, Kh, Vh, kbytes, kr, vr, xb, w, qf, dof, acc, lse2, delta, sl2);
   } else {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
-    dqrs_loop<DT, false>(nt, Kh, Vh, kbytes, kr, vr, xb, w, qf, dof, acc, 0.f, 0.f, sl2);
+    dqrs_loop<DT, D, false>(nt, Kh, Vh, kbytes, kr, vr, xb, w, qf, dof, acc, 0.f, 0.f, sl2);
     const auto rq = make_rsrc_at(dQg + hr.qo, q0 * ROWB, nq * ROWB);
     store_rows16<DT, D>(acc, scale, rq, (32 * grp + w.l32) * ROWB, w.hf);
   }
@@ -1053,19 +1066,27 @@ int launch_bwd(const FaBwdLaunch& a, float sl2, float scale) {
   float* delta = lse2 + rows;
   if (rows > 0) {
     int rc = 0;
-    if constexpr (D == 256) {
-      const int64_t threads = rows * (D / 8);
-      const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
-      rc = launch_kernel(bwd_prep<DT, D>, grid, block, st, (const u16*)a.o, (const u16*)a.dout, a.lse, lse2, delta,
-                         rows);
-      if (rc != 0) return rc;
-      const int nqt = (int)((a.Nq + 127) / 128);
-      if (nqt > 0)
-        rc = launch_kernel(bwd_dq_rs<DT, CAUSAL, VARLEN>, dim3((unsigned)(a.BH * nqt)), dim3(512), st,
-                           (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, (const float*)lse2,
-                           (const float*)delta, (u16*)a.dq, (int)a.BH, (int)a.Nq, (int)a.Nk, nqt, sl2, scale,
-                           a.cu_q, a.cu_k, H, tq, tk);
-    } else {
+    // The role-split dQ kernel (128 query rows a workgroup) at D = 256, and
+    // at D = 128 where the 256-row kernel would leave CUs without a
+    // workgroup; it takes its row statistics from bwd_prep.
+    bool rs = false;
+    if constexpr (D >= 128)
+      rs = D == 256 || a.BH * ((a.Nq + 32 * kWavesDQ - 1) / (32 * kWavesDQ)) < a.cus;
+    if (rs) {
+      if constexpr (D >= 128) {
+        const int64_t threads = rows * (D / 8);
+        const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+        rc = launch_kernel(bwd_prep<DT, D>, grid, block, st, (const u16*)a.o, (const u16*)a.dout, a.lse, lse2,
+                           delta, rows);
+        if (rc != 0) return rc;
+        const int nqt = (int)((a.Nq + 127) / 128);
+        if (nqt > 0)
+          rc = launch_kernel(bwd_dq_rs<DT, D, CAUSAL, VARLEN>, dim3((unsigned)(a.BH * nqt)), dim3(512), st,
+                             (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout,
+                             (const float*)lse2, (const float*)delta, (u16*)a.dq, (int)a.BH, (int)a.Nq, (int)a.Nk,
+                             nqt, sl2, scale, a.cu_q, a.cu_k, H, tq, tk);
+      }
+    } else if constexpr (D <= 128) {
       constexpr int NWQ = kWavesDQ;
       const int nqt = (int)((a.Nq + 32 * NWQ - 1) / (32 * NWQ));
       if (nqt > 0)
