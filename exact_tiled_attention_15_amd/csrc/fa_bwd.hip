@@ -781,7 +781,8 @@ __global__ __launch_bounds__(64 * kWavesKV, 3) void bwd_dkdv(const u16* __restri
 // fits two waves per SIMD, and one wave's exponentials and softmax-gradient
 // arithmetic run while its sibling's MFMAs do.  A tile takes two barriers:
 // the first (tile complete) opens the score phase, the second (P written)
-// the gradient phase.  Q/dO tiles stream through a 3-stage ring; each key
+// the gradient phase; at D = 128 the dS wave's dK product of a tile runs in
+// the next tile's score phase.  Q/dO tiles stream through a 3-stage ring; each key
 // group's P travels in fp32, so dS is computed exactly as with one wave.
 // At D = 256 the K or V fragment (64 registers) and the fp32 gradient (128)
 // of 32 keys leave a wave few registers, so the tiles have 32 rows and the
@@ -840,6 +841,12 @@ __device__ __forceinline__ void lds_write_barrier() {
   asm volatile("" ::: "memory");
 }
 
+template <bool FIRST, class T>
+__device__ __forceinline__ T& pick(T& a, T& b) {
+  if constexpr (FIRST) return a;
+  else return b;
+}
+
 // Score MFMAs of the two-role kernel: x[n] = A(block n) frag^T over the tile
 // `as` (Q or dO rows; one 32-row block n per 32 rows), operands read PRE
 // MFMAs ahead.
@@ -886,7 +893,8 @@ template <int DT, int D, bool CAUSAL, bool PW>
 __device__ __forceinline__ void kv2_tile(const u16* Qh, const u16* dOh, int qbytes, const float* l2h,
                                          const float* dlh, int Nq, int t0, int j, int nt, const unsigned char* src,
                                          unsigned char* dst, float* xp, const Wave16& w, int wk0,
-                                         const u32x4 (&frag)[D / 16], f32x16 (&acc)[D / 32], float sl2) {
+                                         const u32x4 (&frag)[D / 16], f32x16 (&acc)[D / 32], float sl2,
+                                         u32x4 (&pk_loop)[kv2_rows<D>() / 32][2], bool& prev_live) {
   constexpr int QR = kv2_rows<D>(), NB = QR / 32, TILEB = QR * D * 2;
   const int t = t0 + j;
   const int q0 = QR * t;
@@ -896,16 +904,30 @@ __device__ __forceinline__ void kv2_tile(const u16* Qh, const u16* dOh, int qbyt
   // Tile j+1 is always in flight: the loads run two tiles past the last one
   // (rows past Nq, read as zeros and never used), so that every tile waits
   // for the same fixed count.
+  // At D = 128 the dS wave adds Q^T dS one tile late, in the next tile's
+  // score phase, beside its sibling's score MFMAs and exponentials (the
+  // second phase then holds the dV MFMAs against the dS arithmetic), and
+  // the tile j+2 loads wait for the second barrier, as they go into the
+  // stage whose Q rows that late product reads.  At D = 256 this order
+  // measured slower.
+  constexpr bool kLate = D != 256;
+  // P wave: P packed for dV; dS wave: dS packed for dK (kept across tiles
+  // only where the dS wave's product runs late).
+  u32x4 pk_tile[NB][2];
+  u32x4 (&pk)[NB][2] = pick<kLate>(pk_loop, pk_tile);
   wait_tile_and_barrier(kv2_loads_per_tile<D>());
-  issue_kv2_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t + kStagesKV2 - 1, dst, w);
+  if constexpr (!kLate) issue_kv2_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t + kStagesKV2 - 1, dst, w);
   // No query of the tile sees the group's keys (causal): nothing to do, but
   // both barriers are still met.
   const bool live = !(CAUSAL && q0 + QR - 1 < wk0);
+  // dS wave: dK^T += Q^T dS of the previous tile (its Q rows in `dst`).
+  if constexpr (kLate && !PW) {
+    if (prev_live) kv2_grads<DT, D>(dst, w, pk, acc);
+  }
   // Queries of the tile below `qlim` (relative to q0) precede this lane's key.
   const int qlim = (CAUSAL && q0 < wk0 + 31) ? wk0 + w.l32 - q0 : 0;
   // Lane l holds key wk0 + l % 32 and queries q0 + 32n + 8g + 4hf + e (r = 4g + e).
   f32x16 x[NB];
-  u32x4 pk[NB][2];  // P wave: P packed for dV; dS wave: dS packed for dK
   if (live) {
     // Score phase: S = Q K^T (P wave) or dP = dO V^T (dS wave), every block.
     kv2_scores<DT, D>(PW ? qs : dos, w, frag, x);
@@ -936,6 +958,7 @@ __device__ __forceinline__ void kv2_tile(const u16* Qh, const u16* dOh, int qbyt
     }
   }
   lds_write_barrier();
+  if constexpr (kLate) issue_kv2_tile<D>(Qh, dOh, qbytes, l2h, dlh, Nq, t + kStagesKV2 - 1, dst, w);
   if (live) {
     if constexpr (!PW) {
       // dS = P (dP - delta), rounded to 16 bits.
@@ -956,9 +979,11 @@ __device__ __forceinline__ void kv2_tile(const u16* Qh, const u16* dOh, int qbyt
           for (int i = 0; i < 4; ++i) pk[n][hh][i] = pack2<DT>(ds[8 * hh + 2 * i], ds[8 * hh + 2 * i + 1]);
       }
     }
-    // Gradient phase: dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave).
-    kv2_grads<DT, D>(PW ? dos : qs, w, pk, acc);
+    // Gradient phase: dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave;
+    // at D = 128 only after the last tile).
+    if (PW || !kLate || j + 1 == nt) kv2_grads<DT, D>(PW ? dos : qs, w, pk, acc);
   }
+  prev_live = live;
 }
 
 // The tile loop of one role over the 3-stage ring (stages passed as the
@@ -973,12 +998,17 @@ __device__ __forceinline__ void kv2_loop(const u16* Qh, const u16* dOh, int qbyt
   // Waits for the fragment and tiles t0 and t0 + 1 (the compiler-tracked
   // loads at D = 256 need no such wait).
   if constexpr (D != 256) settle_loads(frag);
+  u32x4 pk[kv2_rows<D>() / 32][2];  // the dS wave's dS of the previous tile (D = 128)
+  bool prev_live = false;
   for (int j = 0; j < nt; j += 3) {
-    kv2_tile<DT, D, CAUSAL, PW>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j, nt, s0, s2, xp, w, wk0, frag, acc, sl2);
+    kv2_tile<DT, D, CAUSAL, PW>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j, nt, s0, s2, xp, w, wk0, frag, acc, sl2, pk,
+                                prev_live);
     if (j + 1 < nt)
-      kv2_tile<DT, D, CAUSAL, PW>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 1, nt, s1, s0, xp, w, wk0, frag, acc, sl2);
+      kv2_tile<DT, D, CAUSAL, PW>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 1, nt, s1, s0, xp, w, wk0, frag, acc, sl2,
+                                  pk, prev_live);
     if (j + 2 < nt)
-      kv2_tile<DT, D, CAUSAL, PW>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 2, nt, s2, s1, xp, w, wk0, frag, acc, sl2);
+      kv2_tile<DT, D, CAUSAL, PW>(Qh, dOh, qbytes, l2h, dlh, nq, t0, j + 2, nt, s2, s1, xp, w, wk0, frag, acc, sl2,
+                                  pk, prev_live);
   }
   // The loads past the last tile complete before the workgroup's LDS is
   // released.
