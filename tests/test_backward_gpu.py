@@ -89,6 +89,21 @@ def test_backward_fp32_grid_sizes(D, causal, B, H, Nq, Nk):
     _compare(w, cpu, dout, grads, tag="fp32-grid")
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,Nq,Nk", [(1, 128, 520, 300), (1, 64, 300, 520)])
+def test_backward_16bit_dq_grid_sizes(dt, causal, B, H, Nq, Nk):
+    # At D = 128 the dQ kernel depends on the grid: with at least as many
+    # 256-row workgroups as CUs (B*H*ceil(Nq/256) = 384 here) the 256-row
+    # kernel that computes the row statistics itself, otherwise (128) the
+    # 128-row role-split kernel after the statistics kernel.  Ragged tails.
+    w = workloads.Workload(f"bwd16grid_{dt}_{'c' if causal else 'n'}_h{H}_{Nq}x{Nk}", B, H, Nq, Nk, 128, dt, causal,
+                           1300 + H + Nq)
+    log(f"case {w.name}")
+    cpu, dout, grads = _run(w)
+    _compare(w, cpu, dout, grads, tag="16bit-grid")
+
+
 @pytest.mark.parametrize("dt,D,causal,Nq,Nk", GRID)
 def test_backward_parity_grid(dt, D, causal, Nq, Nk):
     w = workloads.Workload(f"bwd_{dt}_d{D}_{'c' if causal else 'n'}_{Nq}x{Nk}", 2, 3, Nq, Nk, D, dt, causal,
