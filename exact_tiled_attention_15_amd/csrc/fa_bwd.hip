@@ -604,6 +604,25 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_rs(const u16* __restrict__ Qg, 
   }
 }
 
+// Key block of a dK/dV workgroup.  Ordered (causal, packed sequences):
+// ascending key blocks over all heads, so that under the causal mask the
+// heaviest workgroups start first.  Otherwise, when the grid divides by
+// the 8 XCDs (block ids go to them in turn), each XCD takes a contiguous
+// run of heads with all their key blocks, so that the workgroups reading
+// one head's Q/dO tiles at the same time share that XCD's L2.
+template <bool ORDERED>
+__device__ __forceinline__ void kv_block(int bid, int BH, int& bh, int& kt) {
+  const int n = (int)gridDim.x, nkt = n / BH;
+  if (!ORDERED && n % 8 == 0) {
+    const int v = (bid & 7) * (n >> 3) + (bid >> 3);
+    bh = v / nkt;
+    kt = v % nkt;
+  } else {
+    bh = bid % BH;
+    kt = bid / BH;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dK / dV kernel.
 // ---------------------------------------------------------------------------
@@ -722,10 +741,8 @@ __global__ __launch_bounds__(64 * kWavesKV, 3) void bwd_dkdv(const u16* __restri
   w.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   w.hf = w.lane >> 5;
   w.l32 = w.lane & 31;
-  // Key blocks in ascending order: under the causal mask the first keys are
-  // seen by the most queries, so the heaviest workgroups start first.
-  const int bid = blockIdx.x;
-  const int bh = bid % BH, kt = bid / BH;
+  int bh, kt;
+  kv_block<CAUSAL || VARLEN>(blockIdx.x, BH, bh, kt);
   const int kb0 = kt * BK;
   const int wk0 = kb0 + 32 * w.wave;
   const HeadRows hr = head_rows<VARLEN>(bh, Nq, Nk, D, cuq, cuk, H, tq, tk);
@@ -1038,10 +1055,8 @@ __global__ __launch_bounds__(64 * kWavesKV2, 1) void bwd_dkdv2(const u16* __rest
   w.l32 = w.lane & 31;
   const int grp = w.wave & 3;
   const bool pwave = w.wave < 4;
-  // Key blocks in ascending order: under the causal mask the first keys are
-  // seen by the most queries, so the heaviest workgroups start first.
-  const int bid = blockIdx.x;
-  const int bh = bid % BH, kt = bid / BH;
+  int bh, kt;
+  kv_block<CAUSAL || VARLEN>(blockIdx.x, BH, bh, kt);
   const int kb0 = kt * BK;
   const int wk0 = kb0 + 32 * grp;
   const HeadRows hr = head_rows<VARLEN>(bh, Nq, Nk, D, cuq, cuk, H, tq, tk);
