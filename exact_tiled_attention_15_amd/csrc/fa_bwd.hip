@@ -204,6 +204,23 @@ __device__ __forceinline__ void load_frag(u32x4 (&f)[D / 16], const u16* base, i
     f[kk] = __builtin_amdgcn_raw_buffer_load_b128(r, w.l32 * D * 2 + (16 * kk + 8 * w.hf) * 2, 0, 0);
 }
 
+// Query tile of a dQ workgroup: the forward's order (tile_of_block: the
+// heaviest causal tiles first) for causal and packed grids; otherwise, when
+// the grid divides by the 8 XCDs (block ids go to them in turn), each XCD
+// takes a contiguous run of heads with all their query tiles, so that the
+// workgroups streaming one head's K/V tiles at the same time share an L2.
+template <bool ORDERED>
+__device__ __forceinline__ void dq_block(int nqt, int BH, int& bh, int& qt) {
+  const int n = BH * nqt, bid = blockIdx.x;
+  if (!ORDERED && n % 8 == 0) {
+    const int v = (bid & 7) * (n >> 3) + (bid >> 3);
+    bh = v / nqt;
+    qt = v % nqt;
+  } else {
+    tile_of_block(nqt, BH, bh, qt);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dQ kernel.
 // ---------------------------------------------------------------------------
@@ -310,7 +327,7 @@ __global__ __launch_bounds__(64 * kWavesDQ, 1) void bwd_dq(const u16* __restrict
   w.hf = w.lane >> 5;
   w.l32 = w.lane & 31;
   int bh, qt;
-  tile_of_block(nqt, BH, bh, qt);
+  dq_block<CAUSAL || VARLEN>(nqt, BH, bh, qt);
   const int q0 = qt * BR;
   const HeadRows hr = head_rows<VARLEN>(bh, Nq, Nk, D, cuq, cuk, H, tq, tk);
   const int nq = hr.nq, nk = hr.nk;
